@@ -1,0 +1,270 @@
+"""Python binding of libmoe: argument marshalling only.
+
+Each function passes torch tensors' device pointers and the current HIP stream
+to the C entry point of the same name (include/moe.h) and raises MoEError on a
+non-OK status.  Output tensors and workspaces are allocated with torch, which
+serves here only as the device-memory and stream provider; every step of the
+layer runs in libmoe's HIP kernels.  There is no fallback: if libmoe.so is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "MoEError", "lib", "library_path", "declared_symbols",
+    "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+    "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM",
+    "moe_route", "moe_dispatch_layout", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
+    "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
+    "moe_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN, MOE_OP_EXPERT_GEMM = range(3)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {moe_status_str(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmoe.so")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "moe_route": [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P],
+    "moe_dispatch_layout": [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _I, _P, _P],
+    "moe_quantize_fp8": [_P, _I, ctypes.c_int64, _I, _P, _P, _P],
+    "moe_grouped_ffn": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
+    "moe_expert_gate_up": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
+    "moe_expert_down": [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _SZ, _P],
+    "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
+    "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
+    "moe_status_str": [_I],
+    "moe_version": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(python -m combine_grouped_gemm_amd.build)")
+        L = ctypes.CDLL(path)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = _SZ if name == "moe_workspace_bytes" else (
+                ctypes.c_char_p if name in ("moe_status_str", "moe_version") else _I)
+        _LIB = L
+    return _LIB
+
+
+def declared_symbols() -> list:
+    """Names of the functions include/moe.h declares."""
+    text = open(_HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+def moe_workspace_bytes(op: int, N: int, H: int, I: int, E: int, k: int, a_dt: int) -> int:
+    return int(lib().moe_workspace_bytes(op, N, H, I, E, k, a_dt))
+
+
+# ------------------------------------------------------------------------------------------
+# marshalling helpers
+# ------------------------------------------------------------------------------------------
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_FP8_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(dt: int) -> torch.dtype:
+    return {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.uint8}[dt]
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------
+
+def moe_route(z: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None, n_group: int = 0,
+              topk_group: int = 0, topk_idx: Optional[torch.Tensor] = None,
+              topk_gate: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    N, E = z.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((N, k), dtype=torch.int32, device=z.device)
+    if topk_gate is None:
+        topk_gate = torch.empty((N, k), dtype=torch.float32, device=z.device)
+    _check("moe_route", lib().moe_route(_ptr(z), N, E, k, _ptr(bias), n_group, topk_group,
+                                        _ptr(topk_idx), _ptr(topk_gate), _stream(z)))
+    return topk_idx, topk_gate
+
+
+def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, out=None, ws: Optional[torch.Tensor] = None):
+    """Returns (n_e [E], offsets [E+1], send_pos [N*k], src_slot [N*k]) int32."""
+    N, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(N * k, dtype=torch.int32, device=dev),
+               torch.empty(N * k, dtype=torch.int32, device=dev))
+    n_e, offsets, send_pos, src_slot = out
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_DISPATCH_LAYOUT, N, 0, 0, E, k, 0), dev)
+    _check("moe_dispatch_layout", lib().moe_dispatch_layout(
+        _ptr(topk_idx), N, k, E, _ptr(n_e), _ptr(offsets), _ptr(send_pos), _ptr(src_slot),
+        _ptr(ws), ws.numel(), _stream(topk_idx)))
+    return n_e, offsets, send_pos, src_slot
+
+
+def moe_permute(x: torch.Tensor, send_pos: torch.Tensor, k: int, perm_dt: Optional[int] = None,
+                x_perm: Optional[torch.Tensor] = None, perm_scale: Optional[torch.Tensor] = None):
+    """x_perm (and the fp8 block scales when perm_dt is MOE_FP8_E4M3)."""
+    N, H = x.shape
+    pdt = _dt(x) if perm_dt is None else perm_dt
+    if x_perm is None:
+        x_perm = torch.empty((N * k, H), dtype=_torch_dt(pdt), device=x.device)
+    if pdt == MOE_FP8_E4M3 and perm_scale is None:
+        perm_scale = torch.empty((N * k, H // 128), dtype=torch.float32, device=x.device)
+    _check("moe_permute", lib().moe_permute(_ptr(x), _dt(x), N, H, k, _ptr(send_pos), _ptr(x_perm),
+                                            pdt, _ptr(perm_scale), _stream(x)))
+    return (x_perm, perm_scale) if pdt == MOE_FP8_E4M3 else x_perm
+
+
+def moe_quantize_fp8(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                     scale: Optional[torch.Tensor] = None):
+    """(codes uint8 of x's shape, fp32 scales [..., cols / 128]) for the rows of x."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(tuple(x.shape[:-1]) + (cols // 128,), dtype=torch.float32, device=x.device)
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(_ptr(x), _dt(x), rows, cols, _ptr(q),
+                                                      _ptr(scale), _stream(x)))
+    return q, scale
+
+
+def moe_expert_gate_up(a: torch.Tensor, offsets: torch.Tensor, w13: torch.Tensor,
+                       a_scale: Optional[torch.Tensor] = None, w13_scale: Optional[torch.Tensor] = None,
+                       h: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    rows, H = a.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    adt = _dt(a)
+    if h is None:
+        h = torch.empty((rows, I), dtype=torch.float32 if adt == MOE_F32 else torch.bfloat16,
+                        device=a.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, adt), a.device)
+    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+        _ptr(a), _ptr(a_scale), adt, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(w13_scale),
+        _ptr(h), _ptr(ws), ws.numel(), _stream(a)))
+    return h
+
+
+def moe_expert_down(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor,
+                    w2_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None):
+    rows, I = h.shape
+    E, H, _ = w2.shape
+    hdt = _dt(h)
+    if out is None:
+        out = torch.empty((rows, H), dtype=h.dtype, device=h.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, hdt), h.device)
+    _check("moe_expert_down", lib().moe_expert_down(
+        _ptr(h), hdt, _ptr(offsets), E, rows, I, H, _ptr(w2), _dt(w2), _ptr(w2_scale), _ptr(out),
+        _dt(out), _ptr(ws), ws.numel(), _stream(h)))
+    return out
+
+
+def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                    a_scale: Optional[torch.Tensor] = None, w13_scale: Optional[torch.Tensor] = None,
+                    w2_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None):
+    rows, H = a.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    adt = _dt(a)
+    odt = MOE_F32 if adt == MOE_F32 else MOE_BF16
+    if out is None:
+        out = torch.empty((rows, H), dtype=_torch_dt(odt), device=a.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, adt), a.device)
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(
+        _ptr(a), _ptr(a_scale), adt, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(w13_scale),
+        _ptr(w2), _ptr(w2_scale), _ptr(out), odt, _ptr(ws), ws.numel(), _stream(a)))
+    return out
+
+
+def moe_combine(expert_out: torch.Tensor, send_pos: torch.Tensor, topk_gate: torch.Tensor,
+                shared_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                y_dtype: Optional[torch.dtype] = None):
+    N, k = topk_gate.shape
+    H = expert_out.shape[1]
+    if y is None:
+        y = torch.empty((N, H), dtype=y_dtype or expert_out.dtype, device=expert_out.device)
+    _check("moe_combine", lib().moe_combine(
+        _ptr(expert_out), _dt(expert_out), N, H, k, _ptr(send_pos), _ptr(topk_gate),
+        _ptr(shared_out), _ptr(y), _dt(y), _stream(expert_out)))
+    return y

@@ -1,0 +1,111 @@
+// Combine (unpermute + gate-weighted sum back to token order):
+//   y_t = sum_{j<k} g_{t,j} * expert_out[send_pos[t*k+j]]  (+ shared_out_t)
+// ("EP / DeepEP explanation" page, sections 2 and 3; "DeepEP" page, section 7: the sum is
+// kept in a wider type than the payload).
+//
+// One workgroup per token; each lane owns 8 consecutive columns, gathers the k expert
+// rows with 16-byte loads (all k loads issued before the sum), accumulates in fp32 in the
+// order j = 0..k-1 then the shared row, rounds once and writes 16 bytes (bf16) or 32 bytes
+// (fp32).  Gates and send positions are uniform across the workgroup.
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+constexpr int kCombThreads = 256;
+
+template <bool kEoF32>
+__device__ __forceinline__ void load8(const void* base, size_t row, int H, int c, float (&v)[8]) {
+  if (kEoF32) {
+    const float4* p = reinterpret_cast<const float4*>(base) + (row * H) / 4 + 2 * c;
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 a = reinterpret_cast<const uint4*>(base)[(row * H) / 8 + c];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
+      v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+}
+
+template <bool kEoF32, bool kYF32>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    const void* __restrict__ eo, int H, int k, const int32_t* __restrict__ send_pos,
+    const float* __restrict__ gate, const void* __restrict__ shared, void* __restrict__ y) {
+  const int t = blockIdx.x;
+  const int32_t* sp = send_pos + static_cast<size_t>(t) * k;
+  const float* g = gate + static_cast<size_t>(t) * k;
+  const int groups8 = H / 8;
+  for (int c = threadIdx.x; c < groups8; c += kCombThreads) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      float v[4][8];
+      int r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r[u] = sp[j + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (r[u] >= 0) {
+          load8<kEoF32>(eo, static_cast<size_t>(r[u]), H, c, v[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float gu = g[j + u];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gu, v[u][i], acc[i]);
+      }
+    }
+    for (; j < k; ++j) {
+      const int r = sp[j];
+      if (r < 0) continue;
+      float v[8];
+      load8<kEoF32>(eo, static_cast<size_t>(r), H, c, v);
+      const float gj = g[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
+    }
+    if (shared != nullptr) {
+      float v[8];
+      load8<kEoF32>(shared, static_cast<size_t>(t), H, c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (kYF32) {
+      float4* p = reinterpret_cast<float4*>(y) + (static_cast<size_t>(t) * H) / 4 + 2 * c;
+      p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      reinterpret_cast<uint4*>(y)[(static_cast<size_t>(t) * H) / 8 + c] = o;
+    }
+  }
+}
+
+hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
+                          const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s) {
+  const dim3 grid(N), block(kCombThreads);
+  if (eo_f32 && y_f32)
+    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+  else if (eo_f32)
+    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+  else if (y_f32)
+    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+  else
+    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,225 @@
+// Host side of libmoe: argument validation, workspace sizing and kernel launches behind
+// the C ABI declared in include/moe.h.  Every check runs before anything is enqueued, and
+// no HIP call is made on an error path.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "moe.h"
+#include "moe_launch.h"
+
+namespace {
+
+constexpr long long kMaxRowsPerLaunch = (1ll << 24);  // one 256-lane workgroup per row
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_bytes(int dt) {
+  switch (dt) {
+    case MOE_F32: return 4;
+    case MOE_BF16: return 2;
+    case MOE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+size_t layout_ws(int N, int k, int E) {
+  const long long nk = static_cast<long long>(N) * k;
+  if (nk <= 0 || E <= 0) return 0;
+  return round256(static_cast<size_t>(moe::layout_num_chunks(nk)) * E * sizeof(int32_t));
+}
+
+size_t h_bytes(int rows, int I, int a_dt) {
+  return round256(static_cast<size_t>(rows) * I * (a_dt == MOE_F32 ? 4 : 2));
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Checks shared by the two expert GEMMs.
+moe_status check_gemm(const int32_t* offsets, int E, int rows, int H, int I, void* ws,
+                      size_t ws_bytes) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || rows < 0 || H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows > 0 && (ws == nullptr || ws_bytes < moe::gemm_schedule_bytes(rows, E))) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "0.1.0"; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_bytes(int op, int N, int H, int I, int E, int k, int a_dt) {
+  if (N < 0 || E < 0) return 0;
+  switch (op) {
+    case MOE_OP_DISPATCH_LAYOUT:
+      if (k < 1 || E < 1) return 0;
+      return layout_ws(N, k, E);
+    case MOE_OP_EXPERT_GEMM:
+      if (E < 1 || N == 0) return 0;
+      return moe::gemm_schedule_bytes(N, E);
+    case MOE_OP_GROUPED_FFN:
+      if (E < 1 || N == 0 || I <= 0 || H <= 0) return 0;
+      return moe::gemm_schedule_bytes(N, E) + h_bytes(N, I, a_dt);
+    default:
+      return 0;
+  }
+}
+
+moe_status moe_route(const float* z, int N, int E, int k, const float* bias, int n_group,
+                     int topk_group, int32_t* topk_idx, float* topk_gate, hipStream_t stream) {
+  if (N < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (n_group < 0 || topk_group < 0) return MOE_ERR_INVALID_ARG;
+  if (n_group > 0) {
+    if (n_group > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
+    if (E % n_group != 0 || topk_group < 1 || topk_group > n_group) return MOE_ERR_INVALID_ARG;
+    if (static_cast<long long>(topk_group) * (E / n_group) < k) return MOE_ERR_INVALID_ARG;
+  } else if (topk_group != 0) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (z == nullptr || topk_idx == nullptr || topk_gate == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route(z, N, E, k, bias, n_group, topk_group, topk_idx, topk_gate, stream));
+}
+
+moe_status moe_dispatch_layout(const int32_t* topk_idx, int N, int k, int E, int32_t* n_e,
+                               int32_t* offsets, int32_t* send_pos, int32_t* src_slot, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  if (N < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (topk_idx == nullptr || n_e == nullptr || offsets == nullptr || send_pos == nullptr ||
+      src_slot == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < layout_ws(N, k, E)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_dispatch_layout(topk_idx, N * k, E, n_e, offsets, send_pos, src_slot,
+                                                reinterpret_cast<int32_t*>(ws), stream));
+}
+
+moe_status moe_permute(const void* x, moe_dtype x_dt, int N, int H, int k,
+                       const int32_t* send_pos, void* x_perm, moe_dtype perm_dt, float* perm_scale,
+                       hipStream_t stream) {
+  if (N < 0 || H <= 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (perm_dt != x_dt && perm_dt != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (k > MOE_MAX_TOPK || N >= kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  const size_t row_bytes = static_cast<size_t>(H) * dtype_bytes(x_dt);
+  if (row_bytes % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (perm_dt == MOE_FP8_E4M3 && H % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (x == nullptr || send_pos == nullptr || x_perm == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  if (perm_dt == MOE_FP8_E4M3) {
+    if (perm_scale == nullptr) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_permute_fp8(x, x_dt == MOE_F32, N, H, k, send_pos,
+                                              reinterpret_cast<uint8_t*>(x_perm), perm_scale, stream));
+  }
+  return hip_status(moe::launch_permute_copy(x, row_bytes, N, k, send_pos, x_perm, stream));
+}
+
+moe_status moe_quantize_fp8(const void* x, moe_dtype x_dt, int64_t rows, int cols, uint8_t* q,
+                            float* scale, hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (cols % 128 != 0 || rows >= kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || q == nullptr || scale == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_permute_fp8(x, x_dt == MOE_F32, rows, cols, 1, nullptr, q, scale, stream));
+}
+
+moe_status moe_expert_gate_up(const void* a, const float* a_scale, moe_dtype a_dt,
+                              const int32_t* offsets, int E, int rows, int H, int I,
+                              const void* w13, const float* w13_scale, void* h, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (a_dt != MOE_F32 && a_dt != MOE_BF16 && a_dt != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  const moe_status st = check_gemm(offsets, E, rows, H, I, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (a == nullptr || w13 == nullptr || h == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w13)) return MOE_ERR_INVALID_ARG;
+  if (a_dt == MOE_FP8_E4M3 && (a_scale == nullptr || w13_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  const int ct = a_dt == MOE_F32 ? 0 : (a_dt == MOE_BF16 ? 1 : 2);
+  return hip_status(moe::launch_grouped_gemm(ct, false, 0, a, a_scale, w13, w13_scale, h,
+                                             a_dt == MOE_F32, offsets, E, rows, H, I, I,
+                                             2ll * I, ws, stream));
+}
+
+moe_status moe_expert_down(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
+                           int I, int H, const void* w2, moe_dtype w2_dt, const float* w2_scale,
+                           void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (h_dt != MOE_F32 && h_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (h_dt == MOE_F32 && (w2_dt != MOE_F32 || out_dt != MOE_F32)) return MOE_ERR_UNSUPPORTED;
+  if (h_dt == MOE_BF16 && ((w2_dt != MOE_BF16 && w2_dt != MOE_FP8_E4M3) || out_dt != MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
+  const moe_status st = check_gemm(offsets, E, rows, H, I, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (h == nullptr || w2 == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w2)) return MOE_ERR_INVALID_ARG;
+  if (w2_dt == MOE_FP8_E4M3 && w2_scale == nullptr) return MOE_ERR_INVALID_ARG;
+  const int ct = h_dt == MOE_F32 ? 0 : 1;
+  return hip_status(moe::launch_grouped_gemm(ct, w2_dt == MOE_FP8_E4M3, 1, h, nullptr, w2, w2_scale,
+                                             out, out_dt == MOE_F32, offsets, E, rows, I, I, H,
+                                             static_cast<long long>(H), ws, stream));
+}
+
+moe_status moe_grouped_ffn(const void* a, const float* a_scale, moe_dtype a_dt,
+                           const int32_t* offsets, int E, int rows, int H, int I, const void* w13,
+                           const float* w13_scale, const void* w2, const float* w2_scale, void* out,
+                           moe_dtype out_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (a_dt != MOE_F32 && a_dt != MOE_BF16 && a_dt != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (out_dt != (a_dt == MOE_F32 ? MOE_F32 : MOE_BF16)) return MOE_ERR_UNSUPPORTED;
+  const moe_status st = check_gemm(offsets, E, rows, H, I, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (ws_bytes < moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt)) return MOE_ERR_WORKSPACE;
+  if (a == nullptr || w13 == nullptr || w2 == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  const size_t sched = moe::gemm_schedule_bytes(rows, E);
+  void* hbuf = static_cast<uint8_t*>(ws) + sched;
+  const moe_dtype h_dt = a_dt == MOE_F32 ? MOE_F32 : MOE_BF16;
+  moe_status s = moe_expert_gate_up(a, a_scale, a_dt, offsets, E, rows, H, I, w13, w13_scale, hbuf,
+                                    ws, sched, stream);
+  if (s != MOE_OK) return s;
+  return moe_expert_down(hbuf, h_dt, offsets, E, rows, I, H, w2, a_dt, w2_scale, out, out_dt, ws,
+                         sched, stream);
+}
+
+moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, int k,
+                       const int32_t* send_pos, const float* topk_gate, const void* shared_out,
+                       void* y, moe_dtype y_dt, hipStream_t stream) {
+  if (N < 0 || H <= 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if ((eo_dt != MOE_F32 && eo_dt != MOE_BF16) || (y_dt != MOE_F32 && y_dt != MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
+  if (k > MOE_MAX_TOPK || N >= kMaxRowsPerLaunch || H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (expert_out == nullptr || send_pos == nullptr || topk_gate == nullptr || y == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(expert_out) || !aligned16(y) || (shared_out != nullptr && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(expert_out, eo_dt == MOE_F32, N, H, k, send_pos, topk_gate,
+                                        shared_out, y, y_dt == MOE_F32, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device-side helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------------------------
+// scalar conversions
+// ------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// OCP e4m3fn encode of a finite fp32 value: round to nearest even, saturate to +-448.
+// Normal range (|v| >= 2^-6): keep the 3 leading fraction bits of the fp32 significand
+// and round on the 20 dropped bits; a carry propagates into the exponent field.
+// Subnormal range: the grid is 2^-9, so round |v| * 2^9 to an integer (0..8; 8 is the
+// code of 2^-6).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {  // 2^-6
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  } else {
+    const uint32_t au = u & 0x7FFFFFFFu;
+    const uint32_t exp = (au >> 23) - 127u + 7u;  // e4m3 exponent field, 1..15
+    const uint32_t keep = (au >> 20) & 7u;
+    const uint32_t rem = au & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
+    code = (exp << 3) + keep + up;
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return code | sign;
+}
+
+// e4m3fn code -> bf16 bits, exact (3 mantissa bits and exponents 2^-9..2^8 fit bf16).
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 0xFu;
+  const uint32_t m = c & 7u;
+  if (e != 0) return s | ((e + 120u) << 7) | (m << 4);
+  // subnormal m * 2^-9: the fp32 value is exact and has at most 3 significant bits
+  return s | (__float_as_uint(static_cast<float>(m) * 0.001953125f) >> 16);
+}
+
+// four e4m3 codes (one per byte) -> four bf16 packed in two dwords
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
+  uint2 r;
+  r.x = e4m3_to_bf16_bits(w & 0xFFu) | (e4m3_to_bf16_bits((w >> 8) & 0xFFu) << 16);
+  r.y = e4m3_to_bf16_bits((w >> 16) & 0xFFu) | (e4m3_to_bf16_bits(w >> 24) << 16);
+  return r;
+}
+
+// ------------------------------------------------------------------------------------
+// wave-level reductions (all lanes receive the result)
+// ------------------------------------------------------------------------------------
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// fp32 -> uint32 whose unsigned order is the float order; +0 and -0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+}  // namespace moe

@@ -1,0 +1,35 @@
+// Internal launchers (one per kernel family); host code in moe_api.cpp validates the
+// arguments before calling any of these.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const float* z, int N, int E, int k, const float* bias, int n_group,
+                        int topk_group, int32_t* topk_idx, float* topk_gate, hipStream_t s);
+
+int layout_chunk_slots(long long nk);
+int layout_num_chunks(long long nk);
+hipError_t launch_dispatch_layout(const int32_t* topk_idx, int nk, int E, int32_t* n_e,
+                                  int32_t* offsets, int32_t* send_pos, int32_t* src_slot,
+                                  int32_t* counts, hipStream_t s);
+
+hipError_t launch_permute_copy(const void* x, size_t row_bytes, int N, int k,
+                               const int32_t* send_pos, void* out, hipStream_t s);
+hipError_t launch_permute_fp8(const void* x, bool f32_in, long long rows, int H, int k,
+                              const int32_t* send_pos, uint8_t* q, float* scale, hipStream_t s);
+
+hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
+                          const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s);
+
+size_t gemm_tile_cap(int rows, int E);
+size_t gemm_schedule_bytes(int rows, int E);
+hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,
+                               const void* b, const float* b_scale, void* out, bool out_f32,
+                               const int32_t* offsets, int E, int rows, int K, int I, int n_out,
+                               long long b_rows, void* sched, hipStream_t s);
+
+}  // namespace moe

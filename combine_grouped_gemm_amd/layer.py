@@ -1,0 +1,121 @@
+"""One GPU's share of a sparse MoE layer as a sequence of libmoe calls on one stream.
+
+    route -> dispatch layout -> permute -> grouped SwiGLU FFN (+ shared expert) -> combine
+
+("MoE part 4" page, section 4 and 4.2; "EP / DeepEP explanation" page, sections 2-3.)
+All buffers are allocated once, at construction, so a forward pass enqueues
+only kernels: no allocation, no host synchronisation, no device-to-host copy.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN,
+               moe_combine, moe_dispatch_layout, moe_grouped_ffn, moe_permute, moe_quantize_fp8,
+               moe_route, moe_workspace_bytes)
+
+
+class MoELayer:
+    """Pre-planned MoE layer for fixed sizes.
+
+    ``dtype``: 'f32' (fp32 everywhere), 'bf16' (bf16 storage, fp32 accumulation) or
+    'fp8' (bf16 hidden states; e4m3 payload and weights with per-128-column fp32
+    scales; bf16 h, expert outputs and y).  Weights come in the storage dtype
+    (bf16 for 'fp8'); the fp8 layer quantizes them once here, with the library's
+    own row quantizer.
+    """
+
+    def __init__(self, N: int, H: int, E: int, k: int, I: int, dtype: str, w13: torch.Tensor,
+                 w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
+                 shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
+                 bias: Optional[torch.Tensor] = None):
+        self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
+        self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
+        dev = w13.device
+        self.device = dev
+        self.fp8 = dtype == "fp8"
+        act = torch.float32 if dtype == "f32" else torch.bfloat16
+        self.act_dtype = act
+        rows = N * k
+        if self.fp8:
+            self.w13, self.w13_scale = moe_quantize_fp8(w13)
+            self.w2, self.w2_scale = moe_quantize_fp8(w2)
+            if shared_w13 is not None:
+                self.sw13, self.sw13_scale = moe_quantize_fp8(shared_w13)
+                self.sw2, self.sw2_scale = moe_quantize_fp8(shared_w2)
+        else:
+            self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, None, None
+            self.sw13, self.sw2 = shared_w13, shared_w2
+            self.sw13_scale = self.sw2_scale = None
+        self.shared = shared_w13 is not None
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.topk_idx = torch.empty((N, k), **i32)
+        self.topk_gate = torch.empty((N, k), dtype=torch.float32, device=dev)
+        self.layout = (torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(rows, **i32),
+                       torch.empty(rows, **i32))
+        self.layout_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_DISPATCH_LAYOUT, N, 0, 0, E, k, 0), 256),
+                                     dtype=torch.uint8, device=dev)
+        a_dt = MOE_FP8_E4M3 if self.fp8 else (MOE_F32 if dtype == "f32" else MOE_BF16)
+        self.a_dt = a_dt
+        self.x_perm = torch.empty((rows, H), dtype=torch.uint8 if self.fp8 else act, device=dev)
+        self.x_perm_scale = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+        self.ffn_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt), 256),
+                                  dtype=torch.uint8, device=dev)
+        self.expert_out = torch.empty((rows, H), dtype=act, device=dev)
+        if self.shared:
+            self.shared_offsets = torch.tensor([0, N], **i32)
+            self.x_q = torch.empty((N, H), dtype=torch.uint8, device=dev) if self.fp8 else None
+            self.x_q_scale = torch.empty((N, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+            self.shared_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, N, H, I, 1, 1, a_dt), 256),
+                                         dtype=torch.uint8, device=dev)
+            self.shared_out = torch.empty((N, H), dtype=act, device=dev)
+        self.y = torch.empty((N, H), dtype=act, device=dev)
+
+    @property
+    def h(self) -> torch.Tensor:
+        """The intermediate h of the last routed FFN (a view into the workspace)."""
+        from . import moe_workspace_bytes as wsb, MOE_OP_EXPERT_GEMM
+        off = wsb(MOE_OP_EXPERT_GEMM, self.N * self.k, self.H, self.I, self.E, 1, self.a_dt)
+        esz = 4 if self.dtype == "f32" else 2
+        n = self.N * self.k * self.I * esz
+        return self.ffn_ws[off:off + n].view(torch.float32 if esz == 4 else torch.bfloat16).view(
+            self.N * self.k, self.I)
+
+    def route(self, z: torch.Tensor):
+        return moe_route(z, self.k, self.bias, self.n_group, self.topk_group, self.topk_idx, self.topk_gate)
+
+    def dispatch(self):
+        return moe_dispatch_layout(self.topk_idx, self.E, self.layout, self.layout_ws)
+
+    def permute(self, x: torch.Tensor):
+        send_pos = self.layout[2]
+        if self.fp8:
+            return moe_permute(x, send_pos, self.k, MOE_FP8_E4M3, self.x_perm, self.x_perm_scale)
+        return moe_permute(x, send_pos, self.k, None, self.x_perm)
+
+    def experts(self):
+        return moe_grouped_ffn(self.x_perm, self.layout[1], self.w13, self.w2, self.x_perm_scale,
+                               self.w13_scale, self.w2_scale, self.expert_out, self.ffn_ws)
+
+    def shared_expert(self, x: torch.Tensor):
+        a, a_scale = x, None
+        if self.fp8:
+            a, a_scale = moe_quantize_fp8(x, self.x_q, self.x_q_scale)
+        return moe_grouped_ffn(a, self.shared_offsets, self.sw13, self.sw2, a_scale, self.sw13_scale,
+                               self.sw2_scale, self.shared_out, self.shared_ws)
+
+    def combine(self):
+        return moe_combine(self.expert_out, self.layout[2], self.topk_gate,
+                           self.shared_out if self.shared else None, self.y)
+
+    def forward(self, x: torch.Tensor, z: torch.Tensor) -> torch.Tensor:
+        self.route(z)
+        self.dispatch()
+        self.permute(x)
+        self.experts()
+        if self.shared:
+            self.shared_expert(x)
+        self.combine()
+        return self.y

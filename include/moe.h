@@ -1,0 +1,242 @@
+/*
+ * moe.h -- C ABI of libmoe: one GPU's share of a sparse Mixture-of-Experts layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, in the notation of the "EP / DeepEP explanation" page (section 2): N tokens
+ * with hidden states x in R^{N x H}, E routed experts, router logits z in R^{N x E}, for
+ * each token t an index set I_t of k experts with gates g_{t,e}, and
+ *
+ *     y_t = sum_{e in I_t} g_{t,e} * Expert_e(x_t),     n_e = |{(t, e) : e in I_t}|.
+ *
+ * The calls run in the order the pages give for a MoE layer ("MoE part 4: DeepEP and
+ * GroupedGEMM", section 4: permute by expert -> grouped GEMM over tokens-per-expert ->
+ * unpermute and weighted sum; section 4.2: router top-k with correction bias and grouped
+ * top-k first):
+ *
+ *     moe_route -> moe_dispatch_layout -> moe_permute -> moe_grouped_ffn -> moe_combine
+ *
+ * On one GPU the dispatch and combine all-to-alls of expert parallelism become the
+ * on-device permute and unpermute.
+ *
+ * Conventions (all entry points):
+ *   - Every array argument is a DEVICE pointer to row-major, contiguous memory.  Row
+ *     bases must be 16-byte aligned (every row length below is a multiple of 16 bytes).
+ *   - The caller owns every buffer, workspaces included.  The library never allocates
+ *     or frees device memory and keeps no pointer after a call returns; it holds no
+ *     state and may be called from several host threads.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).  There is no
+ *     host synchronisation and no device-to-host copy inside any call; stream order is
+ *     the completion signal.  Buffers may be reused once later work on the stream runs.
+ *   - Arguments are validated on the host before anything is enqueued; a failed check
+ *     returns an error status and enqueues nothing.  A launch failure reported by the
+ *     HIP runtime returns MOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - N == 0 (or rows == 0) is valid and enqueues nothing.
+ *   - Non-finite logits or activations give unspecified (but memory-safe) results.
+ *   - Index arrays are int32 (N * k < 2^31); byte offsets inside kernels are 64-bit.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a size, pointer or combination of arguments is invalid   */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request outside what this library implements       */
+  MOE_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required       */
+  MOE_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing         */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2 /* OCP e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits, max 448 */
+} moe_dtype;
+
+/* Workspace query ids for moe_workspace_bytes(). */
+typedef enum {
+  MOE_OP_DISPATCH_LAYOUT = 0,
+  MOE_OP_GROUPED_FFN = 1, /* includes the [rows, I] intermediate h                      */
+  MOE_OP_EXPERT_GEMM = 2  /* moe_expert_gate_up / moe_expert_down: tile schedule only   */
+} moe_op;
+
+/* Limits of this implementation. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_GROUPS 64
+#define MOE_FP8_BLOCK 128 /* columns per fp32 scale of an fp8 row */
+
+/*
+ * moe_route -- router top-k with optional bias and group limit, renormalised gates.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (logits z, index set I_t, gates
+ * g_{t,e}); "MoE part 4" page, section 4.2 (top-k with a per-expert correction bias,
+ * grouped top-k, renormalisation); "Wide EP" page, section "Group-limited routing" (pick
+ * groups first, then the top-k experts inside the allowed groups).
+ *
+ *   z          [N, E] fp32 router logits.
+ *   bias       [E] fp32 added to every token's logits before selection and gating, or NULL.
+ *   n_group, topk_group
+ *              0, 0 = no group limit.  Otherwise the experts form n_group contiguous
+ *              groups of E / n_group; a group's score is its largest biased logit; each
+ *              token keeps the topk_group best groups (equal scores: lower group id).
+ *   topk_idx   [N, k] int32 out: slot j is the j-th largest allowed biased logit; equal
+ *              logits go to the lower expert index; +0 and -0 compare equal.
+ *   topk_gate  [N, k] fp32 out: g_{t,j} = exp(z'_j - z'_0) / sum_j' exp(z'_j' - z'_0),
+ *              z' the biased logits of the selected experts (softmax over all experts,
+ *              restricted to I_t and renormalised).
+ * Requires 1 <= k <= min(E, 32), E <= 1024; with groups: n_group <= 64, E % n_group == 0,
+ * 1 <= topk_group <= n_group and k <= topk_group * E / n_group.
+ */
+moe_status moe_route(const float* z, int N, int E, int k, const float* bias, int n_group,
+                     int topk_group, int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
+/*
+ * moe_dispatch_layout -- expert histogram, offsets and the three index maps.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (n_e), section 3 (bucket tokens
+ * by target expert, metadata built on the GPU without host sync) and section 6 (token ->
+ * send position, send position -> expert-local position, return position -> token).
+ * Slot s = t * k + j names the pair (token t, its j-th expert).
+ *
+ *   topk_idx   [N * k] int32 expert ids in [0, E).  An id outside [0, E) is not counted
+ *              and its send_pos is set to -1.
+ *   n_e        [E] int32 out: rows per expert.
+ *   offsets    [E + 1] int32 out: exclusive prefix sum of n_e (offsets[E] = valid pairs).
+ *   send_pos   [N * k] int32 out: row of slot s in the expert-ordered buffer.  Rows of one
+ *              expert are ordered by ascending slot (hence ascending token).
+ *              Expert-local position = send_pos[s] - offsets[topk_idx[s]].
+ *   src_slot   [N * k] int32 out: src_slot[send_pos[s]] = s (the return map); entries
+ *              at rows >= offsets[E] are left untouched.
+ *   ws         workspace of at least moe_workspace_bytes(MOE_OP_DISPATCH_LAYOUT, N, 0,
+ *              0, E, k, 0) bytes.
+ * Deterministic: no atomic operation's order reaches an output.
+ */
+moe_status moe_dispatch_layout(const int32_t* topk_idx, int N, int k, int E, int32_t* n_e,
+                               int32_t* offsets, int32_t* send_pos, int32_t* src_slot, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_permute -- x_perm[send_pos[t * k + j]] = x[t] (the local stand-in of dispatch).
+ *
+ * Definition: "EP / DeepEP explanation" page, section 3 (tokens bucketed by expert into a
+ * layout the grouped GEMM can use) and section 6 (an fp8 payload's scales share the
+ * token's index); "MoE part 4" page, section 4 (permute by expert).
+ *
+ *   x          [N, H] of x_dt (MOE_F32 or MOE_BF16).
+ *   send_pos   [N * k] int32 from moe_dispatch_layout; slots with send_pos < 0 are skipped.
+ *   x_perm     [N * k, H] of perm_dt out.  perm_dt == x_dt copies rows.  perm_dt ==
+ *              MOE_FP8_E4M3 (x_dt must be MOE_BF16 or MOE_F32) quantizes each token once
+ *              per 128-column block: s = fp32(amax / 448) (1 when amax = 0),
+ *              q = e4m3(fp32(x / s)) with round-to-nearest-even and saturation at 448,
+ *              and writes k copies.
+ *   perm_scale [N * k, H / 128] fp32 out, the block scales of each row (fp8 only, else
+ *              ignored and may be NULL).
+ * Requires H * sizeof(x_dt) % 16 == 0; H % 128 == 0 for fp8.
+ */
+moe_status moe_permute(const void* x, moe_dtype x_dt, int N, int H, int k,
+                       const int32_t* send_pos, void* x_perm, moe_dtype perm_dt, float* perm_scale,
+                       hipStream_t stream);
+
+/*
+ * moe_quantize_fp8 -- the per-(row, 128-column block) e4m3 quantization of moe_permute
+ * applied to every row of a matrix in place order (used to quantize expert weights).
+ *
+ *   x [rows, cols] of x_dt (MOE_BF16 or MOE_F32) -> q [rows, cols] uint8 codes and
+ *   scale [rows, cols / 128] fp32.  Requires cols % 128 == 0.
+ */
+moe_status moe_quantize_fp8(const void* x, moe_dtype x_dt, int64_t rows, int cols, uint8_t* q,
+                            float* scale, hipStream_t stream);
+
+/*
+ * moe_grouped_ffn -- every expert's SwiGLU FFN on its rows, as grouped GEMMs.
+ *
+ * Definition: "MoE part 4" page, section 2 (one launch for many expert GEMMs with
+ * differing row counts; it does not change the layer's mathematics) and section 4.1 (an
+ * expert is FC1 -> activation -> FC2).  For each expert e and its rows
+ * [offsets[e], offsets[e+1]) of the expert-ordered buffer a:
+ *
+ *     h   = silu(a W_gate,e^T) * (a W_up,e^T),   silu(v) = v / (1 + exp(-v))
+ *     out = h W_down,e^T
+ *
+ *   a         [rows, H] of a_dt: MOE_F32, MOE_BF16 or MOE_FP8_E4M3 (then a_scale
+ *             [rows, H / 128] fp32 holds its block scales).
+ *   offsets   [E + 1] int32 device array (from moe_dispatch_layout).  Rows at or beyond
+ *             offsets[E] are not computed.  A shared expert is one more call with E = 1
+ *             and offsets = {0, N} on x.
+ *   w13       [E, 2I, H]: rows 0..I-1 of each expert are W_gate, rows I..2I-1 W_up.
+ *   w2        [E, H, I]: W_down.
+ *             Weights are of a_dt's kind: MOE_F32 with f32 activations, MOE_BF16 with
+ *             bf16, MOE_FP8_E4M3 with fp8 (w13_scale [E, 2I, H / 128] and w2_scale
+ *             [E, H, I / 128] fp32 block scales, one per output row and 128 columns).
+ *   out       [rows, H] of out_dt (MOE_F32 for f32 layers, else MOE_BF16).
+ *   ws        workspace of moe_workspace_bytes(MOE_OP_GROUPED_FFN, ...) bytes; it holds
+ *             the intermediate h [rows, I] (fp32 for f32 layers, else bf16).
+ * Accumulation is fp32.  fp8 layers sum each 128-wide K block in fp32, then scale it by
+ * the product of the two block scales; the down projection reads bf16 h against fp8
+ * W_down, scaled per 128-wide K block.
+ * Requires H % 64 == 0 and I % 64 == 0 (H % 128 == 0, I % 128 == 0 for fp8).
+ */
+moe_status moe_grouped_ffn(const void* a, const float* a_scale, moe_dtype a_dt,
+                           const int32_t* offsets, int E, int rows, int H, int I, const void* w13,
+                           const float* w13_scale, const void* w2, const float* w2_scale, void* out,
+                           moe_dtype out_dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_gate_up / moe_expert_down -- the two grouped GEMMs of moe_grouped_ffn as
+ * separate calls (same definitions and argument meanings).  h is [rows, I], fp32 for f32
+ * layers and bf16 otherwise.  ws needs moe_workspace_bytes(MOE_OP_EXPERT_GEMM, ...).
+ */
+moe_status moe_expert_gate_up(const void* a, const float* a_scale, moe_dtype a_dt,
+                              const int32_t* offsets, int E, int rows, int H, int I,
+                              const void* w13, const float* w13_scale, void* h, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+moe_status moe_expert_down(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
+                           int I, int H, const void* w2, moe_dtype w2_dt, const float* w2_scale,
+                           void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * moe_combine -- y_t = sum_{j<k} g_{t,j} * expert_out[send_pos[t*k+j]] (+ shared_out_t).
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (y_t, with an optional shared
+ * branch) and section 3 (the source sums the returned rows with the gates in original
+ * token order); "DeepEP" page, section 7 (the combine sums in higher precision).
+ *
+ *   expert_out [rows, H] of eo_dt (MOE_F32 or MOE_BF16), rows >= max(send_pos) + 1.
+ *   send_pos   [N * k] int32; slots with send_pos < 0 are skipped.
+ *   topk_gate  [N, k] fp32.
+ *   shared_out [N, H] of eo_dt, added with gate 1, or NULL.
+ *   y          [N, H] of y_dt (MOE_F32 or MOE_BF16) out.
+ * The sum is fp32 in the order j = 0..k-1, then the shared row; one rounding to y_dt.
+ * Requires H * sizeof(eo_dt) % 16 == 0 and H % 8 == 0.
+ */
+moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, int k,
+                       const int32_t* send_pos, const float* topk_gate, const void* shared_out,
+                       void* y, moe_dtype y_dt, hipStream_t stream);
+
+/*
+ * moe_workspace_bytes -- bytes of workspace `op` needs for these sizes (0 if none).
+ * For MOE_OP_GROUPED_FFN and MOE_OP_EXPERT_GEMM pass the GEMMs' row count as N.
+ * Arguments that an op does not use are ignored.  Returns 0 for invalid sizes.
+ */
+size_t moe_workspace_bytes(int op, int N, int H, int I, int E, int k, int a_dt);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status status);
+
+/* Library version string ("major.minor.patch"). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

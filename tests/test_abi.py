@@ -1,0 +1,101 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects
+invalid arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+
+import pytest
+
+import combine_grouped_gemm_amd as moe
+from combine_grouped_gemm_amd import (MOE_BF16, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
+                                      MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_OK)
+
+FAKE = 4096  # a non-null, 16-byte aligned host integer: never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = moe.declared_symbols()
+    assert {"moe_route", "moe_dispatch_layout", "moe_permute", "moe_grouped_ffn", "moe_combine",
+            "moe_workspace_bytes", "moe_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    assert moe.moe_status_str(MOE_OK) == "ok"
+    assert "workspace" in moe.moe_status_str(MOE_ERR_WORKSPACE)
+    assert moe.moe_version().count(".") == 2
+
+
+def test_route_validation(L):
+    r = lambda *a: L.moe_route(*a)
+    assert r(FAKE, 4, 8, 9, None, 0, 0, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG      # k > E
+    assert r(FAKE, 4, 8, 0, None, 0, 0, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG      # k = 0
+    assert r(FAKE, 4, 2048, 8, None, 0, 0, FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED   # E > 1024
+    assert r(FAKE, 4, 64, 33, None, 0, 0, FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED    # k > 32
+    assert r(FAKE, 4, 10, 2, None, 4, 2, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG     # E % n_group
+    assert r(FAKE, 4, 16, 8, None, 8, 2, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG     # k > 2 groups * 2
+    assert r(FAKE, 4, 16, 2, None, 8, 9, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG     # topk_group > n_group
+    assert r(FAKE, 4, 16, 2, None, 0, 2, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG     # topk_group w/o groups
+    assert r(None, 4, 16, 2, None, 0, 0, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG     # null z
+    assert r(None, 0, 16, 2, None, 0, 0, None, None, None) == MOE_OK                  # N = 0: no-op
+
+
+def test_layout_validation_and_workspace(L):
+    ws = moe.moe_workspace_bytes(moe.MOE_OP_DISPATCH_LAYOUT, 8192, 0, 0, 256, 8, 0)
+    assert ws >= 64 * 256 * 4 and ws % 256 == 0
+    f = L.moe_dispatch_layout
+    assert f(FAKE, 8192, 8, 256, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == MOE_ERR_WORKSPACE
+    assert f(FAKE, 8192, 8, 256, FAKE, FAKE, FAKE, FAKE, None, ws, None) == MOE_ERR_WORKSPACE
+    assert f(FAKE, 8192, 0, 256, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(None, 0, 8, 256, None, None, None, None, None, 0, None) == MOE_OK
+
+
+def test_permute_validation(L):
+    f = L.moe_permute
+    assert f(FAKE, MOE_BF16, 4, 100, 2, FAKE, FAKE, MOE_BF16, None, None) == MOE_ERR_UNSUPPORTED  # 200 B rows
+    assert f(FAKE, MOE_BF16, 4, 192, 2, FAKE, FAKE, MOE_FP8_E4M3, FAKE, None) == MOE_ERR_UNSUPPORTED  # H % 128
+    assert f(FAKE, MOE_BF16, 4, 256, 2, FAKE, FAKE, MOE_FP8_E4M3, None, None) == MOE_ERR_INVALID_ARG  # no scales
+    assert f(FAKE, MOE_BF16, 4, 256, 2, FAKE, FAKE, MOE_F32, None, None) == MOE_ERR_UNSUPPORTED     # bf16 -> f32
+    assert f(FAKE + 8, MOE_BF16, 4, 256, 2, FAKE, FAKE, MOE_BF16, None, None) == MOE_ERR_INVALID_ARG  # misaligned
+    assert f(None, MOE_BF16, 0, 256, 2, None, None, MOE_BF16, None, None) == MOE_OK
+
+
+def test_ffn_validation_and_workspace(L):
+    rows, H, I, E = 65536, 7168, 2048, 256
+    ws = moe.moe_workspace_bytes(moe.MOE_OP_GROUPED_FFN, rows, H, I, E, 1, MOE_BF16)
+    sched = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16)
+    assert ws == sched + rows * I * 2
+    f = L.moe_grouped_ffn
+    args = lambda **kw: dict(dict(a=FAKE, a_scale=None, a_dt=MOE_BF16, offsets=FAKE, E=E, rows=rows,
+                                  H=H, I=I, w13=FAKE, w13_scale=None, w2=FAKE, w2_scale=None,
+                                  out=FAKE, out_dt=MOE_BF16, ws=FAKE, ws_bytes=ws, s=None), **kw)
+    call = lambda **kw: f(*args(**kw).values())
+    assert call(ws_bytes=ws - 1) == MOE_ERR_WORKSPACE
+    assert call(H=7000) == MOE_ERR_UNSUPPORTED
+    assert call(I=2000) == MOE_ERR_UNSUPPORTED
+    assert call(E=0) == MOE_ERR_INVALID_ARG
+    assert call(E=2048) == MOE_ERR_INVALID_ARG
+    assert call(out_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
+    assert call(a_dt=MOE_FP8_E4M3, a_scale=None) == MOE_ERR_INVALID_ARG
+    assert call(offsets=None) == MOE_ERR_INVALID_ARG
+    assert call(rows=0, ws=None, ws_bytes=0) == MOE_OK
+
+
+def test_combine_validation(L):
+    f = L.moe_combine
+    assert f(FAKE, MOE_BF16, 4, 100, 2, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_FP8_E4M3, 4, 128, 2, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 4, 128, 0, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
+    assert f(None, MOE_BF16, 4, 128, 2, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
+    assert f(None, MOE_BF16, 0, 128, 2, None, None, None, None, MOE_BF16, None) == MOE_OK
+
+
+def test_no_cpu_fallback_in_binding():
+    import inspect
+    src = inspect.getsource(moe)
+    assert "oracle" not in src.replace("no fallback", "")

@@ -1,0 +1,330 @@
+"""GPU parity of each libmoe entry point against the CPU oracle, on seeded inputs.
+
+Indices and layout maps are compared bit for bit; the fp8 codec bit for bit;
+floating-point outputs within bars derived from the arithmetic (see each test).
+Every call goes through the C ABI (combine_grouped_gemm_amd -> libmoe.so).
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_grouped_gemm_amd as moe
+import workload as w
+from oracle import moe_oracle as oracle
+from tests.gpu_util import bf16_round, bf16_ulp, f64, say, sync, token_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _loaded():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    moe.lib()
+
+
+def _logits(N, E, seed, ties=False):
+    z = w.normal((N, E), w.stream_key(seed, w.T_WR, 77), "cpu", torch.float32, std=1.0)
+    if ties:
+        z = torch.floor(z * 2.0) / 2.0  # few distinct values: ties everywhere
+    return z
+
+
+# ------------------------------------------------------------------------------------------
+# route
+# ------------------------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    # name, N, E, k, n_group, topk_group, bias, ties
+    ("tiny", 256, 8, 2, 0, 0, False, False),
+    ("decode", 128, 256, 8, 0, 0, False, False),
+    ("groups_8_of_4", 1000, 256, 8, 8, 4, False, False),
+    ("groups_bias", 777, 256, 8, 8, 4, True, False),
+    ("E1_k1", 33, 1, 1, 0, 0, False, False),
+    ("k_eq_E", 65, 16, 16, 0, 0, False, False),
+    ("E1024_k32", 70, 1024, 32, 0, 0, True, False),
+    ("E100_groups", 90, 100, 7, 4, 3, False, False),
+    ("E64_groups64", 50, 64, 5, 64, 5, False, False),
+    ("ties", 500, 32, 6, 0, 0, False, True),
+    ("ties_groups", 500, 32, 6, 4, 2, False, True),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_matches_oracle(case):
+    name, N, E, k, ng, tg, use_bias, ties = case
+    say(f"route {name}")
+    z = _logits(N, E, seed=hash(name) % 1000, ties=ties)
+    bias = (w.normal((E,), w.stream_key(5, w.T_PERM, E), "cpu", torch.float32, std=0.5)
+            if use_bias else None)
+    idx, gate = moe.moe_route(z.to(DEV), k, None if bias is None else bias.to(DEV), ng, tg)
+    sync()
+    ridx, rgate = oracle.route(z.numpy(), k, None if bias is None else bias.numpy(), ng, tg)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy().astype(np.float64) - rgate).max() <= 1e-6
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"])
+def test_route_full_config_logits(name):
+    cfg = w.CONFIGS[name]
+    say(f"route config {name}")
+    x = w.hidden_states(cfg, DEV)
+    z = w.router_logits(x, w.router_weight(cfg))
+    b = w.zipf_bias(cfg)
+    idx, gate = moe.moe_route(z.to(DEV), cfg.k, None if b is None else b.to(DEV), cfg.n_group, cfg.topk_group)
+    sync()
+    ridx, rgate = oracle.route(z.numpy(), cfg.k, None if b is None else b.numpy(), cfg.n_group, cfg.topk_group)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy().astype(np.float64) - rgate).max() <= 1e-6
+
+
+# ------------------------------------------------------------------------------------------
+# dispatch layout
+# ------------------------------------------------------------------------------------------
+
+LAYOUT_CASES = [
+    ("round_robin", 512, 256, 8, "round_robin"),
+    ("hot", 1000, 64, 4, "hot"),
+    ("random_small", 37, 5, 3, "random"),
+    ("random_cfg3", 8192, 256, 8, "random"),
+    ("random_ragged", 3001, 77, 6, "random"),
+    ("N1", 1, 8, 2, "random"),
+    ("E1", 129, 1, 1, "random"),
+    ("k1", 4097, 8, 1, "random"),
+    ("E1024", 700, 1024, 32, "random"),
+    ("many_chunks", 600000, 64, 8, "random"),   # 4.8M slots: more than 4096 chunks of 1024
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=[c[0] for c in LAYOUT_CASES])
+def test_dispatch_layout_matches_oracle(case):
+    name, N, E, k, kind = case
+    say(f"layout {name}")
+    idx = w.fixed_route(N, E, k, kind, seed=len(name))
+    out1 = moe.moe_dispatch_layout(idx.to(DEV), E)
+    out2 = moe.moe_dispatch_layout(idx.to(DEV), E)
+    sync()
+    ref = oracle.dispatch_layout(idx.numpy(), E)
+    for got, r, again in zip(out1, ref, out2):
+        g = got.cpu().numpy()
+        assert np.array_equal(g, r)
+        assert np.array_equal(g, again.cpu().numpy())  # deterministic
+
+
+def test_dispatch_layout_skips_out_of_range_ids():
+    N, E, k = 300, 16, 4
+    idx = w.fixed_route(N, E, k, "random", seed=9).clone()
+    idx[5, 1] = -1
+    idx[17, 0] = E
+    idx[200, 3] = 1 << 20
+    n_e, off, sp, ss = moe.moe_dispatch_layout(idx.to(DEV), E)
+    sync()
+    flat = idx.reshape(-1).numpy()
+    valid = (flat >= 0) & (flat < E)
+    sp = sp.cpu().numpy()
+    assert np.all(sp[~valid] == -1)
+    assert np.array_equal(n_e.cpu().numpy(), np.bincount(flat[valid], minlength=E))
+    assert off.cpu().numpy()[E] == valid.sum()
+    assert np.array_equal(np.sort(sp[valid]), np.arange(valid.sum()))
+    ss = ss.cpu().numpy()
+    assert np.array_equal(ss[sp[valid]], np.nonzero(valid)[0])
+
+
+# ------------------------------------------------------------------------------------------
+# permute and the fp8 codec
+# ------------------------------------------------------------------------------------------
+
+PERMUTE_CASES = [
+    # name, N, H, E, k, dtype
+    ("bf16", 1000, 1024, 32, 4, torch.bfloat16),
+    ("f32", 256, 128, 8, 2, torch.float32),
+    ("bf16_H8", 33, 8, 4, 2, torch.bfloat16),
+    ("bf16_k1", 100, 7168, 8, 1, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES, ids=[c[0] for c in PERMUTE_CASES])
+def test_permute_copy_bit_exact(case):
+    name, N, H, E, k, dt = case
+    say(f"permute {name}")
+    x = w.normal((N, H), w.stream_key(3, w.T_X, H), DEV, dt)
+    idx = w.fixed_route(N, E, k, "random", seed=N)
+    _, _, sp, _ = moe.moe_dispatch_layout(idx.to(DEV), E)
+    xp = moe.moe_permute(x, sp, k)
+    sync()
+    _, _, rsp, _ = oracle.dispatch_layout(idx.numpy(), E)
+    view = torch.int16 if dt == torch.bfloat16 else torch.int32
+    ref = oracle.permute(x.cpu().view(view).numpy(), rsp, k)
+    assert np.array_equal(xp.cpu().view(view).numpy(), ref)
+
+
+def test_round_trip_identity_experts_and_token_ids():
+    """permute -> identity experts -> combine gives back x; printable ids survive."""
+    N, H, E, k = 1500, 256, 64, 6
+    x = torch.zeros((N, H), dtype=torch.bfloat16)
+    x[:, 0] = (torch.arange(N) // 256).to(torch.bfloat16)
+    x[:, 1] = (torch.arange(N) % 256).to(torch.bfloat16)
+    x[:, 2:] = w.normal((N, H - 2), w.stream_key(1, w.T_X, 5), "cpu", torch.bfloat16)
+    z = _logits(N, E, seed=4)
+    idx, gate = moe.moe_route(z.to(DEV), k)
+    n_e, off, sp, ss = moe.moe_dispatch_layout(idx, E)
+    xg = x.to(DEV)
+    xp = moe.moe_permute(xg, sp, k)
+    y = moe.moe_combine(xp, sp, gate)
+    sync()
+    tok = (xp[:, 0].float() * 256 + xp[:, 1].float()).long().cpu().numpy()
+    assert np.array_equal(tok, ss.cpu().numpy() // k)
+    assert torch.equal(y.cpu(), x)  # sum of the gates is 1 to within 1e-7, far below a bf16 step
+
+
+def _blocky(rows, cols, seed, dt=torch.bfloat16):
+    """Rows with per-block magnitudes from 2^-30 to 2^12, a zero block and exact ties."""
+    x = w.normal((rows, cols), w.stream_key(seed, w.T_EO, cols), "cpu", torch.float32, std=1.0)
+    nb = cols // 128
+    expo = (torch.arange(rows * nb) % 43 - 30).reshape(rows, nb).to(torch.float32)
+    x = x * torch.repeat_interleave(torch.exp2(expo), 128, dim=1)
+    x[0, :128] = 0.0
+    if rows > 1:
+        x[1, :128] = 3.0  # all equal: every element maps to 448
+    return x.to(dt)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=["bf16_in", "f32_in"])
+def test_quantize_fp8_bit_exact(dt):
+    say(f"quantize {dt}")
+    x = _blocky(300, 1024, 2, dt)
+    q, s = moe.moe_quantize_fp8(x.to(DEV))
+    sync()
+    rq, rs = oracle.quantize_blocks(x.to(torch.float32).numpy())
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+def test_permute_fp8_bit_exact():
+    N, H, E, k = 400, 2048, 16, 4
+    say("permute fp8")
+    x = _blocky(N, H, 7)
+    idx = w.fixed_route(N, E, k, "random", seed=3)
+    _, _, sp, _ = moe.moe_dispatch_layout(idx.to(DEV), E)
+    xq, xs = moe.moe_permute(x.to(DEV), sp, k, moe.MOE_FP8_E4M3)
+    sync()
+    _, _, rsp, _ = oracle.dispatch_layout(idx.numpy(), E)
+    rq, rs = oracle.quantize_blocks(x.to(torch.float32).numpy())
+    assert np.array_equal(xq.cpu().numpy(), oracle.permute(rq, rsp, k))
+    assert np.array_equal(xs.cpu().numpy(), oracle.permute(rs, rsp, k))
+
+
+# ------------------------------------------------------------------------------------------
+# grouped GEMMs
+# ------------------------------------------------------------------------------------------
+
+GEMM_CASES = [
+    # name, n_e per expert, H, I, dtype
+    ("bf16_ragged", [0, 1, 127, 128, 129, 300, 0, 5], 512, 256, "bf16"),
+    ("bf16_one_expert", [1000], 1024, 384, "bf16"),
+    ("bf16_empty_tail", [64, 0, 0, 0], 256, 128, "bf16"),
+    ("f32_ragged", [60, 0, 200, 1, 70], 256, 256, "f32"),
+    ("fp8_ragged", [3, 0, 17, 128, 130, 1], 512, 256, "fp8"),
+    ("bf16_wide_K", [200, 90], 7168, 256, "bf16"),
+]
+
+
+def _gemm_inputs(n_e, H, I, dtype, seed):
+    E, rows = len(n_e), sum(n_e)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    a = w.normal((rows, H), w.stream_key(seed, w.T_X, 1), DEV, dt)
+    w13 = w.normal((E, 2 * I, H), w.stream_key(seed, w.T_W13, 1), DEV, dt)
+    w2 = w.normal((E, H, I), w.stream_key(seed, w.T_W2, 1), DEV, dt)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(n_e)]), dtype=torch.int32, device=DEV)
+    return a, w13, w2, offs
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_grouped_ffn_matches_oracle(case):
+    name, n_e, H, I, dtype = case
+    say(f"gemm {name}")
+    a, w13, w2, offs = _gemm_inputs(n_e, H, I, dtype, seed=len(name))
+    offs_np = offs.cpu().numpy()
+    if dtype == "fp8":
+        aq, asc = moe.moe_quantize_fp8(a)
+        q13, s13 = moe.moe_quantize_fp8(w13)
+        q2, s2 = moe.moe_quantize_fp8(w2)
+        h = moe.moe_expert_gate_up(aq, offs, q13, asc, s13)
+        out = moe.moe_expert_down(h, offs, q2, s2)
+        out2 = moe.moe_grouped_ffn(aq, offs, q13, q2, asc, s13, s2)
+        sync()
+        ra = oracle.dequantize_blocks(*oracle.quantize_blocks(a.float().cpu().numpy()))
+        E = len(n_e)
+        r13 = [oracle.dequantize_blocks(*oracle.quantize_blocks(w13[e].float().cpu().numpy())) for e in range(E)]
+        r2 = [oracle.dequantize_blocks(*oracle.quantize_blocks(w2[e].float().cpu().numpy())) for e in range(E)]
+        rh, rout = oracle.grouped_ffn(ra, offs_np, lambda e: r13[e], lambda e: r2[e])
+        bar = 1e-2
+    else:
+        h = moe.moe_expert_gate_up(a, offs, w13)
+        out = moe.moe_expert_down(h, offs, w2)
+        out2 = moe.moe_grouped_ffn(a, offs, w13, w2)
+        sync()
+        rh, rout = oracle.grouped_ffn(f64(a), offs_np, f64(w13), f64(w2))
+        bar = 1e-5 if dtype == "f32" else 1e-2
+    assert token_rel_err(f64(h), rh) <= bar
+    assert token_rel_err(f64(out), rout) <= bar
+    assert torch.equal(out, out2)
+
+
+def test_expert_down_on_generated_h():
+    """The down GEMM alone, on an h that no other kernel produced."""
+    n_e, H, I = [70, 0, 300, 3], 1024, 512
+    rows, E = sum(n_e), len(n_e)
+    h = w.normal((rows, I), w.stream_key(8, w.T_EO, 2), DEV, torch.bfloat16, std=0.05)
+    w2 = w.normal((E, H, I), w.stream_key(8, w.T_W2, 2), DEV, torch.bfloat16)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(n_e)]), dtype=torch.int32, device=DEV)
+    out = moe.moe_expert_down(h, offs, w2)
+    sync()
+    ref = np.zeros((rows, H))
+    o = offs.cpu().numpy()
+    hh, ww = f64(h), f64(w2)
+    for e in range(E):
+        ref[o[e]:o[e + 1]] = hh[o[e]:o[e + 1]] @ ww[e].T
+    # fp32 accumulation then one bf16 rounding: within one bf16 step of the exact value
+    got = f64(out)
+    assert np.all(np.abs(got - ref) <= bf16_ulp(ref) + 1e-6 * np.abs(ref).max())
+
+
+# ------------------------------------------------------------------------------------------
+# combine
+# ------------------------------------------------------------------------------------------
+
+COMBINE_CASES = [
+    ("bf16_shared", 700, 1024, 32, 8, torch.bfloat16, True),
+    ("bf16", 513, 7168, 16, 2, torch.bfloat16, False),
+    ("f32", 256, 128, 8, 2, torch.float32, False),
+    ("k3", 100, 64, 8, 3, torch.bfloat16, True),
+    ("k32", 50, 256, 64, 32, torch.bfloat16, False),
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_CASES, ids=[c[0] for c in COMBINE_CASES])
+def test_combine_matches_oracle(case):
+    name, N, H, E, k, dt, shared = case
+    say(f"combine {name}")
+    cfg = w.CONFIGS["tiny_f32"]
+    eo = w.synthetic_rows(N * k, H, 11, cfg, DEV, dt)
+    sh = w.synthetic_rows(N, H, 12, cfg, DEV, dt) if shared else None
+    gate = w.random_gates(N, k, seed=5)
+    idx = w.fixed_route(N, E, k, "random", seed=6)
+    _, _, sp, _ = moe.moe_dispatch_layout(idx.to(DEV), E)
+    y = moe.moe_combine(eo, sp, gate.to(DEV), sh)
+    sync()
+    _, _, rsp, _ = oracle.dispatch_layout(idx.numpy(), E)
+    ref = oracle.combine(f64(eo), rsp, gate.numpy().astype(np.float64), k, None if sh is None else f64(sh))
+    got = f64(y)
+    if dt == torch.float32:
+        assert token_rel_err(got, ref) <= 1e-6
+    else:
+        # fp32 sum of k+1 terms, then one rounding: within one bf16 step of the rounded
+        # exact sum, plus the fp32 accumulation bound (k+1) * 2^-24 * sum of |terms|
+        # (which dominates where the sum cancels to almost nothing)
+        mag = oracle.combine(np.abs(f64(eo)), rsp, np.abs(gate.numpy().astype(np.float64)), k,
+                             None if sh is None else np.abs(f64(sh)))
+        tol = bf16_ulp(ref) * 1.0001 + (k + 1) * 2.0 ** -24 * mag
+        assert np.all(np.abs(got - bf16_round(ref)) <= tol)
