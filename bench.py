@@ -1,0 +1,256 @@
+"""Benchmark: one GPU's share of a sparse MoE layer on MI355X through libmoe.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+route -> dispatch layout -> permute -> grouped gate/up GEMM + SwiGLU -> grouped
+down GEMM -> shared expert (when the workload has one) -> combine.  Inputs and
+weights are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dsv3_bf16]
+
+Prints one JSON line.  Kernel durations come from HIP events recorded on the
+stream the kernels run on, around every call of every timed step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_MFMA = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
+METRIC = "MoE-layer tokens/s; grouped-GEMM MFMA util; permute/combine HBM GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic_{}.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="dsv3_bf16")
+    p.add_argument("--cpu-tokens", type=int, default=16,
+                   help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(cfg, n_e):
+    """Algorithmic bytes and flops of each step (what the method must move or compute)."""
+    import numpy as np
+    N, H, E, k, I = cfg.N, cfg.H, cfg.E, cfg.k, cfg.I
+    rows = N * k
+    act = 4 if cfg.dtype == "f32" else 2          # x, h, expert outputs, y
+    pay = 1 if cfg.dtype == "fp8" else act        # permuted payload
+    wb = 1 if cfg.dtype == "fp8" else act         # weights
+    touched = int((np.asarray(n_e) > 0).sum())
+    fp8_scale = 4.0 / 128 if cfg.dtype == "fp8" else 0.0
+    d = {}
+    d["route"] = {"bytes": N * E * 4 + (E * 4 if cfg.zipf_s else 0) + rows * 8}
+    d["layout"] = {"bytes": rows * 4 + (2 * E + 1) * 4 + 2 * rows * 4}
+    d["permute"] = {"bytes": N * H * act + rows * H * (pay + fp8_scale)}
+    d["gate_up"] = {"bytes": touched * 2 * I * H * (wb + fp8_scale) + rows * H * (pay + fp8_scale) + rows * I * 2,
+                    "flops": 4.0 * rows * H * I}
+    d["down"] = {"bytes": touched * H * I * (wb + fp8_scale) + rows * I * 2 + rows * H * act,
+                 "flops": 2.0 * rows * H * I}
+    if cfg.shared:
+        d["shared"] = {"bytes": 3 * I * H * wb + N * H * act + N * I * 2 + N * H * act,
+                       "flops": 6.0 * N * H * I}
+    d["combine"] = {"bytes": (rows + (N if cfg.shared else 0)) * H * act + N * H * act + rows * 8}
+    return d
+
+
+def cpu_baseline(cfg, inp, T):
+    """The oracle, as it stands, on the first T tokens of the batch (weights staged on the host)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle
+
+    T = min(T, cfg.N)
+    x = inp["x"][:T].detach().cpu()
+    z = inp["z_cpu"][:T].numpy()
+    b = inp["bias_cpu"]
+    idx, _ = moe_oracle.route(z, cfg.k, None if b is None else b.numpy(), cfg.n_group, cfg.topk_group)
+    need = sorted(set(int(e) for e in idx.reshape(-1)))
+    w13 = {e: inp["w13"][e].detach().cpu() for e in need}   # staged on the host, not timed
+    w2 = {e: inp["w2"][e].detach().cpu() for e in need}
+    fp8 = cfg.dtype == "fp8"
+    if cfg.shared:
+        sw13, sw2 = inp["sw13"][0].cpu(), inp["sw2"][0].cpu()
+    t0 = time.perf_counter()
+    if fp8:
+        q13 = {e: moe_oracle.quantize_blocks(w13[e].float().numpy()) for e in need}
+        q2 = {e: moe_oracle.quantize_blocks(w2[e].float().numpy()) for e in need}
+        moe_oracle.moe_layer(x.float().numpy(), z, cfg.k, lambda e: q13[e][0], lambda e: q2[e][0],
+                             n_group=cfg.n_group, topk_group=cfg.topk_group, fp8=True,
+                             w13_scale=lambda e: q13[e][1], w2_scale=lambda e: q2[e][1])
+    else:
+        kw = {}
+        if cfg.shared:
+            kw = dict(shared_w13=sw13.double().numpy(), shared_w2=sw2.double().numpy())
+        moe_oracle.moe_layer(x.double().numpy(), z, cfg.k, lambda e: w13[e].double().numpy(),
+                             lambda e: w2[e].double().numpy(), bias=None if b is None else b.numpy(),
+                             n_group=cfg.n_group, topk_group=cfg.topk_group, **kw)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {T} of {cfg.N} tokens of the same batch through the whole oracle layer "
+                      f"({len(need)} experts touched; float64; weights staged on the host before timing); "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workload
+    import combine_grouped_gemm_amd as moe
+    from combine_grouped_gemm_amd.layer import MoELayer
+
+    cfg = workload.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    moe.lib()
+    log(args, f"generating {cfg.name} inputs on the GPU")
+    inp = workload.make_layer_inputs(cfg, dev)
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"])
+    x, z = inp["x"], inp["z"]
+    torch.cuda.synchronize()
+
+    rows = cfg.N * cfg.k
+    h_buf = layer.h
+    from combine_grouped_gemm_amd import moe_expert_down, moe_expert_gate_up
+
+    sched_ws = layer.ffn_ws  # the schedule lives at the start of the FFN workspace
+
+    stages = [("route", lambda: layer.route(z)),
+              ("layout", layer.dispatch),
+              ("permute", lambda: layer.permute(x)),
+              ("gate_up", lambda: moe_expert_gate_up(layer.x_perm, layer.layout[1], layer.w13,
+                                                     layer.x_perm_scale, layer.w13_scale, h_buf, sched_ws)),
+              ("down", lambda: moe_expert_down(h_buf, layer.layout[1], layer.w2, layer.w2_scale,
+                                               layer.expert_out, sched_ws))]
+    if cfg.shared:
+        stages.append(("shared", lambda: layer.shared_expert(x)))
+    stages.append(("combine", layer.combine))
+
+    def step():
+        for _, f in stages:
+            f()
+
+    log(args, f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    log(args, f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(stages):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: [] for name, _ in stages}
+    step_ms = []
+    for s in range(args.steps):
+        for i, (name, _) in enumerate(stages):
+            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
+        step_ms.append(ev[s][0].elapsed_time(ev[s][len(stages)]))
+    ms_per_step = wall * 1e3 / args.steps
+    value = cfg.N / (ms_per_step / 1e3)
+
+    n_e = layer.layout[0].cpu().numpy()
+    alg = algorithmic(cfg, n_e)
+    kernels = {}
+    for name, times in per.items():
+        t = sorted(times)
+        avg = sum(t) / len(t)
+        k = {"avg_ms": round(avg, 4), "median_ms": round(t[len(t) // 2], 4),
+             "p99_ms": round(t[min(len(t) - 1, int(math.ceil(0.99 * len(t))) - 1)], 4)}
+        a = alg.get(name, {})
+        if "bytes" in a:
+            k["GB_per_s"] = round(a["bytes"] / (avg * 1e-3) / 1e9, 1)
+            k["hbm_frac"] = round(a["bytes"] / (avg * 1e-3) / PEAK_HBM, 4)
+        if "flops" in a:
+            k["TFLOP_per_s"] = round(a["flops"] / (avg * 1e-3) / 1e12, 1)
+            k["mfma_frac"] = round(a["flops"] / (avg * 1e-3) / PEAK_MFMA[cfg.dtype], 4)
+        kernels[name] = k
+
+    g = alg["gate_up"]
+    g_avg = sum(per["gate_up"]) / len(per["gate_up"]) * 1e-3
+    t_mfma = g["flops"] / PEAK_MFMA[cfg.dtype]
+    t_hbm = g["bytes"] / PEAK_HBM
+    traffic = None
+    tf = TRAFFIC_FILE.format(cfg.name)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_sha") == source_sha(os.path.join(ROOT, "combine_grouped_gemm_amd", "csrc", "grouped_gemm.hip")):
+            traffic = rec.get("bytes_per_launch")
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(g["bytes"] / g_avg / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(g["flops"] / g_avg / 1e12, 1),
+                "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)"
+    roof["algorithmic_bytes"] = int(g["bytes"])
+    roof["algorithmic_flops"] = g["flops"]
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        log(args, f"CPU oracle baseline on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if cfg.dtype == "fp8" else cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}"
+                               + (f" groups {cfg.topk_group}/{cfg.n_group}" if cfg.n_group else "")
+                               + (" +shared expert" if cfg.shared else "")
+                               + (f" zipf bias s={cfg.zipf_s}" if cfg.zipf_s else ""),
+                   "global_batch": cfg.N, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),
+                                   "down": kernels["down"].get("mfma_frac")},
+        "permute_hbm_GBps": kernels["permute"]["GB_per_s"],
+        "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
+        "imbalance": round(float(n_e.max() / n_e.mean()), 4),
+        "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,21 +6,22 @@
 //   down:     out[r, :] = h[r] . W_down,e^T
 //
 // Operands are K-contiguous (a [rows, K], weights [n, K]), so both MFMA operands are
-// 16-byte row fragments.  A workgroup (4 waves, 2 x 2) computes a 128-row x 128-column
-// tile with v_mfma_f32_32x32x16 (bf16 and fp8) or v_mfma_f32_32x32x2 (fp32); K advances
-// in 128-byte stages through double-buffered, padded LDS, the next stage's global loads
-// in flight while the current one is multiplied.
+// 16-byte row fragments.  A workgroup (4 waves, 2 x 2) computes a 128-row x 256-column
+// tile; each wave owns 64 x 128 (2 x 4 blocks of v_mfma_f32_32x32x16 for bf16 and fp8,
+// v_mfma_f32_32x32x2 for fp32), so every 16-wide K step reads 6 fragments from LDS for 8
+// MFMAs.  K advances in 128-byte stages: two stages of global loads are in flight in
+// registers while the current stage, double-buffered in padded LDS, is multiplied.
 //
-// The gate/up tile takes 64 rows of W_gate and the same 64 rows of W_up, so each wave
+// The gate/up tile takes 128 rows of W_gate and the same 128 rows of W_up, so each wave
 // holds matching gate and up accumulators and applies SwiGLU in registers; h is written
 // once.
 //
 // Tile schedule: a one-workgroup prologue turns offsets into a per-expert m-tile prefix.
-// The GEMM is persistent: the logical tiles are ordered expert -> n-block -> m-tile (the
-// m-tiles sharing a weight block are adjacent) and split into 8 contiguous ranges, one
-// per XCD (workgroup i runs on XCD i mod 8), so tiles that share weights and activation
-// rows share an L2.  Every tile has the same cost whatever the skew of n_e, so ragged and
-// hot experts spread evenly over the CUs.
+// The GEMM is persistent (one workgroup per CU): the logical tiles are ordered expert ->
+// n-block -> m-tile (the m-tiles sharing a weight block are adjacent) and split into 8
+// contiguous ranges, one per XCD (workgroup i runs on XCD i mod 8), so tiles that share
+// weights and activation rows run together under one L2.  Every tile costs the same
+// whatever the skew of n_e, so ragged and hot experts spread evenly over the CUs.
 //
 // fp8 layers: the gate/up GEMM multiplies e4m3 codes on the fp8 MFMA, sums each 128-wide
 // K block in a separate fp32 accumulator and adds it scaled by a_scale[row] *
@@ -38,11 +39,13 @@ enum { CT_F32 = 0, CT_BF16 = 1, CT_FP8 = 2 };
 enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
 
 constexpr int GBM = 128;          // rows of a tile
-constexpr int GBN = 128;          // weight rows of a tile
+constexpr int GBN = 256;          // weight rows of a tile (gate/up: 128 gate + 128 up)
 constexpr int GKB = 128;          // bytes of K per row and stage (compute type)
 constexpr int GPITCH = GKB + 16;  // padded LDS row pitch: 8 consecutive rows hit 8 bank groups
 constexpr int GTHREADS = 256;
 constexpr int kNumXcd = 8;
+constexpr int kAChunks = GBM * (GKB / 16) / GTHREADS;  // 16-byte A chunks per thread and stage (4)
+constexpr int kBChunks = GBN * (GKB / 16) / GTHREADS;  // B chunks per thread and stage (8)
 
 template <int CT> struct CTraits;
 template <> struct CTraits<CT_F32> { static constexpr int esz = 4; };
@@ -126,30 +129,40 @@ __device__ __forceinline__ f32x16_t mma(const Frag<CT_FP8>& a, const Frag<CT_FP8
 __device__ __forceinline__ f32x16_t mma(const Frag<CT_F32>& a, const Frag<CT_F32>& b, f32x16_t c) {
   // lanes 0-31 supply k = s and lanes 32-63 k = 8 + s of the 16-wide step; the same
   // assignment on both operands makes the 8 products sum over all 16 k.
-  const float av[8] = {__uint_as_float(a.v0.x), __uint_as_float(a.v0.y), __uint_as_float(a.v0.z),
-                       __uint_as_float(a.v0.w), __uint_as_float(a.v1.x), __uint_as_float(a.v1.y),
-                       __uint_as_float(a.v1.z), __uint_as_float(a.v1.w)};
-  const float bv[8] = {__uint_as_float(b.v0.x), __uint_as_float(b.v0.y), __uint_as_float(b.v0.z),
-                       __uint_as_float(b.v0.w), __uint_as_float(b.v1.x), __uint_as_float(b.v1.y),
-                       __uint_as_float(b.v1.z), __uint_as_float(b.v1.w)};
-#pragma unroll
-  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v0.x), __uint_as_float(b.v0.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v0.y), __uint_as_float(b.v0.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v0.z), __uint_as_float(b.v0.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v0.w), __uint_as_float(b.v0.w), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v1.x), __uint_as_float(b.v1.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v1.y), __uint_as_float(b.v1.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v1.z), __uint_as_float(b.v1.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v1.w), __uint_as_float(b.v1.w), c, 0, 0, 0);
   return c;
 }
 
-// CT: compute type held in LDS.  B8: B is stored as e4m3 and converted to bf16 (CT_BF16)
-// on its way to LDS.  Scaled: per-128-K block scales (CT_FP8: A and B; B8: B only).
+// Weight row of tile row `row` (0..GBN-1).
+template <int MODE>
+__device__ __forceinline__ long long weight_row(int row, int nblk, int I, int n_out) {
+  if (MODE == MODE_GATE_UP)
+    return row < GBN / 2 ? static_cast<long long>(nblk) * (GBN / 2) + row
+                         : I + static_cast<long long>(nblk) * (GBN / 2) + (row - GBN / 2);
+  long long r = static_cast<long long>(nblk) * GBN + row;
+  return r < n_out ? r : n_out - 1;
+}
+
 template <int CT, bool B8, int MODE>
-__global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int esz = CTraits<CT>::esz;
   constexpr int BK = GKB / esz;                 // K elements per stage
   constexpr int KSTEPS = BK / 16;               // 16-wide MFMA steps per stage
   constexpr bool kScaled = (CT == CT_FP8) || B8;
   constexpr int kStagesPerBlock = 128 / BK;     // stages per 128-wide scale block
-  constexpr int kStageBytes = GBM * GPITCH;
+  constexpr int kAStage = GBM * GPITCH;
+  constexpr int kBStage = GBN * GPITCH;
+  constexpr int kBGlobal = B8 ? 8 : 16;         // global bytes per B chunk
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kBStage];
   __shared__ float lds_sa[2][GBM];
   __shared__ float lds_sb[2][GBN];
 
@@ -157,8 +170,10 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  const int t_row = tid >> 3;        // tile row of chunk 0 (chunk i: + 32 i)
+  const int t_c = tid & 7;           // 16-byte column chunk
 
-  const int nN = MODE == MODE_GATE_UP ? p.I / 64 : p.n_out / GBN;
+  const int nN = MODE == MODE_GATE_UP ? p.I / (GBN / 2) : (p.n_out + GBN - 1) / GBN;
   const long long total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
@@ -167,9 +182,16 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs p) {
   const long long t_end = total * (xcd + 1) / kNumXcd;
 
   const int nk = p.K / BK;
-  const size_t a_row_bytes = static_cast<size_t>(p.K) * esz;
-  const size_t b_row_bytes = static_cast<size_t>(p.K) * (B8 ? 1 : esz);
+  const uint32_t a_rb = static_cast<uint32_t>(p.K) * esz;            // A row bytes
+  const uint32_t b_rb = static_cast<uint32_t>(p.K) * (B8 ? 1 : esz);  // B row bytes
   const int kblocks = p.K / 128;
+
+  // LDS offsets (bytes within a stage buffer)
+  const int frag_k = (lane >> 5) * 8 * esz;
+  const int a_frag = (wm * 64 + (lane & 31)) * GPITCH + frag_k;            // + mb * 32 rows
+  const int b_frag = MODE == MODE_GATE_UP ? (wn * 64 + (lane & 31)) * GPITCH + frag_k   // + (nb>>1)*128 + (nb&1)*32 rows
+                                          : (wn * 128 + (lane & 31)) * GPITCH + frag_k; // + nb * 32 rows
+  const int st_off = t_row * GPITCH + t_c * 16;                            // + i * 32 rows
 
   for (long long L = t_beg + slot; L < t_end; L += per_xcd) {
     // ---- decode the logical tile: expert -> n-block -> m-tile
@@ -183,148 +205,160 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs p) {
     seg_lo = seg_lo < 0 ? 0 : (seg_lo > p.rows ? p.rows : seg_lo);
     seg_hi = seg_hi < seg_lo ? seg_lo : (seg_hi > p.rows ? p.rows : seg_hi);
     const int m0 = seg_lo + mtile * GBM;
-    const int mend = seg_hi;
+    const int mlast = seg_hi - 1 - m0;   // last valid tile row (rows past it re-read it)
 
-    // ---- per-thread global sources: 4 A chunks and 4 B chunks per stage
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
-    int lds_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + GTHREADS * i;
-      const int row = q >> 3, c = q & 7;
-      int ar = m0 + row;
-      ar = ar < mend ? ar : mend - 1;
-      a_src[i] = p.a + static_cast<size_t>(ar) * a_row_bytes + c * 16;
-      long long br;
-      if (MODE == MODE_GATE_UP)
-        br = row < 64 ? static_cast<long long>(nblk) * 64 + row : p.I + static_cast<long long>(nblk) * 64 + (row - 64);
-      else
-        br = static_cast<long long>(nblk) * GBN + row;
-      b_src[i] = p.b + (static_cast<size_t>(e) * p.b_rows + br) * b_row_bytes + c * (B8 ? 8 : 16);
-      lds_off[i] = row * GPITCH + c * 16;
-    }
-    // scale sources: threads 0..127 -> A row scales, 128..255 -> B row scales
-    const float* s_src = nullptr;
-    if (kScaled) {
-      if (tid < GBM) {
-        if (CT == CT_FP8) {
-          int ar = m0 + tid;
-          ar = ar < mend ? ar : mend - 1;
-          s_src = p.a_scale + static_cast<size_t>(ar) * kblocks;
-        }
-      } else {
-        const int row = tid - GBM;
-        long long br;
-        if (MODE == MODE_GATE_UP)
-          br = row < 64 ? static_cast<long long>(nblk) * 64 + row : p.I + static_cast<long long>(nblk) * 64 + (row - 64);
-        else
-          br = static_cast<long long>(nblk) * GBN + row;
-        s_src = p.b_scale + (static_cast<size_t>(e) * p.b_rows + br) * kblocks;
-      }
-    }
+    // uniform tile bases; per-chunk offsets are 32-bit
+    const uint8_t* a_tile = p.a + static_cast<size_t>(m0) * a_rb;
+    const long long b_row0 = MODE == MODE_GATE_UP ? static_cast<long long>(nblk) * (GBN / 2)
+                                                  : static_cast<long long>(nblk) * GBN;
+    const uint8_t* b_tile = p.b + (static_cast<size_t>(e) * p.b_rows + b_row0) * b_rb;
+    const int b_rows_left = MODE == MODE_GATE_UP ? GBN : static_cast<int>(p.n_out - b_row0);  // valid B tile rows
+    const float* sa_tile = CT == CT_FP8 ? p.a_scale + static_cast<size_t>(m0) * kblocks : nullptr;
+    const float* sb_tile = kScaled ? p.b_scale + (static_cast<size_t>(e) * p.b_rows + b_row0) * kblocks : nullptr;
 
-    uint4 ra[4], rb[4];
-    float rs = 1.0f;
-    auto load_stage = [&](int ks) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + static_cast<size_t>(ks) * GKB);
-      if (B8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint2 w = *reinterpret_cast<const uint2*>(b_src[i] + static_cast<size_t>(ks) * BK);
-          const uint2 lo = e4m3x4_to_bf16x4(w.x), hi = e4m3x4_to_bf16x4(w.y);
-          rb[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + static_cast<size_t>(ks) * GKB);
-      }
-      if (kScaled && s_src != nullptr) rs = s_src[(ks * BK) / 128];
+    struct Regs {
+      uint4 a[kAChunks];
+      uint4 b[kBChunks];
+      uint2 b8[kBChunks];
+      float sa, sb;
     };
-    auto store_stage = [&](int buf) {
+
+    auto b_tile_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
+      // weight row (relative to b_row0) of tile row r
+      if (MODE == MODE_GATE_UP) return r < GBN / 2 ? r : static_cast<uint32_t>(p.I) + (r - GBN / 2);
+      return r < b_rows_left ? r : b_rows_left - 1;
+    };
+
+    auto issue = [&](Regs& r, int ks) __attribute__((always_inline)) {
+      const uint8_t* ab = a_tile + static_cast<size_t>(ks) * GKB;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(&lds_a[buf][lds_off[i]]) = ra[i];
-        *reinterpret_cast<uint4*>(&lds_b[buf][lds_off[i]]) = rb[i];
+      for (int i = 0; i < kAChunks; ++i) {
+        int row = t_row + 32 * i;
+        row = row < mlast ? row : mlast;
+        r.a[i] = *reinterpret_cast<const uint4*>(ab + (static_cast<uint32_t>(row) * a_rb + t_c * 16));
+      }
+      const uint8_t* bb = b_tile + static_cast<size_t>(ks) * (B8 ? BK : GKB);
+#pragma unroll
+      for (int i = 0; i < kBChunks; ++i) {
+        const uint32_t off = b_tile_row(t_row + 32 * i) * b_rb + t_c * kBGlobal;
+        if (B8) r.b8[i] = *reinterpret_cast<const uint2*>(bb + off);
+        else r.b[i] = *reinterpret_cast<const uint4*>(bb + off);
       }
       if (kScaled) {
-        if (tid < GBM) lds_sa[buf][tid] = rs;
-        else lds_sb[buf][tid - GBM] = rs;
+        const int kb = (ks * BK) / 128;
+        r.sa = 1.0f;
+        if (CT == CT_FP8 && tid < GBM) r.sa = sa_tile[static_cast<size_t>(tid < mlast ? tid : mlast) * kblocks + kb];
+        r.sb = sb_tile[static_cast<size_t>(b_tile_row(tid)) * kblocks + kb];
+      }
+    };
+    auto commit = [&](Regs& r, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < kAChunks; ++i) *reinterpret_cast<uint4*>(&lds_a[buf][st_off + i * 32 * GPITCH]) = r.a[i];
+#pragma unroll
+      for (int i = 0; i < kBChunks; ++i) {
+        uint4 v;
+        if (B8) {
+          const uint2 lo = e4m3x4_to_bf16x4(r.b8[i].x), hi = e4m3x4_to_bf16x4(r.b8[i].y);
+          v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+          v = r.b[i];
+        }
+        *reinterpret_cast<uint4*>(&lds_b[buf][st_off + i * 32 * GPITCH]) = v;
+      }
+      if (kScaled) {
+        if (tid < GBM) lds_sa[buf][tid] = r.sa;
+        lds_sb[buf][tid] = r.sb;
       }
     };
 
-    f32x16_t acc[2][2];
-    f32x16_t part[2][2];
+    f32x16_t acc[2][4];
+    f32x16_t part[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 4; ++j) {
         acc[i][j] = f32x16_t{};
-        part[i][j] = f32x16_t{};
+        if (kScaled) part[i][j] = f32x16_t{};
       }
 
-    // fragment addresses inside a stage buffer
-    const int frag_k = (lane >> 5) * 8 * esz;
-    int a_frag[2], b_frag[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) a_frag[mb] = (wm * 64 + mb * 32 + (lane & 31)) * GPITCH + frag_k;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int brow = MODE == MODE_GATE_UP ? nb * 64 + wn * 32 : wn * 64 + nb * 32;
-      b_frag[nb] = (brow + (lane & 31)) * GPITCH + frag_k;
-    }
-
-    __syncthreads();  // the previous tile's last reads of both buffers are done
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    for (int ks = 0; ks < nk; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < nk) load_stage(ks + 1);
+    auto b_frag_row = [](int nb) constexpr -> int {
+      return MODE == MODE_GATE_UP ? (nb >> 1) * (GBN / 2) + (nb & 1) * 32 : nb * 32;
+    };
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        Frag<CT> fa[2], fb[2];
+        Frag<CT> fa[2], fb[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) fa[mb].load(&lds_a[cur][a_frag[mb] + s * 16 * esz]);
+        for (int mb = 0; mb < 2; ++mb) fa[mb].load(&lds_a[buf][a_frag + mb * 32 * GPITCH + s * 16 * esz]);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) fb[nb].load(&lds_b[cur][b_frag[nb] + s * 16 * esz]);
+        for (int nb = 0; nb < 4; ++nb) fb[nb].load(&lds_b[buf][b_frag + b_frag_row(nb) * GPITCH + s * 16 * esz]);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
+          for (int nb = 0; nb < 4; ++nb) {
             if (kScaled)
               part[mb][nb] = mma(fa[mb], fb[nb], part[mb][nb]);
             else
               acc[mb][nb] = mma(fa[mb], fb[nb], acc[mb][nb]);
           }
       }
-      if (kScaled && ((ks + 1) % kStagesPerBlock == 0)) {
+    };
+    auto apply_scales = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int brow = MODE == MODE_GATE_UP ? nb * 64 + wn * 32 : wn * 64 + nb * 32;
-          const float sb = lds_sb[cur][brow + (lane & 31)];
+      for (int nb = 0; nb < 4; ++nb) {
+        const int brow = (MODE == MODE_GATE_UP ? wn * 64 : wn * 128) + b_frag_row(nb);
+        const float sb = lds_sb[buf][brow + (lane & 31)];
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float sc = sb;
-              if (CT == CT_FP8) {
-                const int r = wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                sc = lds_sa[cur][r] * sb;
-              }
-              acc[mb][nb][v] += part[mb][nb][v] * sc;
-              part[mb][nb][v] = 0.0f;
-            }
+          for (int v = 0; v < 16; ++v) {
+            float sc = sb;
+            if (CT == CT_FP8) sc = lds_sa[buf][wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] * sb;
+            acc[mb][nb][v] += part[mb][nb][v] * sc;
+            part[mb][nb][v] = 0.0f;
           }
         }
       }
-      if (ks + 1 < nk) store_stage(cur ^ 1);
+    };
+
+    __syncthreads();  // the previous tile's last reads of both LDS buffers are done
+    if (!kScaled) {
+      // two stages of global loads in flight: stage ks in LDS buffer ks & 1, stages ks+1
+      // and ks+2 in registers
+      Regs r0, r1;
+      issue(r0, 0);
+      if (nk > 1) issue(r1, 1);
+      commit(r0, 0);
       __syncthreads();
+      for (int ks = 0; ks < nk; ks += 2) {
+        if (ks + 2 < nk) issue(r0, ks + 2);
+        compute(0);
+        if (ks + 1 < nk) commit(r1, 1);
+        __syncthreads();
+        if (ks + 1 >= nk) break;
+        if (ks + 3 < nk) issue(r1, ks + 3);
+        compute(1);
+        if (ks + 2 < nk) commit(r0, 0);
+        __syncthreads();
+      }
+    } else {
+      // one stage in flight (the scaled variants hold a second set of accumulators)
+      Regs r0;
+      issue(r0, 0);
+      commit(r0, 0);
+      __syncthreads();
+      for (int ks = 0; ks < nk; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < nk) issue(r0, ks + 1);
+        compute(cur);
+        if ((ks + 1) % kStagesPerBlock == 0) apply_scales(cur);
+        if (ks + 1 < nk) commit(r0, cur ^ 1);
+        __syncthreads();
+      }
     }
 
     // ---- epilogue
+    const int mend = seg_hi;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -332,16 +366,22 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs p) {
         const int r = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= mend) continue;
         if (MODE == MODE_GATE_UP) {
-          const float g = acc[mb][0][v];
-          const float u = acc[mb][1][v];
-          const float hv = g / (1.0f + expf(-g)) * u;
-          const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * 64 + wn * 32 + (lane & 31);
-          if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
-          else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(hv);
-        } else {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            const size_t o = static_cast<size_t>(r) * p.n_out + static_cast<size_t>(nblk) * GBN + wn * 64 + nb * 32 + (lane & 31);
+            const float g = acc[mb][nb][v];
+            const float u = acc[mb][nb + 2][v];
+            const float hv = g / (1.0f + expf(-g)) * u;
+            const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * (GBN / 2) + wn * 64 +
+                             nb * 32 + (lane & 31);
+            if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
+            else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(hv);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int col = nblk * GBN + wn * 128 + nb * 32 + (lane & 31);
+            if (col >= p.n_out) continue;
+            const size_t o = static_cast<size_t>(r) * p.n_out + col;
             if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = acc[mb][nb][v];
             else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[mb][nb][v]);
           }
@@ -359,8 +399,8 @@ size_t gemm_schedule_bytes(int rows, int E) {
 }
 
 static int persistent_grid() {
-  // 256 CUs x 2 resident workgroups; a multiple of the 8 XCDs
-  return 512;
+  // one workgroup per CU (256 CUs); a multiple of the 8 XCDs
+  return 256;
 }
 
 hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,

@@ -1,0 +1,194 @@
+"""Whole-layer GPU parity: route -> layout -> permute -> grouped FFN (+ shared) -> combine.
+
+Small versions of the five workloads are compared element by element at every
+intermediate.  At the workloads' full sizes (in the launch configuration the
+benchmark times) the routing and layout arrays and the permuted payload are
+compared in full, bit for bit; h and the expert outputs on every row of a few
+sampled experts (largest, smallest non-empty, one more); y and the shared
+expert on sampled tokens, each computed one by one by the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workload as w
+from combine_grouped_gemm_amd.layer import MoELayer
+from oracle import moe_oracle as oracle
+from tests.gpu_util import f64, say, sync, token_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+# per-token relative error bars on y (max over tokens of ||dy_t||_inf / ||y_t||_inf)
+Y_BAR = {"f32": 2e-2, "bf16": 2e-2, "fp8": 6e-2}
+# tighter bars expected from the arithmetic: fp32 end to end; bf16 rounding of h,
+# the expert outputs and y (3 roundings of 2^-9 relative, on the row's scale)
+Y_EXPECT = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+GEMM_BAR = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+
+SMALL = {
+    "tiny_f32": w.CONFIGS["tiny_f32"],
+    "mixtral_small": w.CONFIGS["mixtral_bf16"].scaled(N=512, H=1024, I=1024),
+    "dsv3_small": w.CONFIGS["dsv3_bf16"].scaled(N=512, H=1024, E=64, I=256),
+    "dsv3_zipf_small": w.CONFIGS["dsv3_zipf_bf16"].scaled(N=512, H=1024, E=64, I=256),
+    "decode_fp8_small": w.CONFIGS["decode_fp8"].scaled(N=64, H=1024, E=64, I=256),
+}
+
+
+def _quantize_rows(a):
+    """Oracle quantization of a float32 matrix, 512 rows at a time (same result as whole)."""
+    qs, ss = [], []
+    for r in range(0, a.shape[0], 512):
+        q, s = oracle.quantize_blocks(a[r:r + 512])
+        qs.append(q)
+        ss.append(s)
+    return np.concatenate(qs), np.concatenate(ss)
+
+
+class OracleWeights:
+    """Expert weights for the oracle, copied from the generator's device tensors on demand.
+
+    bf16/f32 layers: float64 values.  fp8 layers: the oracle's own quantization
+    of the same bf16 values, dequantized to float64.
+    """
+
+    def __init__(self, w13, w2, fp8):
+        self.w13, self.w2, self.fp8 = w13, w2, fp8
+        self.c13, self.c2 = {}, {}
+
+    def _get(self, t, e, cache):
+        if e not in cache:
+            a = t[e].detach().cpu().to(torch.float32).numpy()
+            cache[e] = oracle.dequantize_blocks(*_quantize_rows(a)) if self.fp8 else a.astype(np.float64)
+        return cache[e]
+
+    def g13(self, e):
+        return self._get(self.w13, e, self.c13)
+
+    def g2(self, e):
+        return self._get(self.w2, e, self.c2)
+
+
+def _build(cfg):
+    say(f"layer {cfg.name} N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} {cfg.dtype}")
+    inp = w.make_layer_inputs(cfg, DEV)
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"])
+    y = layer.forward(inp["x"], inp["z"])
+    sync()
+    return inp, layer, y
+
+
+def _check_routing(cfg, inp, layer):
+    b = inp["bias_cpu"]
+    ridx, rgate = oracle.route(inp["z_cpu"].numpy(), cfg.k, None if b is None else b.numpy(),
+                               cfg.n_group, cfg.topk_group)
+    assert np.array_equal(layer.topk_idx.cpu().numpy(), ridx)
+    assert np.abs(layer.topk_gate.cpu().numpy().astype(np.float64) - rgate).max() <= 1e-6
+    lay = oracle.dispatch_layout(ridx, cfg.E)
+    for got, ref in zip(layer.layout, lay):
+        assert np.array_equal(got.cpu().numpy(), ref)
+    return ridx, rgate, lay
+
+
+def _check_permute(cfg, inp, layer, send_pos):
+    """Bit-exact permuted payload; returns the oracle's permuted rows as float64 values."""
+    x = inp["x"].cpu()
+    if cfg.dtype == "fp8":
+        q, s = _quantize_rows(x.to(torch.float32).numpy())
+        pq, ps = oracle.permute(q, send_pos, cfg.k), oracle.permute(s, send_pos, cfg.k)
+        assert np.array_equal(layer.x_perm.cpu().numpy(), pq)
+        assert np.array_equal(layer.x_perm_scale.cpu().numpy(), ps)
+        return None, (q, s)
+    view = torch.int32 if cfg.dtype == "f32" else torch.int16
+    assert np.array_equal(layer.x_perm.cpu().view(view).numpy(), oracle.permute(x.view(view).numpy(), send_pos, cfg.k))
+    return x.to(torch.float64).numpy(), None
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small_all_intermediates(name):
+    cfg = SMALL[name]
+    inp, layer, y = _build(cfg)
+    ridx, rgate, (n_e, off, sp, ss) = _check_routing(cfg, inp, layer)
+    xs, _ = _check_permute(cfg, inp, layer, sp)
+    ow = OracleWeights(inp["w13"], inp["w2"], cfg.dtype == "fp8")
+    kw = {}
+    if cfg.shared:
+        kw = dict(shared_w13=f64(inp["sw13"][0]), shared_w2=f64(inp["sw2"][0]))
+    if cfg.dtype == "fp8":
+        ref = oracle.moe_layer(inp["x"].cpu().to(torch.float32).numpy(), inp["z_cpu"].numpy(), cfg.k,
+                               lambda e: _quantize_rows(inp["w13"][e].cpu().float().numpy())[0],
+                               lambda e: _quantize_rows(inp["w2"][e].cpu().float().numpy())[0],
+                               bias=None, n_group=cfg.n_group, topk_group=cfg.topk_group, fp8=True,
+                               w13_scale=lambda e: _quantize_rows(inp["w13"][e].cpu().float().numpy())[1],
+                               w2_scale=lambda e: _quantize_rows(inp["w2"][e].cpu().float().numpy())[1], **kw)
+    else:
+        b = inp["bias_cpu"]
+        ref = oracle.moe_layer(xs, inp["z_cpu"].numpy(), cfg.k, ow.g13, ow.g2,
+                               bias=None if b is None else b.numpy(), n_group=cfg.n_group,
+                               topk_group=cfg.topk_group, **kw)
+    assert np.array_equal(ref["topk_idx"], ridx)
+    valid = ref["h"].shape[1] > 0
+    if valid:
+        assert token_rel_err(f64(layer.h), ref["h"]) <= GEMM_BAR[cfg.dtype]
+        assert token_rel_err(f64(layer.expert_out), ref["expert_out"]) <= GEMM_BAR[cfg.dtype]
+    if cfg.shared:
+        assert token_rel_err(f64(layer.shared_out), ref["shared_out"]) <= GEMM_BAR[cfg.dtype]
+    err = token_rel_err(f64(y), ref["y"])
+    say(f"  y max per-token relative error {err:.3e}, imbalance {ref['imbalance']:.3f}")
+    assert err <= Y_BAR[cfg.dtype]
+    assert err <= Y_EXPECT[cfg.dtype]
+
+
+FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
+SAMPLE_TOKENS = {"mixtral_bf16": 8, "dsv3_bf16": 4, "dsv3_zipf_bf16": 4, "decode_fp8": 2}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size_sampled(name):
+    cfg = w.CONFIGS[name]
+    inp, layer, y = _build(cfg)
+    ridx, rgate, (n_e, off, sp, ss) = _check_routing(cfg, inp, layer)
+    say(f"  routing + layout bit-exact; imbalance {oracle.imbalance(n_e):.3f}, "
+        f"max n_e {n_e.max()}, empty experts {(n_e == 0).sum()}")
+    xs, xq = _check_permute(cfg, inp, layer, sp)
+    say("  permuted payload bit-exact")
+    fp8 = cfg.dtype == "fp8"
+    ow = OracleWeights(inp["w13"], inp["w2"], fp8)
+
+    def a_rows(rows):  # the oracle's permuted activation rows (float64 values)
+        toks = ss[rows] // cfg.k
+        if fp8:
+            q, s = xq
+            return oracle.dequantize_blocks(q[toks], s[toks])
+        return xs[toks]
+
+    # every row of a few experts: the largest, the smallest non-empty and one more
+    nz = np.nonzero(n_e)[0]
+    experts = sorted({int(nz[np.argmax(n_e[nz])]), int(nz[np.argmin(n_e[nz])]), int(nz[len(nz) // 2])})
+    h_gpu, eo_gpu = layer.h, layer.expert_out
+    for e in experts:
+        rows = np.arange(off[e], off[e + 1])
+        rh, ro = oracle.expert_ffn(a_rows(rows), ow.g13(e), ow.g2(e))
+        assert token_rel_err(f64(h_gpu[off[e]:off[e + 1]]), rh) <= GEMM_BAR[cfg.dtype]
+        assert token_rel_err(f64(eo_gpu[off[e]:off[e + 1]]), ro) <= GEMM_BAR[cfg.dtype]
+    say(f"  grouped GEMMs match on experts {experts} (n_e {[int(n_e[e]) for e in experts]})")
+
+    # y on sampled tokens: y_t = sum_j g_tj Expert_{I_t[j]}(x_t) (+ shared), by the oracle
+    S = SAMPLE_TOKENS[name]
+    toks = np.linspace(0, cfg.N - 1, S).astype(np.int64)
+    eo_s = np.zeros((S * cfg.k, cfg.H))
+    for i, t in enumerate(toks):
+        for j in range(cfg.k):
+            e = int(ridx[t, j])
+            slot = int(sp[t * cfg.k + j])
+            _, eo_s[i * cfg.k + j] = oracle.expert_ffn(a_rows(np.array([slot])), ow.g13(e), ow.g2(e))
+    sh = None
+    if cfg.shared:
+        _, sh = oracle.expert_ffn(xs[toks], f64(inp["sw13"][0]), f64(inp["sw2"][0]))
+        assert token_rel_err(f64(layer.shared_out[torch.from_numpy(toks).to(DEV)]), sh) <= GEMM_BAR[cfg.dtype]
+    ref = oracle.combine(eo_s, np.arange(S * cfg.k), rgate[toks], cfg.k, sh)
+    err = token_rel_err(f64(y[torch.from_numpy(toks).to(DEV)]), ref)
+    say(f"  y on tokens {toks.tolist()}: max per-token relative error {err:.3e}")
+    assert err <= Y_BAR[cfg.dtype]
+    assert err <= Y_EXPECT[cfg.dtype]
