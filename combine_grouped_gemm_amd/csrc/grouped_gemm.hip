@@ -391,6 +391,237 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Unscaled bf16 / fp32 variant with direct-to-LDS loads.
+//
+// global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS at
+// base + 16 * lane, so a stage needs no staging registers and three stages fit in LDS:
+// stage ks+2 is loading while stage ks is multiplied.  One wave instruction fills one
+// 1 KiB group of 8 tile rows (128 bytes each); groups are 1040 bytes apart, and inside a
+// group the 16-byte chunk c of row r sits in slot c ^ (r & 7), so the fragment reads of 8
+// (and of 16) consecutive rows hit distinct banks.  The wait for a stage is explicit
+// (s_waitcnt vmcnt) followed by a plain s_barrier, which keeps the two later stages in
+// flight across the barrier.
+// ------------------------------------------------------------------------------------
+
+constexpr int kGroupBytes = 1040;                       // 8 rows x 128 B + 16 B gap
+constexpr int kAGroups = GBM / 8;                       // 16
+constexpr int kBGroups = GBN / 8;                       // 32
+constexpr int kStageBytesDma = (kAGroups + kBGroups) * kGroupBytes;  // 49920
+constexpr int kDmaStages = 3;
+constexpr int kDmaPerStage = (kAGroups + kBGroups) / 4;  // DMA instructions per wave and stage (12)
+
+__device__ __forceinline__ void wait_vmcnt_dma_stage() {
+  // vmcnt <= kDmaPerStage: every load older than the newest stage has landed
+  static_assert(kDmaPerStage == 12, "s_waitcnt immediate below assumes 12 loads per stage");
+  __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory");
+}
+__device__ __forceinline__ void wait_vmcnt_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane.  Issued as
+// inline assembly so that the compiler adds no wait of its own before later LDS reads;
+// every wait for these loads is the explicit s_waitcnt above.  M0 holds the LDS base;
+// one wait state separates its write from the load that reads it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  __asm__ volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "s"(lds_base)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void block_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+
+template <int CT, int MODE>
+__global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs p) {
+  constexpr int esz = CTraits<CT>::esz;
+  constexpr int BK = GKB / esz;                 // K elements per stage
+  constexpr int KSTEPS = BK / 16;               // 16-wide MFMA steps per stage
+  static_assert(CT != CT_FP8, "fp8 layers use the scaled kernel");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * kStageBytesDma];
+  const uint32_t lds_addr0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l7 = lane & 7;
+  const int lrow = lane >> 3;                  // row inside a DMA group
+  const int lchunk = (lane & 7) ^ lrow;        // global chunk this lane loads
+
+  const int nN = MODE == MODE_GATE_UP ? p.I / (GBN / 2) : (p.n_out + GBN - 1) / GBN;
+  const long long total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int slot = blockIdx.x / kNumXcd;
+  const int per_xcd = gridDim.x / kNumXcd;
+  const long long t_beg = total * xcd / kNumXcd;
+  const long long t_end = total * (xcd + 1) / kNumXcd;
+
+  const int nk = p.K / BK;
+  const uint32_t a_rb = static_cast<uint32_t>(p.K) * esz;
+  const uint32_t b_rb = a_rb;
+
+  // fragment rows (tile coordinates) and their byte offsets inside an operand region
+  auto row_addr = [](int r) { return (r >> 3) * kGroupBytes + (r & 7) * 128; };
+  int a_frag[2], b_frag[4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) a_frag[mb] = row_addr(wm * 64 + mb * 32 + (lane & 31));
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int r = MODE == MODE_GATE_UP ? (nb >> 1) * (GBN / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31)
+                                       : wn * 128 + nb * 32 + (lane & 31);
+    b_frag[nb] = row_addr(r) + kAGroups * kGroupBytes;
+  }
+  // swizzled chunk offsets of each k-step: chunk (c ^ (row & 7)), row & 7 == lane & 7
+  const int h = lane >> 5;
+  int koff[KSTEPS][2];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    if (CT == CT_F32) {
+      koff[s][0] = ((4 * s + 2 * h) ^ l7) * 16;
+      koff[s][1] = ((4 * s + 2 * h + 1) ^ l7) * 16;
+    } else {
+      koff[s][0] = ((2 * s + h) ^ l7) * 16;
+      koff[s][1] = 0;
+    }
+  }
+
+  for (long long L = t_beg + slot; L < t_end; L += per_xcd) {
+    const int e = p.tile_expert[L / nN];
+    const int pe = p.tile_prefix[e];
+    const int mt_e = p.tile_prefix[e + 1] - pe;
+    const long long local = L - static_cast<long long>(pe) * nN;
+    const int nblk = static_cast<int>(local / mt_e);
+    const int mtile = static_cast<int>(local % mt_e);
+    int seg_lo = p.offsets[e], seg_hi = p.offsets[e + 1];
+    seg_lo = seg_lo < 0 ? 0 : (seg_lo > p.rows ? p.rows : seg_lo);
+    seg_hi = seg_hi < seg_lo ? seg_lo : (seg_hi > p.rows ? p.rows : seg_hi);
+    const int m0 = seg_lo + mtile * GBM;
+    const int mlast = seg_hi - 1 - m0;
+
+    const uint8_t* a_tile = p.a + static_cast<size_t>(m0) * a_rb;
+    const long long b_row0 = MODE == MODE_GATE_UP ? static_cast<long long>(nblk) * (GBN / 2)
+                                                  : static_cast<long long>(nblk) * GBN;
+    const uint8_t* b_tile = p.b + (static_cast<size_t>(e) * p.b_rows + b_row0) * b_rb;
+    const int b_rows_left = MODE == MODE_GATE_UP ? GBN : static_cast<int>(p.n_out - b_row0);
+
+    // this lane's source offsets (32-bit, relative to the tile bases) for its DMA groups:
+    // wave w loads A groups w, w+4, .. and B groups w, w+4, ..
+    uint32_t a_src[kAGroups / 4], b_src[kBGroups / 4];
+#pragma unroll
+    for (int i = 0; i < kAGroups / 4; ++i) {
+      int r = (wave + 4 * i) * 8 + lrow;
+      r = r < mlast ? r : mlast;
+      a_src[i] = static_cast<uint32_t>(r) * a_rb + lchunk * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < kBGroups / 4; ++i) {
+      const int r = (wave + 4 * i) * 8 + lrow;
+      uint32_t wr;
+      if (MODE == MODE_GATE_UP) wr = r < GBN / 2 ? r : static_cast<uint32_t>(p.I) + (r - GBN / 2);
+      else wr = r < b_rows_left ? r : b_rows_left - 1;
+      b_src[i] = wr * b_rb + lchunk * 16;
+    }
+
+    auto issue = [&](int ks, int buf) __attribute__((always_inline)) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          lds_addr0 + static_cast<uint32_t>(buf * kStageBytesDma + wave * kGroupBytes));
+      const uint8_t* ab = a_tile + static_cast<size_t>(ks) * GKB;
+      const uint8_t* bb = b_tile + static_cast<size_t>(ks) * GKB;
+#pragma unroll
+      for (int i = 0; i < kAGroups / 4; ++i) dma16(ab + a_src[i], base + 4 * i * kGroupBytes);
+#pragma unroll
+      for (int i = 0; i < kBGroups / 4; ++i) dma16(bb + b_src[i], base + (kAGroups + 4 * i) * kGroupBytes);
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+      const uint8_t* base = lds + buf * kStageBytesDma;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        Frag<CT> fa[2], fb[4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if constexpr (CT == CT_F32) {
+            fa[mb].v0 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][0]);
+            fa[mb].v1 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][1]);
+          } else {
+            fa[mb].load(base + a_frag[mb] + koff[s][0]);
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          if constexpr (CT == CT_F32) {
+            fb[nb].v0 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][0]);
+            fb[nb].v1 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][1]);
+          } else {
+            fb[nb].load(base + b_frag[nb] + koff[s][0]);
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma(fa[mb], fb[nb], acc[mb][nb]);
+      }
+    };
+
+    // the previous tile's epilogue stores and LDS reads are finished before reuse
+    wait_vmcnt_all();
+    block_barrier();
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    int buf = 0;
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) wait_vmcnt_dma_stage();
+      else wait_vmcnt_all();
+      block_barrier();  // stage ks landed for every wave; stage ks-1's buffer is free
+      if (ks + 2 < nk) issue(ks + 2, buf == 0 ? 2 : buf - 1);
+      compute(buf);
+      buf = buf == 2 ? 0 : buf + 1;
+    }
+
+    const int mend = seg_hi;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r >= mend) continue;
+        if (MODE == MODE_GATE_UP) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const float g = acc[mb][nb][v];
+            const float u = acc[mb][nb + 2][v];
+            const float hv = g / (1.0f + expf(-g)) * u;
+            const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * (GBN / 2) + wn * 64 +
+                             nb * 32 + (lane & 31);
+            if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
+            else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(hv);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int col = nblk * GBN + wn * 128 + nb * 32 + (lane & 31);
+            if (col >= p.n_out) continue;
+            const size_t o = static_cast<size_t>(r) * p.n_out + col;
+            if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = acc[mb][nb][v];
+            else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[mb][nb][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
 size_t gemm_tile_cap(int rows, int E) { return static_cast<size_t>((rows + GBM - 1) / GBM) + E; }
 
 size_t gemm_schedule_bytes(int rows, int E) {
@@ -432,15 +663,18 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)
+#define MOE_LAUNCH_DMA(CT_, MODE_) \
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<CT_, MODE_>), grid, block, 0, s, p)
   if (mode == MODE_GATE_UP) {
-    if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_GATE_UP);
-    else if (ct == CT_BF16) MOE_LAUNCH(CT_BF16, false, MODE_GATE_UP);
+    if (ct == CT_F32) MOE_LAUNCH_DMA(CT_F32, MODE_GATE_UP);
+    else if (ct == CT_BF16) MOE_LAUNCH_DMA(CT_BF16, MODE_GATE_UP);
     else MOE_LAUNCH(CT_FP8, false, MODE_GATE_UP);
   } else {
-    if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_DOWN);
+    if (ct == CT_F32) MOE_LAUNCH_DMA(CT_F32, MODE_DOWN);
     else if (b8) MOE_LAUNCH(CT_BF16, true, MODE_DOWN);
-    else MOE_LAUNCH(CT_BF16, false, MODE_DOWN);
+    else MOE_LAUNCH_DMA(CT_BF16, MODE_DOWN);
   }
+#undef MOE_LAUNCH_DMA
 #undef MOE_LAUNCH
   return hipGetLastError();
 }
