@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--config", default="dsv3_bf16")
     p.add_argument("--cpu-tokens", type=int, default=16,
                    help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -158,6 +160,17 @@ def main():
     def step():
         for _, f in stages:
             f()
+
+    if args.copy_probe_mib > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch scale the
+        # byte counters read for the MoE kernels
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log(args, f"warmup {args.warmup}")
     for _ in range(args.warmup):

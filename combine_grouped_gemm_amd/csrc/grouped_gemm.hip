@@ -544,33 +544,43 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
+    // fragments of the next k-step are read from LDS while the current step's MFMAs run
+    auto load_frags = [&](const uint8_t* base, int s, Frag<CT> (&fa)[2], Frag<CT> (&fb)[4])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if constexpr (CT == CT_F32) {
+          fa[mb].v0 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][0]);
+          fa[mb].v1 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][1]);
+        } else {
+          fa[mb].load(base + a_frag[mb] + koff[s][0]);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if constexpr (CT == CT_F32) {
+          fb[nb].v0 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][0]);
+          fb[nb].v1 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][1]);
+        } else {
+          fb[nb].load(base + b_frag[nb] + koff[s][0]);
+        }
+      }
+    };
     auto compute = [&](int buf) __attribute__((always_inline)) {
       const uint8_t* base = lds + buf * kStageBytesDma;
+      Frag<CT> fa[2][2], fb[2][4];
+      load_frags(base, 0, fa[0], fb[0]);
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        Frag<CT> fa[2], fb[4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          if constexpr (CT == CT_F32) {
-            fa[mb].v0 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][0]);
-            fa[mb].v1 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][1]);
-          } else {
-            fa[mb].load(base + a_frag[mb] + koff[s][0]);
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          if constexpr (CT == CT_F32) {
-            fb[nb].v0 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][0]);
-            fb[nb].v1 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][1]);
-          } else {
-            fb[nb].load(base + b_frag[nb] + koff[s][0]);
-          }
-        }
+        // the next step's reads are issued before this step's MFMAs (scheduling fences keep
+        // the order, so both fragment sets are live and the reads overlap the MFMAs)
+        if (s + 1 < KSTEPS) load_frags(base, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma(fa[mb], fb[nb], acc[mb][nb]);
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma(fa[s & 1][mb], fb[s & 1][nb], acc[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
