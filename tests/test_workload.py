@@ -65,3 +65,13 @@ def test_fixed_routes_have_distinct_experts():
         idx = w.fixed_route(300, 16, 5, kind).numpy()
         assert idx.shape == (300, 5) and idx.dtype == np.int32
         assert all(len(set(row)) == 5 for row in idx.tolist())
+
+
+def test_batched_expert_generation_matches_per_expert_streams():
+    cfg = w.CONFIGS["dsv3_bf16"].scaled(E=5, H=256, I=128)
+    a13, a2 = w.all_expert_weights(cfg, "cpu")
+    b13 = w._normal_streams([w.stream_key(cfg.seed, w.T_W13, e) for e in range(5)], (256, 256), "cpu",
+                            torch.bfloat16)
+    b2 = w._normal_streams([w.stream_key(cfg.seed, w.T_W2, e) for e in range(5)], (256, 128), "cpu",
+                           torch.bfloat16)
+    assert torch.equal(a13, b13) and torch.equal(a2, b2)

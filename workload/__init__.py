@@ -259,15 +259,42 @@ def expert_w2(cfg: MoEConfig, e: int, device="cpu", dtype=None, shared: bool = F
                   dtype or storage_dtype(cfg))
 
 
+def _normal_streams(keys, shape, device, dtype, std: float = WEIGHT_STD) -> torch.Tensor:
+    """[len(keys), *shape]: stream b is exactly ``normal(shape, keys[b])``, made in one pass."""
+    numel = int(np.prod(shape))
+    dev = torch.device(device)
+    k1 = torch.tensor([k & _M32 for k in keys], dtype=torch.int64, device=dev)[:, None]
+    k2 = torch.tensor([(k * 0x9E3779B1) & _M32 for k in keys], dtype=torch.int64, device=dev)[:, None]
+    i = torch.arange(numel, dtype=torch.int64, device=dev)[None, :]
+    h = _mix32(_mix32(i ^ k1) ^ k2)
+    vals = _table_on(dev, std)[h >> (32 - _TABLE_BITS)]
+    return vals.reshape((len(keys),) + tuple(shape)).to(dtype)
+
+
 def all_expert_weights(cfg: MoEConfig, device="cpu", shared: bool = False):
-    """(w13 [E, 2I, H], w2 [E, H, I]) in the storage dtype, generated expert by expert."""
+    """(w13 [E, 2I, H], w2 [E, H, I]) in the storage dtype.
+
+    Expert e's matrices are the streams ``expert_w13(cfg, e)`` / ``expert_w2(cfg, e)``;
+    off the CPU several experts are generated per pass (about 2^27 elements at a time),
+    which gives the same values with a few hundred launches instead of tens of thousands.
+    """
     E = 1 if shared else cfg.E
     dt = storage_dtype(cfg)
     w13 = torch.empty((E, 2 * cfg.I, cfg.H), dtype=dt, device=device)
     w2 = torch.empty((E, cfg.H, cfg.I), dtype=dt, device=device)
-    for e in range(E):
-        w13[e] = expert_w13(cfg, e, device, dt, shared)
-        w2[e] = expert_w2(cfg, e, device, dt, shared)
+    if torch.device(device).type == "cpu":
+        for e in range(E):
+            w13[e] = expert_w13(cfg, e, device, dt, shared)
+            w2[e] = expert_w2(cfg, e, device, dt, shared)
+        return w13, w2
+    t13, t2 = (T_SW13, T_SW2) if shared else (T_W13, T_W2)
+    per = max(1, (1 << 27) // (2 * cfg.I * cfg.H))
+    for e0 in range(0, E, per):
+        es = list(range(e0, min(E, e0 + per)))
+        w13[e0:e0 + len(es)] = _normal_streams([stream_key(cfg.seed, t13, e) for e in es],
+                                               (2 * cfg.I, cfg.H), device, dt)
+        w2[e0:e0 + len(es)] = _normal_streams([stream_key(cfg.seed, t2, e) for e in es],
+                                              (cfg.H, cfg.I), device, dt)
     return w13, w2
 
 
