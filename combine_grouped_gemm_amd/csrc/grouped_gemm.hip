@@ -397,17 +397,18 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
 // global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS at
 // base + 16 * lane, so a stage needs no staging registers and three stages fit in LDS:
 // stage ks+2 is loading while stage ks is multiplied.  One wave instruction fills one
-// 1 KiB group of 8 tile rows (128 bytes each); groups are 1040 bytes apart, and inside a
-// group the 16-byte chunk c of row r sits in slot c ^ (r & 7), so the fragment reads of 8
-// (and of 16) consecutive rows hit distinct banks.  The wait for a stage is explicit
+// 1 KiB group of 8 tile rows (128 bytes each).  The 16-byte chunk c of row r sits in slot
+// c ^ (r & 7) ^ ((r >> 3) & 1): the LDS serves a 16-byte-per-lane read 16 lanes at a time
+// from 64 four-byte banks, and with this key any 16 consecutive rows of one chunk land in
+// 16 distinct 16-byte bank slots (the 8-row key alone repeats every 8 rows).  The wait for a stage is explicit
 // (s_waitcnt vmcnt) followed by a plain s_barrier, which keeps the two later stages in
 // flight across the barrier.
 // ------------------------------------------------------------------------------------
 
-constexpr int kGroupBytes = 1040;                       // 8 rows x 128 B + 16 B gap
+constexpr int kGroupBytes = 1024;                       // 8 rows x 128 B
 constexpr int kAGroups = GBM / 8;                       // 16
 constexpr int kBGroups = GBN / 8;                       // 32
-constexpr int kStageBytesDma = (kAGroups + kBGroups) * kGroupBytes;  // 49920
+constexpr int kStageBytesDma = (kAGroups + kBGroups) * kGroupBytes;  // 49152
 constexpr int kDmaStages = 3;
 constexpr int kDmaPerStage = (kAGroups + kBGroups) / 4;  // DMA instructions per wave and stage (12)
 
@@ -417,6 +418,10 @@ __device__ __forceinline__ void wait_vmcnt_dma_stage() {
   __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory");
 }
 __device__ __forceinline__ void wait_vmcnt_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_2stages() { __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory"); }
+// lgkmcnt(0) with vmcnt and expcnt left at their maxima; as a builtin (not inline asm)
+// the compiler sees that every earlier LDS read has completed
+__device__ __forceinline__ void wait_lgkmcnt_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 typedef __attribute__((address_space(3))) uint8_t lds_byte;
 
@@ -441,6 +446,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
   constexpr int BK = GKB / esz;                 // K elements per stage
   constexpr int KSTEPS = BK / 16;               // 16-wide MFMA steps per stage
   static_assert(CT != CT_FP8, "fp8 layers use the scaled kernel");
+  static_assert(KSTEPS % 2 == 0, "a stage must end in fragment set 1 so the next starts in set 0");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * kStageBytesDma];
   const uint32_t lds_addr0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
@@ -451,7 +457,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
   const int wm = wave & 1, wn = wave >> 1;
   const int l7 = lane & 7;
   const int lrow = lane >> 3;                  // row inside a DMA group
-  const int lchunk = (lane & 7) ^ lrow;        // global chunk this lane loads
+  // global chunk this lane loads: the slot it fills is lane & 7, the row's key is
+  // lrow ^ (group & 1), and every group this wave fills has parity wave & 1
+  const int lchunk = (lane & 7) ^ lrow ^ (wave & 1);
 
   const int nN = MODE == MODE_GATE_UP ? p.I / (GBN / 2) : (p.n_out + GBN - 1) / GBN;
   const long long total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
   const uint32_t b_rb = a_rb;
 
   // fragment rows (tile coordinates) and their byte offsets inside an operand region
-  auto row_addr = [](int r) { return (r >> 3) * kGroupBytes + (r & 7) * 128; };
+  auto row_addr = [](int r) { return r * 128; };
   int a_frag[2], b_frag[4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) a_frag[mb] = row_addr(wm * 64 + mb * 32 + (lane & 31));
@@ -476,16 +484,18 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
                                        : wn * 128 + nb * 32 + (lane & 31);
     b_frag[nb] = row_addr(r) + kAGroups * kGroupBytes;
   }
-  // swizzled chunk offsets of each k-step: chunk (c ^ (row & 7)), row & 7 == lane & 7
+  // swizzled chunk offsets of each k-step; fragment rows start at multiples of 32, so a
+  // row's key (row & 7) ^ ((row >> 3) & 1) is the lane's
   const int h = lane >> 5;
+  const int key = l7 ^ ((lane >> 3) & 1);
   int koff[KSTEPS][2];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     if (CT == CT_F32) {
-      koff[s][0] = ((4 * s + 2 * h) ^ l7) * 16;
-      koff[s][1] = ((4 * s + 2 * h + 1) ^ l7) * 16;
+      koff[s][0] = ((4 * s + 2 * h) ^ key) * 16;
+      koff[s][1] = ((4 * s + 2 * h + 1) ^ key) * 16;
     } else {
-      koff[s][0] = ((2 * s + h) ^ l7) * 16;
+      koff[s][0] = ((2 * s + h) ^ key) * 16;
       koff[s][1] = 0;
     }
   }
@@ -527,15 +537,19 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
       b_src[i] = wr * b_rb + lchunk * 16;
     }
 
-    auto issue = [&](int ks, int buf) __attribute__((always_inline)) {
+    // DMA of stage ks into LDS buffer buf: this wave's 12 group loads, issued in slices so
+    // they can sit between MFMAs
+    auto dma_slice = [&](int ks, int buf, int first, int count) __attribute__((always_inline)) {
       const uint32_t base = __builtin_amdgcn_readfirstlane(
           lds_addr0 + static_cast<uint32_t>(buf * kStageBytesDma + wave * kGroupBytes));
       const uint8_t* ab = a_tile + static_cast<size_t>(ks) * GKB;
       const uint8_t* bb = b_tile + static_cast<size_t>(ks) * GKB;
 #pragma unroll
-      for (int i = 0; i < kAGroups / 4; ++i) dma16(ab + a_src[i], base + 4 * i * kGroupBytes);
-#pragma unroll
-      for (int i = 0; i < kBGroups / 4; ++i) dma16(bb + b_src[i], base + (kAGroups + 4 * i) * kGroupBytes);
+      for (int j = 0; j < kDmaPerStage; ++j) {
+        if (j < first || j >= first + count) continue;
+        if (j < kAGroups / 4) dma16(ab + a_src[j], base + 4 * j * kGroupBytes);
+        else dma16(bb + b_src[j - kAGroups / 4], base + (kAGroups + 4 * (j - kAGroups / 4)) * kGroupBytes);
+      }
     };
 
     f32x16_t acc[2][4];
@@ -544,9 +558,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-    // fragments of the next k-step are read from LDS while the current step's MFMAs run
-    auto load_frags = [&](const uint8_t* base, int s, Frag<CT> (&fa)[2], Frag<CT> (&fb)[4])
+    auto load_frags = [&](int buf, int s, Frag<CT> (&fa)[2], Frag<CT> (&fb)[4])
         __attribute__((always_inline)) {
+      const uint8_t* base = lds + buf * kStageBytesDma;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if constexpr (CT == CT_F32) {
@@ -566,39 +580,68 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
         }
       }
     };
-    auto compute = [&](int buf) __attribute__((always_inline)) {
-      const uint8_t* base = lds + buf * kStageBytesDma;
-      Frag<CT> fa[2][2], fb[2][4];
-      load_frags(base, 0, fa[0], fb[0]);
+    // the 8 MFMAs of one k-step; after MFMA i, run `between(i)` (kept in place by
+    // scheduling fences so that it issues while the MFMA pipe is busy)
+    auto mfma_step = [&](Frag<CT> (&fa)[2], Frag<CT> (&fb)[4], auto&& between) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        // the next step's reads are issued before this step's MFMAs (scheduling fences keep
-        // the order, so both fragment sets are live and the reads overlap the MFMAs)
-        if (s + 1 < KSTEPS) load_frags(base, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      for (int i = 0; i < 8; ++i) {
+        acc[i >> 2][i & 3] = mma(fa[i >> 2], fb[i & 3], acc[i >> 2][i & 3]);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma(fa[s & 1][mb], fb[s & 1][nb], acc[mb][nb]);
+        between(i);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    auto nothing = [](int) __attribute__((always_inline)) {};
 
-    // the previous tile's epilogue stores and LDS reads are finished before reuse
-    wait_vmcnt_all();
+    // ---- pipeline.  Stage ks lives in LDS buffer ks % 3; stages ks+1 and ks+2 are in
+    // flight.  During the last k-step of stage ks: wait for stage ks+1, barrier (every wave
+    // is past its reads of buffer ks % 3), read the first fragments of stage ks+1, and
+    // issue stage ks+3 into buffer ks % 3 between the MFMAs.
+    wait_vmcnt_all();  // the previous tile's epilogue stores have drained
+    block_barrier();   // and every wave is past its last LDS reads
+    dma_slice(0, 0, 0, kDmaPerStage);
+    if (nk > 1) dma_slice(1, 1, 0, kDmaPerStage);
+    if (nk > 2) dma_slice(2, 2, 0, kDmaPerStage);
+    if (nk > 2) wait_vmcnt_2stages();
+    else if (nk > 1) wait_vmcnt_dma_stage();
+    else wait_vmcnt_all();
     block_barrier();
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
+
+    Frag<CT> f0a[2], f0b[4], f1a[2], f1b[4];
+    load_frags(0, 0, f0a, f0b);
     int buf = 0;
     for (int ks = 0; ks < nk; ++ks) {
-      if (ks + 1 < nk) wait_vmcnt_dma_stage();
-      else wait_vmcnt_all();
-      block_barrier();  // stage ks landed for every wave; stage ks-1's buffer is free
-      if (ks + 2 < nk) issue(ks + 2, buf == 0 ? 2 : buf - 1);
-      compute(buf);
-      buf = buf == 2 ? 0 : buf + 1;
+      const int nbuf = buf == 2 ? 0 : buf + 1;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        Frag<CT>(&ca)[2] = (s & 1) ? f1a : f0a;
+        Frag<CT>(&cb)[4] = (s & 1) ? f1b : f0b;
+        Frag<CT>(&na)[2] = (s & 1) ? f0a : f1a;
+        Frag<CT>(&nb)[4] = (s & 1) ? f0b : f1b;
+        if (s + 1 < KSTEPS) {
+          load_frags(buf, s + 1, na, nb);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_step(ca, cb, nothing);
+        } else {
+          // last k-step of stage ks
+          if (ks + 1 < nk) {
+            wait_lgkmcnt_all();                 // this wave's reads of buffer `buf` are done
+            if (ks + 2 < nk) wait_vmcnt_dma_stage();  // stage ks+1 has landed (ks+2 in flight)
+            else wait_vmcnt_all();
+            block_barrier();
+            load_frags(nbuf, 0, na, nb);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // one MFMA sequence on every path (branching around MFMAs would make the
+          // accumulators merge through copies); only the DMA slices are conditional
+          const bool more = ks + 3 < nk;
+          mfma_step(ca, cb, [&](int i) __attribute__((always_inline)) {
+            if (more && i < 6) dma_slice(ks + 3, buf, 2 * i, 2);
+          });
+        }
+      }
+      buf = nbuf;
     }
-
     const int mend = seg_hi;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {

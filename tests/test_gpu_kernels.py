@@ -328,3 +328,12 @@ def test_combine_matches_oracle(case):
                              None if sh is None else np.abs(f64(sh)))
         tol = bf16_ulp(ref) * 1.0001 + (k + 1) * 2.0 ** -24 * mag
         assert np.all(np.abs(got - bf16_round(ref)) <= tol)
+
+
+def test_generator_device_matches_host():
+    """The counter-based generator gives the same tensors on the GPU as on the CPU."""
+    cfg = w.CONFIGS["dsv3_bf16"].scaled(E=7, H=512, I=256)
+    g13, g2 = w.all_expert_weights(cfg, DEV)
+    c13, c2 = w.all_expert_weights(cfg, "cpu")
+    assert torch.equal(g13.cpu(), c13) and torch.equal(g2.cpu(), c2)
+    assert torch.equal(w.hidden_states(cfg, DEV).cpu(), w.hidden_states(cfg, "cpu"))
