@@ -410,15 +410,18 @@ constexpr int kAGroups = GBM / 8;                       // 16
 constexpr int kBGroups = GBN / 8;                       // 32
 constexpr int kStageBytesDma = (kAGroups + kBGroups) * kGroupBytes;  // 49152
 constexpr int kDmaStages = 3;
-constexpr int kDmaPerStage = (kAGroups + kBGroups) / 4;  // DMA instructions per wave and stage (12)
+constexpr int kDmaWaves = 8;                            // 2 x 4 waves, two per SIMD
+constexpr int kDmaThreads = kDmaWaves * 64;
+constexpr int kDmaPerStage = (kAGroups + kBGroups) / kDmaWaves;  // DMA instructions per wave and stage (6)
+constexpr int kDmaA = kAGroups / kDmaWaves;             // of which A groups (2)
 
 __device__ __forceinline__ void wait_vmcnt_dma_stage() {
   // vmcnt <= kDmaPerStage: every load older than the newest stage has landed
-  static_assert(kDmaPerStage == 12, "s_waitcnt immediate below assumes 12 loads per stage");
-  __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  static_assert(kDmaPerStage == 6, "s_waitcnt immediates assume 6 loads per wave and stage");
+  __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
 }
 __device__ __forceinline__ void wait_vmcnt_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt_2stages() { __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_2stages() { __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
 // lgkmcnt(0) with vmcnt and expcnt left at their maxima; as a builtin (not inline asm)
 // the compiler sees that every earlier LDS read has completed
 __device__ __forceinline__ void wait_lgkmcnt_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -441,7 +444,7 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 __device__ __forceinline__ void block_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
 
 template <int CT, int MODE>
-__global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kDmaThreads, 1) void grouped_gemm_dma_kernel(GemmArgs p) {
   constexpr int esz = CTraits<CT>::esz;
   constexpr int BK = GKB / esz;                 // K elements per stage
   constexpr int KSTEPS = BK / 16;               // 16-wide MFMA steps per stage
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;   // 2 x 4 waves; each owns 64 x 64 of the tile
   const int l7 = lane & 7;
   const int lrow = lane >> 3;                  // row inside a DMA group
   // global chunk this lane loads: the slot it fills is lane & 7, the row's key is
@@ -475,13 +478,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
 
   // fragment rows (tile coordinates) and their byte offsets inside an operand region
   auto row_addr = [](int r) { return r * 128; };
-  int a_frag[2], b_frag[4];
+  int a_frag[2], b_frag[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) a_frag[mb] = row_addr(wm * 64 + mb * 32 + (lane & 31));
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int r = MODE == MODE_GATE_UP ? (nb >> 1) * (GBN / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31)
-                                       : wn * 128 + nb * 32 + (lane & 31);
+  for (int nb = 0; nb < 2; ++nb) {
+    // gate/up: block 0 = 32 W_gate rows, block 1 = the same 32 W_up rows
+    const int r = MODE == MODE_GATE_UP ? nb * (GBN / 2) + wn * 32 + (lane & 31)
+                                       : wn * 64 + nb * 32 + (lane & 31);
     b_frag[nb] = row_addr(r) + kAGroups * kGroupBytes;
   }
   // swizzled chunk offsets of each k-step; fragment rows start at multiples of 32, so a
@@ -520,24 +524,24 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
     const int b_rows_left = MODE == MODE_GATE_UP ? GBN : static_cast<int>(p.n_out - b_row0);
 
     // this lane's source offsets (32-bit, relative to the tile bases) for its DMA groups:
-    // wave w loads A groups w, w+4, .. and B groups w, w+4, ..
-    uint32_t a_src[kAGroups / 4], b_src[kBGroups / 4];
+    // wave w loads A groups w, w+8 and B groups w, w+8, w+16, w+24
+    uint32_t a_src[kDmaA], b_src[kDmaPerStage - kDmaA];
 #pragma unroll
-    for (int i = 0; i < kAGroups / 4; ++i) {
-      int r = (wave + 4 * i) * 8 + lrow;
+    for (int i = 0; i < kDmaA; ++i) {
+      int r = (wave + kDmaWaves * i) * 8 + lrow;
       r = r < mlast ? r : mlast;
       a_src[i] = static_cast<uint32_t>(r) * a_rb + lchunk * 16;
     }
 #pragma unroll
-    for (int i = 0; i < kBGroups / 4; ++i) {
-      const int r = (wave + 4 * i) * 8 + lrow;
+    for (int i = 0; i < kDmaPerStage - kDmaA; ++i) {
+      const int r = (wave + kDmaWaves * i) * 8 + lrow;
       uint32_t wr;
       if (MODE == MODE_GATE_UP) wr = r < GBN / 2 ? r : static_cast<uint32_t>(p.I) + (r - GBN / 2);
       else wr = r < b_rows_left ? r : b_rows_left - 1;
       b_src[i] = wr * b_rb + lchunk * 16;
     }
 
-    // DMA of stage ks into LDS buffer buf: this wave's 12 group loads, issued in slices so
+    // DMA of stage ks into LDS buffer buf: this wave's 6 group loads, issued in slices so
     // they can sit between MFMAs
     auto dma_slice = [&](int ks, int buf, int first, int count) __attribute__((always_inline)) {
       const uint32_t base = __builtin_amdgcn_readfirstlane(
@@ -547,18 +551,18 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
       for (int j = 0; j < kDmaPerStage; ++j) {
         if (j < first || j >= first + count) continue;
-        if (j < kAGroups / 4) dma16(ab + a_src[j], base + 4 * j * kGroupBytes);
-        else dma16(bb + b_src[j - kAGroups / 4], base + (kAGroups + 4 * (j - kAGroups / 4)) * kGroupBytes);
+        if (j < kDmaA) dma16(ab + a_src[j], base + kDmaWaves * j * kGroupBytes);
+        else dma16(bb + b_src[j - kDmaA], base + (kAGroups + kDmaWaves * (j - kDmaA)) * kGroupBytes);
       }
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-    auto load_frags = [&](int buf, int s, Frag<CT> (&fa)[2], Frag<CT> (&fb)[4])
+    auto load_frags = [&](int buf, int s, Frag<CT> (&fa)[2], Frag<CT> (&fb)[2])
         __attribute__((always_inline)) {
       const uint8_t* base = lds + buf * kStageBytesDma;
 #pragma unroll
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
         }
       }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < 2; ++nb) {
         if constexpr (CT == CT_F32) {
           fb[nb].v0 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][0]);
           fb[nb].v1 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][1]);
@@ -580,12 +584,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
         }
       }
     };
-    // the 8 MFMAs of one k-step; after MFMA i, run `between(i)` (kept in place by
+    // the 4 MFMAs of one k-step; after MFMA i, run `between(i)` (kept in place by
     // scheduling fences so that it issues while the MFMA pipe is busy)
-    auto mfma_step = [&](Frag<CT> (&fa)[2], Frag<CT> (&fb)[4], auto&& between) __attribute__((always_inline)) {
+    auto mfma_step = [&](Frag<CT> (&fa)[2], Frag<CT> (&fb)[2], auto&& between) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[i >> 2][i & 3] = mma(fa[i >> 2], fb[i & 3], acc[i >> 2][i & 3]);
+      for (int i = 0; i < 4; ++i) {
+        acc[i >> 1][i & 1] = mma(fa[i >> 1], fb[i & 1], acc[i >> 1][i & 1]);
         __builtin_amdgcn_sched_barrier(0);
         between(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
     else wait_vmcnt_all();
     block_barrier();
 
-    Frag<CT> f0a[2], f0b[4], f1a[2], f1b[4];
+    Frag<CT> f0a[2], f0b[2], f1a[2], f1b[2];
     load_frags(0, 0, f0a, f0b);
     int buf = 0;
     for (int ks = 0; ks < nk; ++ks) {
@@ -615,9 +619,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         Frag<CT>(&ca)[2] = (s & 1) ? f1a : f0a;
-        Frag<CT>(&cb)[4] = (s & 1) ? f1b : f0b;
+        Frag<CT>(&cb)[2] = (s & 1) ? f1b : f0b;
         Frag<CT>(&na)[2] = (s & 1) ? f0a : f1a;
-        Frag<CT>(&nb)[4] = (s & 1) ? f0b : f1b;
+        Frag<CT>(&nb)[2] = (s & 1) ? f0b : f1b;
         if (s + 1 < KSTEPS) {
           load_frags(buf, s + 1, na, nb);
           __builtin_amdgcn_sched_barrier(0);
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
           // accumulators merge through copies); only the DMA slices are conditional
           const bool more = ks + 3 < nk;
           mfma_step(ca, cb, [&](int i) __attribute__((always_inline)) {
-            if (more && i < 6) dma_slice(ks + 3, buf, 2 * i, 2);
+            if (more && i < 3) dma_slice(ks + 3, buf, 2 * i, 2);
           });
         }
       }
@@ -650,20 +654,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_dma_kernel(GemmArgs 
         const int r = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= mend) continue;
         if (MODE == MODE_GATE_UP) {
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const float g = acc[mb][nb][v];
-            const float u = acc[mb][nb + 2][v];
-            const float hv = g / (1.0f + expf(-g)) * u;
-            const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * (GBN / 2) + wn * 64 +
-                             nb * 32 + (lane & 31);
-            if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
-            else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(hv);
-          }
+          const float g = acc[mb][0][v];
+          const float u = acc[mb][1][v];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * (GBN / 2) + wn * 32 +
+                           (lane & 31);
+          if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
+          else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(hv);
         } else {
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int col = nblk * GBN + wn * 128 + nb * 32 + (lane & 31);
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col = nblk * GBN + wn * 64 + nb * 32 + (lane & 31);
             if (col >= p.n_out) continue;
             const size_t o = static_cast<size_t>(r) * p.n_out + col;
             if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = acc[mb][nb][v];
@@ -717,7 +718,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)
 #define MOE_LAUNCH_DMA(CT_, MODE_) \
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<CT_, MODE_>), grid, block, 0, s, p)
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<CT_, MODE_>), grid, dim3(kDmaThreads), 0, s, p)
   if (mode == MODE_GATE_UP) {
     if (ct == CT_F32) MOE_LAUNCH_DMA(CT_F32, MODE_GATE_UP);
     else if (ct == CT_BF16) MOE_LAUNCH_DMA(CT_BF16, MODE_GATE_UP);
