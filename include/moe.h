@@ -182,7 +182,7 @@ moe_status moe_quantize_fp8(const void* x, moe_dtype x_dt, int64_t rows, int col
  * Accumulation is fp32.  fp8 layers sum each 128-wide K block in fp32, then scale it by
  * the product of the two block scales; the down projection reads bf16 h against fp8
  * W_down, scaled per 128-wide K block.
- * Requires H % 64 == 0 and I % 64 == 0 (H % 128 == 0, I % 128 == 0 for fp8).
+ * Requires H % 128 == 0 and I % 128 == 0.
  */
 moe_status moe_grouped_ffn(const void* a, const float* a_scale, moe_dtype a_dt,
                            const int32_t* offsets, int E, int rows, int H, int I, const void* w13,
