@@ -392,46 +392,61 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------------------
-// Unscaled bf16 / fp32 variant with direct-to-LDS loads.
+// Unscaled bf16 variant with direct-to-LDS loads.
 //
+// A workgroup of WM x 4 waves computes a 128-row x BN-column tile (gate/up: BN/2 W_gate
+// rows + the same BN/2 W_up rows -> BN/2 h columns); each wave owns 128/WM x BN/4 on
+// v_mfma_f32_32x32x16_bf16.  K advances in stages of ROWB bytes per row;
 // global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS at
-// base + 16 * lane, so a stage needs no staging registers and three stages fit in LDS:
-// stage ks+2 is loading while stage ks is multiplied.  One wave instruction fills one
-// 1 KiB group of 8 tile rows (128 bytes each).  The 16-byte chunk c of row r sits in slot
-// c ^ (r & 7) ^ ((r >> 3) & 1): the LDS serves a 16-byte-per-lane read 16 lanes at a time
-// from 64 four-byte banks, and with this key any 16 consecutive rows of one chunk land in
-// 16 distinct 16-byte bank slots (the 8-row key alone repeats every 8 rows).  The wait for a stage is explicit
-// (s_waitcnt vmcnt) followed by a plain s_barrier, which keeps the two later stages in
-// flight across the barrier.
+// base + 16 * lane, so a stage needs no staging registers.  One wave instruction fills a
+// 1 KiB group of 1024/ROWB tile rows.  Inside a row the 16-byte chunk c sits in slot
+// c ^ key(r): the LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 four-byte
+// banks, and the key makes any 16 consecutive rows of one chunk land in 16 distinct
+// 16-byte bank slots.  Stage waits are explicit (s_waitcnt vmcnt) followed by a plain
+// s_barrier, which keeps the later stages in flight across the barrier.
 // ------------------------------------------------------------------------------------
 
-constexpr int kGroupBytes = 1024;                       // 8 rows x 128 B
-constexpr int kAGroups = GBM / 8;                       // 16
-constexpr int kBGroups = GBN / 8;                       // 32
-constexpr int kStageBytesDma = (kAGroups + kBGroups) * kGroupBytes;  // 49152
-constexpr int kDmaStages = 3;
-constexpr int kDmaWaves = 8;                            // 2 x 4 waves, two per SIMD
-constexpr int kDmaThreads = kDmaWaves * 64;
-constexpr int kDmaPerStage = (kAGroups + kBGroups) / kDmaWaves;  // DMA instructions per wave and stage (6)
-constexpr int kDmaA = kAGroups / kDmaWaves;             // of which A groups (2)
+constexpr int kDM = 128;                                // rows of a tile
+constexpr int kDGroup = 1024;                           // bytes of one DMA wave instruction
+template <int BN, int ROWB, int STAGES, int WM>
+struct DmaCfg {
+  static constexpr int kWaves = WM * 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRowsPerGroup = kDGroup / ROWB;
+  static constexpr int kChunks = ROWB / 16;             // 16-byte chunks per row and stage
+  static constexpr int kAGroups = kDM / kRowsPerGroup;
+  static constexpr int kBGroups = BN / kRowsPerGroup;
+  static constexpr int kStageBytes = (kAGroups + kBGroups) * kDGroup;
+  static constexpr int kPerWave = (kAGroups + kBGroups) / kWaves;   // DMA instructions per wave and stage
+  static constexpr int kAPerWave = kAGroups / kWaves;
+  static constexpr int kKSteps = ROWB / 32;             // 16-wide bf16 k-steps per stage
+  static constexpr int kNB = BN / 4 / 32;               // 32-column blocks per wave
+  static constexpr int kMB = kDM / WM / 32;             // 32-row blocks per wave
+  static_assert(kAGroups % kWaves == 0 && kBGroups % kWaves == 0, "groups spread evenly");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
+  // swizzle key of tile row r (rows of a fragment start at multiples of 32)
+  __device__ static __forceinline__ int key(int r) {
+    return ROWB == 128 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
+  }
+};
 
-__device__ __forceinline__ void wait_vmcnt_dma_stage() {
-  // vmcnt <= kDmaPerStage: every load older than the newest stage has landed
-  static_assert(kDmaPerStage == 6, "s_waitcnt immediates assume 6 loads per wave and stage");
-  __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
-__device__ __forceinline__ void wait_vmcnt_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt_2stages() { __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
 // lgkmcnt(0) with vmcnt and expcnt left at their maxima; as a builtin (not inline asm)
 // the compiler sees that every earlier LDS read has completed
 __device__ __forceinline__ void wait_lgkmcnt_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void block_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) uint8_t lds_byte;
 
 // 16 bytes per lane from global memory into LDS at lds_base + 16 * lane.  Issued as
 // inline assembly so that the compiler adds no wait of its own before later LDS reads;
-// every wait for these loads is the explicit s_waitcnt above.  M0 holds the LDS base;
-// one wait state separates its write from the load that reads it.
+// every wait for these loads is explicit.  M0 holds the LDS base; one wait state
+// separates its write from the load that reads it.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   __asm__ volatile(
       "s_mov_b32 m0, %1\n\t"
@@ -441,30 +456,35 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
       : "v"(gptr), "s"(lds_base)
       : "memory", "m0");
 }
-__device__ __forceinline__ void block_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
 
-template <int CT, int MODE>
-__global__ __launch_bounds__(kDmaThreads, 1) void grouped_gemm_dma_kernel(GemmArgs p) {
-  constexpr int esz = CTraits<CT>::esz;
-  constexpr int BK = GKB / esz;                 // K elements per stage
-  constexpr int KSTEPS = BK / 16;               // 16-wide MFMA steps per stage
-  static_assert(CT != CT_FP8, "fp8 layers use the scaled kernel");
+template <int MODE, int BN, int ROWB, int STAGES, int WM>
+__global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs p) {
+  using C = DmaCfg<BN, ROWB, STAGES, WM>;
+  constexpr int KSTEPS = C::kKSteps;
+  constexpr int NB = C::kNB;
+  constexpr int MB = C::kMB;
+  constexpr int kDmaWaves = C::kWaves;
+  constexpr int kWR = kDM / WM;                 // rows per wave
+  constexpr int PER = C::kPerWave;
   static_assert(KSTEPS % 2 == 0, "a stage must end in fragment set 1 so the next starts in set 0");
+  static_assert(MODE != MODE_GATE_UP || NB % 2 == 0, "gate/up pairs");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * kStageBytesDma];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStageBytes];
   const uint32_t lds_addr0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;   // 2 x 4 waves; each owns 64 x 64 of the tile
-  const int l7 = lane & 7;
-  const int lrow = lane >> 3;                  // row inside a DMA group
-  // global chunk this lane loads: the slot it fills is lane & 7, the row's key is
-  // lrow ^ (group & 1), and every group this wave fills has parity wave & 1
-  const int lchunk = (lane & 7) ^ lrow ^ (wave & 1);
+  const int wm = wave % WM, wn = wave / WM;     // each wave owns kWR x BN/4 of the tile
+  const int lrow = lane / C::kChunks;           // row inside a DMA group
+  // global chunk this lane loads: the slot it fills is lane % kChunks, XOR the row's key.
+  // Every group this wave fills has the parity of the wave (groups w, w + waves, ...; 16 A
+  // groups of 8 rows precede the B groups), which the 128-byte key needs for bit 3 of the row.
+  const int lchunk = (lane % C::kChunks) ^ C::key(lrow + (ROWB == 128 ? (wave & 1) * 8 : 0));
 
-  const int nN = MODE == MODE_GATE_UP ? p.I / (GBN / 2) : (p.n_out + GBN - 1) / GBN;
+  const int n_cols = MODE == MODE_GATE_UP ? p.I : p.n_out;
+  const int tile_cols = MODE == MODE_GATE_UP ? BN / 2 : BN;
+  const int nN = (n_cols + tile_cols - 1) / tile_cols;
   const long long total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
@@ -472,36 +492,24 @@ __global__ __launch_bounds__(kDmaThreads, 1) void grouped_gemm_dma_kernel(GemmAr
   const long long t_beg = total * xcd / kNumXcd;
   const long long t_end = total * (xcd + 1) / kNumXcd;
 
-  const int nk = p.K / BK;
-  const uint32_t a_rb = static_cast<uint32_t>(p.K) * esz;
-  const uint32_t b_rb = a_rb;
+  const int nk = p.K / (ROWB / 2);
+  const uint32_t rb = static_cast<uint32_t>(p.K) * 2;   // row bytes of both operands
 
-  // fragment rows (tile coordinates) and their byte offsets inside an operand region
-  auto row_addr = [](int r) { return r * 128; };
-  int a_frag[2], b_frag[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) a_frag[mb] = row_addr(wm * 64 + mb * 32 + (lane & 31));
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    // gate/up: block 0 = 32 W_gate rows, block 1 = the same 32 W_up rows
-    const int r = MODE == MODE_GATE_UP ? nb * (GBN / 2) + wn * 32 + (lane & 31)
-                                       : wn * 64 + nb * 32 + (lane & 31);
-    b_frag[nb] = row_addr(r) + kAGroups * kGroupBytes;
-  }
-  // swizzled chunk offsets of each k-step; fragment rows start at multiples of 32, so a
-  // row's key (row & 7) ^ ((row >> 3) & 1) is the lane's
+  const int key = C::key(lane & 31);
   const int h = lane >> 5;
-  const int key = l7 ^ ((lane >> 3) & 1);
-  int koff[KSTEPS][2];
+  int koff[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    if (CT == CT_F32) {
-      koff[s][0] = ((4 * s + 2 * h) ^ key) * 16;
-      koff[s][1] = ((4 * s + 2 * h + 1) ^ key) * 16;
-    } else {
-      koff[s][0] = ((2 * s + h) ^ key) * 16;
-      koff[s][1] = 0;
-    }
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = ((2 * s + h) ^ key) * 16;
+  int a_frag[MB], b_frag[NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) a_frag[mb] = (wm * kWR + mb * 32 + (lane & 31)) * ROWB;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    // gate/up: the first NB/2 blocks are W_gate rows, the last NB/2 the same W_up rows
+    const int r = MODE == MODE_GATE_UP
+                      ? (nb / (NB / 2)) * (BN / 2) + wn * (BN / 8) + (nb % (NB / 2)) * 32 + (lane & 31)
+                      : wn * (BN / 4) + nb * 32 + (lane & 31);
+    b_frag[nb] = C::kAGroups * kDGroup + r * ROWB;
   }
 
   for (long long L = t_beg + slot; L < t_end; L += per_xcd) {
@@ -514,82 +522,66 @@ __global__ __launch_bounds__(kDmaThreads, 1) void grouped_gemm_dma_kernel(GemmAr
     int seg_lo = p.offsets[e], seg_hi = p.offsets[e + 1];
     seg_lo = seg_lo < 0 ? 0 : (seg_lo > p.rows ? p.rows : seg_lo);
     seg_hi = seg_hi < seg_lo ? seg_lo : (seg_hi > p.rows ? p.rows : seg_hi);
-    const int m0 = seg_lo + mtile * GBM;
+    const int m0 = seg_lo + mtile * kDM;
     const int mlast = seg_hi - 1 - m0;
+    const int c0 = nblk * tile_cols;
+    const int clast = n_cols - 1 - c0;
 
-    const uint8_t* a_tile = p.a + static_cast<size_t>(m0) * a_rb;
-    const long long b_row0 = MODE == MODE_GATE_UP ? static_cast<long long>(nblk) * (GBN / 2)
-                                                  : static_cast<long long>(nblk) * GBN;
-    const uint8_t* b_tile = p.b + (static_cast<size_t>(e) * p.b_rows + b_row0) * b_rb;
-    const int b_rows_left = MODE == MODE_GATE_UP ? GBN : static_cast<int>(p.n_out - b_row0);
+    const uint8_t* a_tile = p.a + static_cast<size_t>(m0) * rb;
+    const uint8_t* b_tile = p.b + static_cast<size_t>(e) * p.b_rows * rb;
 
-    // this lane's source offsets (32-bit, relative to the tile bases) for its DMA groups:
-    // wave w loads A groups w, w+8 and B groups w, w+8, w+16, w+24
-    uint32_t a_src[kDmaA], b_src[kDmaPerStage - kDmaA];
+    // this lane's source offsets; wave w fills groups w, w + waves, ... (A groups first).
+    // Rows past the segment (A) or past the matrix (B) re-read the last valid one.
+    uint32_t src[PER];
 #pragma unroll
-    for (int i = 0; i < kDmaA; ++i) {
-      int r = (wave + kDmaWaves * i) * 8 + lrow;
-      r = r < mlast ? r : mlast;
-      a_src[i] = static_cast<uint32_t>(r) * a_rb + lchunk * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < kDmaPerStage - kDmaA; ++i) {
-      const int r = (wave + kDmaWaves * i) * 8 + lrow;
-      uint32_t wr;
-      if (MODE == MODE_GATE_UP) wr = r < GBN / 2 ? r : static_cast<uint32_t>(p.I) + (r - GBN / 2);
-      else wr = r < b_rows_left ? r : b_rows_left - 1;
-      b_src[i] = wr * b_rb + lchunk * 16;
+    for (int j = 0; j < PER; ++j) {
+      const int g = wave + kDmaWaves * j;
+      if (j < C::kAPerWave) {
+        int r = g * C::kRowsPerGroup + lrow;
+        r = r < mlast ? r : mlast;
+        src[j] = static_cast<uint32_t>(r) * rb + lchunk * 16;
+      } else {
+        const int r = (g - C::kAGroups) * C::kRowsPerGroup + lrow;   // tile weight row
+        uint32_t wr;
+        if (MODE == MODE_GATE_UP) {
+          const int c = r % (BN / 2);
+          const int cc = c < clast ? c : clast;
+          wr = (r < BN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(c0 + cc);
+        } else {
+          wr = static_cast<uint32_t>(c0 + (r < clast ? r : clast));
+        }
+        src[j] = wr * rb + lchunk * 16;
+      }
     }
 
-    // DMA of stage ks into LDS buffer buf: this wave's 6 group loads, issued in slices so
-    // they can sit between MFMAs
-    auto dma_slice = [&](int ks, int buf, int first, int count) __attribute__((always_inline)) {
+    auto dma_slice = [&](int ks, int buf, int j) __attribute__((always_inline)) {
       const uint32_t base = __builtin_amdgcn_readfirstlane(
-          lds_addr0 + static_cast<uint32_t>(buf * kStageBytesDma + wave * kGroupBytes));
-      const uint8_t* ab = a_tile + static_cast<size_t>(ks) * GKB;
-      const uint8_t* bb = b_tile + static_cast<size_t>(ks) * GKB;
-#pragma unroll
-      for (int j = 0; j < kDmaPerStage; ++j) {
-        if (j < first || j >= first + count) continue;
-        if (j < kDmaA) dma16(ab + a_src[j], base + kDmaWaves * j * kGroupBytes);
-        else dma16(bb + b_src[j - kDmaA], base + (kAGroups + kDmaWaves * (j - kDmaA)) * kGroupBytes);
-      }
+          lds_addr0 + static_cast<uint32_t>(buf * C::kStageBytes + (wave + kDmaWaves * j) * kDGroup));
+      const size_t k_off = static_cast<size_t>(ks) * ROWB;
+      dma16((j < C::kAPerWave ? a_tile : b_tile) + k_off + src[j], base);
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
 
-    auto load_frags = [&](int buf, int s, Frag<CT> (&fa)[2], Frag<CT> (&fb)[2])
+    auto load_frags = [&](int buf, int s, Frag<CT_BF16> (&fa)[MB], Frag<CT_BF16> (&fb)[NB])
         __attribute__((always_inline)) {
-      const uint8_t* base = lds + buf * kStageBytesDma;
+      const uint8_t* base = lds + buf * C::kStageBytes;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        if constexpr (CT == CT_F32) {
-          fa[mb].v0 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][0]);
-          fa[mb].v1 = *reinterpret_cast<const uint4*>(base + a_frag[mb] + koff[s][1]);
-        } else {
-          fa[mb].load(base + a_frag[mb] + koff[s][0]);
-        }
-      }
+      for (int mb = 0; mb < MB; ++mb) fa[mb].load(base + a_frag[mb] + koff[s]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if constexpr (CT == CT_F32) {
-          fb[nb].v0 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][0]);
-          fb[nb].v1 = *reinterpret_cast<const uint4*>(base + b_frag[nb] + koff[s][1]);
-        } else {
-          fb[nb].load(base + b_frag[nb] + koff[s][0]);
-        }
-      }
+      for (int nb = 0; nb < NB; ++nb) fb[nb].load(base + b_frag[nb] + koff[s]);
     };
-    // the 4 MFMAs of one k-step; after MFMA i, run `between(i)` (kept in place by
+    // the MB*NB MFMAs of one k-step; after MFMA i, run `between(i)` (kept in place by
     // scheduling fences so that it issues while the MFMA pipe is busy)
-    auto mfma_step = [&](Frag<CT> (&fa)[2], Frag<CT> (&fb)[2], auto&& between) __attribute__((always_inline)) {
+    auto mfma_step = [&](Frag<CT_BF16> (&fa)[MB], Frag<CT_BF16> (&fb)[NB], auto&& between)
+        __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i >> 1][i & 1] = mma(fa[i >> 1], fb[i & 1], acc[i >> 1][i & 1]);
+      for (int i = 0; i < MB * NB; ++i) {
+        acc[i / NB][i % NB] = mma(fa[i / NB], fb[i % NB], acc[i / NB][i % NB]);
         __builtin_amdgcn_sched_barrier(0);
         between(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -597,84 +589,109 @@ __global__ __launch_bounds__(kDmaThreads, 1) void grouped_gemm_dma_kernel(GemmAr
     };
     auto nothing = [](int) __attribute__((always_inline)) {};
 
-    // ---- pipeline.  Stage ks lives in LDS buffer ks % 3; stages ks+1 and ks+2 are in
-    // flight.  During the last k-step of stage ks: wait for stage ks+1, barrier (every wave
-    // is past its reads of buffer ks % 3), read the first fragments of stage ks+1, and
-    // issue stage ks+3 into buffer ks % 3 between the MFMAs.
-    wait_vmcnt_all();  // the previous tile's epilogue stores have drained
+    // ---- pipeline (STAGES LDS buffers).  Stage ks lives in buffer ks % STAGES.  While
+    // stage ks is multiplied, stage ks+STAGES-1 is loaded into the buffer stage ks-1 used:
+    // its loads are spread over the MFMAs of every k-step but the last (a burst of them
+    // would overflow the address unit's queue and stall the issuing waves).  At the start
+    // of the last k-step each wave waits for stage ks+1, the barrier makes that hold for all
+    // waves and frees buffer ks % STAGES, and the first fragments of stage ks+1 are read
+    // while the last k-step's MFMAs run.
+    static_assert(STAGES == 2 || STAGES == 3, "two or three buffers");
+    constexpr int kAhead = STAGES - 1;                     // stages loading while one is used
+    constexpr int kSlots = (KSTEPS - 1) * MB * NB;         // MFMA slots that may carry a load
+    static_assert(PER <= kSlots, "not enough MFMA slots to spread a stage's loads");
+    wait_vmcnt<0>();   // the previous tile's epilogue stores have drained
     block_barrier();   // and every wave is past its last LDS reads
-    dma_slice(0, 0, 0, kDmaPerStage);
-    if (nk > 1) dma_slice(1, 1, 0, kDmaPerStage);
-    if (nk > 2) dma_slice(2, 2, 0, kDmaPerStage);
-    if (nk > 2) wait_vmcnt_2stages();
-    else if (nk > 1) wait_vmcnt_dma_stage();
-    else wait_vmcnt_all();
+    for (int st = 0; st < kAhead && st < nk; ++st)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) dma_slice(st, st, j);
+    if (kAhead == 2 && nk > 1) wait_vmcnt<(kAhead - 1) * PER>();
+    else wait_vmcnt<0>();
     block_barrier();
 
-    Frag<CT> f0a[2], f0b[2], f1a[2], f1b[2];
+    Frag<CT_BF16> f0a[MB], f0b[NB], f1a[MB], f1b[NB];
     load_frags(0, 0, f0a, f0b);
     int buf = 0;
     for (int ks = 0; ks < nk; ++ks) {
-      const int nbuf = buf == 2 ? 0 : buf + 1;
+      const int nbuf = buf == STAGES - 1 ? 0 : buf + 1;
+      const int lbuf = buf == 0 ? STAGES - 1 : buf - 1;    // (ks + STAGES - 1) % STAGES
+      const bool load_next = ks + kAhead < nk;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        Frag<CT>(&ca)[2] = (s & 1) ? f1a : f0a;
-        Frag<CT>(&cb)[2] = (s & 1) ? f1b : f0b;
-        Frag<CT>(&na)[2] = (s & 1) ? f0a : f1a;
-        Frag<CT>(&nb)[2] = (s & 1) ? f0b : f1b;
+        Frag<CT_BF16>(&ca)[MB] = (s & 1) ? f1a : f0a;
+        Frag<CT_BF16>(&cb)[NB] = (s & 1) ? f1b : f0b;
+        Frag<CT_BF16>(&na)[MB] = (s & 1) ? f0a : f1a;
+        Frag<CT_BF16>(&nb)[NB] = (s & 1) ? f0b : f1b;
         if (s + 1 < KSTEPS) {
           load_frags(buf, s + 1, na, nb);
           __builtin_amdgcn_sched_barrier(0);
-          mfma_step(ca, cb, nothing);
+          // load j of stage ks+kAhead goes after MFMA slot (j * kSlots) / PER
+          mfma_step(ca, cb, [&](int i) __attribute__((always_inline)) {
+            const int slot_i = s * MB * NB + i;
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+              if ((j * kSlots) / PER == slot_i && load_next) dma_slice(ks + kAhead, lbuf, j);
+          });
         } else {
           // last k-step of stage ks
           if (ks + 1 < nk) {
-            wait_lgkmcnt_all();                 // this wave's reads of buffer `buf` are done
-            if (ks + 2 < nk) wait_vmcnt_dma_stage();  // stage ks+1 has landed (ks+2 in flight)
-            else wait_vmcnt_all();
+            wait_lgkmcnt_all();                       // this wave's reads of buffer `buf` are done
+            // stage ks+1 landed; with three buffers stage ks+2 may stay in flight
+            if (kAhead == 2 && load_next) wait_vmcnt<(kAhead - 1) * PER>();
+            else wait_vmcnt<0>();
             block_barrier();
             load_frags(nbuf, 0, na, nb);
           }
           __builtin_amdgcn_sched_barrier(0);
-          // one MFMA sequence on every path (branching around MFMAs would make the
-          // accumulators merge through copies); only the DMA slices are conditional
-          const bool more = ks + 3 < nk;
-          mfma_step(ca, cb, [&](int i) __attribute__((always_inline)) {
-            if (more && i < 3) dma_slice(ks + 3, buf, 2 * i, 2);
-          });
+          mfma_step(ca, cb, nothing);
         }
       }
       buf = nbuf;
     }
+
+    // ---- epilogue
     const int mend = seg_hi;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = m0 + wm * kWR + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= mend) continue;
         if (MODE == MODE_GATE_UP) {
-          const float g = acc[mb][0][v];
-          const float u = acc[mb][1][v];
-          const float hv = g / (1.0f + expf(-g)) * u;
-          const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * (GBN / 2) + wn * 32 +
-                           (lane & 31);
-          if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
-          else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(hv);
+#pragma unroll
+          for (int nb = 0; nb < NB / 2; ++nb) {
+            const int col = c0 + wn * (BN / 8) + nb * 32 + (lane & 31);
+            if (col >= n_cols) continue;
+            const float g = acc[mb][nb][v];
+            const float u = acc[mb][nb + NB / 2][v];
+            const float hv = g / (1.0f + expf(-g)) * u;
+            reinterpret_cast<uint16_t*>(p.out)[static_cast<size_t>(r) * p.I + col] = f32_to_bf16(hv);
+          }
         } else {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int col = nblk * GBN + wn * 64 + nb * 32 + (lane & 31);
-            if (col >= p.n_out) continue;
-            const size_t o = static_cast<size_t>(r) * p.n_out + col;
-            if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = acc[mb][nb][v];
-            else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[mb][nb][v]);
+          for (int nb = 0; nb < NB; ++nb) {
+            const int col = c0 + wn * (BN / 4) + nb * 32 + (lane & 31);
+            if (col >= n_cols) continue;
+            reinterpret_cast<uint16_t*>(p.out)[static_cast<size_t>(r) * p.n_out + col] = f32_to_bf16(acc[mb][nb][v]);
           }
         }
       }
     }
   }
 }
+
+#ifndef MOE_DMA_BN
+#define MOE_DMA_BN 256
+#endif
+#ifndef MOE_DMA_ROWB
+#define MOE_DMA_ROWB 128
+#endif
+#ifndef MOE_DMA_STAGES
+#define MOE_DMA_STAGES 3
+#endif
+#ifndef MOE_DMA_WM
+#define MOE_DMA_WM 2
+#endif
 
 size_t gemm_tile_cap(int rows, int E) { return static_cast<size_t>((rows + GBM - 1) / GBM) + E; }
 
@@ -717,16 +734,17 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)
-#define MOE_LAUNCH_DMA(CT_, MODE_) \
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<CT_, MODE_>), grid, dim3(kDmaThreads), 0, s, p)
+#define MOE_LAUNCH_DMA(MODE_) \
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>), grid, \
+                     dim3(DmaCfg<MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>::kThreads), 0, s, p)
   if (mode == MODE_GATE_UP) {
-    if (ct == CT_F32) MOE_LAUNCH_DMA(CT_F32, MODE_GATE_UP);
-    else if (ct == CT_BF16) MOE_LAUNCH_DMA(CT_BF16, MODE_GATE_UP);
+    if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_GATE_UP);
+    else if (ct == CT_BF16) MOE_LAUNCH_DMA(MODE_GATE_UP);
     else MOE_LAUNCH(CT_FP8, false, MODE_GATE_UP);
   } else {
-    if (ct == CT_F32) MOE_LAUNCH_DMA(CT_F32, MODE_DOWN);
+    if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_DOWN);
     else if (b8) MOE_LAUNCH(CT_BF16, true, MODE_DOWN);
-    else MOE_LAUNCH_DMA(CT_BF16, MODE_DOWN);
+    else MOE_LAUNCH_DMA(MODE_DOWN);
   }
 #undef MOE_LAUNCH_DMA
 #undef MOE_LAUNCH
