@@ -30,7 +30,7 @@ def hipcc() -> str:
 
 
 def _flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             # packed fp32 VALU instructions are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -27,6 +27,8 @@
 // K block in a separate fp32 accumulator and adds it scaled by a_scale[row] *
 // w_scale[col]; the down GEMM converts e4m3 W_down to bf16 (exactly) on its way to LDS,
 // multiplies against bf16 h, and scales each 128-wide K block by w_scale[col].
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -475,7 +477,10 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;     // each wave owns kWR x BN/4 of the tile
+  // each wave owns kWR x BN/4 of the tile.  Waves w and w+4 share a SIMD (waves are placed
+  // round-robin), so giving them different row halves keeps both SIMD slots busy when a
+  // ragged tile leaves one half without rows.
+  const int wm = wave / 4, wn = wave % 4;
   const int lrow = lane / C::kChunks;           // row inside a DMA group
   // global chunk this lane loads: the slot it fills is lane % kChunks, XOR the row's key.
   // Every group this wave fills has the parity of the wave (groups w, w + waves, ...; 16 A
@@ -567,21 +572,23 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
 
-    auto load_frags = [&](int buf, int s, Frag<CT_BF16> (&fa)[MB], Frag<CT_BF16> (&fb)[NB])
+    auto load_frags = [&]<int ACT>(int buf, int s, Frag<CT_BF16> (&fa)[MB], Frag<CT_BF16> (&fb)[NB])
         __attribute__((always_inline)) {
       const uint8_t* base = lds + buf * C::kStageBytes;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) fa[mb].load(base + a_frag[mb] + koff[s]);
+      for (int mb = 0; mb < ACT; ++mb) fa[mb].load(base + a_frag[mb] + koff[s]);
+      if (ACT > 0) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) fb[nb].load(base + b_frag[nb] + koff[s]);
+        for (int nb = 0; nb < NB; ++nb) fb[nb].load(base + b_frag[nb] + koff[s]);
+      }
     };
     // the MB*NB MFMAs of one k-step; after MFMA i, run `between(i)` (kept in place by
     // scheduling fences so that it issues while the MFMA pipe is busy)
-    auto mfma_step = [&](Frag<CT_BF16> (&fa)[MB], Frag<CT_BF16> (&fb)[NB], auto&& between)
+    auto mfma_step = [&]<int ACT>(Frag<CT_BF16> (&fa)[MB], Frag<CT_BF16> (&fb)[NB], auto&& between)
         __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < MB * NB; ++i) {
-        acc[i / NB][i % NB] = mma(fa[i / NB], fb[i % NB], acc[i / NB][i % NB]);
+        if (i / NB < ACT) acc[i / NB][i % NB] = mma(fa[i / NB], fb[i % NB], acc[i / NB][i % NB]);
         __builtin_amdgcn_sched_barrier(0);
         between(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -609,45 +616,56 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
     else wait_vmcnt<0>();
     block_barrier();
 
-    Frag<CT_BF16> f0a[MB], f0b[NB], f1a[MB], f1b[NB];
-    load_frags(0, 0, f0a, f0b);
-    int buf = 0;
-    for (int ks = 0; ks < nk; ++ks) {
-      const int nbuf = buf == STAGES - 1 ? 0 : buf + 1;
-      const int lbuf = buf == 0 ? STAGES - 1 : buf - 1;    // (ks + STAGES - 1) % STAGES
-      const bool load_next = ks + kAhead < nk;
+    // 32-row blocks of this wave that hold rows of the segment: MFMAs and fragment reads of
+    // the others are skipped (the loads and barriers are the same on every path)
+    int act = (mlast + 1 - wm * kWR + 31) / 32;
+    act = act < 0 ? 0 : (act > MB ? MB : act);
+
+    auto k_loop = [&](auto act_c) __attribute__((always_inline)) {
+      constexpr int ACT = decltype(act_c)::value;
+      Frag<CT_BF16> f0a[MB], f0b[NB], f1a[MB], f1b[NB];
+      load_frags.template operator()<ACT>(0, 0, f0a, f0b);
+      int buf = 0;
+      for (int ks = 0; ks < nk; ++ks) {
+        const int nbuf = buf == STAGES - 1 ? 0 : buf + 1;
+        const int lbuf = buf == 0 ? STAGES - 1 : buf - 1;    // (ks + STAGES - 1) % STAGES
+        const bool load_next = ks + kAhead < nk;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        Frag<CT_BF16>(&ca)[MB] = (s & 1) ? f1a : f0a;
-        Frag<CT_BF16>(&cb)[NB] = (s & 1) ? f1b : f0b;
-        Frag<CT_BF16>(&na)[MB] = (s & 1) ? f0a : f1a;
-        Frag<CT_BF16>(&nb)[NB] = (s & 1) ? f0b : f1b;
-        if (s + 1 < KSTEPS) {
-          load_frags(buf, s + 1, na, nb);
-          __builtin_amdgcn_sched_barrier(0);
-          // load j of stage ks+kAhead goes after MFMA slot (j * kSlots) / PER
-          mfma_step(ca, cb, [&](int i) __attribute__((always_inline)) {
-            const int slot_i = s * MB * NB + i;
+        for (int s = 0; s < KSTEPS; ++s) {
+          Frag<CT_BF16>(&ca)[MB] = (s & 1) ? f1a : f0a;
+          Frag<CT_BF16>(&cb)[NB] = (s & 1) ? f1b : f0b;
+          Frag<CT_BF16>(&na)[MB] = (s & 1) ? f0a : f1a;
+          Frag<CT_BF16>(&nb)[NB] = (s & 1) ? f0b : f1b;
+          if (s + 1 < KSTEPS) {
+            load_frags.template operator()<ACT>(buf, s + 1, na, nb);
+            __builtin_amdgcn_sched_barrier(0);
+            // load j of stage ks+kAhead goes after MFMA slot (j * kSlots) / PER
+            mfma_step.template operator()<ACT>(ca, cb, [&](int i) __attribute__((always_inline)) {
+              const int slot_i = s * MB * NB + i;
 #pragma unroll
-            for (int j = 0; j < PER; ++j)
-              if ((j * kSlots) / PER == slot_i && load_next) dma_slice(ks + kAhead, lbuf, j);
-          });
-        } else {
-          // last k-step of stage ks
-          if (ks + 1 < nk) {
-            wait_lgkmcnt_all();                       // this wave's reads of buffer `buf` are done
-            // stage ks+1 landed; with three buffers stage ks+2 may stay in flight
-            if (kAhead == 2 && load_next) wait_vmcnt<(kAhead - 1) * PER>();
-            else wait_vmcnt<0>();
-            block_barrier();
-            load_frags(nbuf, 0, na, nb);
+              for (int j = 0; j < PER; ++j)
+                if ((j * kSlots) / PER == slot_i && load_next) dma_slice(ks + kAhead, lbuf, j);
+            });
+          } else {
+            // last k-step of stage ks
+            if (ks + 1 < nk) {
+              wait_lgkmcnt_all();                       // this wave's reads of buffer `buf` are done
+              // stage ks+1 landed; with three buffers stage ks+2 may stay in flight
+              if (kAhead == 2 && load_next) wait_vmcnt<(kAhead - 1) * PER>();
+              else wait_vmcnt<0>();
+              block_barrier();
+              load_frags.template operator()<ACT>(nbuf, 0, na, nb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step.template operator()<ACT>(ca, cb, nothing);
           }
-          __builtin_amdgcn_sched_barrier(0);
-          mfma_step(ca, cb, nothing);
         }
+        buf = nbuf;
       }
-      buf = nbuf;
-    }
+    };
+    if (act == MB) k_loop(std::integral_constant<int, MB>{});
+    else if (act > 0) k_loop(std::integral_constant<int, (MB > 1 ? 1 : MB)>{});
+    else k_loop(std::integral_constant<int, 0>{});
 
     // ---- epilogue
     const int mend = seg_hi;
