@@ -1,0 +1,42 @@
+// Arguments shared by the grouped expert GEMM kernels and their launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { CT_F32 = 0, CT_BF16 = 1, CT_FP8 = 2 };
+enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
+
+constexpr int kNumXcd = 8;
+
+struct GemmArgs {
+  const uint8_t* a;            // [rows, K] compute-type elements (e4m3 codes for CT_FP8)
+  const float* a_scale;        // [rows, K / 128]            (CT_FP8)
+  const uint8_t* b;            // [E, b_rows, K]: compute type, or e4m3 codes when B8
+  const float* b_scale;        // [E, b_rows, K / 128]       (CT_FP8, B8)
+  void* out;                   // gate/up: h [rows, I]; down: out [rows, H]
+  const int32_t* offsets;      // [E + 1]
+  const int32_t* tile_prefix;  // [E + 1]  m-tiles before each expert
+  const int32_t* tile_expert;  // [tile_cap]  m-tile -> expert
+  int E, K, rows, I, n_out, tile_cap;
+  long long b_rows;
+  int out_f32;
+};
+
+// Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot
+// index out of range.
+__device__ __forceinline__ void expert_segment(const GemmArgs& p, int e, int& lo, int& hi) {
+  lo = p.offsets[e];
+  hi = p.offsets[e + 1];
+  lo = lo < 0 ? 0 : (lo > p.rows ? p.rows : lo);
+  hi = hi < lo ? lo : (hi > p.rows ? p.rows : hi);
+}
+
+// Weight-streaming kernel for few rows per expert (grouped_gemm_stream.hip); the tile
+// schedule in `p` must have been built with 16-row m-tiles.
+constexpr int kStreamTileRows = 16;
+hipError_t launch_grouped_gemm_stream(int mode, const GemmArgs& p, hipStream_t s);
+
+}  // namespace moe

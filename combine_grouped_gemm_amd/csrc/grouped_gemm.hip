@@ -29,6 +29,7 @@
 // multiplies against bf16 h, and scales each 128-wide K block by w_scale[col].
 #include <type_traits>
 
+#include "grouped_gemm.h"
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -37,15 +38,12 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-enum { CT_F32 = 0, CT_BF16 = 1, CT_FP8 = 2 };
-enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
 
 constexpr int GBM = 128;          // rows of a tile
 constexpr int GBN = 256;          // weight rows of a tile (gate/up: 128 gate + 128 up)
 constexpr int GKB = 128;          // bytes of K per row and stage (compute type)
 constexpr int GPITCH = GKB + 16;  // padded LDS row pitch: 8 consecutive rows hit 8 bank groups
 constexpr int GTHREADS = 256;
-constexpr int kNumXcd = 8;
 constexpr int kAChunks = GBM * (GKB / 16) / GTHREADS;  // 16-byte A chunks per thread and stage (4)
 constexpr int kBChunks = GBN * (GKB / 16) / GTHREADS;  // B chunks per thread and stage (8)
 
@@ -54,24 +52,11 @@ template <> struct CTraits<CT_F32> { static constexpr int esz = 4; };
 template <> struct CTraits<CT_BF16> { static constexpr int esz = 2; };
 template <> struct CTraits<CT_FP8> { static constexpr int esz = 1; };
 
-struct GemmArgs {
-  const uint8_t* a;            // [rows, K] compute-type elements (e4m3 codes for CT_FP8)
-  const float* a_scale;        // [rows, K / 128]            (CT_FP8)
-  const uint8_t* b;            // [E, b_rows, K]: compute type, or e4m3 codes when B8
-  const float* b_scale;        // [E, b_rows, K / 128]       (CT_FP8, B8)
-  void* out;                   // gate/up: h [rows, I]; down: out [rows, H]
-  const int32_t* offsets;      // [E + 1]
-  const int32_t* tile_prefix;  // [E + 1]
-  const int32_t* tile_expert;  // [tile_cap]
-  int E, K, rows, I, n_out, tile_cap;
-  long long b_rows;
-  int out_f32;
-};
-
-// Tile schedule prologue: m-tiles of each expert, their prefix and the m-tile -> expert
-// table.  Offsets are clamped into [0, rows] so malformed input cannot index out of range.
+// Tile schedule prologue: m-tiles (of tile_rows rows) of each expert, their prefix and the
+// m-tile -> expert table.  Offsets are clamped into [0, rows] so malformed input cannot
+// index out of range.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int rows, int tile_cap,
+                                                           int rows, int tile_rows, int tile_cap,
                                                            int32_t* __restrict__ prefix,
                                                            int32_t* __restrict__ tile_expert) {
   __shared__ int32_t tot[1024];
@@ -81,7 +66,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     int lo = offsets[e], hi = offsets[e + 1];
     lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
     hi = hi < lo ? lo : (hi > rows ? rows : hi);
-    mt = (hi - lo + GBM - 1) / GBM;
+    mt = (hi - lo + tile_rows - 1) / tile_rows;
   }
   tot[e] = mt;
   __syncthreads();
@@ -711,7 +696,10 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
 #define MOE_DMA_WM 2
 #endif
 
-size_t gemm_tile_cap(int rows, int E) { return static_cast<size_t>((rows + GBM - 1) / GBM) + E; }
+// m-tiles at the finest granularity any kernel uses (16 rows)
+size_t gemm_tile_cap(int rows, int E) {
+  return static_cast<size_t>((rows + kStreamTileRows - 1) / kStreamTileRows) + E;
+}
 
 size_t gemm_schedule_bytes(int rows, int E) {
   const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E);
@@ -730,8 +718,15 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   int32_t* prefix = reinterpret_cast<int32_t*>(sched);
   int32_t* tile_expert = prefix + E + 1;
   const int cap = static_cast<int>(gemm_tile_cap(rows, E));
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, cap, prefix,
-                     tile_expert);
+  // few rows per expert and e4m3 weights: the weight-streaming kernel (16-row m-tiles)
+  const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) &&
+                      static_cast<long long>(rows) <= static_cast<long long>(kStreamTileRows) * E &&
+                      (mode == MODE_GATE_UP ? I % 64 == 0 : n_out % 128 == 0) &&
+                      static_cast<long long>(gemm_tile_cap(rows, E)) * (mode == MODE_GATE_UP ? I / 64 : n_out / 128) <
+                          (1LL << 31);
+  const int tile_rows = stream ? kStreamTileRows : GBM;
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
+                     prefix, tile_expert);
   GemmArgs p;
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.a_scale = a_scale;
@@ -749,6 +744,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.tile_cap = cap;
   p.b_rows = b_rows;
   p.out_f32 = out_f32 ? 1 : 0;
+  if (stream) return launch_grouped_gemm_stream(mode, p, s);
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)

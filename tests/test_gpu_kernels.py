@@ -226,6 +226,10 @@ GEMM_CASES = [
     ("f32_ragged", [60, 0, 200, 1, 70], 256, 256, "f32"),
     ("fp8_ragged", [3, 0, 17, 128, 130, 1], 512, 256, "fp8"),
     ("bf16_wide_K", [200, 90], 7168, 256, "bf16"),
+    # at most 16 rows per expert on average with e4m3 weights: the weight-streaming kernels
+    ("fp8_decode_ragged", [0, 1, 2, 5, 16, 17, 33, 0, 3, 0, 9, 1, 4, 0, 7, 12], 1024, 256, "fp8"),
+    ("fp8_decode_one_k_block", [1, 0], 128, 128, "fp8"),
+    ("fp8_decode_wide", [4, 0, 7], 7168, 2048, "fp8"),
 ]
 
 
@@ -288,6 +292,37 @@ def test_expert_down_on_generated_h():
     # fp32 accumulation then one bf16 rounding: within one bf16 step of the exact value
     got = f64(out)
     assert np.all(np.abs(got - ref) <= bf16_ulp(ref) + 1e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("n_e", [[16] * 16, [128, 128]], ids=["streaming", "tiled"])
+def test_expert_down_e4m3_weights_every_code(n_e):
+    """Down GEMM on e4m3 weights holding every finite code, read back exactly.
+
+    Row r of h is one-hot at K index r, so out[r, n] = decode(W_e[n, r]) * s_e[n, r // 128]
+    with no rounding, also not in the bf16 output: the scales 1, 1.25, 1.5, 1.75 keep every
+    product within 8 significant bits.  Across n the codes (n + 7 r + 3 e) mod 256 take
+    every value (NaN codes 0x7f and 0xff replaced by 0), so each row checks every code's
+    conversion.
+    """
+    E, rows, I, H = len(n_e), sum(n_e), 256, 256
+    say(f"down e4m3 every code, n_e {n_e[:2]}...")
+    h = torch.zeros((rows, I), dtype=torch.bfloat16)
+    h[torch.arange(rows), torch.arange(rows)] = 1.0
+    n = np.arange(H)[None, :, None]
+    kk = np.arange(I)[None, None, :]
+    ee = np.arange(E)[:, None, None]
+    codes = ((n + 7 * kk + 3 * ee) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    scale = (1.0 + ((np.arange(H)[None, :, None] + np.arange(I // 128)[None, None, :]) % 4) / 4.0)
+    scale = np.broadcast_to(scale, (E, H, I // 128)).astype(np.float32)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(n_e)]), dtype=torch.int32, device=DEV)
+    q2, s2 = torch.from_numpy(codes).to(DEV), torch.from_numpy(np.ascontiguousarray(scale)).to(DEV)
+    out = moe.moe_expert_down(h.to(DEV), offs, q2, s2)
+    sync()
+    expert = np.repeat(np.arange(E), n_e)
+    r = np.arange(rows)
+    ref = oracle.e4m3_decode(codes[expert, :, r]) * scale[expert, :, r // 128].astype(np.float64)
+    assert np.array_equal(f64(out), ref)
 
 
 # ------------------------------------------------------------------------------------------
