@@ -51,8 +51,8 @@ struct StreamStage {
   static constexpr int kA = MODE == MODE_GATE_UP ? 2 : 4;  // 16-byte A loads per lane and K block
   uint4 b[kSCB][2];
   uint4 a[kA];
-  float sa;                                                // gate/up: a_scale of row l % 16
-  float sb[kSCB];
+  float sa;      // gate/up: a_scale of row l % 16
+  float sb[2];   // w_scale of weight row l % 16 of blocks l / 16 and l / 16 + 4
 };
 
 // Panel weight-row offset of block cb: gate/up takes 64 gate rows and the matching 64 up
@@ -63,8 +63,11 @@ __device__ __forceinline__ int panel_row(int cb, int I) {
   return 16 * cb;
 }
 
-template <int MODE, int STAGES, int WG_PER_CU>
+// VEC: the K blocks per row are a multiple of 4, and the scales are loaded as float4 groups
+// of 4 consecutive K blocks, one load per row every 4 steps.
+template <int MODE, int STAGES, int WG_PER_CU, bool VEC>
 __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_kernel(GemmArgs p) {
+  static_assert(!VEC || STAGES <= 4, "a scale group is reloaded 4 steps after it is taken");
   constexpr bool kGU = MODE == MODE_GATE_UP;
   constexpr int kPanelCols = kGU ? 64 : 128;        // output columns of a panel
   constexpr int kAEsz = kGU ? 1 : 2;                // bytes per A element
@@ -91,9 +94,12 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
   if (n_my == 0) return;
   const int total = n_my * nk;   // steps
 
-  // lane offsets that hold for every tile: weight row c of each block, K quarter q
+  // lane offsets that hold for every tile: weight row c of each block, K quarter q; the
+  // weight scales of row c of blocks q and q + 4 (one load each per K block, handed to the
+  // lanes that need them by ds_bpermute)
   const uint32_t voff_b = static_cast<uint32_t>(c) * K + 32 * q;
-  const uint32_t voff_sb = static_cast<uint32_t>(c) * kblocks;
+  const uint32_t voff_sb0 = static_cast<uint32_t>(panel_row<MODE>(q, p.I) + c) * kblocks;
+  const uint32_t voff_sb1 = static_cast<uint32_t>(panel_row<MODE>(q + 4, p.I) + c) * kblocks;
 
   struct Tile {
     int e, m0, seg_hi, row0;
@@ -147,6 +153,13 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
       set_load_tile(ld_j);
     }
   };
+  // scale groups (VEC): taken into g_cur by the compute cursor at K blocks 0 mod 4, loaded
+  // into g_next by the load cursor at the same K blocks, at most 4 steps earlier
+  struct ScaleGroup {
+    float4 sb[2];
+    float4 sa;
+  };
+  ScaleGroup g_cur, g_next;
   auto issue = [&](StreamStage<MODE>& st) __attribute__((always_inline)) {
     const uint8_t* bk = ld_b + static_cast<size_t>(ld_kb) * 128;
 #pragma unroll
@@ -158,10 +171,17 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
     const uint8_t* ak = ld_a + static_cast<size_t>(ld_kb) * 128 * kAEsz + voff_a;
 #pragma unroll
     for (int i = 0; i < StreamStage<MODE>::kA; ++i) st.a[i] = *reinterpret_cast<const uint4*>(ak + 16 * i);
-    if (kGU) st.sa = ld_sa[voff_sa + ld_kb];
-#pragma unroll
-    for (int cb = 0; cb < kSCB; ++cb)
-      st.sb[cb] = ld_sb[static_cast<size_t>(panel_row<MODE>(cb, p.I)) * kblocks + voff_sb + ld_kb];
+    if constexpr (VEC) {
+      if ((ld_kb & 3) == 0) {
+        if (kGU) g_next.sa = *reinterpret_cast<const float4*>(ld_sa + voff_sa + ld_kb);
+        g_next.sb[0] = *reinterpret_cast<const float4*>(ld_sb + voff_sb0 + ld_kb);
+        g_next.sb[1] = *reinterpret_cast<const float4*>(ld_sb + voff_sb1 + ld_kb);
+      }
+    } else {
+      if (kGU) st.sa = ld_sa[voff_sa + ld_kb];
+      st.sb[0] = ld_sb[voff_sb0 + ld_kb];
+      st.sb[1] = ld_sb[voff_sb1 + ld_kb];
+    }
   };
 
   // ---- compute cursor
@@ -200,19 +220,37 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
       }
     }
     // scale this K block's products into the totals; D row 4 q + v, column c
+    float sb_own[2], sa_own = 0.0f;
+    if constexpr (VEC) {
+      if ((c_kb & 3) == 0) g_cur = g_next;
+      sb_own[0] = g_cur.sb[0].x;
+      sb_own[1] = g_cur.sb[1].x;
+      sa_own = g_cur.sa.x;
+      // shift the next K block's scales into .x
+#pragma unroll
+      for (int h = 0; h < 2; ++h) g_cur.sb[h] = make_float4(g_cur.sb[h].y, g_cur.sb[h].z, g_cur.sb[h].w, 0.0f);
+      if (kGU) g_cur.sa = make_float4(g_cur.sa.y, g_cur.sa.z, g_cur.sa.w, 0.0f);
+    } else {
+      sb_own[0] = st.sb[0];
+      sb_own[1] = st.sb[1];
+      if (kGU) sa_own = st.sa;
+    }
+    float sb[kSCB];
+#pragma unroll
+    for (int cb = 0; cb < kSCB; ++cb) sb[cb] = __shfl(sb_own[cb >> 2], c + 16 * (cb & 3), 64);
     if constexpr (kGU) {
       float sav[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sav[v] = __shfl(st.sa, 4 * q + v, 64);
+      for (int v = 0; v < 4; ++v) sav[v] = __shfl(sa_own, 4 * q + v, 64);
 #pragma unroll
       for (int cb = 0; cb < kSCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[cb][v] += part[cb][v] * (sav[v] * st.sb[cb]);
+        for (int v = 0; v < 4; ++v) acc[cb][v] += part[cb][v] * (sav[v] * sb[cb]);
     } else {
 #pragma unroll
       for (int cb = 0; cb < kSCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[cb][v] += part[cb][v] * st.sb[cb];
+        for (int v = 0; v < 4; ++v) acc[cb][v] += part[cb][v] * sb[cb];
     }
   };
 
@@ -279,12 +317,18 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
 
 hipError_t launch_grouped_gemm_stream(int mode, const GemmArgs& p, hipStream_t s) {
   const dim3 grid(256 * MOE_STREAM_WG_PER_CU), block(kSWaves * 64);
-  if (mode == MODE_GATE_UP)
-    hipLaunchKernelGGL((grouped_gemm_stream_kernel<MODE_GATE_UP, MOE_STREAM_STAGES, MOE_STREAM_WG_PER_CU>),
-                       grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((grouped_gemm_stream_kernel<MODE_DOWN, MOE_STREAM_STAGES, MOE_STREAM_WG_PER_CU>),
-                       grid, block, 0, s, p);
+  const bool vec = (p.K / 128) % 4 == 0;
+#define MOE_LAUNCH_STREAM(MODE_, VEC_)                                                                      \
+  hipLaunchKernelGGL((grouped_gemm_stream_kernel<MODE_, MOE_STREAM_STAGES, MOE_STREAM_WG_PER_CU, VEC_>), grid, \
+                     block, 0, s, p)
+  if (mode == MODE_GATE_UP) {
+    if (vec) MOE_LAUNCH_STREAM(MODE_GATE_UP, true);
+    else MOE_LAUNCH_STREAM(MODE_GATE_UP, false);
+  } else {
+    if (vec) MOE_LAUNCH_STREAM(MODE_DOWN, true);
+    else MOE_LAUNCH_STREAM(MODE_DOWN, false);
+  }
+#undef MOE_LAUNCH_STREAM
   return hipGetLastError();
 }
 
