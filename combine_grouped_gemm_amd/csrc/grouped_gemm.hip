@@ -28,6 +28,7 @@
 // w_scale[col]; the down GEMM converts e4m3 W_down to bf16 (exactly) on its way to LDS,
 // multiplies against bf16 h, and scales each 128-wide K block by w_scale[col].
 #include <type_traits>
+#include <utility>
 
 #include "grouped_gemm.h"
 #include "moe_common.h"
@@ -393,6 +394,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
 // s_barrier, which keeps the later stages in flight across the barrier.
 // ------------------------------------------------------------------------------------
 
+#ifndef MOE_DMA_OCC
+#define MOE_DMA_OCC 1   // workgroups per CU
+#endif
+
 constexpr int kDM = 128;                                // rows of a tile
 constexpr int kDGroup = 1024;                           // bytes of one DMA wave instruction
 template <int BN, int ROWB, int STAGES, int WM>
@@ -445,7 +450,7 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 }
 
 template <int MODE, int BN, int ROWB, int STAGES, int WM>
-__global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel(GemmArgs p) {
   using C = DmaCfg<BN, ROWB, STAGES, WM>;
   constexpr int KSTEPS = C::kKSteps;
   constexpr int NB = C::kNB;
@@ -456,6 +461,7 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
   static_assert(KSTEPS % 2 == 0, "a stage must end in fragment set 1 so the next starts in set 0");
   static_assert(MODE != MODE_GATE_UP || NB % 2 == 0, "gate/up pairs");
 
+  static_assert(STAGES * C::kStageBytes * MOE_DMA_OCC <= 160 * 1024, "LDS of the resident workgroups");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStageBytes];
   const uint32_t lds_addr0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
 
@@ -588,8 +594,14 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
     // of the last k-step each wave waits for stage ks+1, the barrier makes that hold for all
     // waves and frees buffer ks % STAGES, and the first fragments of stage ks+1 are read
     // while the last k-step's MFMAs run.
-    static_assert(STAGES == 2 || STAGES == 3, "two or three buffers");
+    static_assert(STAGES >= 2 && (STAGES - 2) * PER < 64, "buffers, and the loads a wait may leave in flight");
     constexpr int kAhead = STAGES - 1;                     // stages loading while one is used
+    // wait until at most n stages of loads remain in flight (n < kAhead)
+    auto wait_stages = [](int n) __attribute__((always_inline)) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((n == I ? wait_vmcnt<I * PER>() : void()), ...);
+      }(std::make_integer_sequence<int, kAhead>{});
+    };
     constexpr int kSlots = (KSTEPS - 1) * MB * NB;         // MFMA slots that may carry a load
     static_assert(PER <= kSlots, "not enough MFMA slots to spread a stage's loads");
     wait_vmcnt<0>();   // the previous tile's epilogue stores have drained
@@ -597,8 +609,7 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
     for (int st = 0; st < kAhead && st < nk; ++st)
 #pragma unroll
       for (int j = 0; j < PER; ++j) dma_slice(st, st, j);
-    if (kAhead == 2 && nk > 1) wait_vmcnt<(kAhead - 1) * PER>();
-    else wait_vmcnt<0>();
+    wait_stages((kAhead < nk ? kAhead : nk) - 1);   // stage 0 landed
     block_barrier();
 
     // 32-row blocks of this wave that hold rows of the segment: MFMAs and fragment reads of
@@ -635,9 +646,8 @@ __global__ __launch_bounds__(WM * 256, 1) void grouped_gemm_dma_kernel(GemmArgs 
             // last k-step of stage ks
             if (ks + 1 < nk) {
               wait_lgkmcnt_all();                       // this wave's reads of buffer `buf` are done
-              // stage ks+1 landed; with three buffers stage ks+2 may stay in flight
-              if (kAhead == 2 && load_next) wait_vmcnt<(kAhead - 1) * PER>();
-              else wait_vmcnt<0>();
+              // stage ks+1 landed; the stages issued after it may stay in flight
+              wait_stages(kAhead - 1 < nk - 2 - ks ? kAhead - 1 : nk - 2 - ks);
               block_barrier();
               load_frags.template operator()<ACT>(nbuf, 0, na, nb);
             }
@@ -749,7 +759,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)
 #define MOE_LAUNCH_DMA(MODE_) \
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>), grid, \
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>), \
+                     dim3(persistent_grid() * MOE_DMA_OCC), \
                      dim3(DmaCfg<MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>::kThreads), 0, s, p)
   if (mode == MODE_GATE_UP) {
     if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_GATE_UP);
