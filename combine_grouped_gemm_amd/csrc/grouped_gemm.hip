@@ -398,7 +398,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
 #define MOE_DMA_OCC 1   // workgroups per CU
 #endif
 
-constexpr int kDM = 128;                                // rows of a tile
+
+#ifndef MOE_DMA_DM
+#define MOE_DMA_DM 128  // rows of a tile
+#endif
+constexpr int kDM = MOE_DMA_DM;
 constexpr int kDGroup = 1024;                           // bytes of one DMA wave instruction
 template <int BN, int ROWB, int STAGES, int WM>
 struct DmaCfg {
@@ -518,8 +522,13 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
     int seg_lo = p.offsets[e], seg_hi = p.offsets[e + 1];
     seg_lo = seg_lo < 0 ? 0 : (seg_lo > p.rows ? p.rows : seg_lo);
     seg_hi = seg_hi < seg_lo ? seg_lo : (seg_hi > p.rows ? p.rows : seg_hi);
-    const int m0 = seg_lo + mtile * kDM;
-    const int mlast = seg_hi - 1 - m0;
+    // the expert's rows are split into mt_e tiles of equal size (a multiple of 32 rows):
+    // the tiles that share a weight panel do equal work and stream it together, which
+    // keeps more of the panel's second and third reads in L2
+    const int rpt = ((seg_hi - seg_lo + mt_e - 1) / mt_e + 31) / 32 * 32;
+    const int m0 = seg_lo + mtile * rpt;
+    const int mend = m0 + rpt < seg_hi ? m0 + rpt : seg_hi;
+    const int mlast = mend - 1 - m0;
     const int c0 = nblk * tile_cols;
     const int clast = n_cols - 1 - c0;
 
@@ -622,10 +631,13 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
       Frag<CT_BF16> f0a[MB], f0b[NB], f1a[MB], f1b[NB];
       load_frags.template operator()<ACT>(0, 0, f0a, f0b);
       int buf = 0;
-      for (int ks = 0; ks < nk; ++ks) {
+      // one stage; LOAD: stage ks + kAhead exists and is loaded now, NEXT: stage ks + 1
+      // exists.  The three kinds of stage run in separate loops, so that no branch on these
+      // conditions sits between the MFMAs (at such a join the compiler's LDS wait before
+      // the first MFMA of the last k-step would also cover the next stage's fresh reads).
+      auto stage = [&]<bool LOAD, bool NEXT>(int ks) __attribute__((always_inline)) {
         const int nbuf = buf == STAGES - 1 ? 0 : buf + 1;
         const int lbuf = buf == 0 ? STAGES - 1 : buf - 1;    // (ks + STAGES - 1) % STAGES
-        const bool load_next = ks + kAhead < nk;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
           Frag<CT_BF16>(&ca)[MB] = (s & 1) ? f1a : f0a;
@@ -640,14 +652,15 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
               const int slot_i = s * MB * NB + i;
 #pragma unroll
               for (int j = 0; j < PER; ++j)
-                if ((j * kSlots) / PER == slot_i && load_next) dma_slice(ks + kAhead, lbuf, j);
+                if (LOAD && (j * kSlots) / PER == slot_i) dma_slice(ks + kAhead, lbuf, j);
             });
           } else {
             // last k-step of stage ks
-            if (ks + 1 < nk) {
+            if constexpr (NEXT) {
               wait_lgkmcnt_all();                       // this wave's reads of buffer `buf` are done
               // stage ks+1 landed; the stages issued after it may stay in flight
-              wait_stages(kAhead - 1 < nk - 2 - ks ? kAhead - 1 : nk - 2 - ks);
+              if constexpr (LOAD) wait_stages(kAhead - 1);
+              else wait_stages(nk - 2 - ks);
               block_barrier();
               load_frags.template operator()<ACT>(nbuf, 0, na, nb);
             }
@@ -656,14 +669,18 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
           }
         }
         buf = nbuf;
-      }
+      };
+      int ks = 0;
+      for (; ks < nk - kAhead; ++ks) stage.template operator()<true, true>(ks);
+      for (; ks < nk - 1; ++ks) stage.template operator()<false, true>(ks);
+      stage.template operator()<false, false>(ks);
     };
-    if (act == MB) k_loop(std::integral_constant<int, MB>{});
-    else if (act > 0) k_loop(std::integral_constant<int, (MB > 1 ? 1 : MB)>{});
-    else k_loop(std::integral_constant<int, 0>{});
+    // one instantiation of the k-loop per number of active 32-row blocks (0..MB)
+    [&]<int... A>(std::integer_sequence<int, A...>) {
+      ((act == A ? k_loop(std::integral_constant<int, A>{}) : void()), ...);
+    }(std::make_integer_sequence<int, MB + 1>{});
 
     // ---- epilogue
-    const int mend = seg_hi;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -734,7 +751,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                       (mode == MODE_GATE_UP ? I % 64 == 0 : n_out % 128 == 0) &&
                       static_cast<long long>(gemm_tile_cap(rows, E)) * (mode == MODE_GATE_UP ? I / 64 : n_out / 128) <
                           (1LL << 31);
-  const int tile_rows = stream ? kStreamTileRows : GBM;
+  const bool dma = ct == CT_BF16 && !b8;   // bf16 operands: the direct-to-LDS kernel
+  const int tile_rows = stream ? kStreamTileRows : (dma ? kDM : GBM);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert);
   GemmArgs p;
