@@ -53,8 +53,11 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic(cfg, n_e):
-    """Algorithmic bytes and flops of each step (what the method must move or compute)."""
+def algorithmic(cfg, n_e, gather=False):
+    """Algorithmic bytes and flops of each step (what the method must move or compute).
+
+    gather: the gate/up GEMM reads its rows straight from x (each token row at least once)
+    instead of from a permuted copy."""
     import numpy as np
     N, H, E, k, I = cfg.N, cfg.H, cfg.E, cfg.k, cfg.I
     rows = N * k
@@ -67,7 +70,8 @@ def algorithmic(cfg, n_e):
     d["route"] = {"bytes": N * E * 4 + (E * 4 if cfg.zipf_s else 0) + rows * 8}
     d["layout"] = {"bytes": rows * 4 + (2 * E + 1) * 4 + 2 * rows * 4}
     d["permute"] = {"bytes": N * H * act + rows * H * (pay + fp8_scale)}
-    d["gate_up"] = {"bytes": touched * 2 * I * H * (wb + fp8_scale) + rows * H * (pay + fp8_scale) + rows * I * 2,
+    a_bytes = N * H * act if gather else rows * H * (pay + fp8_scale)
+    d["gate_up"] = {"bytes": touched * 2 * I * H * (wb + fp8_scale) + a_bytes + rows * I * 2,
                     "flops": 4.0 * rows * H * I}
     d["down"] = {"bytes": touched * H * I * (wb + fp8_scale) + rows * I * 2 + rows * H * act,
                  "flops": 2.0 * rows * H * I}
@@ -140,19 +144,13 @@ def main():
     x, z = inp["x"], inp["z"]
     torch.cuda.synchronize()
 
-    rows = cfg.N * cfg.k
-    h_buf = layer.h
-    from combine_grouped_gemm_amd import moe_expert_down, moe_expert_gate_up
-
-    sched_ws = layer.ffn_ws  # the schedule lives at the start of the FFN workspace
-
+    # the layer's own calls, one stage each (bf16 layers fold the permute into gate/up)
     stages = [("route", lambda: layer.route(z)),
-              ("layout", layer.dispatch),
-              ("permute", lambda: layer.permute(x)),
-              ("gate_up", lambda: moe_expert_gate_up(layer.x_perm, layer.layout[1], layer.w13,
-                                                     layer.x_perm_scale, layer.w13_scale, h_buf, sched_ws)),
-              ("down", lambda: moe_expert_down(h_buf, layer.layout[1], layer.w2, layer.w2_scale,
-                                               layer.expert_out, sched_ws))]
+              ("layout", layer.dispatch)]
+    if not layer.gather:
+        stages.append(("permute", lambda: layer.permute(x)))
+    stages += [("gate_up", lambda: layer.gate_up(x)),
+               ("down", layer.down)]
     if cfg.shared:
         stages.append(("shared", lambda: layer.shared_expert(x)))
     stages.append(("combine", layer.combine))
@@ -199,7 +197,7 @@ def main():
     value = cfg.N / (ms_per_step / 1e3)
 
     n_e = layer.layout[0].cpu().numpy()
-    alg = algorithmic(cfg, n_e)
+    alg = algorithmic(cfg, n_e, layer.gather)
     kernels = {}
     for name, times in per.items():
         t = sorted(times)
@@ -233,7 +231,8 @@ def main():
                 "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic
-    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)"
+    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU, rows gathered from x (moe_expert_gate_up_gathered)"
+                      if layer.gather else "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)")
     roof["algorithmic_bytes"] = int(g["bytes"])
     roof["algorithmic_flops"] = g["flops"]
 
@@ -257,7 +256,8 @@ def main():
         "kernels": kernels,
         "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),
                                    "down": kernels["down"].get("mfma_frac")},
-        "permute_hbm_GBps": kernels["permute"]["GB_per_s"],
+        "permute_hbm_GBps": kernels["permute"]["GB_per_s"] if "permute" in kernels else None,
+        "permute_folded_into_gate_up": layer.gather,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),

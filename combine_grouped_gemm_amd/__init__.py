@@ -55,6 +55,7 @@ _SIGS = {
     "moe_quantize_fp8": [_P, _I, ctypes.c_int64, _I, _P, _P, _P],
     "moe_grouped_ffn": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "moe_expert_gate_up": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
+    "moe_expert_gate_up_gathered": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
     "moe_expert_down": [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _SZ, _P],
     "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
@@ -219,6 +220,25 @@ def moe_expert_gate_up(a: torch.Tensor, offsets: torch.Tensor, w13: torch.Tensor
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
         _ptr(a), _ptr(a_scale), adt, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(w13_scale),
         _ptr(h), _ptr(ws), ws.numel(), _stream(a)))
+    return h
+
+
+def moe_expert_gate_up_gathered(x: torch.Tensor, src_slot: torch.Tensor, k: int, offsets: torch.Tensor,
+                                w13: torch.Tensor, rows: Optional[int] = None, h: Optional[torch.Tensor] = None,
+                                ws: Optional[torch.Tensor] = None):
+    """Gate/up GEMM whose row r reads token src_slot[r] // k of x (no permuted copy)."""
+    N, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if rows is None:
+        rows = src_slot.numel()
+    if h is None:
+        h = torch.empty((rows, I), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16), x.device)
+    _check("moe_expert_gate_up_gathered", lib().moe_expert_gate_up_gathered(
+        _ptr(x), _dt(x), N, _ptr(src_slot), k, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(h),
+        _ptr(ws), ws.numel(), _stream(x)))
     return h
 
 

@@ -20,6 +20,8 @@ struct GemmArgs {
   const int32_t* offsets;      // [E + 1]
   const int32_t* tile_prefix;  // [E + 1]  m-tiles before each expert
   const int32_t* tile_expert;  // [tile_cap]  m-tile -> expert
+  const int32_t* a_rows;       // [rows] or null: row r of the operand is row a_rows[r] / a_div of a
+  int a_div, a_nrows;          // (gathered operand: a has a_nrows rows)
   int E, K, rows, I, n_out, tile_cap;
   long long b_rows;
   int out_f32;

@@ -532,7 +532,9 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
     const int c0 = nblk * tile_cols;
     const int clast = n_cols - 1 - c0;
 
-    const uint8_t* a_tile = p.a + static_cast<size_t>(m0) * rb;
+    // gathered operand: tile row r is row a_rows[m0 + r] / a_div of a (the launcher checks
+    // that a_nrows * rb fits in 32 bits)
+    const uint8_t* a_tile = p.a_rows ? p.a : p.a + static_cast<size_t>(m0) * rb;
     const uint8_t* b_tile = p.b + static_cast<size_t>(e) * p.b_rows * rb;
 
     // this lane's source offsets; wave w fills groups w, w + waves, ... (A groups first).
@@ -544,6 +546,11 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
       if (j < C::kAPerWave) {
         int r = g * C::kRowsPerGroup + lrow;
         r = r < mlast ? r : mlast;
+        if (p.a_rows) {
+          int t = p.a_rows[m0 + r] / p.a_div;
+          t = t < 0 ? 0 : (t < p.a_nrows ? t : p.a_nrows - 1);
+          r = t;
+        }
         src[j] = static_cast<uint32_t>(r) * rb + lchunk * 16;
       } else {
         const int r = (g - C::kAGroups) * C::kRowsPerGroup + lrow;   // tile weight row
@@ -741,7 +748,8 @@ static int persistent_grid() {
 hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,
                                const void* b, const float* b_scale, void* out, bool out_f32,
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,
-                               long long b_rows, void* sched, hipStream_t s) {
+                               long long b_rows, void* sched, hipStream_t s, const int32_t* a_rows,
+                               int a_div, int a_nrows) {
   int32_t* prefix = reinterpret_cast<int32_t*>(sched);
   int32_t* tile_expert = prefix + E + 1;
   const int cap = static_cast<int>(gemm_tile_cap(rows, E));
@@ -764,6 +772,9 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.offsets = offsets;
   p.tile_prefix = prefix;
   p.tile_expert = tile_expert;
+  p.a_rows = a_rows;
+  p.a_div = a_div > 0 ? a_div : 1;
+  p.a_nrows = a_nrows;
   p.E = E;
   p.K = K;
   p.rows = rows;

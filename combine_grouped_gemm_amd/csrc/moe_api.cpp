@@ -164,6 +164,23 @@ moe_status moe_expert_gate_up(const void* a, const float* a_scale, moe_dtype a_d
                                              2ll * I, ws, stream));
 }
 
+moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
+                                       int k, const int32_t* offsets, int E, int rows, int H, int I,
+                                       const void* w13, void* h, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  if (x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const moe_status st = check_gemm(offsets, E, rows, H, I, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (N < 0 || k < 1 || k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (N == 0 || x == nullptr || src_slot == nullptr || w13 == nullptr || h == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13)) return MOE_ERR_INVALID_ARG;
+  if (static_cast<long long>(N) * H * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_grouped_gemm(1, false, 0, x, nullptr, w13, nullptr, h, false, offsets,
+                                             E, rows, H, I, I, 2ll * I, ws, stream, src_slot, k, N));
+}
+
 moe_status moe_expert_down(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                            int I, int H, const void* w2, moe_dtype w2_dt, const float* w2_scale,
                            void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,

@@ -30,6 +30,7 @@ size_t gemm_schedule_bytes(int rows, int E);
 hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,
                                const void* b, const float* b_scale, void* out, bool out_f32,
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,
-                               long long b_rows, void* sched, hipStream_t s);
+                               long long b_rows, void* sched, hipStream_t s,
+                               const int32_t* a_rows = nullptr, int a_div = 1, int a_nrows = 0);
 
 }  // namespace moe

@@ -5,6 +5,11 @@
 ("MoE part 4" page, section 4 and 4.2; "EP / DeepEP explanation" page, sections 2-3.)
 All buffers are allocated once, at construction, so a forward pass enqueues
 only kernels: no allocation, no host synchronisation, no device-to-host copy.
+
+bf16 layers fold the permute into the gate/up GEMM by default (``gather=True``): its
+operand rows are read straight from x through the layout's src_slot map, so the
+permuted copy of x is never written.  f32 and fp8 layers (the fp8 permute also
+quantizes) run the permute kernel.
 """
 from __future__ import annotations
 
@@ -13,8 +18,9 @@ from typing import Optional
 import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN,
-               moe_combine, moe_dispatch_layout, moe_grouped_ffn, moe_permute, moe_quantize_fp8,
-               moe_route, moe_workspace_bytes)
+               moe_combine, moe_dispatch_layout, moe_expert_down, moe_expert_gate_up,
+               moe_expert_gate_up_gathered, moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route,
+               moe_workspace_bytes)
 
 
 class MoELayer:
@@ -30,12 +36,13 @@ class MoELayer:
     def __init__(self, N: int, H: int, E: int, k: int, I: int, dtype: str, w13: torch.Tensor,
                  w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
                  shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
-                 bias: Optional[torch.Tensor] = None):
+                 bias: Optional[torch.Tensor] = None, gather: bool = True):
         self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
         self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
         dev = w13.device
         self.device = dev
         self.fp8 = dtype == "fp8"
+        self.gather = gather and dtype == "bf16"
         act = torch.float32 if dtype == "f32" else torch.bfloat16
         self.act_dtype = act
         rows = N * k
@@ -59,7 +66,8 @@ class MoELayer:
                                      dtype=torch.uint8, device=dev)
         a_dt = MOE_FP8_E4M3 if self.fp8 else (MOE_F32 if dtype == "f32" else MOE_BF16)
         self.a_dt = a_dt
-        self.x_perm = torch.empty((rows, H), dtype=torch.uint8 if self.fp8 else act, device=dev)
+        self.x_perm = None if self.gather else torch.empty((rows, H), dtype=torch.uint8 if self.fp8 else act,
+                                                          device=dev)
         self.x_perm_scale = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
         self.ffn_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt), 256),
                                   dtype=torch.uint8, device=dev)
@@ -90,12 +98,30 @@ class MoELayer:
         return moe_dispatch_layout(self.topk_idx, self.E, self.layout, self.layout_ws)
 
     def permute(self, x: torch.Tensor):
+        """The permuted payload (nothing to do when the gate/up GEMM gathers its rows)."""
         send_pos = self.layout[2]
+        if self.gather:
+            return None
         if self.fp8:
             return moe_permute(x, send_pos, self.k, MOE_FP8_E4M3, self.x_perm, self.x_perm_scale)
         return moe_permute(x, send_pos, self.k, None, self.x_perm)
 
-    def experts(self):
+    def gate_up(self, x: torch.Tensor):
+        """Grouped gate/up GEMM + SwiGLU into h (gathered layers read x directly)."""
+        if self.gather:
+            return moe_expert_gate_up_gathered(x, self.layout[3], self.k, self.layout[1], self.w13,
+                                               h=self.h, ws=self.ffn_ws)
+        return moe_expert_gate_up(self.x_perm, self.layout[1], self.w13, self.x_perm_scale, self.w13_scale,
+                                  self.h, self.ffn_ws)
+
+    def down(self):
+        """Grouped down GEMM of h into the expert outputs."""
+        return moe_expert_down(self.h, self.layout[1], self.w2, self.w2_scale, self.expert_out, self.ffn_ws)
+
+    def experts(self, x: Optional[torch.Tensor] = None):
+        if self.gather:
+            self.gate_up(x)
+            return self.down()
         return moe_grouped_ffn(self.x_perm, self.layout[1], self.w13, self.w2, self.x_perm_scale,
                                self.w13_scale, self.w2_scale, self.expert_out, self.ffn_ws)
 
@@ -114,7 +140,7 @@ class MoELayer:
         self.route(z)
         self.dispatch()
         self.permute(x)
-        self.experts()
+        self.experts(x)
         if self.shared:
             self.shared_expert(x)
         self.combine()

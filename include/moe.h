@@ -204,6 +204,29 @@ moe_status moe_expert_down(const void* h, moe_dtype h_dt, const int32_t* offsets
                            hipStream_t stream);
 
 /*
+ * moe_expert_gate_up_gathered -- moe_expert_gate_up with the permute folded into the
+ * operand loads: row r of the expert-ordered operand is read straight from x, token
+ * src_slot[r] / k, so the permuted copy is never written.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 3 (the dispatch sends each token's
+ * row to the slots of its selected experts) and "MoE part 4" page, section 2 (the grouped
+ * GEMM over the expert-ordered rows); the result equals moe_permute followed by
+ * moe_expert_gate_up on the same rows, bit for bit.
+ *
+ *   x         [N, H] bf16 tokens (x_dt must be MOE_BF16).
+ *   src_slot  [rows] int32 device array from moe_dispatch_layout: row r holds slot t*k + j.
+ *             A token index outside [0, N) is clamped into it (no fault; that row's result
+ *             is then meaningless).
+ *   k, N      slots per token and number of tokens.
+ *   offsets, E, rows, H, I, w13, h, ws: as for moe_expert_gate_up.
+ * Requires H % 128 == 0, I % 128 == 0 and N * H * 2 < 2^32 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
+                                       int k, const int32_t* offsets, int E, int rows, int H, int I,
+                                       const void* w13, void* h, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/*
  * moe_combine -- y_t = sum_{j<k} g_{t,j} * expert_out[send_pos[t*k+j]] (+ shared_out_t).
  *
  * Definition: "EP / DeepEP explanation" page, section 2 (y_t, with an optional shared

@@ -86,6 +86,25 @@ def test_ffn_validation_and_workspace(L):
     assert call(rows=0, ws=None, ws_bytes=0) == MOE_OK
 
 
+def test_gathered_gate_up_validation(L):
+    rows, H, I, E, N, k = 65536, 7168, 2048, 256, 8192, 8
+    sched = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16)
+    f = L.moe_expert_gate_up_gathered
+    args = lambda **kw: dict(dict(x=FAKE, x_dt=MOE_BF16, N=N, src_slot=FAKE, k=k, offsets=FAKE, E=E,
+                                  rows=rows, H=H, I=I, w13=FAKE, h=FAKE, ws=FAKE, ws_bytes=sched, s=None), **kw)
+    call = lambda **kw: f(*args(**kw).values())
+    assert call(x_dt=MOE_FP8_E4M3) == MOE_ERR_UNSUPPORTED
+    assert call(x_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
+    assert call(ws_bytes=sched - 1) == MOE_ERR_WORKSPACE
+    assert call(k=0) == MOE_ERR_INVALID_ARG
+    assert call(src_slot=None) == MOE_ERR_INVALID_ARG
+    assert call(N=0) == MOE_ERR_INVALID_ARG
+    assert call(N=300000) == MOE_ERR_UNSUPPORTED        # N * H * 2 >= 2^32
+    assert call(H=7000) == MOE_ERR_UNSUPPORTED
+    assert call(x=FAKE + 8) == MOE_ERR_INVALID_ARG
+    assert call(rows=0, ws=None, ws_bytes=0) == MOE_OK
+
+
 def test_combine_validation(L):
     f = L.moe_combine
     assert f(FAKE, MOE_BF16, 4, 100, 2, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_UNSUPPORTED

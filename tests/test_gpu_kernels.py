@@ -275,6 +275,32 @@ def test_grouped_ffn_matches_oracle(case):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("E,k,N,H,I,mode", [(16, 4, 300, 512, 256, "random"), (8, 2, 1000, 1024, 384, "hot"),
+                                             (64, 8, 96, 7168, 256, "random")])
+def test_gate_up_gathered_equals_permuted(E, k, N, H, I, mode):
+    """Gate/up reading rows straight from x through src_slot == permute then gate/up, bit for bit."""
+    say(f"gathered gate/up E={E} k={k} N={N} H={H} I={I} {mode}")
+    x = w.normal((N, H), w.stream_key(11, w.T_X, E), DEV, torch.bfloat16)
+    w13 = w.normal((E, 2 * I, H), w.stream_key(11, w.T_W13, E), DEV, torch.bfloat16)
+    idx = w.fixed_route(N, E, k, mode, seed=E)
+    n_e, offs, sp, ss = moe.moe_dispatch_layout(idx.to(DEV), E)
+    xp = moe.moe_permute(x, sp, k)
+    h_ref = moe.moe_expert_gate_up(xp, offs, w13)
+    h = moe.moe_expert_gate_up_gathered(x, ss, k, offs, w13)
+    sync()
+    assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))
+    # and against the oracle on every row
+    rows = np.arange(N * k)
+    o = offs.cpu().numpy()
+    ref = np.zeros((N * k, I))
+    xf, wf, toks = f64(x), f64(w13), ss.cpu().numpy() // k
+    for e in range(E):
+        r = rows[o[e]:o[e + 1]]
+        if len(r):
+            ref[r] = oracle.expert_ffn(xf[toks[r]], wf[e], np.zeros((H, I)))[0]
+    assert token_rel_err(f64(h), ref) <= 1e-2
+
+
 def test_expert_down_on_generated_h():
     """The down GEMM alone, on an h that no other kernel produced."""
     n_e, H, I = [70, 0, 300, 3], 1024, 512

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import combine_grouped_gemm_amd as moe
 import workload as w
 from combine_grouped_gemm_amd.layer import MoELayer
 from oracle import moe_oracle as oracle
@@ -101,7 +102,10 @@ def _check_permute(cfg, inp, layer, send_pos):
         assert np.array_equal(layer.x_perm_scale.cpu().numpy(), ps)
         return None, (q, s)
     view = torch.int32 if cfg.dtype == "f32" else torch.int16
-    assert np.array_equal(layer.x_perm.cpu().view(view).numpy(), oracle.permute(x.view(view).numpy(), send_pos, cfg.k))
+    x_perm = layer.x_perm
+    if x_perm is None:   # the gate/up GEMM gathered its rows from x: permute explicitly
+        x_perm = moe.moe_permute(inp["x"], layer.layout[2], cfg.k)
+    assert np.array_equal(x_perm.cpu().view(view).numpy(), oracle.permute(x.view(view).numpy(), send_pos, cfg.k))
     return x.to(torch.float64).numpy(), None
 
 
