@@ -4,15 +4,17 @@
 // kept in a wider type than the payload).
 //
 // One workgroup per token; each lane owns 8 consecutive columns, gathers the k expert
-// rows with 16-byte loads (all k loads issued before the sum), accumulates in fp32 in the
-// order j = 0..k-1 then the shared row, rounds once and writes 16 bytes (bf16) or 32 bytes
-// (fp32).  Gates and send positions are uniform across the workgroup.
+// rows with 16-byte loads (up to 8 rows' loads issued before the sum), accumulates in fp32
+// in the order j = 0..k-1 then the shared row, rounds once and writes 16 bytes (bf16) or
+// 32 bytes (fp32).  Gates and send positions are uniform across the workgroup, whose size
+// (128 or 256 lanes) divides the row's 8-column groups when it can, so that no pass over
+// the row leaves lanes idle.
 #include "moe_common.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-constexpr int kCombThreads = 256;
+constexpr int kCombMaxThreads = 256;
 
 template <bool kEoF32>
 __device__ __forceinline__ void load8(const void* base, size_t row, int H, int c, float (&v)[8]) {
@@ -32,38 +34,43 @@ __device__ __forceinline__ void load8(const void* base, size_t row, int H, int c
   }
 }
 
+template <int U, bool kEoF32>
+__device__ __forceinline__ void gather_sum(const void* eo, const int32_t* sp, const float* g, int H, int c,
+                                           float (&acc)[8]) {
+  float v[U][8];
+  int r[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) r[u] = sp[u];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (r[u] >= 0) {
+      load8<kEoF32>(eo, static_cast<size_t>(r[u]), H, c, v[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float gu = g[u];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(gu, v[u][i], acc[i]);
+  }
+}
+
 template <bool kEoF32, bool kYF32>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+__global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(
     const void* __restrict__ eo, int H, int k, const int32_t* __restrict__ send_pos,
     const float* __restrict__ gate, const void* __restrict__ shared, void* __restrict__ y) {
   const int t = blockIdx.x;
   const int32_t* sp = send_pos + static_cast<size_t>(t) * k;
   const float* g = gate + static_cast<size_t>(t) * k;
   const int groups8 = H / 8;
-  for (int c = threadIdx.x; c < groups8; c += kCombThreads) {
+  for (int c = threadIdx.x; c < groups8; c += blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int j = 0;
-    for (; j + 4 <= k; j += 4) {
-      float v[4][8];
-      int r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = sp[j + u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (r[u] >= 0) {
-          load8<kEoF32>(eo, static_cast<size_t>(r[u]), H, c, v[u]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float gu = g[j + u];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gu, v[u][i], acc[i]);
-      }
-    }
+    for (; j + 8 <= k; j += 8) gather_sum<8, kEoF32>(eo, sp + j, g + j, H, c, acc);
+    for (; j + 4 <= k; j += 4) gather_sum<4, kEoF32>(eo, sp + j, g + j, H, c, acc);
     for (; j < k; ++j) {
       const int r = sp[j];
       if (r < 0) continue;
@@ -96,7 +103,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
                           const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s) {
-  const dim3 grid(N), block(kCombThreads);
+  const int groups8 = H / 8;
+  const dim3 grid(N), block(groups8 % 256 == 0 || groups8 % 128 != 0 ? 256 : 128);
   if (eo_f32 && y_f32)
     hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
   else if (eo_f32)
