@@ -230,6 +230,8 @@ GEMM_CASES = [
     ("fp8_decode_ragged", [0, 1, 2, 5, 16, 17, 33, 0, 3, 0, 9, 1, 4, 0, 7, 12], 1024, 256, "fp8"),
     ("fp8_decode_one_k_block", [1, 0], 128, 128, "fp8"),
     ("fp8_decode_wide", [4, 0, 7], 7168, 2048, "fp8"),
+    ("fp8_decode_odd_k_blocks", [2, 16, 0, 9], 1152, 384, "fp8"),   # 9 and 3 K blocks: scales one by one
+    ("fp8_decode_16_per_expert", [16] * 8, 512, 256, "fp8"),        # rows = 16 E exactly
 ]
 
 
@@ -276,7 +278,7 @@ def test_grouped_ffn_matches_oracle(case):
 
 
 @pytest.mark.parametrize("E,k,N,H,I,mode", [(16, 4, 300, 512, 256, "random"), (8, 2, 1000, 1024, 384, "hot"),
-                                             (64, 8, 96, 7168, 256, "random")])
+                                             (64, 8, 96, 7168, 256, "random"), (4, 1, 333, 256, 128, "random")])
 def test_gate_up_gathered_equals_permuted(E, k, N, H, I, mode):
     """Gate/up reading rows straight from x through src_slot == permute then gate/up, bit for bit."""
     say(f"gathered gate/up E={E} k={k} N={N} H={H} I={I} {mode}")

@@ -144,6 +144,20 @@ def test_layer_small_all_intermediates(name):
     assert err <= Y_EXPECT[cfg.dtype]
 
 
+def test_layer_gathered_equals_permuted():
+    """The bf16 layer with the permute folded into gate/up == the layer with the permute kernel, bit for bit."""
+    cfg = SMALL["dsv3_small"]
+    inp = w.make_layer_inputs(cfg, DEV)
+    ys = []
+    for gather in (True, False):
+        layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                         inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"], gather=gather)
+        assert layer.gather == gather
+        ys.append(layer.forward(inp["x"], inp["z"]).clone())
+    sync()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+
+
 FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
 SAMPLE_TOKENS = {"mixtral_bf16": 8, "dsv3_bf16": 4, "dsv3_zipf_bf16": 4, "decode_fp8": 2}
 
