@@ -3,12 +3,13 @@
 // ("EP / DeepEP explanation" page, sections 2 and 3; "DeepEP" page, section 7: the sum is
 // kept in a wider type than the payload).
 //
-// One workgroup per token; each lane owns 8 consecutive columns, gathers the k expert
-// rows with 16-byte loads (up to 8 rows' loads issued before the sum), accumulates in fp32
-// in the order j = 0..k-1 then the shared row, rounds once and writes 16 bytes (bf16) or
-// 32 bytes (fp32).  Gates and send positions are uniform across the workgroup, whose size
-// (128 or 256 lanes) divides the row's 8-column groups when it can, so that no pass over
-// the row leaves lanes idle.
+// Each workgroup takes one token and one span of its columns (the row is split into
+// `spans` spans, so that small batches still fill the GPU); each lane owns 8 consecutive
+// columns, gathers the k expert rows with 16-byte loads (up to 8 rows' loads issued before
+// the sum), accumulates in fp32 in the order j = 0..k-1 then the shared row, rounds once
+// and writes 16 bytes (bf16) or 32 bytes (fp32).  Gates and send positions are uniform
+// across the workgroup, whose size (128 or 256 lanes) divides the row's 8-column groups
+// when it can, so that no pass over the row leaves lanes idle.
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -61,12 +62,15 @@ __device__ __forceinline__ void gather_sum(const void* eo, const int32_t* sp, co
 template <bool kEoF32, bool kYF32>
 __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(
     const void* __restrict__ eo, int H, int k, const int32_t* __restrict__ send_pos,
-    const float* __restrict__ gate, const void* __restrict__ shared, void* __restrict__ y) {
-  const int t = blockIdx.x;
+    const float* __restrict__ gate, const void* __restrict__ shared, void* __restrict__ y, int spans) {
+  const int t = blockIdx.x / spans;
+  const int span = blockIdx.x % spans;
   const int32_t* sp = send_pos + static_cast<size_t>(t) * k;
   const float* g = gate + static_cast<size_t>(t) * k;
   const int groups8 = H / 8;
-  for (int c = threadIdx.x; c < groups8; c += blockDim.x) {
+  const int per_span = (groups8 + spans - 1) / spans;
+  const int c_end = (span + 1) * per_span < groups8 ? (span + 1) * per_span : groups8;
+  for (int c = span * per_span + threadIdx.x; c < c_end; c += blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int j = 0;
     for (; j + 8 <= k; j += 8) gather_sum<8, kEoF32>(eo, sp + j, g + j, H, c, acc);
@@ -104,15 +108,24 @@ __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
                           const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s) {
   const int groups8 = H / 8;
-  const dim3 grid(N), block(groups8 % 256 == 0 || groups8 % 128 != 0 ? 256 : 128);
+  const int threads = groups8 % 256 == 0 || groups8 % 128 != 0 ? 256 : 128;
+  // small batches: split each row into up to one span per workgroup pass, for ~8
+  // workgroups per CU
+  const int passes = (groups8 + threads - 1) / threads;
+  int spans = 1;
+  if (N < 2048) {
+    const int want = (2048 + N - 1) / N;
+    spans = want < passes ? want : passes;
+  }
+  const dim3 grid(static_cast<unsigned>(static_cast<long long>(N) * spans)), block(threads);
   if (eo_f32 && y_f32)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
   else if (eo_f32)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
   else if (y_f32)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
   else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y);
+    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
   return hipGetLastError();
 }
 
