@@ -196,8 +196,24 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = cfg.N / (ms_per_step / 1e3)
 
+    if layer.gather:
+        # the layer folds the permute into gate/up; the permute kernel (the standalone
+        # moe_permute, same rows) is timed on its own after the layer, outside `value`
+        xp = torch.empty((cfg.N * cfg.k, cfg.H), dtype=x.dtype, device=dev)
+        pev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        moe.moe_permute(x, layer.layout[2], cfg.k, None, xp)
+        torch.cuda.synchronize()
+        pev[0].record(stream)
+        for s in range(args.steps):
+            moe.moe_permute(x, layer.layout[2], cfg.k, None, xp)
+            pev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        per["permute (standalone)"] = [pev[s].elapsed_time(pev[s + 1]) for s in range(args.steps)]
+        del xp
+
     n_e = layer.layout[0].cpu().numpy()
     alg = algorithmic(cfg, n_e, layer.gather)
+    alg["permute (standalone)"] = alg["permute"]
     kernels = {}
     for name, times in per.items():
         t = sorted(times)
@@ -256,7 +272,8 @@ def main():
         "kernels": kernels,
         "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),
                                    "down": kernels["down"].get("mfma_frac")},
-        "permute_hbm_GBps": kernels["permute"]["GB_per_s"] if "permute" in kernels else None,
+        "permute_hbm_GBps": (kernels["permute"] if "permute" in kernels
+                             else kernels["permute (standalone)"])["GB_per_s"],
         "permute_folded_into_gate_up": layer.gather,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
