@@ -211,6 +211,20 @@ def main():
         per["permute (standalone)"] = [pev[s].elapsed_time(pev[s + 1]) for s in range(args.steps)]
         del xp
 
+    # the machine's practical copy rate (context for the HBM fractions): torch's device copy
+    # of 1 GiB, read + write bytes over its event time
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    cev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = round(2 * 5 * (1 << 30) / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9, 1)
+    del csrc, cdst
+
     n_e = layer.layout[0].cpu().numpy()
     alg = algorithmic(cfg, n_e, layer.gather)
     alg["permute (standalone)"] = alg["permute"]
@@ -277,6 +291,7 @@ def main():
         "permute_folded_into_gate_up": layer.gather,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
+        "device_copy_GBps": copy_GBps,
         "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
     }
     print(json.dumps(out), flush=True)
