@@ -39,6 +39,8 @@ def parse():
                    help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
+    p.add_argument("--serial", action="store_true",
+                   help="run the shared expert on the main stream too (no overlap)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -140,24 +142,44 @@ def main():
     log(args, f"generating {cfg.name} inputs on the GPU")
     inp = workload.make_layer_inputs(cfg, dev)
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
-                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"])
+                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
+                     overlap_shared=not args.serial)
     x, z = inp["x"], inp["z"]
     torch.cuda.synchronize()
 
-    # the layer's own calls, one stage each (bf16 layers fold the permute into gate/up)
+    # the layer's own calls, one stage each, as MoELayer.forward issues them (bf16 layers fold
+    # the permute into gate/up; the shared expert runs on the layer's side stream)
+    stream = torch.cuda.current_stream()
     stages = [("route", lambda: layer.route(z)),
               ("layout", layer.dispatch)]
     if not layer.gather:
         stages.append(("permute", lambda: layer.permute(x)))
     stages += [("gate_up", lambda: layer.gate_up(x)),
                ("down", layer.down)]
-    if cfg.shared:
+    if cfg.shared and layer.side is None:
         stages.append(("shared", lambda: layer.shared_expert(x)))
     stages.append(("combine", layer.combine))
+    side = layer.side
 
-    def step():
-        for _, f in stages:
+    def step(ev=None):
+        """One forward; ev: per-stage (start, end) event pairs to record, or None."""
+        if side is not None:
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                if ev is not None:
+                    ev["shared"][0].record(side)
+                layer.shared_expert(x)
+                if ev is not None:
+                    ev["shared"][1].record(side)
+                layer.shared_done.record(side)
+        for name, f in stages:
+            if name == "combine" and side is not None:
+                stream.wait_event(layer.shared_done)
+            if ev is not None:
+                ev[name][0].record(stream)
             f()
+            if ev is not None:
+                ev[name][1].record(stream)
 
     if args.copy_probe_mib > 0:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch scale the
@@ -175,24 +197,19 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    names = [n for n, _ in stages] + (["shared"] if side is not None else [])
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+          for _ in range(args.steps)]
     log(args, f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, (_, f) in enumerate(stages):
-            f()
-            ev[s][i + 1].record(stream)
+        step(ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {name: [] for name, _ in stages}
-    step_ms = []
-    for s in range(args.steps):
-        for i, (name, _) in enumerate(stages):
-            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
-        step_ms.append(ev[s][0].elapsed_time(ev[s][len(stages)]))
+    per = {n: [ev[s][n][0].elapsed_time(ev[s][n][1]) for s in range(args.steps)] for n in names}
+    first = "shared" if side is not None else stages[0][0]
+    step_ms = [ev[s][first][0].elapsed_time(ev[s]["combine"][1]) for s in range(args.steps)]
     ms_per_step = wall * 1e3 / args.steps
     value = cfg.N / (ms_per_step / 1e3)
 
@@ -289,6 +306,7 @@ def main():
         "permute_hbm_GBps": (kernels["permute"] if "permute" in kernels
                              else kernels["permute (standalone)"])["GB_per_s"],
         "permute_folded_into_gate_up": layer.gather,
+        "shared_expert_on_side_stream": side is not None,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,

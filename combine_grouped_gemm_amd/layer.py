@@ -36,7 +36,7 @@ class MoELayer:
     def __init__(self, N: int, H: int, E: int, k: int, I: int, dtype: str, w13: torch.Tensor,
                  w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
                  shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
-                 bias: Optional[torch.Tensor] = None, gather: bool = True):
+                 bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = True):
         self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
         self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
         dev = w13.device
@@ -79,6 +79,10 @@ class MoELayer:
             self.shared_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, N, H, I, 1, 1, a_dt), 256),
                                          dtype=torch.uint8, device=dev)
             self.shared_out = torch.empty((N, H), dtype=act, device=dev)
+        # the shared expert needs only x: it runs on a second stream (default priority)
+        # beside route / layout / the routed FFN, and combine waits for it
+        self.side = torch.cuda.Stream(device=dev) if self.shared and overlap_shared else None
+        self.shared_done = torch.cuda.Event() if self.side is not None else None
         self.y = torch.empty((N, H), dtype=act, device=dev)
 
     @property
@@ -136,12 +140,26 @@ class MoELayer:
         return moe_combine(self.expert_out, self.layout[2], self.topk_gate,
                            self.shared_out if self.shared else None, self.y)
 
+    def launch_shared_side(self, x: torch.Tensor):
+        """Enqueue the shared expert on the side stream, after the work queued so far."""
+        main = torch.cuda.current_stream(self.device)
+        self.side.wait_stream(main)
+        x.record_stream(self.side)
+        with torch.cuda.stream(self.side):
+            self.shared_expert(x)
+            self.shared_done.record(self.side)
+
     def forward(self, x: torch.Tensor, z: torch.Tensor) -> torch.Tensor:
+        if self.side is not None:
+            self.launch_shared_side(x)
         self.route(z)
         self.dispatch()
         self.permute(x)
         self.experts(x)
         if self.shared:
-            self.shared_expert(x)
+            if self.side is not None:
+                torch.cuda.current_stream(self.device).wait_event(self.shared_done)
+            else:
+                self.shared_expert(x)
         self.combine()
         return self.y
