@@ -41,4 +41,10 @@ __device__ __forceinline__ void expert_segment(const GemmArgs& p, int e, int& lo
 constexpr int kStreamTileRows = 16;
 hipError_t launch_grouped_gemm_stream(int mode, const GemmArgs& p, hipStream_t s);
 
+// bf16 kernel on 256 x 256 tiles (grouped_gemm_wide.hip); the tile schedule in `p` must
+// have been built with 256-row m-tiles, K must be a multiple of 128, and every operand
+// offset (b_rows * K * 2 per expert; a_nrows * K * 2 when gathered) must fit in 32 bits.
+constexpr int kWideTileRows = 256;
+hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s);
+
 }  // namespace moe

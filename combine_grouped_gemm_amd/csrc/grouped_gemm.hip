@@ -30,14 +30,13 @@
 #include <type_traits>
 #include <utility>
 
+#include "gemm_device.h"
 #include "grouped_gemm.h"
 #include "moe_common.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 
 constexpr int GBM = 128;          // rows of a tile
@@ -404,9 +403,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
 #endif
 constexpr int kDM = MOE_DMA_DM;
 constexpr int kDGroup = 1024;                           // bytes of one DMA wave instruction
-template <int BN, int ROWB, int STAGES, int WM>
+template <int BN, int ROWB, int STAGES, int WM, int WN>
 struct DmaCfg {
-  static constexpr int kWaves = WM * 4;
+  static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRowsPerGroup = kDGroup / ROWB;
   static constexpr int kChunks = ROWB / 16;             // 16-byte chunks per row and stage
@@ -416,9 +415,10 @@ struct DmaCfg {
   static constexpr int kPerWave = (kAGroups + kBGroups) / kWaves;   // DMA instructions per wave and stage
   static constexpr int kAPerWave = kAGroups / kWaves;
   static constexpr int kKSteps = ROWB / 32;             // 16-wide bf16 k-steps per stage
-  static constexpr int kNB = BN / 4 / 32;               // 32-column blocks per wave
+  static constexpr int kNB = BN / WN / 32;              // 32-column blocks per wave
   static constexpr int kMB = kDM / WM / 32;             // 32-row blocks per wave
   static_assert(kAGroups % kWaves == 0 && kBGroups % kWaves == 0, "groups spread evenly");
+  static_assert(ROWB != 128 || kWaves % 2 == 0, "the 128-byte swizzle needs the group parity of the wave");
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
   // swizzle key of tile row r (rows of a fragment start at multiples of 32)
   __device__ static __forceinline__ int key(int r) {
@@ -426,41 +426,13 @@ struct DmaCfg {
   }
 };
 
-// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-// lgkmcnt(0) with vmcnt and expcnt left at their maxima; as a builtin (not inline asm)
-// the compiler sees that every earlier LDS read has completed
-__device__ __forceinline__ void wait_lgkmcnt_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void block_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
-
-typedef __attribute__((address_space(3))) uint8_t lds_byte;
-
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane.  Issued as
-// inline assembly so that the compiler adds no wait of its own before later LDS reads;
-// every wait for these loads is explicit.  M0 holds the LDS base; one wait state
-// separates its write from the load that reads it.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  __asm__ volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(gptr), "s"(lds_base)
-      : "memory", "m0");
-}
-
-template <int MODE, int BN, int ROWB, int STAGES, int WM>
-__global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel(GemmArgs p) {
-  using C = DmaCfg<BN, ROWB, STAGES, WM>;
+template <int MODE, int BN, int ROWB, int STAGES, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, MOE_DMA_OCC) void grouped_gemm_dma_kernel(GemmArgs p) {
+  using C = DmaCfg<BN, ROWB, STAGES, WM, WN>;
   constexpr int KSTEPS = C::kKSteps;
   constexpr int NB = C::kNB;
   constexpr int MB = C::kMB;
   constexpr int kDmaWaves = C::kWaves;
-  constexpr int kWR = kDM / WM;                 // rows per wave
   constexpr int PER = C::kPerWave;
   static_assert(KSTEPS % 2 == 0, "a stage must end in fragment set 1 so the next starts in set 0");
   static_assert(MODE != MODE_GATE_UP || NB % 2 == 0, "gate/up pairs");
@@ -472,10 +444,10 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // each wave owns kWR x BN/4 of the tile.  Waves w and w+4 share a SIMD (waves are placed
-  // round-robin), so giving them different row halves keeps both SIMD slots busy when a
-  // ragged tile leaves one half without rows.
-  const int wm = wave / 4, wn = wave % 4;
+  // each wave owns MB 32-row blocks x BN/WN columns of the tile.  Row blocks are dealt to
+  // the WM row waves in turn (wave wm takes blocks wm, wm + WM, ...), so a ragged tile
+  // still spreads its rows evenly over the SIMDs.
+  const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane / C::kChunks;           // row inside a DMA group
   // global chunk this lane loads: the slot it fills is lane % kChunks, XOR the row's key.
   // Every group this wave fills has the parity of the wave (groups w, w + waves, ...; 16 A
@@ -502,13 +474,13 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
   for (int s = 0; s < KSTEPS; ++s) koff[s] = ((2 * s + h) ^ key) * 16;
   int a_frag[MB], b_frag[NB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) a_frag[mb] = (wm * kWR + mb * 32 + (lane & 31)) * ROWB;
+  for (int mb = 0; mb < MB; ++mb) a_frag[mb] = ((mb * WM + wm) * 32 + (lane & 31)) * ROWB;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     // gate/up: the first NB/2 blocks are W_gate rows, the last NB/2 the same W_up rows
     const int r = MODE == MODE_GATE_UP
-                      ? (nb / (NB / 2)) * (BN / 2) + wn * (BN / 8) + (nb % (NB / 2)) * 32 + (lane & 31)
-                      : wn * (BN / 4) + nb * 32 + (lane & 31);
+                      ? (nb / (NB / 2)) * (BN / 2) + wn * (BN / (2 * WN)) + (nb % (NB / 2)) * 32 + (lane & 31)
+                      : wn * (BN / WN) + nb * 32 + (lane & 31);
     b_frag[nb] = C::kAGroups * kDGroup + r * ROWB;
   }
 
@@ -630,7 +602,7 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
 
     // 32-row blocks of this wave that hold rows of the segment: MFMAs and fragment reads of
     // the others are skipped (the loads and barriers are the same on every path)
-    int act = (mlast + 1 - wm * kWR + 31) / 32;
+    int act = ((mlast + 32) / 32 - wm + WM - 1) / WM;
     act = act < 0 ? 0 : (act > MB ? MB : act);
 
     auto k_loop = [&](auto act_c) __attribute__((always_inline)) {
@@ -692,12 +664,12 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm * kWR + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = m0 + (mb * WM + wm) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= mend) continue;
         if (MODE == MODE_GATE_UP) {
 #pragma unroll
           for (int nb = 0; nb < NB / 2; ++nb) {
-            const int col = c0 + wn * (BN / 8) + nb * 32 + (lane & 31);
+            const int col = c0 + wn * (BN / (2 * WN)) + nb * 32 + (lane & 31);
             if (col >= n_cols) continue;
             const float g = acc[mb][nb][v];
             const float u = acc[mb][nb + NB / 2][v];
@@ -707,7 +679,7 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
         } else {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            const int col = c0 + wn * (BN / 4) + nb * 32 + (lane & 31);
+            const int col = c0 + wn * (BN / WN) + nb * 32 + (lane & 31);
             if (col >= n_cols) continue;
             reinterpret_cast<uint16_t*>(p.out)[static_cast<size_t>(r) * p.n_out + col] = f32_to_bf16(acc[mb][nb][v]);
           }
@@ -729,6 +701,9 @@ __global__ __launch_bounds__(WM * 256, MOE_DMA_OCC) void grouped_gemm_dma_kernel
 #ifndef MOE_DMA_WM
 #define MOE_DMA_WM 2
 #endif
+#ifndef MOE_DMA_WN
+#define MOE_DMA_WN 4
+#endif
 
 // m-tiles at the finest granularity any kernel uses (16 rows)
 size_t gemm_tile_cap(int rows, int E) {
@@ -739,6 +714,13 @@ size_t gemm_schedule_bytes(int rows, int E) {
   const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E);
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
+
+// 256 x 256 tiles for: 0 no GEMM, 1 gate/up, 2 gate/up and down.  On the weight-streaming
+// shapes here the wide tiles win for gate/up (K = H) and lose for down (K = I, where the
+// per-tile pipeline fill and drain weigh 3.5x more), so down keeps the 128 x 256 tiles.
+#ifndef MOE_GEMM_WIDE
+#define MOE_GEMM_WIDE 1
+#endif
 
 static int persistent_grid() {
   // one workgroup per CU (256 CUs); a multiple of the 8 XCDs
@@ -759,8 +741,14 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                       (mode == MODE_GATE_UP ? I % 64 == 0 : n_out % 128 == 0) &&
                       static_cast<long long>(gemm_tile_cap(rows, E)) * (mode == MODE_GATE_UP ? I / 64 : n_out / 128) <
                           (1LL << 31);
-  const bool dma = ct == CT_BF16 && !b8;   // bf16 operands: the direct-to-LDS kernel
-  const int tile_rows = stream ? kStreamTileRows : (dma ? kDM : GBM);
+  const bool dma = ct == CT_BF16 && !b8;   // bf16 operands: the direct-to-LDS kernels
+  // 256 x 256 tiles while every operand offset fits the kernel's 32-bit arithmetic
+  const long long rbytes = 2LL * K;
+  const bool wide = (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= 2) && dma && K % 128 == 0 &&
+                    (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 &&
+                    b_rows * rbytes < (1LL << 32) &&
+                    (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
+  const int tile_rows = stream ? kStreamTileRows : (wide ? kWideTileRows : (dma ? kDM : GBM));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert);
   GemmArgs p;
@@ -784,13 +772,15 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.b_rows = b_rows;
   p.out_f32 = out_f32 ? 1 : 0;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
+  if (wide) return launch_grouped_gemm_wide(mode, p, s);
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)
 #define MOE_LAUNCH_DMA(MODE_) \
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>), \
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM, \
+                                              MOE_DMA_WN>), \
                      dim3(persistent_grid() * MOE_DMA_OCC), \
-                     dim3(DmaCfg<MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM>::kThreads), 0, s, p)
+                     dim3(DmaCfg<MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM, MOE_DMA_WN>::kThreads), 0, s, p)
   if (mode == MODE_GATE_UP) {
     if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_GATE_UP);
     else if (ct == CT_BF16) MOE_LAUNCH_DMA(MODE_GATE_UP);
