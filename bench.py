@@ -39,6 +39,8 @@ def parse():
                    help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
+    p.add_argument("--no-gather", action="store_true",
+                   help="bf16: run the permute and read the gate/up rows from its copy")
     p.add_argument("--serial", action="store_true",
                    help="run the shared expert on the main stream too (no overlap)")
     p.add_argument("--quiet", action="store_true")
@@ -50,9 +52,18 @@ def log(args, msg):
         print(msg, file=sys.stderr, flush=True)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(*paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# sources of the dominant kernel (the routed gate/up GEMM): a stored traffic figure is used
+# only while they are unchanged since its counters were taken
+GEMM_SOURCES = [os.path.join(ROOT, "combine_grouped_gemm_amd", "csrc", n)
+                for n in ("grouped_gemm_wide.hip", "gemm_device.h")]
 
 
 def algorithmic(cfg, n_e, gather=False):
@@ -143,7 +154,7 @@ def main():
     inp = workload.make_layer_inputs(cfg, dev)
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
-                     overlap_shared=not args.serial)
+                     gather=not args.no_gather, overlap_shared=not args.serial)
     x, z = inp["x"], inp["z"]
     torch.cuda.synchronize()
 
@@ -268,7 +279,7 @@ def main():
     tf = TRAFFIC_FILE.format(cfg.name)
     if os.path.exists(tf):
         rec = json.load(open(tf))
-        if rec.get("source_sha") == source_sha(os.path.join(ROOT, "combine_grouped_gemm_amd", "csrc", "grouped_gemm.hip")):
+        if rec.get("source_sha") == source_sha(*GEMM_SOURCES):
             traffic = rec.get("bytes_per_launch")
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(g["bytes"] / g_avg / 1e9, 1), "peak": PEAK_HBM / 1e9,

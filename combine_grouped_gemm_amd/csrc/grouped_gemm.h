@@ -25,6 +25,8 @@ struct GemmArgs {
   int E, K, rows, I, n_out, tile_cap;
   long long b_rows;
   int out_f32;
+  int32_t* tile_counter;       // [kNumXcd] next tile of each XCD's range (zeroed by the schedule
+                               // prologue), or null: tiles dealt round-robin
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot

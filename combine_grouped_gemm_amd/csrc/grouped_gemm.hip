@@ -58,7 +58,8 @@ template <> struct CTraits<CT_FP8> { static constexpr int esz = 1; };
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int rows, int tile_rows, int tile_cap,
                                                            int32_t* __restrict__ prefix,
-                                                           int32_t* __restrict__ tile_expert) {
+                                                           int32_t* __restrict__ tile_expert,
+                                                           int32_t* __restrict__ tile_counter) {
   __shared__ int32_t tot[1024];
   const int e = threadIdx.x;
   int mt = 0;
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     for (int i = 0; i < mt && start + i < tile_cap; ++i) tile_expert[start + i] = e;
   }
   if (e == E - 1) prefix[E] = tot[e] < tile_cap ? tot[e] : tile_cap;
+  if (e < kNumXcd) tile_counter[e] = 0;
 }
 
 template <int CT>
@@ -711,7 +713,7 @@ size_t gemm_tile_cap(int rows, int E) {
 }
 
 size_t gemm_schedule_bytes(int rows, int E) {
-  const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E);
+  const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E) + kNumXcd;
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 
@@ -721,6 +723,10 @@ size_t gemm_schedule_bytes(int rows, int E) {
 #ifndef MOE_GEMM_WIDE
 #define MOE_GEMM_WIDE 1
 #endif
+#ifndef MOE_WIDE_DYNAMIC
+#define MOE_WIDE_DYNAMIC 1
+#endif
+constexpr bool kWideDynamic = MOE_WIDE_DYNAMIC != 0;
 
 static int persistent_grid() {
   // one workgroup per CU (256 CUs); a multiple of the 8 XCDs
@@ -735,6 +741,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   int32_t* prefix = reinterpret_cast<int32_t*>(sched);
   int32_t* tile_expert = prefix + E + 1;
   const int cap = static_cast<int>(gemm_tile_cap(rows, E));
+  int32_t* tile_counter = tile_expert + cap;
   // few rows per expert and e4m3 weights: the weight-streaming kernel (16-row m-tiles)
   const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) &&
                       static_cast<long long>(rows) <= static_cast<long long>(kStreamTileRows) * E &&
@@ -750,7 +757,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                     (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
   const int tile_rows = stream ? kStreamTileRows : (wide ? kWideTileRows : (dma ? kDM : GBM));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
-                     prefix, tile_expert);
+                     prefix, tile_expert, tile_counter);
   GemmArgs p;
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.a_scale = a_scale;
@@ -771,8 +778,12 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.tile_cap = cap;
   p.b_rows = b_rows;
   p.out_f32 = out_f32 ? 1 : 0;
+  p.tile_counter = nullptr;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
-  if (wide) return launch_grouped_gemm_wide(mode, p, s);
+  if (wide) {
+    p.tile_counter = kWideDynamic ? tile_counter : nullptr;
+    return launch_grouped_gemm_wide(mode, p, s);
+  }
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)

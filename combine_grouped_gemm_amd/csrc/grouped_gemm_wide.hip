@@ -98,7 +98,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     b_frag[nb] = r * kRowB;
   }
 
-  for (long long L = t_beg + slot; L < t_end; L += per_xcd) {
+  // the next tile: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.
+  // With the counter, the m-tiles that share a weight panel (adjacent in the order) start
+  // together on two CUs and stream the panel through L2 once, whatever the earlier tiles
+  // cost.  The index reaches the other waves through the last word of ring slot 2, which no
+  // load writes before the prologue's barrier.
+  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes - 4);
+  long long L = t_beg + slot;
+  for (;; L += per_xcd) {
+    if (p.tile_counter) {
+      __syncthreads();   // every wave is done with LDS and memory of the previous tile
+      if (tid == 0) *tile_word = atomicAdd(p.tile_counter + xcd, 1);
+      __syncthreads();
+      L = t_beg + *tile_word;
+    }
+    if (L >= t_end) break;
     const int e = p.tile_expert[L / nN];
     const int pe = p.tile_prefix[e];
     const int mt_e = p.tile_prefix[e + 1] - pe;
