@@ -41,8 +41,9 @@ def parse():
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     p.add_argument("--no-gather", action="store_true",
                    help="bf16: run the permute and read the gate/up rows from its copy")
-    p.add_argument("--serial", action="store_true",
-                   help="run the shared expert on the main stream too (no overlap)")
+    p.add_argument("--overlap", action="store_true",
+                   help="run the shared expert on a second stream beside the routed path (it then "
+                        "holds the CUs while route/layout wait, so per-stage times mix)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -154,7 +155,7 @@ def main():
     inp = workload.make_layer_inputs(cfg, dev)
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
-                     gather=not args.no_gather, overlap_shared=not args.serial)
+                     gather=not args.no_gather, overlap_shared=args.overlap)
     x, z = inp["x"], inp["z"]
     torch.cuda.synchronize()
 

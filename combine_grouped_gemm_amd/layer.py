@@ -36,7 +36,7 @@ class MoELayer:
     def __init__(self, N: int, H: int, E: int, k: int, I: int, dtype: str, w13: torch.Tensor,
                  w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
                  shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
-                 bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = True):
+                 bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = False):
         self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
         self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
         dev = w13.device

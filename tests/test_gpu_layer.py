@@ -158,6 +158,24 @@ def test_layer_gathered_equals_permuted():
     assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
 
 
+def test_layer_shared_on_side_stream_equals_serial():
+    """The shared expert on a second stream (combine waits for it) == all on one stream, bit for
+    bit, over several forwards in a row."""
+    cfg = SMALL["dsv3_small"]
+    inp = w.make_layer_inputs(cfg, DEV)
+    ys = []
+    for overlap in (True, False):
+        layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                         inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
+                         overlap_shared=overlap)
+        assert (layer.side is not None) == overlap
+        for _ in range(3):
+            y = layer.forward(inp["x"], inp["z"])
+        ys.append(y.clone())
+    sync()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+
+
 FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
 SAMPLE_TOKENS = {"mixtral_bf16": 8, "dsv3_bf16": 4, "dsv3_zipf_bf16": 4, "decode_fp8": 2}
 
