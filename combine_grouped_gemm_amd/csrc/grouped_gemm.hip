@@ -717,11 +717,11 @@ size_t gemm_schedule_bytes(int rows, int E) {
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 
-// 256 x 256 tiles for: 0 no GEMM, 1 gate/up, 2 gate/up and down.  On the weight-streaming
-// shapes here the wide tiles win for gate/up (K = H) and lose for down (K = I, where the
-// per-tile pipeline fill and drain weigh 3.5x more), so down keeps the 128 x 256 tiles.
+// 256 x 256 tiles for: 0 no GEMM, 1 gate/up, 2 gate/up and routed down (E > 1), 3 every
+// bf16 GEMM.  A single dense down GEMM (the shared expert: 8192 x 7168 outputs) makes 3.5
+// wide tiles per CU but exactly 7 of 128 x 256, so it keeps the smaller tiles.
 #ifndef MOE_GEMM_WIDE
-#define MOE_GEMM_WIDE 1
+#define MOE_GEMM_WIDE 2
 #endif
 #ifndef MOE_WIDE_DYNAMIC
 #define MOE_WIDE_DYNAMIC 1
@@ -751,7 +751,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const bool dma = ct == CT_BF16 && !b8;   // bf16 operands: the direct-to-LDS kernels
   // 256 x 256 tiles while every operand offset fits the kernel's 32-bit arithmetic
   const long long rbytes = 2LL * K;
-  const bool wide = (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= 2) && dma && K % 128 == 0 &&
+  const bool wide = (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= (E > 1 ? 2 : 3)) && dma &&
+                    K % 128 == 0 &&
                     (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 &&
                     b_rows * rbytes < (1LL << 32) &&
                     (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);

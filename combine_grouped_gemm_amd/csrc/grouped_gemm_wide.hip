@@ -98,21 +98,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     b_frag[nb] = r * kRowB;
   }
 
-  // the next tile: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.
-  // With the counter, the m-tiles that share a weight panel (adjacent in the order) start
-  // together on two CUs and stream the panel through L2 once, whatever the earlier tiles
-  // cost.  The index reaches the other waves through the last word of ring slot 2, which no
-  // load writes before the prologue's barrier.
+  // Tiles: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.  With
+  // the counter, tiles adjacent in the order (the m-tiles sharing a weight panel, the
+  // n-blocks sharing activation rows) start close together in time whatever the earlier
+  // tiles cost.  Wave 0 takes the index of the tile after next while the current tile's
+  // first stage loads, and hands it to the other waves at the tile boundary through the last
+  // word of ring slot 2 (no load writes that slot between a boundary and the first stage).
   int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes - 4);
+  const bool dynamic = p.tile_counter != nullptr;
+  int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
   long long L = t_beg + slot;
-  for (;; L += per_xcd) {
-    if (p.tile_counter) {
-      __syncthreads();   // every wave is done with LDS and memory of the previous tile
-      if (tid == 0) *tile_word = atomicAdd(p.tile_counter + xcd, 1);
-      __syncthreads();
-      L = t_beg + *tile_word;
-    }
-    if (L >= t_end) break;
+  if (dynamic) {
+    if (tid == 0) *tile_word = atomicAdd(p.tile_counter + xcd, 1);
+    __syncthreads();
+    L = t_beg + *tile_word;
+  }
+  if (L >= t_end) return;
+
+  struct Tile {
+    int m0, mend, mlast, c0;
+    const uint8_t* a;
+    const uint8_t* b;
+    uint32_t a_src[kLd], b_src[kLd];
+  };
+  auto setup = [&](long long L, Tile& t) __attribute__((always_inline)) {
     const int e = p.tile_expert[L / nN];
     const int pe = p.tile_prefix[e];
     const int mt_e = p.tile_prefix[e + 1] - pe;
@@ -122,71 +131,77 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     int seg_lo, seg_hi;
     expert_segment(p, e, seg_lo, seg_hi);
     const int rpt = ((seg_hi - seg_lo + mt_e - 1) / mt_e + 31) / 32 * 32;
-    const int m0 = seg_lo + mtile * rpt;
-    const int mend = m0 + rpt < seg_hi ? m0 + rpt : seg_hi;
-    const int mlast = mend - 1 - m0;
-    const int c0 = nblk * tile_cols;
-    const int clast = n_cols - 1 - c0;
-
+    t.m0 = seg_lo + mtile * rpt;
+    t.mend = t.m0 + rpt < seg_hi ? t.m0 + rpt : seg_hi;
+    t.mlast = t.mend - 1 - t.m0;
+    t.c0 = nblk * tile_cols;
+    const int clast = n_cols - 1 - t.c0;
     // gathered operand: tile row r is row a_rows[m0 + r] / a_div of a (the launcher checks
     // that a_nrows * rb fits in 32 bits); rows past the segment or the matrix re-read the
     // last valid one
-    const uint8_t* a_tile = p.a_rows ? p.a : p.a + static_cast<size_t>(m0) * rb;
-    const uint8_t* b_tile = p.b + static_cast<size_t>(e) * p.b_rows * rb;
-    uint32_t a_src[kLd], b_src[kLd];
+    t.a = p.a_rows ? p.a : p.a + static_cast<size_t>(t.m0) * rb;
+    t.b = p.b + static_cast<size_t>(e) * p.b_rows * rb;
 #pragma unroll
     for (int j = 0; j < kLd; ++j) {
       const int r = (wave + 4 * j) * 8 + lrow;   // tile row of this lane's loads
-      int ra = r < mlast ? r : mlast;
+      int ra = r < t.mlast ? r : t.mlast;
       if (p.a_rows) {
-        int t = p.a_rows[m0 + ra] / p.a_div;
-        ra = t < 0 ? 0 : (t < p.a_nrows ? t : p.a_nrows - 1);
+        int tok = p.a_rows[t.m0 + ra] / p.a_div;
+        ra = tok < 0 ? 0 : (tok < p.a_nrows ? tok : p.a_nrows - 1);
       }
-      a_src[j] = static_cast<uint32_t>(ra) * rb + lchunk * 16;
+      t.a_src[j] = static_cast<uint32_t>(ra) * rb + lchunk * 16;
       uint32_t wr;
       if (MODE == MODE_GATE_UP) {
         const int c = r % (kTN / 2);
         const int cc = c < clast ? c : clast;
-        wr = (r < kTN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(c0 + cc);
+        wr = (r < kTN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(t.c0 + cc);
       } else {
-        wr = static_cast<uint32_t>(c0 + (r < clast ? r : clast));
+        wr = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
       }
-      b_src[j] = wr * rb + lchunk * 16;
+      t.b_src[j] = wr * rb + lchunk * 16;
     }
+  };
+  // activation rows of stage ks into buffer buf; weight rows of stage ks into ring slot ws
+  auto load_a = [&](const Tile& t, int ks, int buf, int j) __attribute__((always_inline)) {
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane(lds0 + static_cast<uint32_t>(buf * kPart + (wave + 4 * j) * 1024));
+    dma16(t.a + static_cast<size_t>(ks) * kRowB + t.a_src[j], base);
+  };
+  auto load_w = [&](const Tile& t, int ks, int ws, int j) __attribute__((always_inline)) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        lds0 + static_cast<uint32_t>(kWBase + ws * kPart + (wave + 4 * j) * 1024));
+    dma16(t.b + static_cast<size_t>(ks) * kRowB + t.b_src[j], base);
+  };
+  // prologue loads of a tile (stage 0 and 1); the caller waits for stage 0 and synchronises.
+  // Wave 0 first takes the counter value for the tile after this one, so that the wait for
+  // stage 0 also covers it.
+  auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
+    if (dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) load_a(t, 0, 0, j);
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) load_w(t, 0, 0, j);
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) load_w(t, 1, 1, j);
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) load_a(t, 1, 1, j);
+  };
 
-    // activation rows of stage ks into buffer buf; weight rows of stage ks into ring slot ws
-    auto load_a = [&](int ks, int buf, int j) __attribute__((always_inline)) {
-      const uint32_t base =
-          __builtin_amdgcn_readfirstlane(lds0 + static_cast<uint32_t>(buf * kPart + (wave + 4 * j) * 1024));
-      dma16(a_tile + static_cast<size_t>(ks) * kRowB + a_src[j], base);
-    };
-    auto load_w = [&](int ks, int ws, int j) __attribute__((always_inline)) {
-      const uint32_t base = __builtin_amdgcn_readfirstlane(
-          lds0 + static_cast<uint32_t>(kWBase + ws * kPart + (wave + 4 * j) * 1024));
-      dma16(b_tile + static_cast<size_t>(ks) * kRowB + b_src[j], base);
-    };
+  Tile cur;
+  setup(L, cur);
+  prologue(cur);
+  wait_vmcnt<2 * kLd>();   // stage 0 (and the counter value) landed; stage 1 may be in flight
+  block_barrier();
 
+  for (;;) {
+    const Tile& t = cur;   // (rewritten at the boundary, after the epilogue's last use)
     f32x16_t acc[kMB][kNB];
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
 #pragma unroll
       for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16_t{};
 
-    // ---- prologue: stage 0 landed; stage 1 (activation buffer 1, ring slot 1) loading
-    wait_vmcnt<0>();   // the previous tile's stores have drained
-    block_barrier();   // and every wave is past its last LDS reads
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_a(0, 0, j);
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_w(0, 0, j);
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_w(1, 1, j);
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_a(1, 1, j);
-    wait_vmcnt<2 * kLd>();
-    block_barrier();
-
-    int act = ((mlast + 32) / 32 - wm + 1) / 2;   // 32-row blocks of this wave that hold rows
+    int act = ((t.mlast + 32) / 32 - wm + 1) / 2;   // 32-row blocks of this wave that hold rows
     act = act < 0 ? 0 : (act > kMB ? kMB : act);
 
     auto k_loop = [&](auto act_c) __attribute__((always_inline)) {
@@ -226,10 +241,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         const int ws1 = ws == 2 ? 0 : ws + 1, ws2 = ws1 == 2 ? 0 : ws1 + 1;
         const int aoff = buf * kPart, boff = kWBase + ws * kPart;
         mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 1, [&](int i) __attribute__((always_inline)) {
-          if (FULL && (i & 3) == 1) load_w(ks + 2, ws2, i >> 2);
+          if (FULL && (i & 3) == 1) load_w(t, ks + 2, ws2, i >> 2);
         });
         mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, [&](int i) __attribute__((always_inline)) {
-          if (FULL && (i & 3) == 1) load_w(ks + 2, ws2, 4 + (i >> 2));
+          if (FULL && (i & 3) == 1) load_w(t, ks + 2, ws2, 4 + (i >> 2));
         });
         mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 3, nothing);
         if constexpr (NEXT) {
@@ -243,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         __builtin_amdgcn_sched_barrier(0);
         mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPart, kWBase + ws1 * kPart, 0,
                                             [&](int i) __attribute__((always_inline)) {
-          if (FULL && (i & 1) == 1) load_a(ks + 2, buf, i >> 1);
+          if (FULL && (i & 1) == 1) load_a(t, ks + 2, buf, i >> 1);
         });
       };
       int ks = 0, ws = 0;
@@ -261,26 +276,37 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       ((act == A ? k_loop(std::integral_constant<int, A>{}) : void()), ...);
     }(std::make_integer_sequence<int, kMB + 1>{});
 
+    // ---- tile boundary: every wave is past its last LDS reads; the next tile is known
+    block_barrier();
+    long long Ln = L + per_xcd;
+    if (dynamic) {
+      if (tid == 0) *tile_word = grabbed;
+      wait_lgkmcnt_all();
+      block_barrier();
+      Ln = t_beg + *tile_word;
+    }
+    const bool more = Ln < t_end;
+
     // ---- epilogue: lane l holds token row (2 mb + wm) * 32 + l % 32 of the tile and, in
     // registers 4q .. 4q+3 of block nb, output columns nb * 32 + 8q + 4 (l / 32) + 0..3:
     // one 8-byte store per run (n_cols % 4 == 0, so a run is all in or all out)
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
-      const int r = m0 + (mb * 2 + wm) * 32 + (lane & 31);
-      if (r >= mend) continue;
+      const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
+      if (r >= t.mend) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (MODE == MODE_GATE_UP) {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            const int col = c0 + wn * 64 + nb * 32 + 8 * q + 4 * hk;
+            const int col = t.c0 + wn * 64 + nb * 32 + 8 * q + 4 * hk;
             if (col >= n_cols) continue;
             float hv[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float g = acc[mb][nb][4 * q + t];
-              const float u = acc[mb][nb + 2][4 * q + t];
-              hv[t] = g / (1.0f + expf(-g)) * u;
+            for (int u = 0; u < 4; ++u) {
+              const float g = acc[mb][nb][4 * q + u];
+              const float up = acc[mb][nb + 2][4 * q + u];
+              hv[u] = g / (1.0f + expf(-g)) * up;
             }
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.I + col) =
                 make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
@@ -288,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         } else {
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int col = c0 + wn * 128 + nb * 32 + 8 * q + 4 * hk;
+            const int col = t.c0 + wn * 128 + nb * 32 + 8 * q + 4 * hk;
             if (col >= n_cols) continue;
             const f32x16_t& a = acc[mb][nb];
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.n_out + col) =
@@ -297,6 +323,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         }
       }
     }
+    if (!more) break;
+    // the next tile's first stages load while these stores drain: the wait below covers the
+    // stores (older) and stage 0, and leaves stage 1 in flight
+    setup(Ln, cur);
+    prologue(cur);
+    wait_vmcnt<2 * kLd>();
+    block_barrier();
+    L = Ln;
   }
 }
 
