@@ -101,9 +101,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // Tiles: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.  With
   // the counter, tiles adjacent in the order (the m-tiles sharing a weight panel, the
   // n-blocks sharing activation rows) start close together in time whatever the earlier
-  // tiles cost.  Wave 0 takes the index of the tile after next while the current tile's
-  // first stage loads, and hands it to the other waves at the tile boundary through the last
-  // word of ring slot 2 (no load writes that slot between a boundary and the first stage).
+  // tiles cost.  Wave 0 takes the next index during the tile's second-to-last stage (late
+  // enough that the take is still close to the start, early enough to hide its latency) and
+  // hands it to the other waves at the tile boundary through the last word of ring slot 2
+  // (no load writes that slot between a boundary and the first stage).
   int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes - 4);
   const bool dynamic = p.tile_counter != nullptr;
   int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
@@ -172,11 +173,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         lds0 + static_cast<uint32_t>(kWBase + ws * kPart + (wave + 4 * j) * 1024));
     dma16(t.b + static_cast<size_t>(ks) * kRowB + t.b_src[j], base);
   };
-  // prologue loads of a tile (stage 0 and 1); the caller waits for stage 0 and synchronises.
-  // Wave 0 first takes the counter value for the tile after this one, so that the wait for
-  // stage 0 also covers it.
+  // prologue loads of a tile (stage 0 and 1); the caller waits for stage 0 and synchronises
   auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
-    if (dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
 #pragma unroll
     for (int j = 0; j < kLd; ++j) load_a(t, 0, 0, j);
 #pragma unroll
@@ -190,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   Tile cur;
   setup(L, cur);
   prologue(cur);
-  wait_vmcnt<2 * kLd>();   // stage 0 (and the counter value) landed; stage 1 may be in flight
+  wait_vmcnt<2 * kLd>();   // stage 0 landed; stage 1 may be in flight
   block_barrier();
 
   for (;;) {
@@ -259,6 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPart, kWBase + ws1 * kPart, 0,
                                             [&](int i) __attribute__((always_inline)) {
           if (FULL && (i & 1) == 1) load_a(t, ks + 2, buf, i >> 1);
+          // second-to-last stage (its wait for loads is behind it): take the next tile
+          if (!FULL && NEXT && i == 0 && dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
         });
       };
       int ks = 0, ws = 0;
