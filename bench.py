@@ -39,6 +39,8 @@ def parse():
                    help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
+    p.add_argument("--no-fuse-shared", action="store_true",
+                   help="run the shared expert as launches of its own instead of inside the routed GEMMs")
     p.add_argument("--no-gather", action="store_true",
                    help="bf16: run the permute and read the gate/up rows from its copy")
     p.add_argument("--overlap", action="store_true",
@@ -67,11 +69,12 @@ GEMM_SOURCES = [os.path.join(ROOT, "combine_grouped_gemm_amd", "csrc", n)
                 for n in ("grouped_gemm_wide.hip", "gemm_device.h")]
 
 
-def algorithmic(cfg, n_e, gather=False):
+def algorithmic(cfg, n_e, gather=False, fused=False):
     """Algorithmic bytes and flops of each step (what the method must move or compute).
 
     gather: the gate/up GEMM reads its rows straight from x (each token row at least once)
-    instead of from a permuted copy."""
+    instead of from a permuted copy.  fused: the shared expert runs inside the routed
+    gate/up and down launches (its work is counted there)."""
     import numpy as np
     N, H, E, k, I = cfg.N, cfg.H, cfg.E, cfg.k, cfg.I
     rows = N * k
@@ -89,7 +92,12 @@ def algorithmic(cfg, n_e, gather=False):
                     "flops": 4.0 * rows * H * I}
     d["down"] = {"bytes": touched * H * I * (wb + fp8_scale) + rows * I * 2 + rows * H * act,
                  "flops": 2.0 * rows * H * I}
-    if cfg.shared:
+    if cfg.shared and fused:
+        d["gate_up"]["bytes"] += 2 * I * H * wb + N * I * 2     # x is read once for both
+        d["gate_up"]["flops"] += 4.0 * N * H * I
+        d["down"]["bytes"] += H * I * wb + N * I * 2 + N * H * act
+        d["down"]["flops"] += 2.0 * N * H * I
+    elif cfg.shared:
         d["shared"] = {"bytes": 3 * I * H * wb + N * H * act + N * I * 2 + N * H * act,
                        "flops": 6.0 * N * H * I}
     d["combine"] = {"bytes": (rows + (N if cfg.shared else 0)) * H * act + N * H * act + rows * 8}
@@ -155,7 +163,8 @@ def main():
     inp = workload.make_layer_inputs(cfg, dev)
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
-                     gather=not args.no_gather, overlap_shared=args.overlap)
+                     gather=not args.no_gather, overlap_shared=args.overlap,
+                     fuse_shared=not args.no_fuse_shared)
     x, z = inp["x"], inp["z"]
     torch.cuda.synchronize()
 
@@ -168,7 +177,7 @@ def main():
         stages.append(("permute", lambda: layer.permute(x)))
     stages += [("gate_up", lambda: layer.gate_up(x)),
                ("down", layer.down)]
-    if cfg.shared and layer.side is None:
+    if cfg.shared and layer.side is None and not layer.fuse:
         stages.append(("shared", lambda: layer.shared_expert(x)))
     stages.append(("combine", layer.combine))
     side = layer.side
@@ -255,7 +264,7 @@ def main():
     del csrc, cdst
 
     n_e = layer.layout[0].cpu().numpy()
-    alg = algorithmic(cfg, n_e, layer.gather)
+    alg = algorithmic(cfg, n_e, layer.gather, layer.fuse)
     alg["permute (standalone)"] = alg["permute"]
     kernels = {}
     for name, times in per.items():
@@ -290,7 +299,9 @@ def main():
                 "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic
-    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU, rows gathered from x (moe_expert_gate_up_gathered)"
+    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU, routed rows gathered from x and the shared expert in the "
+                      "same launch (moe_expert_gate_up_gathered_shared)" if layer.fuse else
+                      "grouped gate/up GEMM + SwiGLU, rows gathered from x (moe_expert_gate_up_gathered)"
                       if layer.gather else "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)")
     roof["algorithmic_bytes"] = int(g["bytes"])
     roof["algorithmic_flops"] = g["flops"]
@@ -319,6 +330,7 @@ def main():
                              else kernels["permute (standalone)"])["GB_per_s"],
         "permute_folded_into_gate_up": layer.gather,
         "shared_expert_on_side_stream": side is not None,
+        "shared_expert_in_routed_launches": layer.fuse,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,

@@ -21,7 +21,8 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
     "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM",
     "moe_route", "moe_dispatch_layout", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
-    "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
+    "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
+    "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
     "moe_version",
 ]
 
@@ -57,6 +58,8 @@ _SIGS = {
     "moe_expert_gate_up": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
     "moe_expert_gate_up_gathered": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
     "moe_expert_down": [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _SZ, _P],
+    "moe_expert_gate_up_gathered_shared": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
+    "moe_expert_down_shared": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P],
     "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
     "moe_status_str": [_I],
@@ -240,6 +243,43 @@ def moe_expert_gate_up_gathered(x: torch.Tensor, src_slot: torch.Tensor, k: int,
         _ptr(x), _dt(x), N, _ptr(src_slot), k, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(h),
         _ptr(ws), ws.numel(), _stream(x)))
     return h
+
+
+def moe_expert_gate_up_gathered_shared(x: torch.Tensor, src_slot: torch.Tensor, k: int, offsets: torch.Tensor,
+                                       w13: torch.Tensor, shared_w13: torch.Tensor, rows: Optional[int] = None,
+                                       h: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Routed gate/up (rows gathered from x) plus the shared expert on all N tokens in one
+    launch: h [rows + N, I], the shared expert's rows last."""
+    N, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if rows is None:
+        rows = src_slot.numel()
+    if h is None:
+        h = torch.empty((rows + N, I), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, MOE_BF16), x.device)
+    _check("moe_expert_gate_up_gathered_shared", lib().moe_expert_gate_up_gathered_shared(
+        _ptr(x), _dt(x), N, _ptr(src_slot), k, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(shared_w13),
+        _ptr(h), _ptr(ws), ws.numel(), _stream(x)))
+    return h
+
+
+def moe_expert_down_shared(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor, shared_w2: torch.Tensor,
+                           rows: int, out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Routed down GEMM over rows [0, rows) of h plus the shared expert's down over the rest:
+    out [h rows, H], the shared expert's rows last."""
+    total, I = h.shape
+    E, H, _ = w2.shape
+    n_shared = total - rows
+    if out is None:
+        out = torch.empty((total, H), dtype=h.dtype, device=h.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, total, H, I, E + 1, 1, MOE_BF16), h.device)
+    _check("moe_expert_down_shared", lib().moe_expert_down_shared(
+        _ptr(h), _dt(h), _ptr(offsets), E, rows, n_shared, I, H, _ptr(w2), _ptr(shared_w2), _ptr(out), _dt(out),
+        _ptr(ws), ws.numel(), _stream(h)))
+    return out
 
 
 def moe_expert_down(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor,

@@ -27,6 +27,8 @@ struct GemmArgs {
   int out_f32;
   int32_t* tile_counter;       // [kNumXcd] next tile of each XCD's range (zeroed by the schedule
                                // prologue), or null: tiles dealt round-robin
+  const uint8_t* shared_b;     // shared expert's weights [b_rows, K] (segment E), or null
+  int shared_rows;             // rows of the shared segment [rows, rows + shared_rows); 0: none
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot

@@ -54,20 +54,25 @@ template <> struct CTraits<CT_FP8> { static constexpr int esz = 1; };
 
 // Tile schedule prologue: m-tiles (of tile_rows rows) of each expert, their prefix and the
 // m-tile -> expert table.  Offsets are clamped into [0, rows] so malformed input cannot
-// index out of range.
+// index out of range.  With shared_rows > 0 a last segment E of shared_rows rows (the
+// shared expert) follows, and prefix has E + 2 entries.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int rows, int tile_rows, int tile_cap,
                                                            int32_t* __restrict__ prefix,
                                                            int32_t* __restrict__ tile_expert,
-                                                           int32_t* __restrict__ tile_counter) {
+                                                           int32_t* __restrict__ tile_counter,
+                                                           int shared_rows) {
   __shared__ int32_t tot[1024];
   const int e = threadIdx.x;
+  const int n_seg = E + (shared_rows > 0 ? 1 : 0);
   int mt = 0;
   if (e < E) {
     int lo = offsets[e], hi = offsets[e + 1];
     lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
     hi = hi < lo ? lo : (hi > rows ? rows : hi);
     mt = (hi - lo + tile_rows - 1) / tile_rows;
+  } else if (e < n_seg) {
+    mt = (shared_rows + tile_rows - 1) / tile_rows;
   }
   tot[e] = mt;
   __syncthreads();
@@ -78,11 +83,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     __syncthreads();
   }
   const int start = tot[e] - mt;
-  if (e < E) {
+  if (e < n_seg) {
     prefix[e] = start < tile_cap ? start : tile_cap;
     for (int i = 0; i < mt && start + i < tile_cap; ++i) tile_expert[start + i] = e;
   }
-  if (e == E - 1) prefix[E] = tot[e] < tile_cap ? tot[e] : tile_cap;
+  if (e == n_seg - 1) prefix[n_seg] = tot[e] < tile_cap ? tot[e] : tile_cap;
   if (e < kNumXcd) tile_counter[e] = 0;
 }
 
@@ -712,6 +717,13 @@ size_t gemm_tile_cap(int rows, int E) {
   return static_cast<size_t>((rows + kStreamTileRows - 1) / kStreamTileRows) + E;
 }
 
+bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long b_rows, int a_nrows,
+                                   bool gathered) {
+  const long long rbytes = 2LL * K;
+  return K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 && b_rows * rbytes < (1LL << 32) &&
+         (gathered ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
+}
+
 size_t gemm_schedule_bytes(int rows, int E) {
   const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E) + kNumXcd;
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
@@ -737,10 +749,12 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                                const void* b, const float* b_scale, void* out, bool out_f32,
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,
                                long long b_rows, void* sched, hipStream_t s, const int32_t* a_rows,
-                               int a_div, int a_nrows) {
+                               int a_div, int a_nrows, const void* shared_b, int shared_rows) {
+  // with a shared segment the schedule covers E + 1 segments and rows + shared_rows rows
+  const int n_seg = E + (shared_rows > 0 ? 1 : 0);
   int32_t* prefix = reinterpret_cast<int32_t*>(sched);
-  int32_t* tile_expert = prefix + E + 1;
-  const int cap = static_cast<int>(gemm_tile_cap(rows, E));
+  int32_t* tile_expert = prefix + n_seg + 1;
+  const int cap = static_cast<int>(gemm_tile_cap(rows + shared_rows, n_seg));
   int32_t* tile_counter = tile_expert + cap;
   // few rows per expert and e4m3 weights: the weight-streaming kernel (16-row m-tiles)
   const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) &&
@@ -751,14 +765,15 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const bool dma = ct == CT_BF16 && !b8;   // bf16 operands: the direct-to-LDS kernels
   // 256 x 256 tiles while every operand offset fits the kernel's 32-bit arithmetic
   const long long rbytes = 2LL * K;
-  const bool wide = (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= (E > 1 ? 2 : 3)) && dma &&
-                    K % 128 == 0 &&
-                    (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 &&
-                    b_rows * rbytes < (1LL << 32) &&
-                    (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
+  const bool wide_ok = dma && K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 &&
+                       b_rows * rbytes < (1LL << 32) &&
+                       (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
+  if (shared_rows > 0 && (!wide_ok || stream)) return hipErrorNotSupported;   // (callers check first)
+  const bool wide = wide_ok && (shared_rows > 0 ||
+                                (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= (E > 1 ? 2 : 3)));
   const int tile_rows = stream ? kStreamTileRows : (wide ? kWideTileRows : (dma ? kDM : GBM));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
-                     prefix, tile_expert, tile_counter);
+                     prefix, tile_expert, tile_counter, shared_rows);
   GemmArgs p;
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.a_scale = a_scale;
@@ -780,6 +795,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.b_rows = b_rows;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tile_counter = nullptr;
+  p.shared_b = reinterpret_cast<const uint8_t*>(shared_b);
+  p.shared_rows = shared_rows;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
   if (wide) {
     p.tile_counter = kWideDynamic ? tile_counter : nullptr;

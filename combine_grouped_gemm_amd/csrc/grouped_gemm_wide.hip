@@ -73,12 +73,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   const int n_cols = MODE == MODE_GATE_UP ? p.I : p.n_out;
   const int tile_cols = MODE == MODE_GATE_UP ? kTN / 2 : kTN;
   const int nN = (n_cols + tile_cols - 1) / tile_cols;
-  const long long total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
+  // routed tiles (expert -> n-block -> m-tile), then the shared segment's (m-tile -> n-block)
+  const long long n_r = static_cast<long long>(p.tile_prefix[p.E]) * nN;
+  const long long n_s = p.shared_rows > 0 ? static_cast<long long>(p.tile_prefix[p.E + 1] - p.tile_prefix[p.E]) * nN : 0;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
-  const long long t_beg = total * xcd / kNumXcd;
-  const long long t_end = total * (xcd + 1) / kNumXcd;
+  // each XCD takes a contiguous range of the routed tiles and one of the shared segment's
+  // (4 m-tiles x all n-blocks for an 8192-row shared expert: its rows are read once per XCD)
+  const long long r_beg = n_r * xcd / kNumXcd, r_cnt = n_r * (xcd + 1) / kNumXcd - r_beg;
+  const long long s_beg = n_s * xcd / kNumXcd, s_cnt = n_s * (xcd + 1) / kNumXcd - s_beg;
+  const long long v_end = r_cnt + s_cnt;   // this XCD's tiles, numbered 0 .. v_end - 1
+  auto tile_of = [&](long long v) __attribute__((always_inline)) {
+    return v < r_cnt ? r_beg + v : n_r + s_beg + (v - r_cnt);
+  };
   const int nk = p.K / 64;                                  // even: K % 128 == 0
   const uint32_t rb = static_cast<uint32_t>(p.K) * 2;       // row bytes of both operands
 
@@ -108,13 +116,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes - 4);
   const bool dynamic = p.tile_counter != nullptr;
   int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
-  long long L = t_beg + slot;
+  long long v = slot;
   if (dynamic) {
     if (tid == 0) *tile_word = atomicAdd(p.tile_counter + xcd, 1);
     __syncthreads();
-    L = t_beg + *tile_word;
+    v = *tile_word;
   }
-  if (L >= t_end) return;
+  if (v >= v_end) return;
 
   struct Tile {
     int m0, mend, mlast, c0;
@@ -123,14 +131,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     uint32_t a_src[kLd], b_src[kLd];
   };
   auto setup = [&](long long L, Tile& t) __attribute__((always_inline)) {
-    const int e = p.tile_expert[L / nN];
-    const int pe = p.tile_prefix[e];
-    const int mt_e = p.tile_prefix[e + 1] - pe;
-    const long long local = L - static_cast<long long>(pe) * nN;
-    const int nblk = static_cast<int>(local / mt_e);
-    const int mtile = static_cast<int>(local % mt_e);
-    int seg_lo, seg_hi;
-    expert_segment(p, e, seg_lo, seg_hi);
+    int e, mt_e, nblk, mtile, seg_lo, seg_hi;
+    if (L < n_r) {
+      e = p.tile_expert[L / nN];
+      const int pe = p.tile_prefix[e];
+      mt_e = p.tile_prefix[e + 1] - pe;
+      const long long local = L - static_cast<long long>(pe) * nN;
+      nblk = static_cast<int>(local / mt_e);
+      mtile = static_cast<int>(local % mt_e);
+      expert_segment(p, e, seg_lo, seg_hi);
+    } else {   // the shared segment [rows, rows + shared_rows), weights shared_b
+      e = p.E;
+      mt_e = p.tile_prefix[p.E + 1] - p.tile_prefix[p.E];
+      const long long local = L - n_r;
+      mtile = static_cast<int>(local / nN);
+      nblk = static_cast<int>(local % nN);
+      seg_lo = p.rows;
+      seg_hi = p.rows + p.shared_rows;
+    }
     const int rpt = ((seg_hi - seg_lo + mt_e - 1) / mt_e + 31) / 32 * 32;
     t.m0 = seg_lo + mtile * rpt;
     t.mend = t.m0 + rpt < seg_hi ? t.m0 + rpt : seg_hi;
@@ -141,13 +159,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     // that a_nrows * rb fits in 32 bits); rows past the segment or the matrix re-read the
     // last valid one
     t.a = p.a_rows ? p.a : p.a + static_cast<size_t>(t.m0) * rb;
-    t.b = p.b + static_cast<size_t>(e) * p.b_rows * rb;
+    t.b = e < p.E ? p.b + static_cast<size_t>(e) * p.b_rows * rb : p.shared_b;
 #pragma unroll
     for (int j = 0; j < kLd; ++j) {
       const int r = (wave + 4 * j) * 8 + lrow;   // tile row of this lane's loads
       int ra = r < t.mlast ? r : t.mlast;
-      if (p.a_rows) {
-        int tok = p.a_rows[t.m0 + ra] / p.a_div;
+      if (p.a_rows) {   // (the shared segment's row r is token r - rows)
+        int tok = e < p.E ? p.a_rows[t.m0 + ra] / p.a_div : t.m0 + ra - p.rows;
         ra = tok < 0 ? 0 : (tok < p.a_nrows ? tok : p.a_nrows - 1);
       }
       t.a_src[j] = static_cast<uint32_t>(ra) * rb + lchunk * 16;
@@ -186,6 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   };
 
   Tile cur;
+  long long L = tile_of(v);
   setup(L, cur);
   prologue(cur);
   wait_vmcnt<2 * kLd>();   // stage 0 landed; stage 1 may be in flight
@@ -278,14 +297,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
     // ---- tile boundary: every wave is past its last LDS reads; the next tile is known
     block_barrier();
-    long long Ln = L + per_xcd;
+    long long vn = v + per_xcd;
     if (dynamic) {
       if (tid == 0) *tile_word = grabbed;
       wait_lgkmcnt_all();
       block_barrier();
-      Ln = t_beg + *tile_word;
+      vn = *tile_word;
     }
-    const bool more = Ln < t_end;
+    const bool more = vn < v_end;
+    const long long Ln = more ? tile_of(vn) : 0;
 
     // ---- epilogue: lane l holds token row (2 mb + wm) * 32 + l % 32 of the tile and, in
     // registers 4q .. 4q+3 of block nb, output columns nb * 32 + 8q + 4 (l / 32) + 0..3:
@@ -330,6 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     prologue(cur);
     wait_vmcnt<2 * kLd>();
     block_barrier();
+    v = vn;
     L = Ln;
   }
 }

@@ -181,6 +181,48 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
                                              E, rows, H, I, I, 2ll * I, ws, stream, src_slot, k, N));
 }
 
+moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
+                                              int k, const int32_t* offsets, int E, int rows, int H, int I,
+                                              const void* w13, const void* shared_w13, void* h, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+  if (x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E < 1 || rows < 0 || N < 0 || H <= 0 || I <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (E >= MOE_MAX_EXPERTS || H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(rows) + N >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (rows + N == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < moe::gemm_schedule_bytes(rows + N, E + 1)) return MOE_ERR_WORKSPACE;
+  if (x == nullptr || shared_w13 == nullptr || h == nullptr || (rows > 0 && (w13 == nullptr || src_slot == nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(shared_w13) || (w13 != nullptr && !aligned16(w13))) return MOE_ERR_INVALID_ARG;
+  if (static_cast<long long>(N) * H * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!moe::grouped_gemm_shared_supported(0, H, I, I, 2ll * I, N, true)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_grouped_gemm(1, false, 0, x, nullptr, w13, nullptr, h, false, offsets,
+                                             E, rows, H, I, I, 2ll * I, ws, stream, src_slot, k, N,
+                                             shared_w13, N));
+}
+
+moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
+                                  int n_shared, int I, int H, const void* w2, const void* shared_w2,
+                                  void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (h_dt != MOE_BF16 || out_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E < 1 || rows < 0 || n_shared < 0 || H <= 0 || I <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (E >= MOE_MAX_EXPERTS || H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(rows) + n_shared >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (rows + n_shared == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < moe::gemm_schedule_bytes(rows + n_shared, E + 1)) return MOE_ERR_WORKSPACE;
+  if (h == nullptr || out == nullptr || (n_shared > 0 && shared_w2 == nullptr) || (rows > 0 && w2 == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || (w2 != nullptr && !aligned16(w2)) || (shared_w2 != nullptr && !aligned16(shared_w2)))
+    return MOE_ERR_INVALID_ARG;
+  if (!moe::grouped_gemm_shared_supported(1, I, I, H, static_cast<long long>(H), 0, false))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_grouped_gemm(1, false, 1, h, nullptr, w2, nullptr, out, false, offsets, E,
+                                             rows, I, I, H, static_cast<long long>(H), ws, stream, nullptr, 1,
+                                             0, shared_w2, n_shared));
+}
+
 moe_status moe_expert_down(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                            int I, int H, const void* w2, moe_dtype w2_dt, const float* w2_scale,
                            void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,

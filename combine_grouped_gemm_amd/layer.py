@@ -9,7 +9,9 @@ only kernels: no allocation, no host synchronisation, no device-to-host copy.
 bf16 layers fold the permute into the gate/up GEMM by default (``gather=True``): its
 operand rows are read straight from x through the layout's src_slot map, so the
 permuted copy of x is never written.  f32 and fp8 layers (the fp8 permute also
-quantizes) run the permute kernel.
+quantizes) run the permute kernel.  bf16 layers with gathered rows also run the shared
+expert inside the routed GEMM launches by default (``fuse_shared=True``): its rows follow
+the routed rows in h and in the expert outputs.
 """
 from __future__ import annotations
 
@@ -17,10 +19,10 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN,
-               moe_combine, moe_dispatch_layout, moe_expert_down, moe_expert_gate_up,
-               moe_expert_gate_up_gathered, moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route,
-               moe_workspace_bytes)
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_EXPERT_GEMM,
+               MOE_OP_GROUPED_FFN, moe_combine, moe_dispatch_layout, moe_expert_down, moe_expert_down_shared,
+               moe_expert_gate_up, moe_expert_gate_up_gathered, moe_expert_gate_up_gathered_shared,
+               moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route, moe_workspace_bytes)
 
 
 class MoELayer:
@@ -36,7 +38,8 @@ class MoELayer:
     def __init__(self, N: int, H: int, E: int, k: int, I: int, dtype: str, w13: torch.Tensor,
                  w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
                  shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
-                 bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = False):
+                 bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = False,
+                 fuse_shared: bool = True):
         self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
         self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
         dev = w13.device
@@ -57,6 +60,7 @@ class MoELayer:
             self.sw13, self.sw2 = shared_w13, shared_w2
             self.sw13_scale = self.sw2_scale = None
         self.shared = shared_w13 is not None
+        self.fuse = bool(fuse_shared and self.shared and self.gather)
         i32 = dict(dtype=torch.int32, device=dev)
         self.topk_idx = torch.empty((N, k), **i32)
         self.topk_gate = torch.empty((N, k), dtype=torch.float32, device=dev)
@@ -69,27 +73,45 @@ class MoELayer:
         self.x_perm = None if self.gather else torch.empty((rows, H), dtype=torch.uint8 if self.fp8 else act,
                                                           device=dev)
         self.x_perm_scale = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
-        self.ffn_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt), 256),
-                                  dtype=torch.uint8, device=dev)
-        self.expert_out = torch.empty((rows, H), dtype=act, device=dev)
-        if self.shared:
+        self.ffn_ws = None if self.fuse else torch.empty(
+            max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt), 256), dtype=torch.uint8, device=dev)
+        if self.fuse:
+            # routed rows then the shared expert's N rows, in h and in the expert outputs
+            self.h_all = torch.empty((rows + N, I), dtype=torch.bfloat16, device=dev)
+            self.out_all = torch.empty((rows + N, H), dtype=act, device=dev)
+            self.fused_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, a_dt),
+                                            256), dtype=torch.uint8, device=dev)
+        else:
+            self._expert_out = torch.empty((rows, H), dtype=act, device=dev)
+        if self.shared and not self.fuse:
             self.shared_offsets = torch.tensor([0, N], **i32)
             self.x_q = torch.empty((N, H), dtype=torch.uint8, device=dev) if self.fp8 else None
             self.x_q_scale = torch.empty((N, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
             self.shared_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, N, H, I, 1, 1, a_dt), 256),
                                          dtype=torch.uint8, device=dev)
-            self.shared_out = torch.empty((N, H), dtype=act, device=dev)
+            self._shared_out = torch.empty((N, H), dtype=act, device=dev)
         # the shared expert needs only x: it runs on a second stream (default priority)
         # beside route / layout / the routed FFN, and combine waits for it
-        self.side = torch.cuda.Stream(device=dev) if self.shared and overlap_shared else None
+        self.side = torch.cuda.Stream(device=dev) if self.shared and overlap_shared and not self.fuse else None
         self.shared_done = torch.cuda.Event() if self.side is not None else None
         self.y = torch.empty((N, H), dtype=act, device=dev)
 
     @property
+    def expert_out(self) -> torch.Tensor:
+        """The routed experts' outputs [N*k, H] of the last forward."""
+        return self.out_all[:self.N * self.k] if self.fuse else self._expert_out
+
+    @property
+    def shared_out(self) -> torch.Tensor:
+        """The shared expert's output [N, H] of the last forward."""
+        return self.out_all[self.N * self.k:] if self.fuse else self._shared_out
+
+    @property
     def h(self) -> torch.Tensor:
         """The intermediate h of the last routed FFN (a view into the workspace)."""
-        from . import moe_workspace_bytes as wsb, MOE_OP_EXPERT_GEMM
-        off = wsb(MOE_OP_EXPERT_GEMM, self.N * self.k, self.H, self.I, self.E, 1, self.a_dt)
+        if self.fuse:
+            return self.h_all[:self.N * self.k]
+        off = moe_workspace_bytes(MOE_OP_EXPERT_GEMM, self.N * self.k, self.H, self.I, self.E, 1, self.a_dt)
         esz = 4 if self.dtype == "f32" else 2
         n = self.N * self.k * self.I * esz
         return self.ffn_ws[off:off + n].view(torch.float32 if esz == 4 else torch.bfloat16).view(
@@ -111,7 +133,11 @@ class MoELayer:
         return moe_permute(x, send_pos, self.k, None, self.x_perm)
 
     def gate_up(self, x: torch.Tensor):
-        """Grouped gate/up GEMM + SwiGLU into h (gathered layers read x directly)."""
+        """Grouped gate/up GEMM + SwiGLU into h (gathered layers read x directly; fused
+        layers also compute the shared expert's rows)."""
+        if self.fuse:
+            return moe_expert_gate_up_gathered_shared(x, self.layout[3], self.k, self.layout[1], self.w13,
+                                                      self.sw13, h=self.h_all, ws=self.fused_ws)
         if self.gather:
             return moe_expert_gate_up_gathered(x, self.layout[3], self.k, self.layout[1], self.w13,
                                                h=self.h, ws=self.ffn_ws)
@@ -120,6 +146,9 @@ class MoELayer:
 
     def down(self):
         """Grouped down GEMM of h into the expert outputs."""
+        if self.fuse:
+            return moe_expert_down_shared(self.h_all, self.layout[1], self.w2, self.sw2, self.N * self.k,
+                                          out=self.out_all, ws=self.fused_ws)
         return moe_expert_down(self.h, self.layout[1], self.w2, self.w2_scale, self.expert_out, self.ffn_ws)
 
     def experts(self, x: Optional[torch.Tensor] = None):
@@ -130,11 +159,13 @@ class MoELayer:
                                self.w13_scale, self.w2_scale, self.expert_out, self.ffn_ws)
 
     def shared_expert(self, x: torch.Tensor):
+        if self.fuse:
+            return None   # computed by gate_up / down
         a, a_scale = x, None
         if self.fp8:
             a, a_scale = moe_quantize_fp8(x, self.x_q, self.x_q_scale)
         return moe_grouped_ffn(a, self.shared_offsets, self.sw13, self.sw2, a_scale, self.sw13_scale,
-                               self.sw2_scale, self.shared_out, self.shared_ws)
+                               self.sw2_scale, self._shared_out, self.shared_ws)
 
     def combine(self):
         return moe_combine(self.expert_out, self.layout[2], self.topk_gate,

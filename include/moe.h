@@ -227,6 +227,37 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
                                        hipStream_t stream);
 
 /*
+ * moe_expert_gate_up_gathered_shared / moe_expert_down_shared -- the routed grouped GEMMs
+ * with the shared expert as one more segment of the same launch.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (the layer output adds a shared
+ * branch that every token takes, with gate 1) and "MoE part 4" page, section 2 (one grouped
+ * launch over all segments).  Rows [0, rows) are the routed rows, exactly as in
+ * moe_expert_gate_up_gathered and moe_expert_down; rows [rows, rows + n) are the shared
+ * expert's, one per token: row rows + t takes token t of x (gate/up) or row rows + t of h
+ * (down), with the shared weights.  The shared rows' results equal a separate
+ * moe_expert_gate_up / moe_expert_down with E = 1 on all n tokens.
+ *
+ *   gate/up:  x [N, H] bf16; src_slot, k, offsets, E, rows, H, I, w13 as for
+ *             moe_expert_gate_up_gathered; shared_w13 [2*I, H] bf16 (W_gate rows, then
+ *             W_up rows); h [rows + N, I] bf16 (shared rows last); n = N.
+ *   down:     h [rows + n_shared, I] bf16; w2 [E, H, I] and shared_w2 [H, I] bf16;
+ *             out [rows + n_shared, H] bf16 (the shared rows last: pass out + rows * H to
+ *             moe_combine as shared_out).
+ *   ws        >= moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + n, H, I, E + 1, 1, MOE_BF16).
+ * bf16 only; requires E < MOE_MAX_EXPERTS, H % 128 == 0, I % 128 == 0 and N * H * 2 < 2^32
+ * (MOE_ERR_UNSUPPORTED otherwise).  rows + n == 0 returns MOE_OK without launching.
+ */
+moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
+                                              int k, const int32_t* offsets, int E, int rows, int H, int I,
+                                              const void* w13, const void* shared_w13, void* h, void* ws,
+                                              size_t ws_bytes, hipStream_t stream);
+moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
+                                  int n_shared, int I, int H, const void* w2, const void* shared_w2,
+                                  void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
  * moe_combine -- y_t = sum_{j<k} g_{t,j} * expert_out[send_pos[t*k+j]] (+ shared_out_t).
  *
  * Definition: "EP / DeepEP explanation" page, section 2 (y_t, with an optional shared

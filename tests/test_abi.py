@@ -118,3 +118,38 @@ def test_no_cpu_fallback_in_binding():
     import inspect
     src = inspect.getsource(moe)
     assert "oracle" not in src.replace("no fallback", "")
+
+
+def test_shared_segment_validation(L):
+    """The fused routed + shared entry points: dtype, shape, workspace and pointer checks happen
+    on the host, before anything is enqueued."""
+    rows, H, I, E, N, k = 65536, 7168, 2048, 256, 8192, 8
+    sched = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, MOE_BF16)
+    assert sched > moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16)
+    f = L.moe_expert_gate_up_gathered_shared
+    args = lambda **kw: dict(dict(x=FAKE, x_dt=MOE_BF16, N=N, src_slot=FAKE, k=k, offsets=FAKE, E=E,
+                                  rows=rows, H=H, I=I, w13=FAKE, sw13=FAKE, h=FAKE, ws=FAKE, ws_bytes=sched,
+                                  s=None), **kw)
+    call = lambda **kw: f(*args(**kw).values())
+    assert call(x_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
+    assert call(ws_bytes=sched - 1) == MOE_ERR_WORKSPACE
+    assert call(sw13=None) == MOE_ERR_INVALID_ARG
+    assert call(src_slot=None) == MOE_ERR_INVALID_ARG
+    assert call(k=0) == MOE_ERR_INVALID_ARG
+    assert call(E=1024) == MOE_ERR_UNSUPPORTED            # E + 1 segments must fit the schedule
+    assert call(I=2000) == MOE_ERR_UNSUPPORTED
+    assert call(N=300000, ws_bytes=1 << 40) == MOE_ERR_UNSUPPORTED   # N * H * 2 >= 2^32
+    assert call(sw13=FAKE + 8) == MOE_ERR_INVALID_ARG
+    assert call(rows=0, N=0, ws=None, ws_bytes=0) == MOE_OK
+    g = L.moe_expert_down_shared
+    dargs = lambda **kw: dict(dict(h=FAKE, h_dt=MOE_BF16, offsets=FAKE, E=E, rows=rows, n=N, I=I, H=H,
+                                   w2=FAKE, sw2=FAKE, out=FAKE, out_dt=MOE_BF16, ws=FAKE, ws_bytes=sched,
+                                   s=None), **kw)
+    dcall = lambda **kw: g(*dargs(**kw).values())
+    assert dcall(h_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
+    assert dcall(out_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
+    assert dcall(ws_bytes=sched - 1) == MOE_ERR_WORKSPACE
+    assert dcall(sw2=None) == MOE_ERR_INVALID_ARG
+    assert dcall(n=-1) == MOE_ERR_INVALID_ARG
+    assert dcall(H=7000) == MOE_ERR_UNSUPPORTED
+    assert dcall(rows=0, n=0, ws=None, ws_bytes=0) == MOE_OK

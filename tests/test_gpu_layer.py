@@ -167,13 +167,35 @@ def test_layer_shared_on_side_stream_equals_serial():
     for overlap in (True, False):
         layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                          inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
-                         overlap_shared=overlap)
+                         overlap_shared=overlap, fuse_shared=False)
         assert (layer.side is not None) == overlap
         for _ in range(3):
             y = layer.forward(inp["x"], inp["z"])
         ys.append(y.clone())
     sync()
     assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+
+
+def test_layer_shared_fused_equals_separate():
+    """The shared expert inside the routed launches == its own launches: the gate/up rows
+    bit for bit (same kernel), the down rows and y within the bf16 bar (the separate dense
+    down runs the 128-row-tile kernel)."""
+    cfg = SMALL["dsv3_small"]
+    inp = w.make_layer_inputs(cfg, DEV)
+    outs = []
+    for fuse in (True, False):
+        layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                         inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
+                         fuse_shared=fuse)
+        assert layer.fuse == fuse
+        y = layer.forward(inp["x"], inp["z"]).clone()
+        outs.append((layer.h.clone(), layer.expert_out.clone(), layer.shared_out.clone(), y))
+    sync()
+    (h0, e0, s0, y0), (h1, e1, s1, y1) = outs
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(e0.view(torch.int16), e1.view(torch.int16))
+    assert token_rel_err(f64(s0), f64(s1)) <= 1e-2
+    assert token_rel_err(f64(y0), f64(y1)) <= 1e-2
 
 
 FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
