@@ -39,6 +39,8 @@ def parse():
                    help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
+    p.add_argument("--gate-in-down", action="store_true",
+                   help="multiply the routed rows by their gates in the down GEMM's epilogue; combine sums")
     p.add_argument("--no-fuse-shared", action="store_true",
                    help="run the shared expert as launches of its own instead of inside the routed GEMMs")
     p.add_argument("--no-gather", action="store_true",
@@ -164,7 +166,7 @@ def main():
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
                      gather=not args.no_gather, overlap_shared=args.overlap,
-                     fuse_shared=not args.no_fuse_shared)
+                     fuse_shared=not args.no_fuse_shared, gate_in_down=args.gate_in_down)
     x, z = inp["x"], inp["z"]
     torch.cuda.synchronize()
 
@@ -331,6 +333,7 @@ def main():
         "permute_folded_into_gate_up": layer.gather,
         "shared_expert_on_side_stream": side is not None,
         "shared_expert_in_routed_launches": layer.fuse,
+        "gates_in_down_epilogue": layer.gate_in_down,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,

@@ -59,7 +59,7 @@ _SIGS = {
     "moe_expert_gate_up_gathered": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
     "moe_expert_down": [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _SZ, _P],
     "moe_expert_gate_up_gathered_shared": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
-    "moe_expert_down_shared": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P],
+    "moe_expert_down_shared": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
     "moe_status_str": [_I],
@@ -266,9 +266,11 @@ def moe_expert_gate_up_gathered_shared(x: torch.Tensor, src_slot: torch.Tensor, 
 
 
 def moe_expert_down_shared(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor, shared_w2: torch.Tensor,
-                           rows: int, out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+                           rows: int, out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                           src_slot: Optional[torch.Tensor] = None, topk_gate: Optional[torch.Tensor] = None):
     """Routed down GEMM over rows [0, rows) of h plus the shared expert's down over the rest:
-    out [h rows, H], the shared expert's rows last."""
+    out [h rows, H], the shared expert's rows last.  With src_slot and topk_gate, routed row r
+    is multiplied by its gate topk_gate.flat[src_slot[r]] in the epilogue."""
     total, I = h.shape
     E, H, _ = w2.shape
     n_shared = total - rows
@@ -277,8 +279,8 @@ def moe_expert_down_shared(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Ten
     if ws is None:
         ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, total, H, I, E + 1, 1, MOE_BF16), h.device)
     _check("moe_expert_down_shared", lib().moe_expert_down_shared(
-        _ptr(h), _dt(h), _ptr(offsets), E, rows, n_shared, I, H, _ptr(w2), _ptr(shared_w2), _ptr(out), _dt(out),
-        _ptr(ws), ws.numel(), _stream(h)))
+        _ptr(h), _dt(h), _ptr(offsets), E, rows, n_shared, I, H, _ptr(w2), _ptr(shared_w2), _ptr(src_slot),
+        _ptr(topk_gate), _ptr(out), _dt(out), _ptr(ws), ws.numel(), _stream(h)))
     return out
 
 
@@ -317,10 +319,14 @@ def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, w13: torch.Tensor, w
     return out
 
 
-def moe_combine(expert_out: torch.Tensor, send_pos: torch.Tensor, topk_gate: torch.Tensor,
+def moe_combine(expert_out: torch.Tensor, send_pos: torch.Tensor, topk_gate: Optional[torch.Tensor],
                 shared_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                y_dtype: Optional[torch.dtype] = None):
-    N, k = topk_gate.shape
+                y_dtype: Optional[torch.dtype] = None, k: Optional[int] = None):
+    """topk_gate None: the expert outputs already carry their gates (pass k)."""
+    if topk_gate is not None:
+        N, k = topk_gate.shape
+    else:
+        N = send_pos.numel() // k
     H = expert_out.shape[1]
     if y is None:
         y = torch.empty((N, H), dtype=y_dtype or expert_out.dtype, device=expert_out.device)

@@ -10,6 +10,8 @@
 // and writes 16 bytes (bf16) or 32 bytes (fp32).  Gates and send positions are uniform
 // across the workgroup, whose size (128 or 256 lanes) divides the row's 8-column groups
 // when it can, so that no pass over the row leaves lanes idle.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -35,7 +37,7 @@ __device__ __forceinline__ void load8(const void* base, size_t row, int H, int c
   }
 }
 
-template <int U, bool kEoF32>
+template <int U, bool kEoF32, bool kGated>
 __device__ __forceinline__ void gather_sum(const void* eo, const int32_t* sp, const float* g, int H, int c,
                                            float (&acc)[8]) {
   float v[U][8];
@@ -53,34 +55,34 @@ __device__ __forceinline__ void gather_sum(const void* eo, const int32_t* sp, co
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const float gu = g[u];
+    const float gu = kGated ? g[u] : 1.0f;   // (fma with 1 is the plain sum)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = fmaf(gu, v[u][i], acc[i]);
   }
 }
 
-template <bool kEoF32, bool kYF32>
+template <bool kEoF32, bool kYF32, bool kGated>
 __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel(
     const void* __restrict__ eo, int H, int k, const int32_t* __restrict__ send_pos,
     const float* __restrict__ gate, const void* __restrict__ shared, void* __restrict__ y, int spans) {
   const int t = blockIdx.x / spans;
   const int span = blockIdx.x % spans;
   const int32_t* sp = send_pos + static_cast<size_t>(t) * k;
-  const float* g = gate + static_cast<size_t>(t) * k;
+  const float* g = kGated ? gate + static_cast<size_t>(t) * k : nullptr;
   const int groups8 = H / 8;
   const int per_span = (groups8 + spans - 1) / spans;
   const int c_end = (span + 1) * per_span < groups8 ? (span + 1) * per_span : groups8;
   for (int c = span * per_span + threadIdx.x; c < c_end; c += blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int j = 0;
-    for (; j + 8 <= k; j += 8) gather_sum<8, kEoF32>(eo, sp + j, g + j, H, c, acc);
-    for (; j + 4 <= k; j += 4) gather_sum<4, kEoF32>(eo, sp + j, g + j, H, c, acc);
+    for (; j + 8 <= k; j += 8) gather_sum<8, kEoF32, kGated>(eo, sp + j, g + j, H, c, acc);
+    for (; j + 4 <= k; j += 4) gather_sum<4, kEoF32, kGated>(eo, sp + j, g + j, H, c, acc);
     for (; j < k; ++j) {
       const int r = sp[j];
       if (r < 0) continue;
       float v[8];
       load8<kEoF32>(eo, static_cast<size_t>(r), H, c, v);
-      const float gj = g[j];
+      const float gj = kGated ? g[j] : 1.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
     }
@@ -118,14 +120,24 @@ hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, cons
     spans = want < passes ? want : passes;
   }
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(N) * spans)), block(threads);
-  if (eo_f32 && y_f32)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
-  else if (eo_f32)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
-  else if (y_f32)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
-  else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
+  // gate == null: the expert outputs already carry their gates (plain sum)
+  auto go = [&](auto eo32, auto y32, auto gated) {
+    hipLaunchKernelGGL((combine_kernel<decltype(eo32)::value, decltype(y32)::value, decltype(gated)::value>), grid,
+                       block, 0, s, eo, H, k, send_pos, gate, shared, y, spans);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (gate != nullptr) {
+    if (eo_f32 && y_f32) go(T{}, T{}, T{});
+    else if (eo_f32) go(T{}, F{}, T{});
+    else if (y_f32) go(F{}, T{}, T{});
+    else go(F{}, F{}, T{});
+  } else {
+    if (eo_f32 && y_f32) go(T{}, T{}, F{});
+    else if (eo_f32) go(T{}, F{}, F{});
+    else if (y_f32) go(F{}, T{}, F{});
+    else go(F{}, F{}, F{});
+  }
   return hipGetLastError();
 }
 

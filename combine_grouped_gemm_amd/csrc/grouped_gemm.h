@@ -29,6 +29,8 @@ struct GemmArgs {
                                // prologue), or null: tiles dealt round-robin
   const uint8_t* shared_b;     // shared expert's weights [b_rows, K] (segment E), or null
   int shared_rows;             // rows of the shared segment [rows, rows + shared_rows); 0: none
+  const int32_t* row_slot;     // down: routed output row r is scaled by row_gate[row_slot[r]]
+  const float* row_gate;       //   (slots clamped into [0, rows)), or both null
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot

@@ -314,6 +314,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     for (int mb = 0; mb < kMB; ++mb) {
       const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
       if (r >= t.mend) continue;
+      // down with gates: a routed row carries the gate of its slot (the shared rows gate 1)
+      float gs = 1.0f;
+      if (MODE == MODE_DOWN && p.row_gate != nullptr && r < p.rows) {
+        int sl = p.row_slot[r];
+        sl = sl < 0 ? 0 : (sl < p.rows ? sl : p.rows - 1);
+        gs = p.row_gate[sl];
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (MODE == MODE_GATE_UP) {
@@ -338,7 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
             if (col >= n_cols) continue;
             const f32x16_t& a = acc[mb][nb];
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.n_out + col) =
-                make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+                make_uint2(pack_bf16x2(a[4 * q] * gs, a[4 * q + 1] * gs),
+                           pack_bf16x2(a[4 * q + 2] * gs, a[4 * q + 3] * gs));
           }
         }
       }

@@ -204,8 +204,8 @@ moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int
 
 moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                                   int n_shared, int I, int H, const void* w2, const void* shared_w2,
-                                  void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+                                  const int32_t* src_slot, const float* topk_gate, void* out,
+                                  moe_dtype out_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (h_dt != MOE_BF16 || out_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (E < 1 || rows < 0 || n_shared < 0 || H <= 0 || I <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
   if (E >= MOE_MAX_EXPERTS || H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
@@ -214,13 +214,14 @@ moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* 
   if (ws == nullptr || ws_bytes < moe::gemm_schedule_bytes(rows + n_shared, E + 1)) return MOE_ERR_WORKSPACE;
   if (h == nullptr || out == nullptr || (n_shared > 0 && shared_w2 == nullptr) || (rows > 0 && w2 == nullptr))
     return MOE_ERR_INVALID_ARG;
+  if ((src_slot == nullptr) != (topk_gate == nullptr)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(h) || (w2 != nullptr && !aligned16(w2)) || (shared_w2 != nullptr && !aligned16(shared_w2)))
     return MOE_ERR_INVALID_ARG;
   if (!moe::grouped_gemm_shared_supported(1, I, I, H, static_cast<long long>(H), 0, false))
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_grouped_gemm(1, false, 1, h, nullptr, w2, nullptr, out, false, offsets, E,
                                              rows, I, I, H, static_cast<long long>(H), ws, stream, nullptr, 1,
-                                             0, shared_w2, n_shared));
+                                             0, shared_w2, n_shared, src_slot, topk_gate));
 }
 
 moe_status moe_expert_down(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
@@ -273,8 +274,7 @@ moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, in
   if (k > MOE_MAX_TOPK || N >= kMaxRowsPerLaunch || H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (N == 0) return MOE_OK;
-  if (expert_out == nullptr || send_pos == nullptr || topk_gate == nullptr || y == nullptr)
-    return MOE_ERR_INVALID_ARG;
+  if (expert_out == nullptr || send_pos == nullptr || y == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned16(expert_out) || !aligned16(y) || (shared_out != nullptr && !aligned16(shared_out)))
     return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_combine(expert_out, eo_dt == MOE_F32, N, H, k, send_pos, topk_gate,

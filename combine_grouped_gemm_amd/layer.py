@@ -39,7 +39,7 @@ class MoELayer:
                  w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
                  shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
                  bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = False,
-                 fuse_shared: bool = True):
+                 fuse_shared: bool = True, gate_in_down: bool = False):
         self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
         self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
         dev = w13.device
@@ -61,6 +61,8 @@ class MoELayer:
             self.sw13_scale = self.sw2_scale = None
         self.shared = shared_w13 is not None
         self.fuse = bool(fuse_shared and self.shared and self.gather)
+        # the routed rows' gates applied in the down GEMM's epilogue (combine then sums)
+        self.gate_in_down = bool(gate_in_down and self.fuse)
         i32 = dict(dtype=torch.int32, device=dev)
         self.topk_idx = torch.empty((N, k), **i32)
         self.topk_gate = torch.empty((N, k), dtype=torch.float32, device=dev)
@@ -147,8 +149,10 @@ class MoELayer:
     def down(self):
         """Grouped down GEMM of h into the expert outputs."""
         if self.fuse:
+            gates = (self.layout[3], self.topk_gate) if self.gate_in_down else (None, None)
             return moe_expert_down_shared(self.h_all, self.layout[1], self.w2, self.sw2, self.N * self.k,
-                                          out=self.out_all, ws=self.fused_ws)
+                                          out=self.out_all, ws=self.fused_ws, src_slot=gates[0],
+                                          topk_gate=gates[1])
         return moe_expert_down(self.h, self.layout[1], self.w2, self.w2_scale, self.expert_out, self.ffn_ws)
 
     def experts(self, x: Optional[torch.Tensor] = None):
@@ -168,8 +172,8 @@ class MoELayer:
                                self.sw2_scale, self._shared_out, self.shared_ws)
 
     def combine(self):
-        return moe_combine(self.expert_out, self.layout[2], self.topk_gate,
-                           self.shared_out if self.shared else None, self.y)
+        return moe_combine(self.expert_out, self.layout[2], None if self.gate_in_down else self.topk_gate,
+                           self.shared_out if self.shared else None, self.y, k=self.k)
 
     def launch_shared_side(self, x: torch.Tensor):
         """Enqueue the shared expert on the side stream, after the work queued so far."""

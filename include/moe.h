@@ -244,6 +244,13 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
  *   down:     h [rows + n_shared, I] bf16; w2 [E, H, I] and shared_w2 [H, I] bf16;
  *             out [rows + n_shared, H] bf16 (the shared rows last: pass out + rows * H to
  *             moe_combine as shared_out).
+ *             src_slot [rows] and topk_gate [rows] (the layout's map and the router's gates,
+ *             slot t*k+j): when both are given the down epilogue multiplies routed row r by
+ *             its gate topk_gate[src_slot[r]] before rounding, so moe_combine is then called
+ *             with topk_gate = NULL.  This is the weighted sum of "MoE part 4" page, section 4
+ *             with its multiply moved into the GEMM (section 4.1: fused MoE kernels take the
+ *             routing metadata into the expert GEMM).  Slots outside [0, rows) are clamped.
+ *             Both NULL: unscaled outputs.  One NULL: MOE_ERR_INVALID_ARG.
  *   ws        >= moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + n, H, I, E + 1, 1, MOE_BF16).
  * bf16 only; requires E < MOE_MAX_EXPERTS, H % 128 == 0, I % 128 == 0 and N * H * 2 < 2^32
  * (MOE_ERR_UNSUPPORTED otherwise).  rows + n == 0 returns MOE_OK without launching.
@@ -254,8 +261,8 @@ moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int
                                               size_t ws_bytes, hipStream_t stream);
 moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                                   int n_shared, int I, int H, const void* w2, const void* shared_w2,
-                                  void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
+                                  const int32_t* src_slot, const float* topk_gate, void* out,
+                                  moe_dtype out_dt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * moe_combine -- y_t = sum_{j<k} g_{t,j} * expert_out[send_pos[t*k+j]] (+ shared_out_t).
@@ -266,7 +273,8 @@ moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* 
  *
  *   expert_out [rows, H] of eo_dt (MOE_F32 or MOE_BF16), rows >= max(send_pos) + 1.
  *   send_pos   [N * k] int32; slots with send_pos < 0 are skipped.
- *   topk_gate  [N, k] fp32.
+ *   topk_gate  [N, k] fp32, or NULL when the expert outputs already carry their gates
+ *              (moe_expert_down_shared with gates): then the rows are summed with weight 1.
  *   shared_out [N, H] of eo_dt, added with gate 1, or NULL.
  *   y          [N, H] of y_dt (MOE_F32 or MOE_BF16) out.
  * The sum is fp32 in the order j = 0..k-1, then the shared row; one rounding to y_dt.

@@ -112,6 +112,9 @@ def test_combine_validation(L):
     assert f(FAKE, MOE_BF16, 4, 128, 0, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
     assert f(None, MOE_BF16, 4, 128, 2, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
     assert f(None, MOE_BF16, 0, 128, 2, None, None, None, None, MOE_BF16, None) == MOE_OK
+    # topk_gate NULL is the gate-free sum (outputs that already carry their gates): accepted
+    assert f(FAKE, MOE_BF16, 0, 128, 2, FAKE, None, None, FAKE, MOE_BF16, None) == MOE_OK
+    assert f(FAKE, MOE_BF16, 4, 128, 2, None, None, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
 
 
 def test_no_cpu_fallback_in_binding():
@@ -143,8 +146,8 @@ def test_shared_segment_validation(L):
     assert call(rows=0, N=0, ws=None, ws_bytes=0) == MOE_OK
     g = L.moe_expert_down_shared
     dargs = lambda **kw: dict(dict(h=FAKE, h_dt=MOE_BF16, offsets=FAKE, E=E, rows=rows, n=N, I=I, H=H,
-                                   w2=FAKE, sw2=FAKE, out=FAKE, out_dt=MOE_BF16, ws=FAKE, ws_bytes=sched,
-                                   s=None), **kw)
+                                   w2=FAKE, sw2=FAKE, slot=None, gate=None, out=FAKE, out_dt=MOE_BF16, ws=FAKE,
+                                   ws_bytes=sched, s=None), **kw)
     dcall = lambda **kw: g(*dargs(**kw).values())
     assert dcall(h_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
     assert dcall(out_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
@@ -153,3 +156,5 @@ def test_shared_segment_validation(L):
     assert dcall(n=-1) == MOE_ERR_INVALID_ARG
     assert dcall(H=7000) == MOE_ERR_UNSUPPORTED
     assert dcall(rows=0, n=0, ws=None, ws_bytes=0) == MOE_OK
+    assert dcall(slot=FAKE) == MOE_ERR_INVALID_ARG     # gates need both the slot map and the gates
+    assert dcall(gate=FAKE) == MOE_ERR_INVALID_ARG

@@ -198,6 +198,36 @@ def test_layer_shared_fused_equals_separate():
     assert token_rel_err(f64(y0), f64(y1)) <= 1e-2
 
 
+def test_layer_gates_in_down_epilogue():
+    """Gates applied in the down GEMM's epilogue (combine then sums with weight 1): the
+    routed outputs equal the gate times the unscaled ones to bf16 rounding, and y matches
+    the oracle's within the bf16 bar."""
+    cfg = SMALL["dsv3_small"]
+    inp = w.make_layer_inputs(cfg, DEV)
+    res = {}
+    for gated in (False, True):
+        layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                         inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
+                         gate_in_down=gated)
+        assert layer.gate_in_down == gated
+        y = layer.forward(inp["x"], inp["z"]).clone()
+        sync()
+        gate_of_row = layer.topk_gate.reshape(-1)[layer.layout[3].long()].float()
+        res[gated] = (y, layer.expert_out.float().clone(), layer.shared_out.clone(), gate_of_row)
+    (y0, e0, s0, g), (y1, e1, s1, _) = res[False], res[True]
+    assert torch.equal(s0.view(torch.int16), s1.view(torch.int16))     # shared rows: gate 1
+    assert token_rel_err(f64(e1), f64(e0 * g[:, None])) <= 1e-2
+    # y against the oracle (which weights the unscaled expert outputs in the combine)
+    b = inp["bias_cpu"]
+    ow = OracleWeights(inp["w13"], inp["w2"], False)
+    ref = oracle.moe_layer(inp["x"].cpu().to(torch.float64).numpy(), inp["z_cpu"].numpy(), cfg.k, ow.g13, ow.g2,
+                           bias=None if b is None else b.numpy(), n_group=cfg.n_group, topk_group=cfg.topk_group,
+                           shared_w13=f64(inp["sw13"][0]), shared_w2=f64(inp["sw2"][0]))
+    err = token_rel_err(f64(y1), ref["y"])
+    say(f"  gates in the down epilogue: y max per-token relative error {err:.3e}")
+    assert err <= Y_BAR[cfg.dtype]
+
+
 FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
 SAMPLE_TOKENS = {"mixtral_bf16": 8, "dsv3_bf16": 4, "dsv3_zipf_bf16": 4, "decode_fp8": 2}
 
