@@ -1,8 +1,8 @@
 """Benchmark: one GPU's share of a sparse MoE layer on MI355X through libmoe.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-route -> dispatch layout -> permute -> grouped gate/up GEMM + SwiGLU -> grouped
-down GEMM -> shared expert (when the workload has one) -> combine.  Inputs and
+router logits -> route -> dispatch layout -> permute -> grouped gate/up GEMM +
+SwiGLU -> grouped down GEMM -> shared expert (when the workload has one) -> combine.  Inputs and
 weights are resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dsv3_bf16]
@@ -86,6 +86,7 @@ def algorithmic(cfg, n_e, gather=False, fused=False):
     touched = int((np.asarray(n_e) > 0).sum())
     fp8_scale = 4.0 / 128 if cfg.dtype == "fp8" else 0.0
     d = {}
+    d["router"] = {"bytes": N * H * act + E * H * act + N * E * 4, "flops": 2.0 * N * H * E}
     d["route"] = {"bytes": N * E * 4 + (E * 4 if cfg.zipf_s else 0) + rows * 8}
     d["layout"] = {"bytes": rows * 4 + (2 * E + 1) * 4 + 2 * rows * 4}
     d["permute"] = {"bytes": N * H * act + rows * H * (pay + fp8_scale)}
@@ -115,9 +116,11 @@ def cpu_baseline(cfg, inp, T):
 
     T = min(T, cfg.N)
     x = inp["x"][:T].detach().cpu()
-    z = inp["z_cpu"][:T].numpy()
+    w_r = inp["w_r"].detach().cpu().double().numpy()
     b = inp["bias_cpu"]
-    idx, _ = moe_oracle.route(z, cfg.k, None if b is None else b.numpy(), cfg.n_group, cfg.topk_group)
+    # the experts the sample touches (to stage their weights on the host before timing)
+    z0 = moe_oracle.router_logits(x.double().numpy(), w_r)
+    idx, _ = moe_oracle.route(z0, cfg.k, None if b is None else b.numpy(), cfg.n_group, cfg.topk_group)
     need = sorted(set(int(e) for e in idx.reshape(-1)))
     w13 = {e: inp["w13"][e].detach().cpu() for e in need}   # staged on the host, not timed
     w2 = {e: inp["w2"][e].detach().cpu() for e in need}
@@ -125,6 +128,7 @@ def cpu_baseline(cfg, inp, T):
     if cfg.shared:
         sw13, sw2 = inp["sw13"][0].cpu(), inp["sw2"][0].cpu()
     t0 = time.perf_counter()
+    z = moe_oracle.router_logits(x.double().numpy(), w_r)
     if fp8:
         q13 = {e: moe_oracle.quantize_blocks(w13[e].float().numpy()) for e in need}
         q2 = {e: moe_oracle.quantize_blocks(w2[e].float().numpy()) for e in need}
@@ -141,7 +145,8 @@ def cpu_baseline(cfg, inp, T):
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {T} of {cfg.N} tokens of the same batch through the whole oracle layer "
+            "sample": f"first {T} of {cfg.N} tokens of the same batch through the whole oracle layer, "
+                      f"router logits included "
                       f"({len(need)} experts touched; float64; weights staged on the host before timing); "
                       f"{dt:.1f} s"}
 
@@ -166,14 +171,15 @@ def main():
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
                      gather=not args.no_gather, overlap_shared=args.overlap,
-                     fuse_shared=not args.no_fuse_shared, gate_in_down=args.gate_in_down)
-    x, z = inp["x"], inp["z"]
+                     fuse_shared=not args.no_fuse_shared, gate_in_down=args.gate_in_down, w_r=inp["w_r"])
+    x = inp["x"]
     torch.cuda.synchronize()
 
     # the layer's own calls, one stage each, as MoELayer.forward issues them (bf16 layers fold
     # the permute into gate/up; the shared expert runs on the layer's side stream)
     stream = torch.cuda.current_stream()
-    stages = [("route", lambda: layer.route(z)),
+    stages = [("router", lambda: layer.router(x)),
+              ("route", lambda: layer.route(layer.z)),
               ("layout", layer.dispatch)]
     if not layer.gather:
         stages.append(("permute", lambda: layer.permute(x)))
@@ -324,6 +330,9 @@ def main():
                                + (f" zipf bias s={cfg.zipf_s}" if cfg.zipf_s else ""),
                    "global_batch": cfg.N, "parallelism": "single GPU"},
         "roofline": roof,
+        "router_logits_in_step": True,
+        "ms_per_step_without_router": round(ms_per_step - kernels["router"]["avg_ms"], 4),
+        "tokens_per_s_without_router": round(cfg.N / ((ms_per_step - kernels["router"]["avg_ms"]) / 1e3), 1),
         "cpu_baseline": cpu,
         "kernels": kernels,
         "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),

@@ -19,8 +19,8 @@ import torch
 __all__ = [
     "MoEError", "lib", "library_path", "declared_symbols",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
-    "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM",
-    "moe_route", "moe_dispatch_layout", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
+    "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM", "MOE_OP_ROUTER",
+    "moe_router_logits", "moe_route", "moe_dispatch_layout", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
     "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
     "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
     "moe_version",
@@ -31,7 +31,7 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
-MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN, MOE_OP_EXPERT_GEMM = range(3)
+MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN, MOE_OP_EXPERT_GEMM, MOE_OP_ROUTER = range(4)
 
 
 class MoEError(RuntimeError):
@@ -50,6 +50,7 @@ _I = ctypes.c_int
 _SZ = ctypes.c_size_t
 
 _SIGS = {
+    "moe_router_logits": [_P, _I, _I, _I, _P, _I, _P, _P, _SZ, _P],
     "moe_route": [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P],
     "moe_dispatch_layout": [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _I, _P, _P],
@@ -148,6 +149,22 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 # ------------------------------------------------------------------------------------------
 # entry points
 # ------------------------------------------------------------------------------------------
+
+def moe_router_logits(x: torch.Tensor, w_r: torch.Tensor, z: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """z [N, E] fp32 = x [N, H] . w_r [E, H]^T (x and w_r of one dtype)."""
+    N, H = x.shape
+    E = w_r.shape[0]
+    if w_r.shape[1] != H or w_r.dtype != x.dtype:
+        raise ValueError("w_r must be [E, H] of x's dtype")
+    if z is None:
+        z = torch.empty((N, E), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_ROUTER, N, H, 0, E, 0, _dt(x)), x.device)
+    _check("moe_router_logits", lib().moe_router_logits(_ptr(x), _dt(x), N, H, _ptr(w_r), E, _ptr(z),
+                                                        _ptr(ws), ws.numel(), _stream(x)))
+    return z
+
 
 def moe_route(z: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None, n_group: int = 0,
               topk_group: int = 0, topk_idx: Optional[torch.Tensor] = None,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "layout.hip", "permute.hip", "combine.hip", "grouped_gemm.hip", "grouped_gemm_stream.hip",
+SOURCES = ["router.hip", "route.hip", "layout.hip", "permute.hip", "combine.hip", "grouped_gemm.hip", "grouped_gemm_stream.hip",
            "grouped_gemm_wide.hip",
            "moe_api.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")

@@ -7,7 +7,7 @@
 namespace moe {
 
 enum { CT_F32 = 0, CT_BF16 = 1, CT_FP8 = 2 };
-enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
+enum { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_ROUTER = 2 };
 
 constexpr int kNumXcd = 8;
 
@@ -31,6 +31,8 @@ struct GemmArgs {
   int shared_rows;             // rows of the shared segment [rows, rows + shared_rows); 0: none
   const int32_t* row_slot;     // down: routed output row r is scaled by row_gate[row_slot[r]]
   const float* row_gate;       //   (slots clamped into [0, rows)), or both null
+  int k_split;                 // router: K is cut into k_split equal parts; part s of every
+                               // output goes to out + s * rows * n_out (fp32)
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot
@@ -51,6 +53,9 @@ hipError_t launch_grouped_gemm_stream(int mode, const GemmArgs& p, hipStream_t s
 // have been built with 256-row m-tiles, K must be a multiple of 128, and every operand
 // offset (b_rows * K * 2 per expert; a_nrows * K * 2 when gathered) must fit in 32 bits.
 constexpr int kWideTileRows = 256;
+// MODE_ROUTER (one segment [0, rows), no tile schedule, static tile order): tile
+// (part s, n-block, m-tile) multiplies columns [s K/k_split, (s+1) K/k_split) of a and b
+// (K / k_split a multiple of 128) and stores its fp32 sums, 16 bytes per run (n_out % 4 == 0).
 hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s);
 
 }  // namespace moe

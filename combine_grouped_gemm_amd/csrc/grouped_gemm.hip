@@ -801,6 +801,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.shared_rows = shared_rows;
   p.row_slot = row_gate != nullptr ? row_slot : nullptr;
   p.row_gate = row_slot != nullptr ? row_gate : nullptr;
+  p.k_split = 1;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
   if (wide) {
     p.tile_counter = kWideDynamic ? tile_counter : nullptr;

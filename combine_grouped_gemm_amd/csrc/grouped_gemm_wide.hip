@@ -3,6 +3,8 @@
 //
 //   gate/up:  h[r, :]   = silu(a[r] . W_gate,e^T) * (a[r] . W_up,e^T)   for r in segment e
 //   down:     out[r, :] = h[r] . W_down,e^T
+//   router:   part_s[t, :] = x[t, K_s] . W_r[:, K_s]^T over the s-th of k_split column ranges
+//             ("EP / DeepEP explanation" page, section 2: logits z = sum_s part_s)
 //
 // A persistent workgroup of 4 waves (2 x 2) per CU computes 256 rows x 256 weight rows;
 // each wave owns 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (accumulators in
@@ -73,9 +75,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   const int n_cols = MODE == MODE_GATE_UP ? p.I : p.n_out;
   const int tile_cols = MODE == MODE_GATE_UP ? kTN / 2 : kTN;
   const int nN = (n_cols + tile_cols - 1) / tile_cols;
+  // router: m-tiles of the single segment [0, rows); tiles ordered part -> n-block -> m-tile,
+  // so with k_split = 8 each XCD's range is one column part (its slice of W_r stays in L2)
+  const int mt_r = MODE == MODE_ROUTER ? (p.rows + kTM - 1) / kTM : 0;
   // routed tiles (expert -> n-block -> m-tile), then the shared segment's (m-tile -> n-block)
-  const long long n_r = static_cast<long long>(p.tile_prefix[p.E]) * nN;
-  const long long n_s = p.shared_rows > 0 ? static_cast<long long>(p.tile_prefix[p.E + 1] - p.tile_prefix[p.E]) * nN : 0;
+  const long long n_r = MODE == MODE_ROUTER ? static_cast<long long>(p.k_split) * mt_r * nN
+                                            : static_cast<long long>(p.tile_prefix[p.E]) * nN;
+  const long long n_s = MODE != MODE_ROUTER && p.shared_rows > 0
+                            ? static_cast<long long>(p.tile_prefix[p.E + 1] - p.tile_prefix[p.E]) * nN
+                            : 0;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
@@ -87,7 +95,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   auto tile_of = [&](long long v) __attribute__((always_inline)) {
     return v < r_cnt ? r_beg + v : n_r + s_beg + (v - r_cnt);
   };
-  const int nk = p.K / 64;                                  // even: K % 128 == 0
+  const int kspan = MODE == MODE_ROUTER ? p.K / p.k_split : p.K;   // K of one tile
+  const int nk = kspan / 64;                                // even: kspan % 128 == 0
   const uint32_t rb = static_cast<uint32_t>(p.K) * 2;       // row bytes of both operands
 
   const int hk = lane >> 5;
@@ -125,14 +134,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   if (v >= v_end) return;
 
   struct Tile {
-    int m0, mend, mlast, c0;
+    int m0, mend, mlast, c0, kp;   // (kp: the router's column part)
     const uint8_t* a;
     const uint8_t* b;
     uint32_t a_src[kLd], b_src[kLd];
   };
   auto setup = [&](long long L, Tile& t) __attribute__((always_inline)) {
-    int e, mt_e, nblk, mtile, seg_lo, seg_hi;
-    if (L < n_r) {
+    int e, mt_e, nblk, mtile, seg_lo, seg_hi, kp = 0;
+    if (MODE == MODE_ROUTER) {
+      e = 0;
+      mt_e = mt_r;
+      const long long per = static_cast<long long>(mt_r) * nN;
+      kp = static_cast<int>(L / per);
+      const int local = static_cast<int>(L - kp * per);
+      nblk = local / mt_r;
+      mtile = local % mt_r;
+      seg_lo = 0;
+      seg_hi = p.rows;
+    } else if (L < n_r) {
       e = p.tile_expert[L / nN];
       const int pe = p.tile_prefix[e];
       mt_e = p.tile_prefix[e + 1] - pe;
@@ -154,12 +173,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     t.mend = t.m0 + rpt < seg_hi ? t.m0 + rpt : seg_hi;
     t.mlast = t.mend - 1 - t.m0;
     t.c0 = nblk * tile_cols;
+    t.kp = kp;
     const int clast = n_cols - 1 - t.c0;
     // gathered operand: tile row r is row a_rows[m0 + r] / a_div of a (the launcher checks
     // that a_nrows * rb fits in 32 bits); rows past the segment or the matrix re-read the
     // last valid one
     t.a = p.a_rows ? p.a : p.a + static_cast<size_t>(t.m0) * rb;
     t.b = e < p.E ? p.b + static_cast<size_t>(e) * p.b_rows * rb : p.shared_b;
+    if (MODE == MODE_ROUTER) {
+      t.a += static_cast<size_t>(kp) * kspan * 2;
+      t.b += static_cast<size_t>(kp) * kspan * 2;
+    }
 #pragma unroll
     for (int j = 0; j < kLd; ++j) {
       const int r = (wave + 4 * j) * 8 + lrow;   // tile row of this lane's loads
@@ -309,7 +333,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
     // ---- epilogue: lane l holds token row (2 mb + wm) * 32 + l % 32 of the tile and, in
     // registers 4q .. 4q+3 of block nb, output columns nb * 32 + 8q + 4 (l / 32) + 0..3:
-    // one 8-byte store per run (n_cols % 4 == 0, so a run is all in or all out)
+    // one 8-byte store per run (16 bytes for fp32 router sums; n_cols % 4 == 0, so a run is
+    // all in or all out)
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
@@ -337,6 +362,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
             }
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.I + col) =
                 make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
+        } else if (MODE == MODE_ROUTER) {
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            const int col = t.c0 + wn * 128 + nb * 32 + 8 * q + 4 * hk;
+            if (col >= n_cols) continue;
+            const f32x16_t& a = acc[mb][nb];
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) +
+                                       (static_cast<size_t>(t.kp) * p.rows + r) * p.n_out + col) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
         } else {
 #pragma unroll
@@ -369,8 +404,10 @@ hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s) 
   const dim3 grid(256), block(kThreads);   // persistent: one workgroup per CU, a multiple of the 8 XCDs
   if (mode == MODE_GATE_UP)
     hipLaunchKernelGGL(grouped_gemm_wide_kernel<MODE_GATE_UP>, grid, block, 0, s, p);
-  else
+  else if (mode == MODE_DOWN)
     hipLaunchKernelGGL(grouped_gemm_wide_kernel<MODE_DOWN>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(grouped_gemm_wide_kernel<MODE_ROUTER>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -76,9 +76,25 @@ size_t moe_workspace_bytes(int op, int N, int H, int I, int E, int k, int a_dt) 
     case MOE_OP_GROUPED_FFN:
       if (E < 1 || N == 0 || I <= 0 || H <= 0) return 0;
       return moe::gemm_schedule_bytes(N, E) + h_bytes(N, I, a_dt);
+    case MOE_OP_ROUTER:
+      if (E < 1 || N == 0 || H <= 0) return 0;
+      return moe::router_ws_bytes(N, H, E, a_dt == MOE_BF16);
     default:
       return 0;
   }
+}
+
+moe_status moe_router_logits(const void* x, moe_dtype x_dt, int N, int H, const void* w_r, int E, float* z,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (N < 0 || H <= 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (x == nullptr || w_r == nullptr || z == nullptr) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::router_ws_bytes(N, H, E, x_dt == MOE_BF16);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_r) || !aligned16(z) || (need > 0 && !aligned16(ws))) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router_logits(x, x_dt == MOE_BF16, N, H, w_r, E, z, ws, stream));
 }
 
 moe_status moe_route(const float* z, int N, int E, int k, const float* bias, int n_group,

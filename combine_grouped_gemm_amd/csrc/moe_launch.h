@@ -22,6 +22,13 @@ hipError_t launch_permute_copy(const void* x, size_t row_bytes, int N, int k,
 hipError_t launch_permute_fp8(const void* x, bool f32_in, long long rows, int H, int k,
                               const int32_t* send_pos, uint8_t* q, float* scale, hipStream_t s);
 
+// router logits: parts of K the bf16 tile kernel uses (0: the plain fp32-FMA kernel),
+// the workspace that many fp32 partial sums need, and the launch
+int router_parts(int N, int H, int E, bool bf16);
+size_t router_ws_bytes(int N, int H, int E, bool bf16);
+hipError_t launch_router_logits(const void* x, bool bf16, int N, int H, const void* w_r, int E, float* z,
+                                void* ws, hipStream_t s);
+
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
                           const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s);
 

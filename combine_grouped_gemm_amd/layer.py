@@ -1,8 +1,11 @@
 """One GPU's share of a sparse MoE layer as a sequence of libmoe calls on one stream.
 
-    route -> dispatch layout -> permute -> grouped SwiGLU FFN (+ shared expert) -> combine
+    router logits -> route -> dispatch layout -> permute -> grouped SwiGLU FFN (+ shared expert)
+    -> combine
 
 ("MoE part 4" page, section 4 and 4.2; "EP / DeepEP explanation" page, sections 2-3.)
+Given the router weight W_r the layer computes the logits z = x W_r^T itself; without
+it, forward takes z.
 All buffers are allocated once, at construction, so a forward pass enqueues
 only kernels: no allocation, no host synchronisation, no device-to-host copy.
 
@@ -20,9 +23,10 @@ from typing import Optional
 import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_EXPERT_GEMM,
-               MOE_OP_GROUPED_FFN, moe_combine, moe_dispatch_layout, moe_expert_down, moe_expert_down_shared,
-               moe_expert_gate_up, moe_expert_gate_up_gathered, moe_expert_gate_up_gathered_shared,
-               moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route, moe_workspace_bytes)
+               MOE_OP_GROUPED_FFN, MOE_OP_ROUTER, moe_combine, moe_dispatch_layout, moe_expert_down,
+               moe_expert_down_shared, moe_expert_gate_up, moe_expert_gate_up_gathered,
+               moe_expert_gate_up_gathered_shared, moe_grouped_ffn, moe_permute, moe_quantize_fp8,
+               moe_route, moe_router_logits, moe_workspace_bytes)
 
 
 class MoELayer:
@@ -32,14 +36,15 @@ class MoELayer:
     'fp8' (bf16 hidden states; e4m3 payload and weights with per-128-column fp32
     scales; bf16 h, expert outputs and y).  Weights come in the storage dtype
     (bf16 for 'fp8'); the fp8 layer quantizes them once here, with the library's
-    own row quantizer.
+    own row quantizer.  ``w_r`` [E, H] (storage dtype): the router weight; the
+    logits then come from moe_router_logits on x.
     """
 
     def __init__(self, N: int, H: int, E: int, k: int, I: int, dtype: str, w13: torch.Tensor,
                  w2: torch.Tensor, shared_w13: Optional[torch.Tensor] = None,
                  shared_w2: Optional[torch.Tensor] = None, n_group: int = 0, topk_group: int = 0,
                  bias: Optional[torch.Tensor] = None, gather: bool = True, overlap_shared: bool = False,
-                 fuse_shared: bool = True, gate_in_down: bool = False):
+                 fuse_shared: bool = True, gate_in_down: bool = False, w_r: Optional[torch.Tensor] = None):
         self.N, self.H, self.E, self.k, self.I = N, H, E, k, I
         self.dtype, self.n_group, self.topk_group, self.bias = dtype, n_group, topk_group, bias
         dev = w13.device
@@ -64,6 +69,12 @@ class MoELayer:
         # the routed rows' gates applied in the down GEMM's epilogue (combine then sums)
         self.gate_in_down = bool(gate_in_down and self.fuse)
         i32 = dict(dtype=torch.int32, device=dev)
+        self.w_r = w_r
+        if w_r is not None:
+            self.z = torch.empty((N, E), dtype=torch.float32, device=dev)
+            x_dt = MOE_F32 if dtype == "f32" else MOE_BF16
+            self.router_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_ROUTER, N, H, 0, E, 0, x_dt), 256),
+                                         dtype=torch.uint8, device=dev)
         self.topk_idx = torch.empty((N, k), **i32)
         self.topk_gate = torch.empty((N, k), dtype=torch.float32, device=dev)
         self.layout = (torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(rows, **i32),
@@ -118,6 +129,10 @@ class MoELayer:
         n = self.N * self.k * self.I * esz
         return self.ffn_ws[off:off + n].view(torch.float32 if esz == 4 else torch.bfloat16).view(
             self.N * self.k, self.I)
+
+    def router(self, x: torch.Tensor):
+        """Router logits z = x W_r^T into self.z."""
+        return moe_router_logits(x, self.w_r, self.z, self.router_ws)
 
     def route(self, z: torch.Tensor):
         return moe_route(z, self.k, self.bias, self.n_group, self.topk_group, self.topk_idx, self.topk_gate)
@@ -184,9 +199,13 @@ class MoELayer:
             self.shared_expert(x)
             self.shared_done.record(self.side)
 
-    def forward(self, x: torch.Tensor, z: torch.Tensor) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:
         if self.side is not None:
             self.launch_shared_side(x)
+        if z is None:
+            if self.w_r is None:
+                raise ValueError("forward needs the logits z, or a layer built with the router weight w_r")
+            z = self.router(x)
         self.route(z)
         self.dispatch()
         self.permute(x)

@@ -13,7 +13,8 @@
  * unpermute and weighted sum; section 4.2: router top-k with correction bias and grouped
  * top-k first):
  *
- *     moe_route -> moe_dispatch_layout -> moe_permute -> moe_grouped_ffn -> moe_combine
+ *     moe_router_logits -> moe_route -> moe_dispatch_layout -> moe_permute -> moe_grouped_ffn
+ *         -> moe_combine
  *
  * On one GPU the dispatch and combine all-to-alls of expert parallelism become the
  * on-device permute and unpermute.
@@ -64,7 +65,8 @@ typedef enum {
 typedef enum {
   MOE_OP_DISPATCH_LAYOUT = 0,
   MOE_OP_GROUPED_FFN = 1, /* includes the [rows, I] intermediate h                      */
-  MOE_OP_EXPERT_GEMM = 2  /* moe_expert_gate_up / moe_expert_down: tile schedule only   */
+  MOE_OP_EXPERT_GEMM = 2, /* moe_expert_gate_up / moe_expert_down: tile schedule only   */
+  MOE_OP_ROUTER = 3       /* moe_router_logits: fp32 partial sums (N, H, E, a_dt = x_dt) */
 } moe_op;
 
 /* Limits of this implementation. */
@@ -72,6 +74,25 @@ typedef enum {
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 64
 #define MOE_FP8_BLOCK 128 /* columns per fp32 scale of an fp8 row */
+
+/*
+ * moe_router_logits -- z = x W_r^T, the router's logits for every token and expert.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (the router maps each token's
+ * hidden state to logits z in R^{N x E}); "MoE part 4" page, section 4.2 (the router's
+ * top-k then reads them).
+ *
+ *   x     [N, H] of x_dt (MOE_BF16 or MOE_F32).
+ *   w_r   [E, H] of x_dt: row e holds expert e's H weights (a linear layer's weight).
+ *   z     [N, E] fp32 out: z[t, e] = sum_h x[t, h] * w_r[e, h], accumulated in fp32.
+ *   ws    workspace of moe_workspace_bytes(MOE_OP_ROUTER, N, H, 0, E, 0, x_dt) bytes (may
+ *         be 0: then ws may be NULL).  bf16 operands with H % 128 == 0 and E % 4 == 0 run on
+ *         the matrix cores with K split into parts whose fp32 partial sums the workspace
+ *         holds; they are added in a fixed order, so z is the same on every call.
+ * x, w_r, z (and a non-empty ws) must be 16-byte aligned.  E <= MOE_MAX_EXPERTS.
+ */
+moe_status moe_router_logits(const void* x, moe_dtype x_dt, int N, int H, const void* w_r, int E, float* z,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * moe_route -- router top-k with optional bias and group limit, renormalised gates.

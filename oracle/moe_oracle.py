@@ -25,7 +25,7 @@ from typing import Callable, Optional, Sequence, Union
 import numpy as np
 
 __all__ = [
-    "E4M3_MAX", "biased_logits", "group_limit_mask", "topk_select", "renormalized_gates", "route",
+    "E4M3_MAX", "router_logits", "biased_logits", "group_limit_mask", "topk_select", "renormalized_gates", "route",
     "dispatch_layout", "permute", "e4m3_decode", "e4m3_encode", "quantize_blocks",
     "dequantize_blocks", "silu", "expert_ffn", "grouped_ffn", "combine", "imbalance", "moe_layer",
 ]
@@ -34,8 +34,20 @@ E4M3_MAX = 448.0  # largest finite OCP e4m3fn value: 1.75 * 2^8
 
 
 # --------------------------------------------------------------------------------------
-# router: top-k over logits, optional group limit, renormalised gates
+# router: logits, top-k over them, optional group limit, renormalised gates
 # --------------------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
+    """z_{t,e} = sum_h x_{t,h} W_r[e, h], summed in float64 and rounded once to fp32.
+
+    [EPX] 2: the router maps each token's hidden state to logits z in R^{N x E}.
+    Readings: a linear map without bias; W_r has one row of H weights per expert
+    (the weight layout of a linear layer); both operands are taken as stored.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    w64 = np.asarray(w_r, dtype=np.float64)
+    return (x64 @ w64.T).astype(np.float32)
+
 
 def biased_logits(z: np.ndarray, bias: Optional[np.ndarray]) -> np.ndarray:
     """z'_{t,e} = z_{t,e} + b_e, one IEEE fp32 addition per element.

@@ -31,6 +31,32 @@ def test_status_strings_and_version():
     assert moe.moe_version().count(".") == 2
 
 
+def test_router_validation_and_workspace(L):
+    ws_b = lambda N, H, E, dt: moe.moe_workspace_bytes(moe.MOE_OP_ROUTER, N, H, 0, E, 0, dt)
+    # DeepSeek-V3 shape: 32 tiles of 256 x 256, K in 8 parts (one per XCD) of fp32 partial sums
+    assert ws_b(8192, 7168, 256, MOE_BF16) == 8 * 8192 * 256 * 4
+    # decode batch: one tile, K in 14 parts (the most parts, up to 16, dividing 56 blocks of 128)
+    assert ws_b(128, 7168, 256, MOE_BF16) == 14 * 128 * 256 * 4
+    # enough tiles for every CU: no parts; fp32 operands and E % 4 != 0: the plain kernel
+    assert ws_b(65536, 7168, 256, MOE_BF16) == 0
+    assert ws_b(256, 128, 8, MOE_F32) == 0
+    assert ws_b(512, 1024, 6, MOE_BF16) == 0
+    ws = ws_b(8192, 7168, 256, MOE_BF16)
+    f = L.moe_router_logits
+    assert f(FAKE, MOE_BF16, -1, 7168, FAKE, 256, FAKE, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8192, 7168, FAKE, 0, FAKE, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8192, 0, FAKE, 256, FAKE, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_FP8_E4M3, 8192, 7168, FAKE, 256, FAKE, FAKE, ws, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 8192, 7168, FAKE, 2048, FAKE, FAKE, ws, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 8192, 7168, None, 256, FAKE, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8192, 7168, FAKE, 256, None, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8192, 7168, FAKE, 256, FAKE, FAKE, ws - 1, None) == MOE_ERR_WORKSPACE
+    assert f(FAKE, MOE_BF16, 8192, 7168, FAKE, 256, FAKE, None, ws, None) == MOE_ERR_WORKSPACE
+    assert f(FAKE + 8, MOE_BF16, 8192, 7168, FAKE, 256, FAKE, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8192, 7168, FAKE, 256, FAKE + 4, FAKE, ws, None) == MOE_ERR_INVALID_ARG
+    assert f(None, MOE_BF16, 0, 7168, None, 256, None, None, 0, None) == MOE_OK
+
+
 def test_route_validation(L):
     r = lambda *a: L.moe_route(*a)
     assert r(FAKE, 4, 8, 9, None, 0, 0, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG      # k > E

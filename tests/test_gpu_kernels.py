@@ -11,7 +11,7 @@ import torch
 import combine_grouped_gemm_amd as moe
 import workload as w
 from oracle import moe_oracle as oracle
-from tests.gpu_util import bf16_round, bf16_ulp, f64, say, sync, token_rel_err
+from tests.gpu_util import bf16_round, bf16_ulp, decision_margin, f64, router_bound, say, sync, token_rel_err
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -64,12 +64,117 @@ def test_route_matches_oracle(case):
     assert np.abs(gate.cpu().numpy().astype(np.float64) - rgate).max() <= 1e-6
 
 
+# ------------------------------------------------------------------------------------------
+# router logits
+# ------------------------------------------------------------------------------------------
+
+def _check_router(x, w_r, z, rows=None):
+    """z vs the oracle on every row (or on the given rows), within the summation bound."""
+    xs = f64(x) if rows is None else f64(x[rows])
+    ws = f64(w_r)
+    ref = oracle.router_logits(xs, ws).astype(np.float64)
+    got = f64(z) if rows is None else f64(z[rows])
+    err = np.abs(got - ref)
+    bound = router_bound(xs, ws, x.shape[1])
+    assert got.shape == ref.shape
+    assert np.all(err <= bound), f"router logits off by {err.max():.3e} (bound {bound.min():.3e})"
+    scale = np.abs(ref).max() if ref.size else 1.0
+    say(f"  router logits max abs error {err.max() if err.size else 0:.3e} (max |z| {scale:.3e})")
+    return ref
+
+
+ROUTER_CASES = [
+    # name, N, H, E, dtype
+    ("f32_tiny", 256, 128, 8, torch.float32),           # plain fp32-FMA kernel
+    ("bf16_E_not_mult4", 300, 256, 6, torch.bfloat16),   # plain kernel, bf16 loads, ragged tokens
+    ("bf16_ragged_tiles", 300, 1024, 64, torch.bfloat16),   # MFMA tiles of 160 + 140 rows, 8 parts
+    ("bf16_two_nblocks", 1000, 512, 260, torch.bfloat16),   # 256 + 4 experts, 4 parts
+    ("bf16_one_row", 1, 256, 16, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_CASES, ids=[c[0] for c in ROUTER_CASES])
+def test_router_logits_small(case):
+    name, N, H, E, dt = case
+    say(f"router {name} N={N} H={H} E={E} {dt}")
+    x = w.normal((N, H), w.stream_key(5, w.T_X, N), DEV, dt)
+    w_r = w.normal((E, H), w.stream_key(5, w.T_WR, E), DEV, dt)
+    z = moe.moe_router_logits(x, w_r)
+    sync()
+    _check_router(x, w_r, z)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mixtral_bf16", "dsv3_bf16", "decode_fp8"])
+def test_router_logits_full_config(name):
+    """Every logit of the workloads' full sizes (8 parts of K at the DeepSeek-V3 shape, 14 at
+    the decode batch, 16 for Mixtral's 8 experts); two calls give identical bits."""
+    cfg = w.CONFIGS[name]
+    say(f"router config {name} N={cfg.N} H={cfg.H} E={cfg.E}")
+    x = w.hidden_states(cfg, DEV)
+    w_r = w.router_weight(cfg, DEV)
+    z = moe.moe_router_logits(x, w_r)
+    z2 = moe.moe_router_logits(x, w_r)
+    sync()
+    assert torch.equal(z, z2)
+    _check_router(x, w_r, z)
+
+
+def test_router_logits_many_tiles_sampled():
+    """257 m-tiles (more tiles than CUs: K is not split, sums go straight to z); the oracle
+    checks the first and last tiles' rows and a random sample."""
+    N, H, E = 257 * 256 - 100, 1024, 256
+    say(f"router many tiles N={N} H={H} E={E}")
+    x = w.normal((N, H), w.stream_key(6, w.T_X), DEV, torch.bfloat16)
+    w_r = w.normal((E, H), w.stream_key(6, w.T_WR), DEV, torch.bfloat16)
+    assert moe.moe_workspace_bytes(moe.MOE_OP_ROUTER, N, H, 0, E, 0, moe.MOE_BF16) == 0
+    z = moe.moe_router_logits(x, w_r)
+    sync()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(300), np.arange(N - 400, N), rng.integers(0, N, 500)]))
+    _check_router(x, w_r, z, torch.from_numpy(rows).to(DEV))
+
+
+def test_router_logits_empty_batch_is_noop():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    w_r = torch.zeros((16, 256), dtype=torch.bfloat16, device=DEV)
+    z = torch.full((0, 16), 7.0, device=DEV)
+    assert moe.moe_router_logits(x, w_r, z).shape == (0, 16)
+
+
+@pytest.mark.parametrize("name", ["dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"])
+def test_router_then_route_full_config(name):
+    """Route on the GPU's logits: wherever its experts differ from the oracle's route on the
+    oracle's logits, the oracle's own decision margin there is within twice the logits'
+    measured difference (a near tie); everywhere else the same experts and gates."""
+    cfg = w.CONFIGS[name]
+    say(f"router + route config {name}")
+    x = w.hidden_states(cfg, DEV)
+    w_r = w.router_weight(cfg, DEV)
+    b = w.zipf_bias(cfg)
+    z = moe.moe_router_logits(x, w_r)
+    idx, gate = moe.moe_route(z, cfg.k, None if b is None else b.to(DEV), cfg.n_group, cfg.topk_group)
+    sync()
+    zr = _check_router(x, w_r, z).astype(np.float32)
+    ridx, rgate = oracle.route(zr, cfg.k, None if b is None else b.numpy(), cfg.n_group, cfg.topk_group)
+    dz = np.abs(f64(z) - zr).max(axis=1)
+    diff = np.any(idx.cpu().numpy() != ridx, axis=1)
+    if diff.any():
+        zb = oracle.biased_logits(zr[diff], None if b is None else b.numpy())
+        m = decision_margin(zb, cfg.k, cfg.n_group, cfg.topk_group)
+        slack = 2 * np.spacing(np.abs(zb).max(axis=1).astype(np.float32)).astype(np.float64)
+        assert np.all(m <= 2 * dz[diff] + slack), "a route differs away from a near tie"
+    say(f"  tokens routed differently (near ties): {int(diff.sum())} of {cfg.N}")
+    same = ~diff
+    gerr = np.abs(gate.cpu().numpy().astype(np.float64)[same] - rgate[same])
+    assert np.all(gerr <= 1e-6 + 4 * dz[same, None])
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"])
 def test_route_full_config_logits(name):
     cfg = w.CONFIGS[name]
     say(f"route config {name}")
     x = w.hidden_states(cfg, DEV)
-    z = w.router_logits(x, w.router_weight(cfg))
+    z = torch.from_numpy(oracle.router_logits(f64(x), f64(w.router_weight(cfg))))
     b = w.zipf_bias(cfg)
     idx, gate = moe.moe_route(z.to(DEV), cfg.k, None if b is None else b.to(DEV), cfg.n_group, cfg.topk_group)
     sync()

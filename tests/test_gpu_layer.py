@@ -15,7 +15,7 @@ import combine_grouped_gemm_amd as moe
 import workload as w
 from combine_grouped_gemm_amd.layer import MoELayer
 from oracle import moe_oracle as oracle
-from tests.gpu_util import f64, say, sync, token_rel_err
+from tests.gpu_util import decision_margin, f64, router_bound, say, sync, token_rel_err, with_logits
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -72,7 +72,7 @@ class OracleWeights:
 
 def _build(cfg):
     say(f"layer {cfg.name} N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} {cfg.dtype}")
-    inp = w.make_layer_inputs(cfg, DEV)
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"])
     y = layer.forward(inp["x"], inp["z"])
@@ -147,7 +147,7 @@ def test_layer_small_all_intermediates(name):
 def test_layer_gathered_equals_permuted():
     """The bf16 layer with the permute folded into gate/up == the layer with the permute kernel, bit for bit."""
     cfg = SMALL["dsv3_small"]
-    inp = w.make_layer_inputs(cfg, DEV)
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
     ys = []
     for gather in (True, False):
         layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
@@ -162,7 +162,7 @@ def test_layer_shared_on_side_stream_equals_serial():
     """The shared expert on a second stream (combine waits for it) == all on one stream, bit for
     bit, over several forwards in a row."""
     cfg = SMALL["dsv3_small"]
-    inp = w.make_layer_inputs(cfg, DEV)
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
     ys = []
     for overlap in (True, False):
         layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
@@ -181,7 +181,7 @@ def test_layer_shared_fused_equals_separate():
     bit for bit (same kernel), the down rows and y within the bf16 bar (the separate dense
     down runs the 128-row-tile kernel)."""
     cfg = SMALL["dsv3_small"]
-    inp = w.make_layer_inputs(cfg, DEV)
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
     outs = []
     for fuse in (True, False):
         layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
@@ -203,7 +203,7 @@ def test_layer_gates_in_down_epilogue():
     routed outputs equal the gate times the unscaled ones to bf16 rounding, and y matches
     the oracle's within the bf16 bar."""
     cfg = SMALL["dsv3_small"]
-    inp = w.make_layer_inputs(cfg, DEV)
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
     res = {}
     for gated in (False, True):
         layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
@@ -226,6 +226,39 @@ def test_layer_gates_in_down_epilogue():
     err = token_rel_err(f64(y1), ref["y"])
     say(f"  gates in the down epilogue: y max per-token relative error {err:.3e}")
     assert err <= Y_BAR[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv3_small", "dsv3_zipf_small"])
+def test_layer_with_router_logits(name):
+    """The layer computes its logits z = x W_r^T itself (moe_router_logits) before the route:
+    z within the fp32 summation bound of the oracle's; the experts equal the oracle's route
+    on the oracle's z except at near ties; y on the other tokens within the layer's bar."""
+    cfg = SMALL[name]
+    say(f"layer with router {cfg.name}")
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"], w_r=inp["w_r"])
+    y = layer.forward(inp["x"])
+    sync()
+    zr = inp["z_cpu"].numpy()
+    dz = np.abs(f64(layer.z) - zr)
+    assert np.all(dz <= router_bound(f64(inp["x"]), f64(inp["w_r"]), cfg.H))
+    b = inp["bias_cpu"]
+    ow = OracleWeights(inp["w13"], inp["w2"], False)
+    kw = dict(shared_w13=f64(inp["sw13"][0]), shared_w2=f64(inp["sw2"][0])) if cfg.shared else {}
+    ref = oracle.moe_layer(f64(inp["x"]), zr, cfg.k, ow.g13, ow.g2, bias=None if b is None else b.numpy(),
+                           n_group=cfg.n_group, topk_group=cfg.topk_group, **kw)
+    diff = np.any(layer.topk_idx.cpu().numpy() != ref["topk_idx"], axis=1)
+    if diff.any():
+        zb = oracle.biased_logits(zr[diff], None if b is None else b.numpy())
+        m = decision_margin(zb, cfg.k, cfg.n_group, cfg.topk_group)
+        slack = 2 * np.spacing(np.abs(zb).max(axis=1).astype(np.float32)).astype(np.float64)
+        assert np.all(m <= 2 * dz[diff].max(axis=1) + slack), "a route differs away from a near tie"
+    same = ~diff
+    err = token_rel_err(f64(y)[same], ref["y"][same])
+    say(f"  z max abs error {dz.max():.3e}; {int(diff.sum())} near-tie tokens; y max per-token relative "
+        f"error {err:.3e}")
+    assert err <= Y_BAR[cfg.dtype] and err <= Y_EXPECT[cfg.dtype]
 
 
 FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]

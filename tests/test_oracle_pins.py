@@ -27,6 +27,61 @@ def _rng(seed):
 
 
 # ------------------------------------------------------------------------------------------
+# router logits
+# ------------------------------------------------------------------------------------------
+
+def brute_router_logits(x, w):
+    """Each logit as the correctly rounded sum (math.fsum) of its H products, then fp32."""
+    N, H = x.shape
+    E = w.shape[0]
+    z = np.empty((N, E), np.float32)
+    for t in range(N):
+        for e in range(E):
+            z[t, e] = np.float32(math.fsum(float(x[t, h]) * float(w[e, h]) for h in range(H)))
+    return z
+
+
+def check_router_vs_bruteforce():
+    rng = _rng(11)
+    # dyadic values: every product and every partial sum is exact in float64
+    x = rng.integers(-16, 17, size=(5, 9)) / 16.0
+    w = rng.integers(-16, 17, size=(4, 9)) / 32.0
+    if not np.array_equal(oracle.router_logits(x, w), brute_router_logits(x, w)):
+        return False
+    x = rng.standard_normal((7, 33)) * 0.02
+    w = rng.standard_normal((6, 33)) * 0.02
+    z = oracle.router_logits(x, w)
+    ref = brute_router_logits(x, w)
+    # a float64 sum lands within one fp32 ulp of the correctly rounded one
+    return z.shape == (7, 6) and bool(np.all(np.abs(z.astype(np.float64) - ref) <= np.spacing(np.abs(ref))))
+
+
+def check_router_selects_permuted_columns():
+    """Rows of W_r that are unit vectors: W_r[e] = u_{pi(e)} gives z[:, e] = x[:, pi(e)] exactly."""
+    perm = np.array([2, 0, 3, 5, 1, 4])   # not its own inverse: a transposed W_r would give pi^-1
+    w = np.zeros((6, 6))
+    w[np.arange(6), perm] = 1.0
+    x = _rng(12).standard_normal((4, 6)).astype(np.float32)
+    return bool(np.array_equal(oracle.router_logits(x, w), x[:, perm]))
+
+
+def test_router_logits_match_bruteforce():
+    assert check_router_vs_bruteforce()
+
+
+def test_router_logits_unit_rows_select_columns():
+    assert check_router_selects_permuted_columns()
+
+
+def test_router_logits_ones_give_row_sums():
+    w = _rng(13).standard_normal((5, 40))
+    z = oracle.router_logits(np.ones((2, 40)), w)
+    ref = np.array([math.fsum(r) for r in w])
+    assert z.shape == (2, 5) and z.dtype == np.float32
+    assert np.all(np.abs(z - ref[None, :]) <= np.spacing(np.abs(ref).astype(np.float32))[None, :])
+
+
+# ------------------------------------------------------------------------------------------
 # top-k selection
 # ------------------------------------------------------------------------------------------
 
@@ -523,7 +578,18 @@ def _mut_group_mask_sum_score(zb, n_group, topk_group):
     return np.repeat(ok, G, axis=1)
 
 
+def _mut_router_experts_reversed(x, w_r):
+    return (np.asarray(x, np.float64) @ np.asarray(w_r, np.float64).T)[:, ::-1].astype(np.float32)
+
+
+def _mut_router_drops_last_column(x, w_r):
+    x, w_r = np.asarray(x, np.float64), np.asarray(w_r, np.float64)
+    return (x[:, :-1] @ w_r[:, :-1].T).astype(np.float32)
+
+
 MUTATIONS = [
+    ("router_logits", _mut_router_experts_reversed, check_router_selects_permuted_columns),
+    ("router_logits", _mut_router_drops_last_column, check_router_vs_bruteforce),
     ("topk_select", _mut_topk_ascending_ties,
      lambda: check_topk_vs_bruteforce() and bool(np.array_equal(
          oracle.topk_select(np.array([[1, 3, 3, 2, 3]], np.float32), 2), [[1, 2]]))),

@@ -5,6 +5,7 @@ import numpy as np
 import torch
 
 import workload as w
+from oracle import moe_oracle as oracle
 
 
 def test_numpy_and_torch_hash_agree():
@@ -44,9 +45,11 @@ def test_normal_table_symmetric_with_std_002():
 def test_router_logit_scale_matches_closed_form():
     cfg = w.CONFIGS["tiny_f32"].scaled(N=2048)
     x = w.hidden_states(cfg)
-    z = w.router_logits(x, w.router_weight(cfg))
+    w_r = w.router_weight(cfg)
+    assert w_r.shape == (cfg.E, cfg.H) and w_r.dtype == x.dtype
+    z = oracle.router_logits(x.double().numpy(), w_r.double().numpy())
     sigma = 0.02 * 0.02 * math.sqrt(cfg.H)
-    assert abs(z.std().item() / sigma - 1) < 0.05
+    assert abs(z.std() / sigma - 1) < 0.05
 
 
 def test_zipf_bias_shape_and_order():

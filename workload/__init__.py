@@ -6,10 +6,7 @@ combine or fp8 coding).  It only produces:
 
 * normally distributed values N(0, 0.02^2) (the pages' workloads draw hidden
   states and weights this way), cast to the workload's storage dtype;
-* router logits ``z = x . W_r`` -- the router's linear projection sits in
-  front of the layer's first call, which takes ``z`` as its input
-  ("the router produces logits z in R^{N x E}", EP/DeepEP explanation page,
-  section 2);
+* the router weight W_r [E, H] (one row per expert) in the storage dtype;
 * the synthetic Zipf skew expressed as a per-expert additive logit bias.
 
 Every random value is a pure function of ``(seed, tensor id, sub-stream,
@@ -215,14 +212,8 @@ def hidden_states(cfg: MoEConfig, device="cpu") -> torch.Tensor:
 
 
 def router_weight(cfg: MoEConfig, device="cpu") -> torch.Tensor:
-    """W_r [H, E] fp32."""
-    return normal((cfg.H, cfg.E), stream_key(cfg.seed, T_WR), device, torch.float32)
-
-
-def router_logits(x: torch.Tensor, w_r: torch.Tensor) -> torch.Tensor:
-    """z = x . W_r with x as stored, accumulated in float64 on the host, rounded once to fp32."""
-    z = x.detach().cpu().to(torch.float64) @ w_r.detach().cpu().to(torch.float64)
-    return z.to(torch.float32)
+    """W_r [E, H] in the storage dtype: row e holds expert e's H router weights."""
+    return normal((cfg.E, cfg.H), stream_key(cfg.seed, T_WR), device, storage_dtype(cfg))
 
 
 def zipf_bias(cfg: MoEConfig) -> Optional[torch.Tensor]:
@@ -332,17 +323,15 @@ def random_gates(N: int, k: int, seed: int = 0) -> torch.Tensor:
 
 
 def make_layer_inputs(cfg: MoEConfig, device="cpu", weights: bool = True) -> dict:
-    """All inputs of one layer call: x, z (and W_r), bias, routed and shared expert weights.
+    """All inputs of one layer call: x, W_r, bias, routed and shared expert weights.
 
-    x and the weights are generated on ``device``; z and bias are computed on
-    the host and moved to ``device``.
+    x, W_r and the expert weights are generated on ``device``; the bias is
+    computed on the host and moved to ``device``.
     """
     x = hidden_states(cfg, device)
-    w_r = router_weight(cfg, "cpu")
-    z = router_logits(x, w_r)
+    w_r = router_weight(cfg, device)
     b = zipf_bias(cfg)
-    out = {"x": x, "w_r": w_r, "z": z.to(device), "z_cpu": z,
-           "bias": None if b is None else b.to(device), "bias_cpu": b}
+    out = {"x": x, "w_r": w_r, "bias": None if b is None else b.to(device), "bias_cpu": b}
     if weights:
         out["w13"], out["w2"] = all_expert_weights(cfg, device)
         if cfg.shared:
