@@ -17,6 +17,8 @@ Pages cited:
   [DGG]  "MoE part 4: DeepEP and GroupedGEMM", sections 2, 4, 4.1, 4.2
   [FSDP] "DeepSeek MoE: EP and FSDP guide", the naive MoE forward list
   [DEP]  "DeepEP" (scholia-log), sections 1 and 7
+  The backward functions follow "DeepSeek MoE: EP and FSDP guide" (the backward
+  mirrors the forward; dispatch's backward is combine) and the chain rule.
 """
 from __future__ import annotations
 
@@ -28,6 +30,8 @@ __all__ = [
     "E4M3_MAX", "router_logits", "biased_logits", "group_limit_mask", "topk_select", "renormalized_gates", "route",
     "dispatch_layout", "permute", "e4m3_decode", "e4m3_encode", "quantize_blocks",
     "dequantize_blocks", "silu", "expert_ffn", "grouped_ffn", "combine", "imbalance", "moe_layer",
+    "combine_backward", "dispatch_backward", "swiglu_backward", "expert_ffn_backward", "gates_backward",
+    "router_backward", "moe_layer_backward",
 ]
 
 E4M3_MAX = 448.0  # largest finite OCP e4m3fn value: 1.75 * 2^8
@@ -372,4 +376,144 @@ def moe_layer(x: np.ndarray, z: np.ndarray, k: int, w13: WeightSource, w2: Weigh
         res["shared_out"] = shared
     res["y"] = combine(out, send_pos, gates, k, shared)
     res["imbalance"] = imbalance(n_e)
+    return res
+
+
+# --------------------------------------------------------------------------------------
+# backward: the gradients of the layer (training)
+# --------------------------------------------------------------------------------------
+# "DeepSeek MoE: EP and FSDP guide": the backward of the EP layer mirrors the forward
+# (the same all-to-alls in reverse), the backward of dispatch being combine, and each
+# expert keeps its own weight gradients.  Top-k selection is piecewise constant: the
+# gradients reach the router only through the gates.
+
+def combine_backward(dy: np.ndarray, send_pos: np.ndarray, gates: np.ndarray, expert_out: np.ndarray,
+                     k: int):
+    """Gradients of y_t = sum_j g_{t,j} o_{send_pos[t*k+j]}: (d_expert_out [rows, H], dg [N, k]).
+
+    d o_row = g_{t,j} dy_t for row = send_pos[t*k+j] (dy dispatched to the slots and
+    scaled by the gates); dg_{t,j} = <dy_t, o_row>.  Rows no slot names get 0.
+    """
+    N = gates.shape[0]
+    sp = np.asarray(send_pos).reshape(N, k)
+    dy = np.asarray(dy, dtype=np.float64)
+    g = np.asarray(gates, dtype=np.float64)
+    eo = np.asarray(expert_out, dtype=np.float64)
+    d_eo = np.zeros_like(eo)
+    dg = np.zeros((N, k))
+    for j in range(k):
+        d_eo[sp[:, j]] = g[:, j:j + 1] * dy
+        dg[:, j] = (dy * eo[sp[:, j]]).sum(axis=1)
+    return d_eo, dg
+
+
+def dispatch_backward(d_perm: np.ndarray, send_pos: np.ndarray, N: int, k: int) -> np.ndarray:
+    """Backward of the dispatch (permute): dx_t = sum_j d_perm[send_pos[t*k+j]], i.e. a combine
+    with weight 1 ("DeepSeek MoE: EP and FSDP guide": dispatch's backward is combine)."""
+    return combine(d_perm, send_pos, np.ones((N, k)), k)
+
+
+def swiglu_backward(gate: np.ndarray, up: np.ndarray, dh: np.ndarray):
+    """h = silu(a) * u  =>  da = dh * u * silu'(a), du = dh * silu(a), with
+    silu'(a) = s(a) (1 + a (1 - s(a))), s the logistic function (float64)."""
+    a = np.asarray(gate, dtype=np.float64)
+    u = np.asarray(up, dtype=np.float64)
+    dh = np.asarray(dh, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-a))
+    return dh * u * s * (1.0 + a * (1.0 - s)), dh * a * s
+
+
+def expert_ffn_backward(a: np.ndarray, w13: np.ndarray, w2: np.ndarray, d_out: np.ndarray) -> dict:
+    """Backward of expert_ffn on rows a [n, H] given d_out [n, H] (float64).
+
+    dh = d_out W_d; dW_d = d_out^T h; (da, du) from swiglu_backward; d_a =
+    [da, du] w13 (W_gate and W_up stacked as in w13); dW13 = [da, du]^T a.
+    Returns d_in [n, H], dw13 [2I, H], dw2 [H, I] and the intermediates
+    (gate and up pre-activations, h, dh, d_au = [da, du] [n, 2I]).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    w13 = np.asarray(w13, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    I = w13.shape[0] // 2
+    gate = a @ w13[:I].T
+    up = a @ w13[I:].T
+    h = silu(gate) * up
+    dh = d_out @ w2
+    da, du = swiglu_backward(gate, up, dh)
+    d_au = np.concatenate([da, du], axis=1)
+    return dict(d_in=d_au @ w13, dw13=d_au.T @ a, dw2=d_out.T @ h, gate=gate, up=up, h=h, dh=dh, d_au=d_au)
+
+
+def gates_backward(gates: np.ndarray, dg: np.ndarray) -> np.ndarray:
+    """Backward of the renormalised softmax over the selected logits: for g = softmax(z'_sel),
+    dz'_j = g_j (dg_j - sum_i g_i dg_i) on the k selected experts (0 elsewhere)."""
+    g = np.asarray(gates, dtype=np.float64)
+    dg = np.asarray(dg, dtype=np.float64)
+    return g * (dg - (g * dg).sum(axis=1, keepdims=True))
+
+
+def router_backward(x: np.ndarray, w_r: np.ndarray, topk_idx: np.ndarray, dz_sel: np.ndarray):
+    """Backward of z = x W_r^T when only the selected logits carry gradient dz_sel [N, k]:
+    dx_t = sum_j dz_sel[t, j] W_r[idx[t, j]] and dW_r[e] = sum over (t, j) with idx = e of
+    dz_sel[t, j] x_t.  (The correction bias enters z' additively: dz = dz'.)"""
+    x = np.asarray(x, dtype=np.float64)
+    w_r = np.asarray(w_r, dtype=np.float64)
+    idx = np.asarray(topk_idx).astype(np.int64)
+    dz = np.asarray(dz_sel, dtype=np.float64)
+    dx = np.zeros_like(x)
+    dw = np.zeros_like(w_r)
+    for j in range(idx.shape[1]):
+        dx += dz[:, j:j + 1] * w_r[idx[:, j]]
+        np.add.at(dw, idx[:, j], dz[:, j:j + 1] * x)
+    return dx, dw
+
+
+def moe_layer_backward(x: np.ndarray, z: np.ndarray, k: int, w13: WeightSource, w2: WeightSource,
+                       dy: np.ndarray, bias: Optional[np.ndarray] = None, n_group: int = 0,
+                       topk_group: int = 0, shared_w13: Optional[np.ndarray] = None,
+                       shared_w2: Optional[np.ndarray] = None, w_r: Optional[np.ndarray] = None) -> dict:
+    """Gradients of moe_layer (bf16/fp32 layers) for the upstream gradient dy [N, H].
+
+    Routes and gates are those of moe_layer on z; the gradient flows through the
+    gates (gates_backward) into the selected logits and, given the router weight
+    W_r (z = x W_r^T), into x and W_r.  Returns dx [N, H], dw13 / dw2 (dicts
+    expert -> gradient, for the experts with rows), the shared expert's dw13 / dw2,
+    dw_r, and the intermediates of every step (d_expert_out, dg, dz_sel, dh, d_au,
+    d_perm, the recomputed gate/up pre-activations and h).
+    """
+    fwd = moe_layer(x, z, k, w13, w2, bias=bias, n_group=n_group, topk_group=topk_group,
+                    shared_w13=shared_w13, shared_w2=shared_w2)
+    x64 = np.asarray(x, dtype=np.float64)
+    N, H = x64.shape
+    offsets, send_pos = fwd["offsets"], fwd["send_pos"]
+    rows = int(offsets[-1])
+    d_eo, dg = combine_backward(dy, send_pos, fwd["gates"], fwd["expert_out"], k)
+    x_perm = fwd["x_perm"].astype(np.float64)
+    d_perm = np.zeros((rows, H))
+    res = dict(fwd=fwd, d_expert_out=d_eo, dg=dg, dw13={}, dw2={})
+    parts = {n: [] for n in ("gate", "up", "h", "dh", "d_au")}
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        b = expert_ffn_backward(x_perm[lo:hi], _weight(w13, e), _weight(w2, e), d_eo[lo:hi])
+        d_perm[lo:hi] = b["d_in"]
+        res["dw13"][e], res["dw2"][e] = b["dw13"], b["dw2"]
+        for n in parts:
+            parts[n].append(b[n])
+    for n, v in parts.items():
+        res[n] = np.concatenate(v) if v else np.zeros((0, 0))
+    res["d_perm"] = d_perm
+    dx = dispatch_backward(d_perm, send_pos, N, k)
+    if shared_w13 is not None:
+        b = expert_ffn_backward(x64, shared_w13, shared_w2, dy)
+        dx = dx + b["d_in"]
+        res["shared"] = b
+        res["shared_dw13"], res["shared_dw2"] = b["dw13"], b["dw2"]
+    res["dz_sel"] = gates_backward(fwd["gates"], dg)
+    if w_r is not None:
+        dx_r, res["dw_r"] = router_backward(x64, w_r, fwd["topk_idx"], res["dz_sel"])
+        dx = dx + dx_r
+    res["dx"] = dx
     return res

@@ -82,6 +82,94 @@ def test_router_logits_ones_give_row_sums():
 
 
 # ------------------------------------------------------------------------------------------
+# backward: analytic gradients against central differences of the forward
+# ------------------------------------------------------------------------------------------
+
+def _train_case(seed=21, N=5, H=8, E=4, k=2, I=4):
+    rng = _rng(seed)
+    return dict(x=rng.standard_normal((N, H)) * 0.5, w_r=rng.standard_normal((E, H)) * 0.5,
+                w13=rng.standard_normal((E, 2 * I, H)) * 0.5, w2=rng.standard_normal((E, H, I)) * 0.5,
+                sw13=rng.standard_normal((2 * I, H)) * 0.5, sw2=rng.standard_normal((H, I)) * 0.5,
+                bias=rng.standard_normal(E) * 0.1, c=rng.standard_normal((N, H)), k=k)
+
+
+def _smooth_loss(p, idx):
+    """L = sum(c * y) with the routes fixed to idx and every step in float64: z = x W_r^T + b
+    (no fp32 rounding), gates = scipy's softmax over the selected logits, each slot's expert
+    and the shared expert evaluated token by token from the SwiGLU definition."""
+    x, w13, w2 = p["x"], p["w13"], p["w2"]
+    I = w13.shape[1] // 2
+    zb = x @ p["w_r"].T + p["bias"][None, :]
+    g = softmax(np.take_along_axis(zb, idx, axis=1), axis=1)
+
+    def ffn(xt, a13, a2):
+        ga, up = a13[:I] @ xt, a13[I:] @ xt
+        return a2 @ (ga * expit(ga) * up)
+    y = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        for j in range(idx.shape[1]):
+            y[t] += g[t, j] * ffn(x[t], w13[idx[t, j]], w2[idx[t, j]])
+        y[t] += ffn(x[t], p["sw13"], p["sw2"])
+    return float((p["c"] * y).sum())
+
+
+def _central_diff(p, name, idx, eps=1e-6):
+    base = p[name]
+    out = np.zeros_like(base)
+    for i in np.ndindex(base.shape):
+        old = base[i]
+        base[i] = old + eps
+        lp = _smooth_loss(p, idx)
+        base[i] = old - eps
+        lm = _smooth_loss(p, idx)
+        base[i] = old
+        out[i] = (lp - lm) / (2 * eps)
+    return out
+
+
+def check_backward_fd(seed=21):
+    p = _train_case(seed)
+    E = p["w13"].shape[0]
+    z = oracle.router_logits(p["x"], p["w_r"])
+    b = oracle.moe_layer_backward(p["x"], z, p["k"], p["w13"], p["w2"], p["c"], bias=p["bias"],
+                                  shared_w13=p["sw13"], shared_w2=p["sw2"], w_r=p["w_r"])
+    idx = b["fwd"]["topk_idx"].astype(np.int64)
+    dw13 = np.stack([b["dw13"].get(e, np.zeros_like(p["w13"][0])) for e in range(E)])
+    dw2 = np.stack([b["dw2"].get(e, np.zeros_like(p["w2"][0])) for e in range(E)])
+    got = dict(x=b["dx"], w_r=b["dw_r"], w13=dw13, w2=dw2, sw13=b["shared_dw13"], sw2=b["shared_dw2"])
+    # the oracle's gates come from fp32 logits: ~1e-7 relative next to the smooth float64 ones
+    return all(np.allclose(got[n], _central_diff(p, n, idx), rtol=1e-5, atol=1e-6) for n in got)
+
+
+def test_backward_matches_central_differences():
+    assert check_backward_fd(21)
+    assert check_backward_fd(22)
+
+
+def test_dispatch_backward_is_the_adjoint_of_permute():
+    rng = _rng(23)
+    N, k, H, E = 7, 3, 5, 6
+    idx = workload.fixed_route(N, E, k, "random", seed=23).numpy()
+    _, _, send_pos, _ = oracle.dispatch_layout(idx, E)
+    x = rng.standard_normal((N, H))
+    Y = rng.standard_normal((N * k, H))
+    lhs = float((oracle.permute(x, send_pos, k) * Y).sum())
+    rhs = float((x * oracle.dispatch_backward(Y, send_pos, N, k)).sum())
+    assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + 1)
+
+
+def test_gates_backward_matches_softmax_jacobian():
+    rng = _rng(24)
+    zsel = rng.standard_normal((4, 3))
+    g = softmax(zsel, axis=1)
+    dg = rng.standard_normal((4, 3))
+    jac = np.einsum("ti,ij->tij", g, np.eye(3)) - np.einsum("ti,tj->tij", g, g)   # d g_i / d z_j
+    assert np.allclose(oracle.gates_backward(g, dg), np.einsum("ti,tij->tj", dg, jac), rtol=1e-12, atol=1e-15)
+    # one expert per token: the gate is constant 1, no gradient reaches the logit
+    assert np.array_equal(oracle.gates_backward(np.ones((3, 1)), rng.standard_normal((3, 1))), np.zeros((3, 1)))
+
+
+# ------------------------------------------------------------------------------------------
 # top-k selection
 # ------------------------------------------------------------------------------------------
 
@@ -587,7 +675,35 @@ def _mut_router_drops_last_column(x, w_r):
     return (x[:, :-1] @ w_r[:, :-1].T).astype(np.float32)
 
 
+def _mut_swiglu_backward_no_chain(gate, up, dh):
+    s = 1.0 / (1.0 + np.exp(-gate))
+    return dh * up * s, dh * gate * s
+
+
+def _mut_gates_backward_no_center(gates, dg):
+    return np.asarray(gates, np.float64) * np.asarray(dg, np.float64)
+
+
+def _mut_combine_backward_unscaled(dy, send_pos, gates, expert_out, k):
+    d_eo, dg = _ORIG_COMBINE_BACKWARD(dy, send_pos, np.ones_like(np.asarray(gates, np.float64)), expert_out, k)
+    return d_eo, dg
+
+
+def _mut_expert_backward_halves_swapped(a, w13, w2, d_out):
+    r = _ORIG_EXPERT_BACKWARD(a, w13, w2, d_out)
+    I = r["d_au"].shape[1] // 2
+    r["dw13"] = np.concatenate([r["d_au"][:, I:], r["d_au"][:, :I]], axis=1).T @ np.asarray(a, np.float64)
+    return r
+
+
+_ORIG_COMBINE_BACKWARD = oracle.combine_backward
+_ORIG_EXPERT_BACKWARD = oracle.expert_ffn_backward
+
 MUTATIONS = [
+    ("swiglu_backward", _mut_swiglu_backward_no_chain, check_backward_fd),
+    ("gates_backward", _mut_gates_backward_no_center, check_backward_fd),
+    ("combine_backward", _mut_combine_backward_unscaled, check_backward_fd),
+    ("expert_ffn_backward", _mut_expert_backward_halves_swapped, check_backward_fd),
     ("router_logits", _mut_router_experts_reversed, check_router_selects_permuted_columns),
     ("router_logits", _mut_router_drops_last_column, check_router_vs_bruteforce),
     ("topk_select", _mut_topk_ascending_ties,
