@@ -19,11 +19,12 @@ import torch
 __all__ = [
     "MoEError", "lib", "library_path", "declared_symbols",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
-    "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM", "MOE_OP_ROUTER",
+    "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM", "MOE_OP_ROUTER", "MOE_OP_EXPERT_DGRAD",
     "moe_router_logits", "moe_route", "moe_dispatch_layout", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
     "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
     "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
-    "moe_version",
+    "moe_version", "moe_combine_backward", "moe_expert_gate_up_preact", "moe_swiglu_backward", "moe_expert_dgrad",
+    "moe_expert_wgrad", "moe_router_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,7 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
-MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN, MOE_OP_EXPERT_GEMM, MOE_OP_ROUTER = range(4)
+MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN, MOE_OP_EXPERT_GEMM, MOE_OP_ROUTER, MOE_OP_EXPERT_DGRAD = range(5)
 
 
 class MoEError(RuntimeError):
@@ -63,6 +64,12 @@ _SIGS = {
     "moe_expert_down_shared": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
+    "moe_combine_backward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P],
+    "moe_expert_gate_up_preact": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
+    "moe_swiglu_backward": [_P, _P, _I, _I, _P, _P, _P],
+    "moe_expert_dgrad": [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
+    "moe_expert_wgrad": [_P, _I, _P, _I, _P, _I, _I, _P, _I, _I, _P, _I, _P],
+    "moe_router_backward": [_P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I, _P],
     "moe_status_str": [_I],
     "moe_version": [],
 }
@@ -351,3 +358,108 @@ def moe_combine(expert_out: torch.Tensor, send_pos: torch.Tensor, topk_gate: Opt
         _ptr(expert_out), _dt(expert_out), N, H, k, _ptr(send_pos), _ptr(topk_gate),
         _ptr(shared_out), _ptr(y), _dt(y), _stream(expert_out)))
     return y
+
+
+# ------------------------------------------------------------------------------------------
+# backward pass
+# ------------------------------------------------------------------------------------------
+
+def moe_combine_backward(dy: torch.Tensor, send_pos: torch.Tensor, topk_gate: torch.Tensor,
+                         expert_out: torch.Tensor, d_expert_out: Optional[torch.Tensor] = None,
+                         d_gate: Optional[torch.Tensor] = None):
+    """(d_expert_out [rows, H] in dy's dtype, d_gate [N, k] fp32) of moe_combine's weighted sum."""
+    N, H = dy.shape
+    k = topk_gate.shape[1]
+    if d_expert_out is None:
+        d_expert_out = torch.empty_like(expert_out, dtype=dy.dtype)
+    if d_gate is None:
+        d_gate = torch.empty((N, k), dtype=torch.float32, device=dy.device)
+    if expert_out.dtype != dy.dtype or d_expert_out.dtype != dy.dtype:
+        raise ValueError("dy, expert_out and d_expert_out share one dtype")
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        _ptr(dy), _dt(dy), N, H, k, _ptr(send_pos), _ptr(topk_gate), _ptr(expert_out), _ptr(d_expert_out),
+        _ptr(d_gate), _stream(dy)))
+    return d_expert_out, d_gate
+
+
+def moe_expert_gate_up_preact(x: torch.Tensor, offsets: torch.Tensor, w13: torch.Tensor, rows: Optional[int] = None,
+                              src_slot: Optional[torch.Tensor] = None, k: int = 1, au: Optional[torch.Tensor] = None,
+                              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """au [rows, 2I] bf16 = a W13_e^T per segment; a = x[src_slot[r] // k] (src_slot given) or x's rows."""
+    N, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if rows is None:
+        rows = src_slot.numel() if src_slot is not None else N
+    if au is None:
+        au = torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16), x.device)
+    _check("moe_expert_gate_up_preact", lib().moe_expert_gate_up_preact(
+        _ptr(x), _dt(x), N, _ptr(src_slot), k, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(au), _ptr(ws),
+        ws.numel(), _stream(x)))
+    return au
+
+
+def moe_swiglu_backward(au: torch.Tensor, dh: torch.Tensor, d_au: Optional[torch.Tensor] = None,
+                        h: Optional[torch.Tensor] = None, want_h: bool = True):
+    """(d_au [rows, 2I], h [rows, I] or None) from the pre-activations au and dh (bf16)."""
+    rows, I = dh.shape
+    if d_au is None:
+        d_au = torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=dh.device)
+    if h is None and want_h:
+        h = torch.empty((rows, I), dtype=torch.bfloat16, device=dh.device)
+    _check("moe_swiglu_backward", lib().moe_swiglu_backward(_ptr(au), _ptr(dh), rows, I, _ptr(d_au), _ptr(h),
+                                                            _stream(dh)))
+    return d_au, h
+
+
+def moe_expert_dgrad(dC: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out [rows, N] bf16 = dC[r] W_e per segment, W [E, K, N] as stored."""
+    rows, K = dC.shape
+    E, K2, N = w.shape
+    if K2 != K:
+        raise ValueError("dC's columns must match the weight's K")
+    if out is None:
+        out = torch.empty((rows, N), dtype=torch.bfloat16, device=dC.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_DGRAD, rows, 0, 0, E, 0, 0), dC.device)
+    _check("moe_expert_dgrad", lib().moe_expert_dgrad(_ptr(dC), _ptr(offsets), E, rows, K, N, _ptr(w), _ptr(out),
+                                                      _ptr(ws), ws.numel(), _stream(dC)))
+    return out
+
+
+def moe_expert_wgrad(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, b_rows: Optional[torch.Tensor] = None,
+                     b_div: int = 1, dw: Optional[torch.Tensor] = None, dw_dtype: torch.dtype = torch.float32,
+                     rows: Optional[int] = None) -> torch.Tensor:
+    """dW [E, M, N] = A_e^T B_e over each segment's rows (B's row r = b[b_rows[r] // b_div] if given)."""
+    E = offsets.numel() - 1
+    M = a.shape[1]
+    N = b.shape[1]
+    if rows is None:
+        rows = a.shape[0]
+    if dw is None:
+        dw = torch.empty((E, M, N), dtype=dw_dtype, device=a.device)
+    _check("moe_expert_wgrad", lib().moe_expert_wgrad(
+        _ptr(a), M, _ptr(b), N, _ptr(b_rows), b_div, b.shape[0], _ptr(offsets), E, rows, _ptr(dw), _dt(dw),
+        _stream(a)))
+    return dw
+
+
+def moe_router_backward(topk_gate: torch.Tensor, d_gate: torch.Tensor, offsets: torch.Tensor,
+                        src_slot: torch.Tensor, x: torch.Tensor, dz: Optional[torch.Tensor] = None,
+                        dw_r: Optional[torch.Tensor] = None, dw_dtype: torch.dtype = torch.float32):
+    """(dz [N, k] fp32 on the selected logits, dW_r [E, H])."""
+    N, k = topk_gate.shape
+    E = offsets.numel() - 1
+    H = x.shape[1]
+    rows = src_slot.numel()
+    if dz is None:
+        dz = torch.empty((N, k), dtype=torch.float32, device=x.device)
+    if dw_r is None:
+        dw_r = torch.empty((E, H), dtype=dw_dtype, device=x.device)
+    _check("moe_router_backward", lib().moe_router_backward(
+        _ptr(topk_gate), _ptr(d_gate), N, k, _ptr(offsets), _ptr(src_slot), E, rows, _ptr(x), _dt(x), H, _ptr(dz),
+        _ptr(dw_r), _dt(dw_r), _stream(x)))
+    return dz, dw_r

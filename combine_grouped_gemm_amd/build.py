@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["router.hip", "route.hip", "layout.hip", "permute.hip", "combine.hip", "grouped_gemm.hip", "grouped_gemm_stream.hip",
-           "grouped_gemm_wide.hip",
+           "grouped_gemm_wide.hip", "grouped_gemm_bwd.hip", "backward.hip",
            "moe_api.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

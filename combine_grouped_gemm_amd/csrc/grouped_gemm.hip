@@ -724,6 +724,13 @@ bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long 
          (gathered ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
 }
 
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int rows, int tile_rows, int cap, int32_t* prefix,
+                              int32_t* tile_expert, int32_t* tile_counter, hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap, prefix,
+                     tile_expert, tile_counter, 0);
+  return hipGetLastError();
+}
+
 size_t gemm_schedule_bytes(int rows, int E) {
   const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E) + kNumXcd;
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);

@@ -76,6 +76,9 @@ size_t moe_workspace_bytes(int op, int N, int H, int I, int E, int k, int a_dt) 
     case MOE_OP_GROUPED_FFN:
       if (E < 1 || N == 0 || I <= 0 || H <= 0) return 0;
       return moe::gemm_schedule_bytes(N, E) + h_bytes(N, I, a_dt);
+    case MOE_OP_EXPERT_DGRAD:
+      if (E < 1 || N == 0) return 0;
+      return moe::bwd_dgrad_ws_bytes(N, E);
     case MOE_OP_ROUTER:
       if (E < 1 || N == 0 || H <= 0) return 0;
       return moe::router_ws_bytes(N, H, E, a_dt == MOE_BF16);
@@ -295,6 +298,92 @@ moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, in
     return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_combine(expert_out, eo_dt == MOE_F32, N, H, k, send_pos, topk_gate,
                                         shared_out, y, y_dt == MOE_F32, stream));
+}
+
+// ---- backward pass
+
+moe_status moe_combine_backward(const void* dy, moe_dtype dt, int N, int H, int k, const int32_t* send_pos,
+                                const float* topk_gate, const void* expert_out, void* d_expert_out, float* d_gate,
+                                hipStream_t stream) {
+  if (N < 0 || H <= 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (k > MOE_MAX_TOPK || static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((static_cast<size_t>(H) * dtype_bytes(dt)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (dy == nullptr || send_pos == nullptr || topk_gate == nullptr || expert_out == nullptr ||
+      d_expert_out == nullptr || d_gate == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(expert_out) || !aligned16(d_expert_out)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine_backward(dy, dt == MOE_F32, N, H, k, send_pos, topk_gate, expert_out,
+                                                 d_expert_out, d_gate, stream));
+}
+
+moe_status moe_expert_gate_up_preact(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot, int k,
+                                     const int32_t* offsets, int E, int rows, int H, int I, const void* w13, void* au,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const moe_status st = check_gemm(offsets, E, rows, H, I, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (src_slot != nullptr && (N < 1 || k < 1 || k > MOE_MAX_TOPK)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || w13 == nullptr || au == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(au)) return MOE_ERR_INVALID_ARG;
+  if (src_slot != nullptr && static_cast<long long>(N) * H * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_grouped_gemm(1, false, 1, x, nullptr, w13, nullptr, au, false, offsets, E, rows, H,
+                                             I, 2 * I, 2ll * I, ws, stream, src_slot, src_slot ? k : 1,
+                                             src_slot ? N : 0));
+}
+
+moe_status moe_swiglu_backward(const void* au, const void* dh, int rows, int I, void* d_au, void* h,
+                               hipStream_t stream) {
+  if (rows < 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (au == nullptr || dh == nullptr || d_au == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(au) || !aligned16(dh) || !aligned16(d_au) || (h != nullptr && !aligned16(h)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_swiglu_backward(au, dh, rows, I, d_au, h, stream));
+}
+
+moe_status moe_expert_dgrad(const void* dC, const int32_t* offsets, int E, int rows, int K, int N, const void* w,
+                            void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (E < 1 || rows < 0 || K <= 0 || N <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || K % 32 != 0 || N % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < moe::bwd_dgrad_ws_bytes(rows, E)) return MOE_ERR_WORKSPACE;
+  if (dC == nullptr || w == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dC) || !aligned16(w) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_expert_dgrad(dC, offsets, E, rows, K, N, w, out, ws, stream));
+}
+
+moe_status moe_expert_wgrad(const void* a, int M, const void* b, int N, const int32_t* b_rows, int b_div,
+                            int b_nrows, const int32_t* offsets, int E, int rows, void* dw, moe_dtype dw_dt,
+                            hipStream_t stream) {
+  if (E < 1 || rows < 0 || M <= 0 || N <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (dw_dt != MOE_F32 && dw_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || M % 128 != 0 || N % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (b_rows != nullptr && (b_div < 1 || b_nrows < 1)) return MOE_ERR_INVALID_ARG;
+  if (dw == nullptr || (rows > 0 && (a == nullptr || b == nullptr))) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dw) || (rows > 0 && (!aligned16(a) || !aligned16(b)))) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_expert_wgrad(a, b, b_rows, b_div, b_nrows, offsets, E, rows, M, N, dw,
+                                             dw_dt == MOE_F32, stream));
+}
+
+moe_status moe_router_backward(const float* topk_gate, const float* d_gate, int N, int k, const int32_t* offsets,
+                               const int32_t* src_slot, int E, int rows, const void* x, moe_dtype x_dt, int H,
+                               float* dz, void* dw_r, moe_dtype dw_dt, hipStream_t stream) {
+  if (N < 0 || k < 1 || E < 1 || rows < 0 || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (dw_dt != MOE_F32 && dw_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || static_cast<long long>(N) * k >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if ((static_cast<size_t>(H) * dtype_bytes(x_dt)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr || dw_r == nullptr) return MOE_ERR_INVALID_ARG;
+  if (N > 0 && (topk_gate == nullptr || d_gate == nullptr || dz == nullptr || x == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (src_slot == nullptr || N == 0)) return MOE_ERR_INVALID_ARG;
+  if (x != nullptr && !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router_backward(topk_gate, d_gate, N, k, offsets, src_slot, E, rows, x,
+                                                x_dt == MOE_F32, H, dz, dw_r, dw_dt == MOE_F32, stream));
 }
 
 }  // extern "C"

@@ -32,6 +32,24 @@ hipError_t launch_router_logits(const void* x, bool bf16, int N, int H, const vo
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
                           const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s);
 
+// backward pass (backward.hip, grouped_gemm_bwd.hip)
+hipError_t launch_combine_backward(const void* dy, bool f32, int N, int H, int k, const int32_t* send_pos,
+                                   const float* gate, const void* eo, void* d_eo, float* d_gate, hipStream_t s);
+hipError_t launch_swiglu_backward(const void* au, const void* dh, long long rows, int I, void* d_au, void* h,
+                                  hipStream_t s);
+hipError_t launch_router_backward(const float* gate, const float* d_gate, int N, int k, const int32_t* offsets,
+                                  const int32_t* src_slot, int E, int rows, const void* x, bool x_f32, int H,
+                                  float* dz, void* dw, bool dw_f32, hipStream_t s);
+size_t bwd_dgrad_ws_bytes(int rows, int E);
+hipError_t launch_expert_dgrad(const void* dC, const int32_t* offsets, int E, int rows, int K, int N, const void* w,
+                               void* out, void* ws, hipStream_t s);
+hipError_t launch_expert_wgrad(const void* a, const void* b, const int32_t* b_rows, int b_div, int b_nrows,
+                               const int32_t* offsets, int E, int rows, int M, int N, void* dw, bool dw_f32,
+                               hipStream_t s);
+// the forward's tile schedule (prefix of m-tiles per segment, m-tile -> segment)
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int rows, int tile_rows, int cap, int32_t* prefix,
+                              int32_t* tile_expert, int32_t* tile_counter, hipStream_t s);
+
 size_t gemm_tile_cap(int rows, int E);
 size_t gemm_schedule_bytes(int rows, int E);
 hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,

@@ -22,11 +22,12 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_EXPERT_GEMM,
-               MOE_OP_GROUPED_FFN, MOE_OP_ROUTER, moe_combine, moe_dispatch_layout, moe_expert_down,
-               moe_expert_down_shared, moe_expert_gate_up, moe_expert_gate_up_gathered,
-               moe_expert_gate_up_gathered_shared, moe_grouped_ffn, moe_permute, moe_quantize_fp8,
-               moe_route, moe_router_logits, moe_workspace_bytes)
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_EXPERT_DGRAD, MOE_OP_EXPERT_GEMM,
+               MOE_OP_GROUPED_FFN, MOE_OP_ROUTER, moe_combine, moe_combine_backward, moe_dispatch_layout,
+               moe_expert_dgrad, moe_expert_down, moe_expert_down_shared, moe_expert_gate_up,
+               moe_expert_gate_up_gathered, moe_expert_gate_up_gathered_shared, moe_expert_gate_up_preact,
+               moe_expert_wgrad, moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route, moe_router_backward,
+               moe_router_logits, moe_swiglu_backward, moe_workspace_bytes)
 
 
 class MoELayer:
@@ -217,3 +218,87 @@ class MoELayer:
                 self.shared_expert(x)
         self.combine()
         return self.y
+
+    # ---- backward (bf16 layers that gather their rows from x)
+
+    def _alloc_backward(self, dw_dtype: torch.dtype):
+        N, H, E, k, I = self.N, self.H, self.E, self.k, self.I
+        rows = N * k
+        dev, bf = self.device, torch.bfloat16
+        b = {}
+        b["d_eo"] = torch.empty((rows, H), dtype=bf, device=dev)
+        b["dg"] = torch.empty((N, k), dtype=torch.float32, device=dev)
+        b["au"] = torch.empty((rows, 2 * I), dtype=bf, device=dev)
+        b["dh"] = torch.empty((rows, I), dtype=bf, device=dev)
+        b["d_au"] = torch.empty((rows, 2 * I), dtype=bf, device=dev)
+        b["h"] = torch.empty((rows, I), dtype=bf, device=dev)
+        b["d_perm"] = torch.empty((rows, H), dtype=bf, device=dev)
+        b["dw13"] = torch.empty((E, 2 * I, H), dtype=dw_dtype, device=dev)
+        b["dw2"] = torch.empty((E, H, I), dtype=dw_dtype, device=dev)
+        b["gemm_ws"] = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, max(rows, N), H, I, E, 1, MOE_BF16),
+                                       256), dtype=torch.uint8, device=dev)
+        b["dgrad_ws"] = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_DGRAD, max(rows, N), 0, 0, E, 0, 0), 256),
+                                    dtype=torch.uint8, device=dev)
+        if self.shared:
+            b["shared_offsets"] = torch.tensor([0, N], dtype=torch.int32, device=dev)
+            b["au_s"] = torch.empty((N, 2 * I), dtype=bf, device=dev)
+            b["dh_s"] = torch.empty((N, I), dtype=bf, device=dev)
+            b["d_au_s"] = torch.empty((N, 2 * I), dtype=bf, device=dev)
+            b["h_s"] = torch.empty((N, I), dtype=bf, device=dev)
+            b["dx_s"] = torch.empty((N, H), dtype=bf, device=dev)
+            b["dsw13"] = torch.empty((1, 2 * I, H), dtype=dw_dtype, device=dev)
+            b["dsw2"] = torch.empty((1, H, I), dtype=dw_dtype, device=dev)
+        if self.w_r is not None:
+            b["dz"] = torch.empty((N, k), dtype=torch.float32, device=dev)
+            b["dw_r"] = torch.empty((E, H), dtype=dw_dtype, device=dev)
+            b["dx_r"] = torch.empty((N, H), dtype=bf, device=dev)
+        b["dx"] = torch.empty((N, H), dtype=bf, device=dev)
+        b["dw_dtype"] = dw_dtype
+        self.grads = b
+
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, dw_dtype: torch.dtype = torch.bfloat16) -> dict:
+        """Gradients of the last forward for the upstream gradient dy [N, H] (bf16).
+
+        The backward mirrors the forward ("DeepSeek MoE: EP and FSDP guide": dispatch's
+        backward is combine): combine backward (d_expert_out, d_gate); the gate/up
+        pre-activations recomputed; dh = d_expert_out W_down; SwiGLU backward; the weight
+        gradients dW_down = d_expert_out^T h and dW13 = d_au^T x per expert; the input
+        gradient of every slot d_au W13; the same for the shared expert on dy; the gates'
+        and router's gradients; dx = the slots' gradients summed back to their tokens plus
+        the shared expert's and the router's.  Buffers are allocated on the first call.
+        Returns the dict of gradient tensors ('dx', 'dw13', 'dw2', 'dsw13', 'dsw2', 'dw_r', ...).
+        """
+        if self.dtype != "bf16" or not self.gather:
+            raise ValueError("the backward pass is built for bf16 layers that gather their rows from x")
+        if self.gate_in_down:
+            raise ValueError("backward needs the unscaled expert outputs (gate_in_down=False)")
+        if getattr(self, "grads", None) is None or self.grads["dw_dtype"] != dw_dtype:
+            self._alloc_backward(dw_dtype)
+        b = self.grads
+        k, N = self.k, self.N
+        rows = N * k
+        offsets, send_pos, src_slot = self.layout[1], self.layout[2], self.layout[3]
+        moe_combine_backward(dy, send_pos, self.topk_gate, self.expert_out, b["d_eo"], b["dg"])
+        moe_expert_gate_up_preact(x, offsets, self.w13, rows, src_slot, k, b["au"], b["gemm_ws"])
+        moe_expert_dgrad(b["d_eo"], offsets, self.w2, b["dh"], b["dgrad_ws"])
+        moe_swiglu_backward(b["au"], b["dh"], b["d_au"], b["h"])
+        moe_expert_wgrad(b["d_eo"], b["h"], offsets, dw=b["dw2"], rows=rows)
+        moe_expert_wgrad(b["d_au"], x, offsets, b_rows=src_slot, b_div=k, dw=b["dw13"], rows=rows)
+        moe_expert_dgrad(b["d_au"], offsets, self.w13, b["d_perm"], b["dgrad_ws"])
+        rest = None
+        if self.shared:
+            so = b["shared_offsets"]
+            moe_expert_gate_up_preact(x, so, self.sw13, N, None, 1, b["au_s"], b["gemm_ws"])
+            moe_expert_dgrad(dy, so, self.sw2, b["dh_s"], b["dgrad_ws"])
+            moe_swiglu_backward(b["au_s"], b["dh_s"], b["d_au_s"], b["h_s"])
+            moe_expert_wgrad(dy, b["h_s"], so, dw=b["dsw2"], rows=N)
+            moe_expert_wgrad(b["d_au_s"], x, so, dw=b["dsw13"], rows=N)
+            moe_expert_dgrad(b["d_au_s"], so, self.sw13, b["dx_s"], b["dgrad_ws"])
+            rest = b["dx_s"]
+        if self.w_r is not None:
+            moe_router_backward(self.topk_gate, b["dg"], offsets, src_slot, x, b["dz"], b["dw_r"])
+            # sum_j dz_tj W_r[e_tj] (+ the shared expert's input gradient)
+            moe_combine(self.w_r, self.topk_idx, b["dz"], rest, b["dx_r"])
+            rest = b["dx_r"]
+        moe_combine(b["d_perm"], send_pos, None, rest, b["dx"], k=k)
+        return b

@@ -66,7 +66,8 @@ typedef enum {
   MOE_OP_DISPATCH_LAYOUT = 0,
   MOE_OP_GROUPED_FFN = 1, /* includes the [rows, I] intermediate h                      */
   MOE_OP_EXPERT_GEMM = 2, /* moe_expert_gate_up / moe_expert_down: tile schedule only   */
-  MOE_OP_ROUTER = 3       /* moe_router_logits: fp32 partial sums (N, H, E, a_dt = x_dt) */
+  MOE_OP_ROUTER = 3,      /* moe_router_logits: fp32 partial sums (N, H, E, a_dt = x_dt) */
+  MOE_OP_EXPERT_DGRAD = 4 /* moe_expert_dgrad: tile schedule (N = rows, E)               */
 } moe_op;
 
 /* Limits of this implementation. */
@@ -304,6 +305,96 @@ moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* 
 moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, int k,
                        const int32_t* send_pos, const float* topk_gate, const void* shared_out,
                        void* y, moe_dtype y_dt, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Backward pass (training).  "DeepSeek MoE: EP and FSDP guide": the backward of the layer
+ * mirrors its forward -- the backward of dispatch is combine (and that of combine a
+ * dispatch of dy, scaled by the gates) -- and each expert keeps its own weight gradients.
+ * Top-k selection is piecewise constant, so gradients reach the router through the gates
+ * only.  For the bf16 layer with upstream gradient dy [N, H]:
+ *
+ *   moe_combine_backward        d_expert_out, d_gate
+ *   moe_expert_gate_up_preact   the gate/up pre-activations au = x W13_e^T (recomputed)
+ *   moe_expert_dgrad            dh = d_expert_out W_down,e
+ *   moe_swiglu_backward         d_au = (da, du), and h recomputed from au
+ *   moe_expert_wgrad            dW_down,e = d_expert_out_e^T h_e,  dW13_e = d_au_e^T x_e
+ *   moe_expert_dgrad            d_perm = d_au W13_e
+ *   moe_router_backward         dz on the selected logits, dW_r
+ *   moe_combine (gates = dz, rows of W_r)  and  moe_combine (gates = NULL, rows of d_perm)
+ *                               dx = sum_j dz_tj W_r[e_tj] + sum_j d_perm[send_pos[t,j]]
+ * (the shared expert: the same GEMMs with E = 1 on all N tokens and d_out = dy).
+ * ------------------------------------------------------------------------------------ */
+
+/*
+ * moe_combine_backward -- gradients of moe_combine's weighted sum.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (y_t = sum_j g_tj o_tj) and the
+ * chain rule: d_expert_out[send_pos[t*k+j]] = g_tj dy_t and d_gate[t*k+j] = <dy_t,
+ * expert_out[send_pos[t*k+j]]> (fp32 sum).  Slots with send_pos < 0 get d_gate 0.
+ *   dy, expert_out, d_expert_out: dt (MOE_BF16 or MOE_F32); dy [N, H]; the others [rows, H].
+ * Requires H * sizeof(dt) % 16 == 0.
+ */
+moe_status moe_combine_backward(const void* dy, moe_dtype dt, int N, int H, int k, const int32_t* send_pos,
+                                const float* topk_gate, const void* expert_out, void* d_expert_out, float* d_gate,
+                                hipStream_t stream);
+
+/*
+ * moe_expert_gate_up_preact -- the gate/up GEMM without its activation: au[r] = a_r W13_e^T
+ * ([rows, 2I] bf16: the gate pre-activations in columns 0..I-1, the up ones in I..2I-1),
+ * a_r = x[src_slot[r] / k] (src_slot given) or row r of x (src_slot NULL: x [rows, H]).
+ * Definition: "MoE part 4" page, section 4.1 (FC1 before the activation).  bf16 only; ws as
+ * for moe_expert_gate_up; H % 128 == 0, I % 128 == 0.
+ */
+moe_status moe_expert_gate_up_preact(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot, int k,
+                                     const int32_t* offsets, int E, int rows, int H, int I, const void* w13, void* au,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_swiglu_backward -- for h = silu(a) * u: da = dh u s(a) (1 + a (1 - s(a))) and
+ * du = dh a s(a), s the logistic function (the chain rule on the SwiGLU of "MoE part 4" page,
+ * section 4.1).  au [rows, 2I] and dh [rows, I] bf16 in; d_au [rows, 2I] bf16 out (da in
+ * columns 0..I-1, du in I..2I-1); h [rows, I] bf16 out = silu(a) u, or NULL.  I % 8 == 0.
+ */
+moe_status moe_swiglu_backward(const void* au, const void* dh, int rows, int I, void* d_au, void* h,
+                               hipStream_t stream);
+
+/*
+ * moe_expert_dgrad -- out[r, :] = dC[r, :] W_e for the rows r of segment e (the input
+ * gradient of an expert GEMM; "MoE part 4" page, section 2: one grouped launch over ragged
+ * segments).  dC [rows, K] bf16; W [E, K, N] bf16 (the forward weight as stored: w2 with
+ * K = H, N = I gives dh; w13 with K = 2I, N = H gives the input gradient); out [rows, N]
+ * bf16; fp32 accumulation.  ws >= moe_workspace_bytes(MOE_OP_EXPERT_DGRAD, rows, 0, 0, E,
+ * 0, 0).  Requires K % 32 == 0, N % 128 == 0, E <= MOE_MAX_EXPERTS.
+ */
+moe_status moe_expert_dgrad(const void* dC, const int32_t* offsets, int E, int rows, int K, int N, const void* w,
+                            void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_wgrad -- dW_e = A_e^T B_e, the weight gradient of every expert over its own
+ * rows ("DeepSeek MoE: EP and FSDP guide": each expert keeps its gradients).  A [rows, M]
+ * bf16; B rows [.., N] bf16: row r of the product uses row r of b, or row b_rows[r] / b_div
+ * (clamped into [0, b_nrows)) when b_rows is given (x through the layout's src_slot map);
+ * dW [E, M, N] of dw_dt (MOE_F32 or MOE_BF16), fp32 accumulation in row order; an expert
+ * without rows gets zeros.  Requires M % 128 == 0, N % 128 == 0.
+ */
+moe_status moe_expert_wgrad(const void* a, int M, const void* b, int N, const int32_t* b_rows, int b_div,
+                            int b_nrows, const int32_t* offsets, int E, int rows, void* dw, moe_dtype dw_dt,
+                            hipStream_t stream);
+
+/*
+ * moe_router_backward -- gradients through the renormalised gates into the router.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 and "MoE part 4" page, section 4.2
+ * (gates = softmax over the selected logits): dz[s] = g_s (d_gate_s - sum_j g_tj d_gate_tj)
+ * over token t's k slots (fp32); z = x W_r^T then gives dW_r[e] = sum over the slots s
+ * routed to e of dz[s] x_{s / k}, summed in the layout's row order (offsets, src_slot from
+ * moe_dispatch_layout; rows = offsets[E]).  The input gradient sum_j dz_tj W_r[e_tj] is a
+ * moe_combine over the rows of W_r with send_pos = topk_idx and gates dz.
+ *   x [N, H] of x_dt (MOE_BF16 or MOE_F32); dz [N, k] fp32 out; dw_r [E, H] of dw_dt out.
+ */
+moe_status moe_router_backward(const float* topk_gate, const float* d_gate, int N, int k, const int32_t* offsets,
+                               const int32_t* src_slot, int E, int rows, const void* x, moe_dtype x_dt, int H,
+                               float* dz, void* dw_r, moe_dtype dw_dt, hipStream_t stream);
 
 /*
  * moe_workspace_bytes -- bytes of workspace `op` needs for these sizes (0 if none).

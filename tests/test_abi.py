@@ -184,3 +184,47 @@ def test_shared_segment_validation(L):
     assert dcall(rows=0, n=0, ws=None, ws_bytes=0) == MOE_OK
     assert dcall(slot=FAKE) == MOE_ERR_INVALID_ARG     # gates need both the slot map and the gates
     assert dcall(gate=FAKE) == MOE_ERR_INVALID_ARG
+
+
+def test_backward_validation_and_workspace(L):
+    ws = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_DGRAD, 65536, 0, 0, 256, 0, 0)
+    # prefix [E+1] + one entry per 128-row tile (rows / 128 + E) + 8 counters, int32, 256-byte rounded
+    assert ws == ((257 + 512 + 256 + 8) * 4 + 255) // 256 * 256
+    f = L.moe_combine_backward
+    assert f(FAKE, MOE_BF16, 4, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_FP8_E4M3, 4, 256, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 4, 100, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 4, 256, 2, FAKE, None, FAKE, FAKE, FAKE, None) == MOE_ERR_INVALID_ARG
+    assert f(None, MOE_BF16, 0, 256, 2, None, None, None, None, None, None) == MOE_OK
+    f = L.moe_expert_gate_up_preact
+    gws = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, 1024, 256, 128, 8, 1, MOE_BF16)
+    assert f(FAKE, MOE_F32, 64, FAKE, 2, FAKE, 8, 128, 256, 128, FAKE, FAKE, FAKE, gws, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 64, FAKE, 2, FAKE, 8, 128, 200, 128, FAKE, FAKE, FAKE, gws, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 64, FAKE, 2, FAKE, 8, 128, 256, 128, FAKE, FAKE, FAKE, 0, None) == MOE_ERR_WORKSPACE
+    assert f(FAKE, MOE_BF16, 64, FAKE, 0, FAKE, 8, 128, 256, 128, FAKE, FAKE, FAKE, gws, None) == MOE_ERR_INVALID_ARG
+    assert f(None, MOE_BF16, 0, None, 1, FAKE, 8, 0, 256, 128, None, None, None, 0, None) == MOE_OK
+    f = L.moe_swiglu_backward
+    assert f(FAKE, FAKE, 4, 12, FAKE, None, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, None, 4, 16, FAKE, None, None) == MOE_ERR_INVALID_ARG
+    assert f(None, None, 0, 16, None, None, None) == MOE_OK
+    f = L.moe_expert_dgrad
+    dws = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_DGRAD, 1024, 0, 0, 8, 0, 0)
+    assert f(FAKE, FAKE, 8, 1024, 100, 256, FAKE, FAKE, FAKE, dws, None) == MOE_ERR_UNSUPPORTED   # K % 32
+    assert f(FAKE, FAKE, 8, 1024, 128, 200, FAKE, FAKE, FAKE, dws, None) == MOE_ERR_UNSUPPORTED   # N % 128
+    assert f(FAKE, FAKE, 8, 1024, 128, 256, FAKE, FAKE, FAKE, dws - 1, None) == MOE_ERR_WORKSPACE
+    assert f(FAKE, FAKE, 0, 1024, 128, 256, FAKE, FAKE, FAKE, dws, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 8, 1024, 128, 256, None, FAKE, FAKE, dws, None) == MOE_ERR_INVALID_ARG
+    assert f(None, FAKE, 8, 0, 128, 256, None, None, None, 0, None) == MOE_OK
+    f = L.moe_expert_wgrad
+    assert f(FAKE, 200, FAKE, 256, None, 1, 0, FAKE, 8, 64, FAKE, MOE_F32, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 256, FAKE, 256, None, 1, 0, FAKE, 8, 64, FAKE, MOE_FP8_E4M3, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 256, FAKE, 256, FAKE, 0, 64, FAKE, 8, 64, FAKE, MOE_F32, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, 256, FAKE, 256, None, 1, 0, FAKE, 8, 64, None, MOE_F32, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, 256, FAKE, 256, None, 1, 0, None, 8, 64, FAKE, MOE_F32, None) == MOE_ERR_INVALID_ARG
+    f = L.moe_router_backward
+    assert f(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 8, FAKE, MOE_FP8_E4M3, 256, FAKE, FAKE, MOE_F32, None) == \
+        MOE_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 4, 2, FAKE, None, 8, 8, FAKE, MOE_BF16, 256, FAKE, FAKE, MOE_F32, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 8, FAKE, MOE_BF16, 100, FAKE, FAKE, MOE_F32, None) == \
+        MOE_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 4, 2, None, FAKE, 8, 8, FAKE, MOE_BF16, 256, FAKE, FAKE, MOE_F32, None) == MOE_ERR_INVALID_ARG

@@ -1,0 +1,295 @@
+"""GPU parity of the backward pass against the oracle's gradients (chain rule in float64).
+
+Each entry point on ragged, seeded inputs with empty and one-row experts; the whole
+layer's gradients on scaled-down workloads element by element; at the DeepSeek-V3 size the
+weight gradients of sampled experts and the input gradient of sampled tokens, each computed
+by the oracle one expert or one token at a time.  Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_grouped_gemm_amd as moe
+import workload as w
+from combine_grouped_gemm_amd.layer import MoELayer
+from oracle import moe_oracle as oracle
+from tests.gpu_util import bf16_ulp, f64, say, sync, token_rel_err, with_logits
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+U32 = 2.0 ** -24
+# per-row relative bar of the layer's gradients: bf16 intermediates (d_expert_out, the
+# recomputed pre-activations, dh, d_au, the slots' input gradients, dx) each round by at
+# most 2^-9 of their row's scale; fp32 sums
+GRAD_BAR = 2e-2
+
+
+def mat_rel_err(got, ref):
+    """max |got - ref| / max |ref| over a whole weight gradient.  Per-row relative errors do
+    not suit weight gradients: for an expert with one row, row j of dW13 is d_au[r, j] x_r,
+    and a single element of d_au carries the cancellation error of dh = d_out W_down (its
+    bf16 inputs round by 2^-9 of terms that can be far larger than their sum)."""
+    den = np.abs(ref).max()
+    return float(np.abs(np.asarray(got, np.float64) - ref).max() / den) if den > 0 else float(np.abs(got).max())
+
+
+def _n(shape, sub, dt=torch.bfloat16, std=0.02):
+    return w.normal(shape, w.stream_key(11, w.T_EO, sub), DEV, dt, std=std)
+
+
+def _layout(N, E, k, seed, empty=()):
+    idx = w.fixed_route(N, E, k, "random", seed=seed).numpy()
+    for e in empty:   # move the slots of these experts to the next expert the token lacks
+        for t in range(N):
+            for j in range(k):
+                if idx[t, j] == e:
+                    free = [c for c in range(E) if c not in idx[t] and c not in empty]
+                    idx[t, j] = free[0]
+    n_e, off, sp, ss = oracle.dispatch_layout(idx, E)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.int32)).to(DEV)
+    return idx, n_e, off, sp, ss, dev(off), dev(sp), dev(ss)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _loaded():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    moe.lib()
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_combine_backward(dt):
+    N, H, E, k = 300, 512, 16, 4
+    say(f"combine backward {dt}")
+    idx, n_e, off, sp, ss, doff, dsp, dss = _layout(N, E, k, 3)
+    dy = _n((N, H), 1, dt)
+    eo = _n((N * k, H), 2, dt)
+    g = w.random_gates(N, k, seed=4)
+    d_eo, dg = moe.moe_combine_backward(dy, dsp, g.to(DEV), eo)
+    sync()
+    r_eo, r_dg = oracle.combine_backward(f64(dy), sp, g.numpy(), f64(eo), k)
+    err = np.abs(f64(d_eo) - r_eo)
+    # one fp32 product, one rounding to dt
+    ulp = bf16_ulp(r_eo) if dt == torch.bfloat16 else np.abs(r_eo) * 2.0 ** -23
+    assert np.all(err <= ulp + 1e-30)
+    bound = 2 * (H + 1) * U32 * (np.abs(f64(dy))[:, None, :] * np.abs(f64(eo))[sp.reshape(N, k)]).sum(axis=2)
+    assert np.all(np.abs(f64(dg) - r_dg) <= bound)
+
+
+def test_swiglu_backward():
+    rows, I = 777, 256
+    say("swiglu backward")
+    au = _n((rows, 2 * I), 5, std=1.5)
+    dh = _n((rows, I), 6, std=0.05)
+    d_au, h = moe.moe_swiglu_backward(au, dh)
+    sync()
+    a, u = f64(au)[:, :I], f64(au)[:, I:]
+    da, du = oracle.swiglu_backward(a, u, f64(dh))
+    ref = np.concatenate([da, du], axis=1)
+    scale = np.abs(f64(dh)).max(axis=1, keepdims=True) * (np.abs(a).max() + 1) * (np.abs(u).max() + 1)
+    assert np.all(np.abs(f64(d_au) - ref) <= bf16_ulp(ref) + 1e-5 * scale)
+    rh = oracle.silu(a) * u
+    assert np.all(np.abs(f64(h) - rh) <= bf16_ulp(rh) + 1e-5 * (np.abs(rh).max() + 1e-30))
+
+
+@pytest.mark.parametrize("gathered", [True, False])
+def test_gate_up_preact(gathered):
+    N, H, E, k, I = 200, 512, 8, 3, 256
+    say(f"gate/up pre-activations gathered={gathered}")
+    idx, n_e, off, sp, ss, doff, dsp, dss = _layout(N, E, k, 7, empty=(2,))
+    x = _n((N, H), 8)
+    w13 = _n((E, 2 * I, H), 9)
+    xp = oracle.permute(f64(x), sp, k)
+    if gathered:
+        au = moe.moe_expert_gate_up_preact(x, doff, w13, N * k, dss, k)
+    else:
+        au = moe.moe_expert_gate_up_preact(torch.from_numpy(xp).to(torch.bfloat16).to(DEV), doff, w13)
+    sync()
+    ref = np.zeros((N * k, 2 * I))
+    for e in range(E):
+        ref[off[e]:off[e + 1]] = xp[off[e]:off[e + 1]] @ f64(w13[e]).T
+    assert token_rel_err(f64(au), ref) <= 1e-2
+
+
+DGRAD_CASES = [
+    # name, N, k, E, K, Nout, empty experts
+    ("ragged", 400, 3, 8, 256, 384, (1,)),
+    ("one_expert", 300, 1, 1, 96, 128, ()),
+    ("many_small", 150, 2, 64, 128, 256, (0, 5)),
+]
+
+
+@pytest.mark.parametrize("case", DGRAD_CASES, ids=[c[0] for c in DGRAD_CASES])
+def test_expert_dgrad(case):
+    name, N, k, E, K, Nout, empty = case
+    say(f"dgrad {name}")
+    idx, n_e, off, sp, ss, doff, dsp, dss = _layout(N, E, k, 10, empty)
+    rows = N * k
+    dC = _n((rows, K), 11)
+    W = _n((E, K, Nout), 12)
+    out = moe.moe_expert_dgrad(dC, doff, W)
+    sync()
+    ref = np.zeros((rows, Nout))
+    for e in range(E):
+        ref[off[e]:off[e + 1]] = f64(dC[off[e]:off[e + 1]]) @ f64(W[e])
+    assert token_rel_err(f64(out), ref) <= 1e-2
+
+
+WGRAD_CASES = [
+    # name, N, k, E, M, Nout, gathered, out dtype, empty experts
+    ("ragged_f32", 400, 3, 8, 256, 384, False, torch.float32, (1,)),
+    ("gathered_bf16", 300, 4, 16, 128, 256, True, torch.bfloat16, (3, 9)),
+    ("one_expert_long", 700, 1, 1, 128, 128, False, torch.float32, ()),
+]
+
+
+@pytest.mark.parametrize("case", WGRAD_CASES, ids=[c[0] for c in WGRAD_CASES])
+def test_expert_wgrad(case):
+    name, N, k, E, M, Nout, gathered, odt, empty = case
+    say(f"wgrad {name}")
+    idx, n_e, off, sp, ss, doff, dsp, dss = _layout(N, E, k, 13, empty)
+    rows = N * k
+    A = _n((rows, M), 14)
+    if gathered:
+        B = _n((N, Nout), 15)
+        dw = moe.moe_expert_wgrad(A, B, doff, b_rows=dss, b_div=k, dw_dtype=odt)
+        Brows = f64(B)[ss // k]
+    else:
+        B = _n((rows, Nout), 15)
+        dw = moe.moe_expert_wgrad(A, B, doff, dw_dtype=odt)
+        Brows = f64(B)
+    sync()
+    got = f64(dw)
+    Af = f64(A)
+    for e in range(E):
+        a, b = Af[off[e]:off[e + 1]], Brows[off[e]:off[e + 1]]
+        ref = a.T @ b
+        bound = 2 * (len(a) + 1) * U32 * (np.abs(a).T @ np.abs(b))
+        if odt == torch.bfloat16:
+            bound = bound + bf16_ulp(ref)
+        assert np.all(np.abs(got[e] - ref) <= bound + 1e-30), f"expert {e} (n_e {n_e[e]})"
+    assert not got[list(empty)].any() if empty else True
+
+
+def test_router_backward():
+    N, H, E, k = 500, 256, 32, 6
+    say("router backward")
+    idx, n_e, off, sp, ss, doff, dsp, dss = _layout(N, E, k, 16, empty=(4,))
+    zsel = w.normal((N, k), w.stream_key(16, w.T_GATE), "cpu", torch.float32, std=1.0).numpy().astype(np.float64)
+    g = np.exp(zsel - zsel.max(axis=1, keepdims=True))
+    g = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+    dg = w.normal((N, k), w.stream_key(17, w.T_GATE), "cpu", torch.float32, std=1.0).numpy()
+    x = _n((N, H), 18)
+    dz, dw_r = moe.moe_router_backward(torch.from_numpy(g).to(DEV), torch.from_numpy(dg).to(DEV), doff, dss, x)
+    sync()
+    rdz = oracle.gates_backward(g, dg)
+    g64, d64 = g.astype(np.float64), dg.astype(np.float64)
+    zb = 4 * (k + 2) * U32 * g64 * (np.abs(d64) + (np.abs(g64 * d64)).sum(axis=1, keepdims=True))
+    assert np.all(np.abs(f64(dz) - rdz) <= zb)
+    _, rdw = oracle.router_backward(f64(x), np.zeros((E, H)), idx, rdz)
+    xs = np.abs(f64(x))
+    rz, zbf = np.abs(rdz).reshape(-1), zb.reshape(-1)
+    for e in range(E):
+        slots = ss[off[e]:off[e + 1]]
+        # the fp32 sum over the expert's slots, plus what the dz differences above can carry
+        bound = ((2 * (len(slots) + 1) * U32 * (rz[slots] + zbf[slots]) + zbf[slots])[:, None] *
+                 xs[slots // k]).sum(axis=0)
+        assert np.all(np.abs(f64(dw_r[e]) - rdw[e]) <= bound + 1e-30)
+    assert not f64(dw_r[4]).any()
+
+
+SMALL = {
+    "dsv3_small": w.CONFIGS["dsv3_bf16"].scaled(N=512, H=1024, E=64, I=256),
+    "dsv3_zipf_small": w.CONFIGS["dsv3_zipf_bf16"].scaled(N=512, H=1024, E=64, I=256),
+    "mixtral_small": w.CONFIGS["mixtral_bf16"].scaled(N=512, H=1024, I=1024),
+}
+
+
+def _layer_for_backward(cfg):
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"], inp.get("sw13"),
+                     inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"], w_r=inp["w_r"])
+    layer.forward(inp["x"], inp["z"])
+    dy = w.normal((cfg.N, cfg.H), w.stream_key(cfg.seed, w.T_EO, 5), DEV, torch.bfloat16, std=1.0)
+    return inp, layer, dy
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_backward_small(name):
+    cfg = SMALL[name]
+    say(f"layer backward {name} N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}")
+    inp, layer, dy = _layer_for_backward(cfg)
+    gr = layer.backward(inp["x"], dy, dw_dtype=torch.float32)
+    sync()
+    b = inp["bias_cpu"]
+    kw = dict(shared_w13=f64(inp["sw13"][0]), shared_w2=f64(inp["sw2"][0])) if cfg.shared else {}
+    ref = oracle.moe_layer_backward(f64(inp["x"]), inp["z_cpu"].numpy(), cfg.k, lambda e: f64(inp["w13"][e]),
+                                    lambda e: f64(inp["w2"][e]), f64(dy), bias=None if b is None else b.numpy(),
+                                    n_group=cfg.n_group, topk_group=cfg.topk_group, w_r=f64(inp["w_r"]), **kw)
+    assert np.array_equal(layer.topk_idx.cpu().numpy(), ref["fwd"]["topk_idx"])
+    errs = {}
+    errs["d_expert_out"] = token_rel_err(f64(gr["d_eo"]), ref["d_expert_out"])
+    errs["d_gate"] = float(np.abs(f64(gr["dg"]) - ref["dg"]).max() / np.abs(ref["dg"]).max())
+    errs["dh"] = token_rel_err(f64(gr["dh"]), ref["dh"])
+    errs["d_au"] = token_rel_err(f64(gr["d_au"]), ref["d_au"])
+    errs["dx"] = token_rel_err(f64(gr["dx"]), ref["dx"])
+    errs["dw13"] = max(mat_rel_err(f64(gr["dw13"][e]), v) for e, v in ref["dw13"].items())
+    errs["dw2"] = max(mat_rel_err(f64(gr["dw2"][e]), v) for e, v in ref["dw2"].items())
+    untouched = [e for e in range(cfg.E) if e not in ref["dw13"]]
+    assert not f64(gr["dw13"][untouched]).any() and not f64(gr["dw2"][untouched]).any()
+    if cfg.shared:
+        errs["dsw13"] = mat_rel_err(f64(gr["dsw13"][0]), ref["shared_dw13"])
+        errs["dsw2"] = mat_rel_err(f64(gr["dsw2"][0]), ref["shared_dw2"])
+    errs["dz"] = float(np.abs(f64(gr["dz"]) - ref["dz_sel"]).max() / np.abs(ref["dz_sel"]).max())
+    errs["dw_r"] = mat_rel_err(f64(gr["dw_r"]), ref["dw_r"])
+    say("  " + ", ".join(f"{n} {v:.2e}" for n, v in errs.items()))
+    for n, v in errs.items():
+        assert v <= GRAD_BAR, n
+
+
+def test_layer_backward_full_size_sampled():
+    """DeepSeek-V3 size: the weight gradients of three experts (largest, smallest non-empty,
+    middle) and the input gradient of four tokens, each from the oracle on that expert's rows
+    or that token alone."""
+    cfg = w.CONFIGS["dsv3_bf16"]
+    say("layer backward dsv3_bf16 full size")
+    inp, layer, dy = _layer_for_backward(cfg)
+    gr = layer.backward(inp["x"], dy)
+    sync()
+    k = cfg.k
+    n_e = layer.layout[0].cpu().numpy()
+    off = layer.layout[1].cpu().numpy()
+    ss = layer.layout[3].cpu().numpy()
+    idx = layer.topk_idx.cpu().numpy()
+    gates = layer.topk_gate.cpu().numpy().astype(np.float64)
+    xs = f64(inp["x"])
+    dys = f64(dy)
+    nz = np.nonzero(n_e)[0]
+    experts = sorted({int(nz[np.argmax(n_e[nz])]), int(nz[np.argmin(n_e[nz])]), int(nz[len(nz) // 2])})
+    for e in experts:
+        slots = ss[off[e]:off[e + 1]]
+        toks = slots // k
+        d_out = gates.reshape(-1)[slots, None] * dys[toks]
+        r = oracle.expert_ffn_backward(xs[toks], f64(inp["w13"][e]), f64(inp["w2"][e]), d_out)
+        e13 = mat_rel_err(f64(gr["dw13"][e]), r["dw13"])
+        e2 = mat_rel_err(f64(gr["dw2"][e]), r["dw2"])
+        say(f"  expert {e} (n_e {n_e[e]}): dw13 {e13:.2e}, dw2 {e2:.2e}")
+        assert e13 <= GRAD_BAR and e2 <= GRAD_BAR
+    # dx of sampled tokens: the slots' input gradients, the shared expert's, the router's
+    w_r = f64(inp["w_r"])
+    sw13, sw2 = f64(inp["sw13"][0]), f64(inp["sw2"][0])
+    for t in np.linspace(0, cfg.N - 1, 4).astype(np.int64):
+        dx = np.zeros(cfg.H)
+        dg = np.zeros(k)
+        for j in range(k):
+            e = int(idx[t, j])
+            _, o = oracle.expert_ffn(xs[t:t + 1], f64(inp["w13"][e]), f64(inp["w2"][e]))
+            dg[j] = float(dys[t] @ o[0])
+            r = oracle.expert_ffn_backward(xs[t:t + 1], f64(inp["w13"][e]), f64(inp["w2"][e]),
+                                           gates[t, j] * dys[t:t + 1])
+            dx += r["d_in"][0]
+        dx += oracle.expert_ffn_backward(xs[t:t + 1], sw13, sw2, dys[t:t + 1])["d_in"][0]
+        dz = oracle.gates_backward(gates[t:t + 1], dg[None])[0]
+        dx += dz @ w_r[idx[t]]
+        err = float(np.abs(f64(gr["dx"][t]) - dx).max() / np.abs(dx).max())
+        say(f"  token {t}: dx relative error {err:.2e}")
+        assert err <= GRAD_BAR
