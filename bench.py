@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--overlap", action="store_true",
                    help="run the shared expert on a second stream beside the routed path (it then "
                         "holds the CUs while route/layout wait, so per-stage times mix)")
+    p.add_argument("--train", action="store_true",
+                   help="time a training step instead: the forward, then the backward pass for a fixed "
+                        "upstream gradient (bf16 layers; weight gradients in bf16)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -104,6 +107,36 @@ def algorithmic(cfg, n_e, gather=False, fused=False):
         d["shared"] = {"bytes": 3 * I * H * wb + N * H * act + N * I * 2 + N * H * act,
                        "flops": 6.0 * N * H * I}
     d["combine"] = {"bytes": (rows + (N if cfg.shared else 0)) * H * act + N * H * act + rows * 8}
+    return d
+
+
+def algorithmic_backward(cfg, n_e):
+    """Algorithmic bytes and flops of each backward step (bf16 operands and gradients)."""
+    import numpy as np
+    N, H, E, k, I = cfg.N, cfg.H, cfg.E, cfg.k, cfg.I
+    rows = N * k
+    touched = int((np.asarray(n_e) > 0).sum())
+
+    def ffn(rows, touched, E, d_out_rows):
+        return {
+            "gate_up_preact": {"bytes": touched * 2 * I * H * 2 + N * H * 2 + rows * 2 * I * 2,
+                               "flops": 4.0 * rows * H * I},
+            "down_dgrad": {"bytes": touched * H * I * 2 + d_out_rows * H * 2 + rows * I * 2,
+                           "flops": 2.0 * rows * H * I},
+            "swiglu_bwd": {"bytes": 2 * (rows * 2 * I * 2 + rows * I * 2)},
+            "down_wgrad": {"bytes": d_out_rows * H * 2 + rows * I * 2 + E * H * I * 2, "flops": 2.0 * rows * H * I},
+            "gate_up_wgrad": {"bytes": rows * 2 * I * 2 + N * H * 2 + E * 2 * I * H * 2,
+                              "flops": 4.0 * rows * H * I},
+            "gate_up_dgrad": {"bytes": touched * 2 * I * H * 2 + rows * 2 * I * 2 + rows * H * 2,
+                              "flops": 4.0 * rows * H * I},
+        }
+    d = {"combine_bwd": {"bytes": N * H * 2 + 2 * rows * H * 2 + rows * 8}}
+    d.update(ffn(rows, touched, E, rows))
+    if cfg.shared:
+        d.update({"shared_" + n: v for n, v in ffn(N, 1, 1, N).items()})
+    d["router_bwd"] = {"bytes": rows * H * 2 + E * H * 2 + rows * 12}
+    d["router_dx"] = {"bytes": E * H * 2 + N * H * 2 * (2 if cfg.shared else 1) + rows * 8}
+    d["dx"] = {"bytes": rows * H * 2 + N * H * 2 * 2 + rows * 4}
     return d
 
 
@@ -189,6 +222,12 @@ def main():
         stages.append(("shared", lambda: layer.shared_expert(x)))
     stages.append(("combine", layer.combine))
     side = layer.side
+    if args.train:
+        if side is not None:
+            raise SystemExit("--train runs the layer on one stream (no --overlap)")
+        dy = workload.normal((cfg.N, cfg.H), workload.stream_key(cfg.seed, workload.T_EO, 5), dev, torch.bfloat16,
+                             std=1.0)
+        stages += layer.backward_steps(x, dy)
 
     def step(ev=None):
         """One forward; ev: per-stage (start, end) event pairs to record, or None."""
@@ -238,7 +277,7 @@ def main():
     wall = time.perf_counter() - t0
     per = {n: [ev[s][n][0].elapsed_time(ev[s][n][1]) for s in range(args.steps)] for n in names}
     first = "shared" if side is not None else stages[0][0]
-    step_ms = [ev[s][first][0].elapsed_time(ev[s]["combine"][1]) for s in range(args.steps)]
+    step_ms = [ev[s][first][0].elapsed_time(ev[s][stages[-1][0]][1]) for s in range(args.steps)]
     ms_per_step = wall * 1e3 / args.steps
     value = cfg.N / (ms_per_step / 1e3)
 
@@ -274,6 +313,8 @@ def main():
     n_e = layer.layout[0].cpu().numpy()
     alg = algorithmic(cfg, n_e, layer.gather, layer.fuse)
     alg["permute (standalone)"] = alg["permute"]
+    if args.train:
+        alg.update(algorithmic_backward(cfg, n_e))
     kernels = {}
     for name, times in per.items():
         t = sorted(times)
@@ -315,7 +356,7 @@ def main():
     roof["algorithmic_flops"] = g["flops"]
 
     cpu = None
-    if args.cpu_tokens > 0:
+    if args.cpu_tokens > 0 and not args.train:
         log(args, f"CPU oracle baseline on {args.cpu_tokens} tokens")
         cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
 
@@ -348,6 +389,29 @@ def main():
         "device_copy_GBps": copy_GBps,
         "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
     }
+    if args.train:
+        fwd_names = [n for n, _ in stages[:len(stages) - len(layer.backward_steps(x, dy))]]
+        bwd_names = [n for n, _ in stages if n not in fwd_names]
+        slow = max((n for n in bwd_names if n in alg), key=lambda n: kernels[n]["avg_ms"])
+        a = alg[slow]
+        t = kernels[slow]["avg_ms"] * 1e-3
+        if "flops" in a and a["flops"] / PEAK_MFMA[cfg.dtype] > a["bytes"] / PEAK_HBM:
+            broof = {"bound": "mfma", "achieved": round(a["flops"] / t / 1e12, 1),
+                     "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
+        else:
+            broof = {"bound": "hbm", "achieved": round(a["bytes"] / t / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s"}
+        broof["frac"] = round(broof["achieved"] / broof["peak"], 4)
+        broof["traffic"] = None
+        broof["kernel"] = f"backward step '{slow}' (the slowest of the backward pass)"
+        out.update({
+            "metric": "MoE-layer training step tokens/s (router logits, forward and backward; bf16 weight "
+                      "gradients)",
+            "forward_ms": round(sum(kernels[n]["avg_ms"] for n in fwd_names), 4),
+            "backward_ms": round(sum(kernels[n]["avg_ms"] for n in bwd_names), 4),
+            "backward_roofline": broof,
+            "cpu_baseline": None,
+        })
     print(json.dumps(out), flush=True)
 
 

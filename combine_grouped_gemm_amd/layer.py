@@ -256,6 +256,57 @@ class MoELayer:
         b["dw_dtype"] = dw_dtype
         self.grads = b
 
+    def backward_steps(self, x: torch.Tensor, dy: torch.Tensor, dw_dtype: torch.dtype = torch.bfloat16) -> list:
+        """The backward pass as (name, call) steps in stream order (see backward)."""
+        if self.dtype != "bf16" or not self.gather:
+            raise ValueError("the backward pass is built for bf16 layers that gather their rows from x")
+        if self.gate_in_down:
+            raise ValueError("backward needs the unscaled expert outputs (gate_in_down=False)")
+        if getattr(self, "grads", None) is None or self.grads["dw_dtype"] != dw_dtype:
+            self._alloc_backward(dw_dtype)
+        b = self.grads
+        k, N = self.k, self.N
+        rows = N * k
+        offsets, send_pos, src_slot = self.layout[1], self.layout[2], self.layout[3]
+        st = [
+            ("combine_bwd", lambda: moe_combine_backward(dy, send_pos, self.topk_gate, self.expert_out, b["d_eo"],
+                                                         b["dg"])),
+            ("gate_up_preact", lambda: moe_expert_gate_up_preact(x, offsets, self.w13, rows, src_slot, k, b["au"],
+                                                                 b["gemm_ws"])),
+            ("down_dgrad", lambda: moe_expert_dgrad(b["d_eo"], offsets, self.w2, b["dh"], b["dgrad_ws"])),
+            ("swiglu_bwd", lambda: moe_swiglu_backward(b["au"], b["dh"], b["d_au"], b["h"])),
+            ("down_wgrad", lambda: moe_expert_wgrad(b["d_eo"], b["h"], offsets, dw=b["dw2"], rows=rows)),
+            ("gate_up_wgrad", lambda: moe_expert_wgrad(b["d_au"], x, offsets, b_rows=src_slot, b_div=k, dw=b["dw13"],
+                                                       rows=rows)),
+            ("gate_up_dgrad", lambda: moe_expert_dgrad(b["d_au"], offsets, self.w13, b["d_perm"], b["dgrad_ws"])),
+        ]
+        rest = None
+        if self.shared:
+            so = b["shared_offsets"]
+            st += [
+                ("shared_preact", lambda: moe_expert_gate_up_preact(x, so, self.sw13, N, None, 1, b["au_s"],
+                                                                    b["gemm_ws"])),
+                ("shared_down_dgrad", lambda: moe_expert_dgrad(dy, so, self.sw2, b["dh_s"], b["dgrad_ws"])),
+                ("shared_swiglu_bwd", lambda: moe_swiglu_backward(b["au_s"], b["dh_s"], b["d_au_s"], b["h_s"])),
+                ("shared_down_wgrad", lambda: moe_expert_wgrad(dy, b["h_s"], so, dw=b["dsw2"], rows=N)),
+                ("shared_gate_up_wgrad", lambda: moe_expert_wgrad(b["d_au_s"], x, so, dw=b["dsw13"], rows=N)),
+                ("shared_gate_up_dgrad", lambda: moe_expert_dgrad(b["d_au_s"], so, self.sw13, b["dx_s"],
+                                                                  b["dgrad_ws"])),
+            ]
+            rest = b["dx_s"]
+        if self.w_r is not None:
+            # sum_j dz_tj W_r[e_tj] (+ the shared expert's input gradient)
+            rest_r = rest
+            st += [
+                ("router_bwd", lambda: moe_router_backward(self.topk_gate, b["dg"], offsets, src_slot, x, b["dz"],
+                                                           b["dw_r"])),
+                ("router_dx", lambda: moe_combine(self.w_r, self.topk_idx, b["dz"], rest_r, b["dx_r"])),
+            ]
+            rest = b["dx_r"]
+        rest_x = rest
+        st.append(("dx", lambda: moe_combine(b["d_perm"], send_pos, None, rest_x, b["dx"], k=k)))
+        return st
+
     def backward(self, x: torch.Tensor, dy: torch.Tensor, dw_dtype: torch.dtype = torch.bfloat16) -> dict:
         """Gradients of the last forward for the upstream gradient dy [N, H] (bf16).
 
@@ -268,37 +319,6 @@ class MoELayer:
         the shared expert's and the router's.  Buffers are allocated on the first call.
         Returns the dict of gradient tensors ('dx', 'dw13', 'dw2', 'dsw13', 'dsw2', 'dw_r', ...).
         """
-        if self.dtype != "bf16" or not self.gather:
-            raise ValueError("the backward pass is built for bf16 layers that gather their rows from x")
-        if self.gate_in_down:
-            raise ValueError("backward needs the unscaled expert outputs (gate_in_down=False)")
-        if getattr(self, "grads", None) is None or self.grads["dw_dtype"] != dw_dtype:
-            self._alloc_backward(dw_dtype)
-        b = self.grads
-        k, N = self.k, self.N
-        rows = N * k
-        offsets, send_pos, src_slot = self.layout[1], self.layout[2], self.layout[3]
-        moe_combine_backward(dy, send_pos, self.topk_gate, self.expert_out, b["d_eo"], b["dg"])
-        moe_expert_gate_up_preact(x, offsets, self.w13, rows, src_slot, k, b["au"], b["gemm_ws"])
-        moe_expert_dgrad(b["d_eo"], offsets, self.w2, b["dh"], b["dgrad_ws"])
-        moe_swiglu_backward(b["au"], b["dh"], b["d_au"], b["h"])
-        moe_expert_wgrad(b["d_eo"], b["h"], offsets, dw=b["dw2"], rows=rows)
-        moe_expert_wgrad(b["d_au"], x, offsets, b_rows=src_slot, b_div=k, dw=b["dw13"], rows=rows)
-        moe_expert_dgrad(b["d_au"], offsets, self.w13, b["d_perm"], b["dgrad_ws"])
-        rest = None
-        if self.shared:
-            so = b["shared_offsets"]
-            moe_expert_gate_up_preact(x, so, self.sw13, N, None, 1, b["au_s"], b["gemm_ws"])
-            moe_expert_dgrad(dy, so, self.sw2, b["dh_s"], b["dgrad_ws"])
-            moe_swiglu_backward(b["au_s"], b["dh_s"], b["d_au_s"], b["h_s"])
-            moe_expert_wgrad(dy, b["h_s"], so, dw=b["dsw2"], rows=N)
-            moe_expert_wgrad(b["d_au_s"], x, so, dw=b["dsw13"], rows=N)
-            moe_expert_dgrad(b["d_au_s"], so, self.sw13, b["dx_s"], b["dgrad_ws"])
-            rest = b["dx_s"]
-        if self.w_r is not None:
-            moe_router_backward(self.topk_gate, b["dg"], offsets, src_slot, x, b["dz"], b["dw_r"])
-            # sum_j dz_tj W_r[e_tj] (+ the shared expert's input gradient)
-            moe_combine(self.w_r, self.topk_idx, b["dz"], rest, b["dx_r"])
-            rest = b["dx_r"]
-        moe_combine(b["d_perm"], send_pos, None, rest, b["dx"], k=k)
-        return b
+        for _, f in self.backward_steps(x, dy, dw_dtype):
+            f()
+        return self.grads
