@@ -125,12 +125,13 @@ def algorithmic_backward(cfg, n_e):
                            "flops": 2.0 * rows * H * I},
             "swiglu_bwd": {"bytes": 2 * (rows * 2 * I * 2 + rows * I * 2)},
             "down_wgrad": {"bytes": d_out_rows * H * 2 + rows * I * 2 + E * H * I * 2, "flops": 2.0 * rows * H * I},
-            "gate_up_wgrad": {"bytes": rows * 2 * I * 2 + N * H * 2 + E * 2 * I * H * 2,
+            "gate_up_wgrad": {"bytes": rows * 2 * I * 2 + d_out_rows * H * 2 + E * 2 * I * H * 2,
                               "flops": 4.0 * rows * H * I},
             "gate_up_dgrad": {"bytes": touched * 2 * I * H * 2 + rows * 2 * I * 2 + rows * H * 2,
                               "flops": 4.0 * rows * H * I},
         }
-    d = {"combine_bwd": {"bytes": N * H * 2 + 2 * rows * H * 2 + rows * 8}}
+    d = {"combine_bwd": {"bytes": N * H * 2 + 2 * rows * H * 2 + rows * 8},
+         "x_permute": {"bytes": N * H * 2 + rows * H * 2}}
     d.update(ffn(rows, touched, E, rows))
     if cfg.shared:
         d.update({"shared_" + n: v for n, v in ffn(N, 1, 1, N).items()})

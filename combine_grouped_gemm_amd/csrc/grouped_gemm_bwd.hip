@@ -223,6 +223,234 @@ __global__ __launch_bounds__(kBwdThreads, 2) void grouped_gemm_bwd_kernel(BwdArg
     }
 }
 
+// ------------------------------------------------------------------------------------
+// The main kernel: 128 x 256 tiles, K in stages of 64 through a three-slot ring of
+// direct-to-LDS loads, and the k-strided operands read out of LDS transposed.
+//
+// An operand whose k index is contiguous in memory (dgrad's dC) lies in LDS as 128 rows of
+// 64 k (128 bytes; 16-byte chunk c of row r in slot c ^ key(r), key(r) = (r & 7) ^ ((r >> 3)
+// & 1)) and is read with one 16-byte LDS read per MFMA fragment.  An operand whose m or n
+// index is contiguous (dgrad's W_e, both wgrad operands) lies in LDS as it lies in memory: 64
+// rows of k, each holding the tile's 128 or 256 columns (chunk c of k-row r in slot
+// c ^ 4 (r & 3)).  Its MFMA fragment (one column, 8 consecutive k per lane) takes two
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives the (i % 4)-th 16-bit
+// element of the 8 bytes that lane 4j + i / 4 of the group addresses, for j = 0..3.  So
+// when source lane s addresses k-row k0 + s / 4 at column c0 + 4 (s % 4), lane i holds
+// column c0 + i at k-rows k0 .. k0 + 3.
+//
+// Each of the 4 waves computes 64 tile rows x 128 columns (2 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, the n-operand first, so a lane's accumulators hold one tile row
+// and runs of 4 adjacent columns).  While stage ks is multiplied, stage ks+2 is loaded into
+// the slot stage ks-1 used; at the end of stage ks each wave waits for its loads of stage
+// ks+1 and the workgroup synchronises.  wgrad rows past an expert's segment read a zero page
+// for the A operand (their B rows are clamped into the segment), so they add nothing.
+// ------------------------------------------------------------------------------------
+namespace wide {
+
+constexpr int kTM = 128, kTN = 256, kKS = 64;
+constexpr int kABytes = kTM * kKS * 2;               // 16 KB
+constexpr int kBBytes = kTN * kKS * 2;               // 32 KB
+constexpr int kStage = kABytes + kBBytes;            // 48 KB
+constexpr int kSlots = 3;
+constexpr int kAOps = kABytes / 1024 / 4;            // 1 KB loads per wave and stage (4)
+constexpr int kBOps = kBBytes / 1024 / 4;            // (8)
+constexpr int kOps = kAOps + kBOps;
+
+__device__ __attribute__((aligned(16))) uint8_t g_zero_page[kTM * 2];
+
+__device__ __forceinline__ int kc_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int mc_key(int k) { return 4 * (k & 3); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// MFMA fragment of a k-strided operand: column `col` of the tile, k-rows 16 s + 8 (l / 32)
+// + 0..7, from a slot whose k-rows are `pitch` bytes long
+__device__ __forceinline__ uint4 tr_frag(uint32_t base, int pitch, int s, int col0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  uint2 h[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 16 * s + 8 * (g >> 1) + 4 * r + (i >> 2);
+    const int byte = (col0 + 16 * (g & 1) + 4 * (i & 3)) * 2;
+    const uint32_t a = base + row * pitch + ((((byte >> 4) ^ mc_key(row)) << 4) | (byte & 15));
+    h[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         reinterpret_cast<lds_v4i16*>(static_cast<uintptr_t>(a))));
+  }
+  return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_bwd_wide_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kStage];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- the tile (as the 128 x 128 kernel, with 256-column n-blocks)
+  const int nN = p.N / kTN;
+  long long total;
+  if (MODE == BWD_DGRAD) total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
+  else total = static_cast<long long>(p.E) * (p.M / kTM) * nN;
+  const int xcd = blockIdx.x % kNumXcd;
+  const long long slot = blockIdx.x / kNumXcd;
+  const long long per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const long long L = xcd * per_xcd + slot;
+  if (slot >= per_xcd || L >= total) return;
+  int e, m0, mcount, n0, klo, kcount;
+  if (MODE == BWD_DGRAD) {
+    int lo_e = 0, hi_e = p.E - 1;
+    while (lo_e < hi_e) {
+      const int mid = (lo_e + hi_e + 1) >> 1;
+      if (static_cast<long long>(p.tile_prefix[mid]) * nN <= L) lo_e = mid;
+      else hi_e = mid - 1;
+    }
+    e = lo_e;
+    const int mt_e = p.tile_prefix[e + 1] - p.tile_prefix[e];
+    const long long local = L - static_cast<long long>(p.tile_prefix[e]) * nN;
+    int lo, hi;
+    seg_of(p, e, lo, hi);
+    m0 = lo + static_cast<int>(local % mt_e) * kTM;
+    mcount = hi - m0 < kTM ? hi - m0 : kTM;
+    n0 = static_cast<int>(local / mt_e) * kTN;
+    klo = 0;
+    kcount = p.K;
+  } else {
+    const int mB = p.M / kTM;
+    e = static_cast<int>(L / (static_cast<long long>(mB) * nN));
+    const int local = static_cast<int>(L - static_cast<long long>(e) * mB * nN);
+    m0 = (local / nN) * kTM;
+    n0 = (local % nN) * kTN;
+    mcount = kTM;
+    int lo, hi;
+    seg_of(p, e, lo, hi);
+    klo = lo;
+    kcount = hi - lo;
+  }
+  const int nk = (kcount + kKS - 1) / kKS;
+
+  // ---- loads of stage ks into ring slot sl: op j < kAOps fills A's 1 KB group wave + 4 j,
+  // op kAOps + j fills B's group wave + 4 j
+  auto issue = [&](int ks, int sl, int j) __attribute__((always_inline)) {
+    const int k0 = ks * kKS;
+    const uint8_t* src;
+    uint32_t dst;
+    if (j < kAOps) {
+      const int g = wave + 4 * j;
+      dst = lds0 + sl * kStage + g * 1024;
+      if (MODE == BWD_DGRAD) {   // 8 rows of 128 bytes
+        int r = 8 * g + (lane >> 3);
+        const int c = (lane & 7) ^ kc_key(r);
+        r = r < mcount ? r : mcount - 1;
+        src = reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(m0 + r) * p.K + k0) * 2 + c * 16;
+      } else {                   // 4 k-rows of 256 bytes (128 m)
+        const int kr = 4 * g + (lane >> 4);
+        const int c = (lane & 15) ^ mc_key(kr);
+        src = k0 + kr < kcount
+                  ? reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(klo + k0 + kr) * p.M + m0) * 2 + c * 16
+                  : g_zero_page + c * 16;
+      }
+    } else {                     // 2 k-rows of 512 bytes (256 n)
+      const int g = wave + 4 * (j - kAOps);
+      dst = lds0 + sl * kStage + kABytes + g * 1024;
+      const int kr = 2 * g + (lane >> 5);
+      const int c = (lane & 31) ^ mc_key(kr);
+      size_t row;
+      if (MODE == BWD_DGRAD) {
+        row = static_cast<size_t>(e) * p.K + k0 + kr;
+      } else {
+        const int kk = k0 + kr < kcount ? k0 + kr : kcount - 1;
+        row = static_cast<size_t>(klo + kk);
+      }
+      src = reinterpret_cast<const uint8_t*>(p.b) + (row * p.N + n0) * 2 + c * 16;
+    }
+    dma16(src, __builtin_amdgcn_readfirstlane(dst));
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  if (nk > 0) {
+#pragma unroll
+    for (int j = 0; j < kOps; ++j) issue(0, 0, j);
+    if (nk > 1) {
+#pragma unroll
+      for (int j = 0; j < kOps; ++j) issue(1, 1, j);
+      wait_vmcnt<kOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    for (int ks = 0; ks < nk; ++ks) {
+      const int sl = ks % kSlots;
+      const uint32_t abase = lds0 + sl * kStage, bbase = abase + kABytes;
+      if (ks + 2 < nk) {
+        const int sl2 = (ks + 2) % kSlots;
+#pragma unroll
+        for (int j = 0; j < kOps; ++j) issue(ks + 2, sl2, j);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 fa[2], fb[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (MODE == BWD_DGRAD) {
+            const int row = wm * 64 + i * 32 + (lane & 31);
+            const int c = (2 * s + (lane >> 5)) ^ kc_key(row);
+            fa[i] = *reinterpret_cast<const uint4*>(lds + (abase - lds0) + row * 128 + c * 16);
+          } else {
+            fa[i] = tr_frag(abase, kTM * 2, s, wm * 64 + i * 32, lane);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = tr_frag(bbase, kTN * 2, s, wn * 128 + j * 32, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mma_bf16(fb[j], fa[i], acc[i][j]);
+      }
+      if (ks + 1 < nk) {
+        wait_lgkmcnt_all();
+        if (ks + 2 < nk) wait_vmcnt<kOps>();
+        else wait_vmcnt<0>();
+        block_barrier();
+      }
+    }
+  }
+
+  // ---- epilogue: lane l holds tile row wm*64 + i*32 + l % 32 and, in registers 4q .. 4q+3
+  // of block j, columns wn*128 + j*32 + 8q + 4 (l / 32) + 0..3
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wm * 64 + i * 32 + (lane & 31);
+    if (MODE == BWD_DGRAD && r >= mcount) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        const f32x16_t& a = acc[i][j];
+        if (MODE == BWD_DGRAD) {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(m0 + r) * p.N + col) =
+              make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+        } else {
+          const size_t o = (static_cast<size_t>(e) * p.M + m0 + r) * p.N + col;
+          if (p.out_f32)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          else
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) =
+                make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+        }
+      }
+  }
+}
+
+}  // namespace wide
+
 unsigned grid_for(long long tiles) {
   const long long per_xcd = (tiles + kNumXcd - 1) / kNumXcd;
   return static_cast<unsigned>(per_xcd * kNumXcd);
@@ -255,8 +483,12 @@ hipError_t launch_expert_dgrad(const void* dC, const int32_t* offsets, int E, in
   p.N = N;
   p.K = K;
   p.b_div = 1;
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_DGRAD>, dim3(grid_for(static_cast<long long>(cap) * (N / kBT))),
-                     dim3(kBwdThreads), 0, s, p);
+  if (N % wide::kTN == 0 && K % wide::kKS == 0)
+    hipLaunchKernelGGL(wide::grouped_gemm_bwd_wide_kernel<BWD_DGRAD>,
+                       dim3(grid_for(static_cast<long long>(cap) * (N / wide::kTN))), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_DGRAD>, dim3(grid_for(static_cast<long long>(cap) * (N / kBT))),
+                       dim3(kBwdThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -276,8 +508,13 @@ hipError_t launch_expert_wgrad(const void* a, const void* b, const int32_t* b_ro
   p.M = M;
   p.N = N;
   p.out_f32 = dw_f32 ? 1 : 0;
-  const long long tiles = static_cast<long long>(E) * (M / kBT) * (N / kBT);
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_WGRAD>, dim3(grid_for(tiles)), dim3(kBwdThreads), 0, s, p);
+  if (b_rows == nullptr && N % wide::kTN == 0) {
+    const long long tiles = static_cast<long long>(E) * (M / wide::kTM) * (N / wide::kTN);
+    hipLaunchKernelGGL(wide::grouped_gemm_bwd_wide_kernel<BWD_WGRAD>, dim3(grid_for(tiles)), dim3(256), 0, s, p);
+  } else {
+    const long long tiles = static_cast<long long>(E) * (M / kBT) * (N / kBT);
+    hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_WGRAD>, dim3(grid_for(tiles)), dim3(kBwdThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -233,6 +233,7 @@ class MoELayer:
         b["d_au"] = torch.empty((rows, 2 * I), dtype=bf, device=dev)
         b["h"] = torch.empty((rows, I), dtype=bf, device=dev)
         b["d_perm"] = torch.empty((rows, H), dtype=bf, device=dev)
+        b["x_perm"] = torch.empty((rows, H), dtype=bf, device=dev)
         b["dw13"] = torch.empty((E, 2 * I, H), dtype=dw_dtype, device=dev)
         b["dw2"] = torch.empty((E, H, I), dtype=dw_dtype, device=dev)
         b["gemm_ws"] = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, max(rows, N), H, I, E, 1, MOE_BF16),
@@ -276,8 +277,10 @@ class MoELayer:
             ("down_dgrad", lambda: moe_expert_dgrad(b["d_eo"], offsets, self.w2, b["dh"], b["dgrad_ws"])),
             ("swiglu_bwd", lambda: moe_swiglu_backward(b["au"], b["dh"], b["d_au"], b["h"])),
             ("down_wgrad", lambda: moe_expert_wgrad(b["d_eo"], b["h"], offsets, dw=b["dw2"], rows=rows)),
-            ("gate_up_wgrad", lambda: moe_expert_wgrad(b["d_au"], x, offsets, b_rows=src_slot, b_div=k, dw=b["dw13"],
-                                                       rows=rows)),
+            # the weight gradient of W13 reads the expert-ordered rows of x (a permuted copy:
+            # the wgrad kernel streams its B operand in layout order)
+            ("x_permute", lambda: moe_permute(x, send_pos, k, None, b["x_perm"])),
+            ("gate_up_wgrad", lambda: moe_expert_wgrad(b["d_au"], b["x_perm"], offsets, dw=b["dw13"], rows=rows)),
             ("gate_up_dgrad", lambda: moe_expert_dgrad(b["d_au"], offsets, self.w13, b["d_perm"], b["dgrad_ws"])),
         ]
         rest = None

@@ -111,7 +111,10 @@ def test_gate_up_preact(gathered):
 
 
 DGRAD_CASES = [
-    # name, N, k, E, K, Nout, empty experts
+    # name, N, k, E, K, Nout, empty experts (Nout % 256 == 0 and K % 64 == 0: the 128 x 256
+    # tile kernel; otherwise the 128 x 128 one)
+    ("wide_ragged", 400, 3, 8, 256, 512, (1,)),
+    ("wide_one_expert", 300, 1, 1, 192, 256, ()),
     ("ragged", 400, 3, 8, 256, 384, (1,)),
     ("one_expert", 300, 1, 1, 96, 128, ()),
     ("many_small", 150, 2, 64, 128, 256, (0, 5)),
@@ -135,7 +138,11 @@ def test_expert_dgrad(case):
 
 
 WGRAD_CASES = [
-    # name, N, k, E, M, Nout, gathered, out dtype, empty experts
+    # name, N, k, E, M, Nout, gathered, out dtype, empty experts (ungathered with Nout % 256
+    # == 0: the 128 x 256 tile kernel; otherwise the 128 x 128 one)
+    ("wide_ragged_f32", 400, 3, 8, 256, 512, False, torch.float32, (1,)),
+    ("wide_bf16_long", 700, 1, 2, 128, 256, False, torch.bfloat16, ()),
+    ("wide_many_small", 150, 2, 64, 384, 256, False, torch.float32, (0, 5)),
     ("ragged_f32", 400, 3, 8, 256, 384, False, torch.float32, (1,)),
     ("gathered_bf16", 300, 4, 16, 128, 256, True, torch.bfloat16, (3, 9)),
     ("one_expert_long", 700, 1, 1, 128, 128, False, torch.float32, ()),
