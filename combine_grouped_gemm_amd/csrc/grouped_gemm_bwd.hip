@@ -224,14 +224,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void grouped_gemm_bwd_kernel(BwdArg
 }
 
 // ------------------------------------------------------------------------------------
-// The main kernel: 128 x 256 tiles, K in stages of 64 through a three-slot ring of
+// The main kernel: 128 x 256 tiles, K in stages of 32 through a three-slot ring of
 // direct-to-LDS loads, and the k-strided operands read out of LDS transposed.
 //
 // An operand whose k index is contiguous in memory (dgrad's dC) lies in LDS as 128 rows of
-// 64 k (128 bytes; 16-byte chunk c of row r in slot c ^ key(r), key(r) = (r & 7) ^ ((r >> 3)
-// & 1)) and is read with one 16-byte LDS read per MFMA fragment.  An operand whose m or n
-// index is contiguous (dgrad's W_e, both wgrad operands) lies in LDS as it lies in memory: 64
-// rows of k, each holding the tile's 128 or 256 columns (chunk c of k-row r in slot
+// 32 k (64 bytes; 16-byte chunk c of row r in slot c ^ ((r >> 2) & 3)) and is read with one
+// 16-byte LDS read per MFMA fragment.  An operand whose m or n index is contiguous (dgrad's
+// W_e, both wgrad operands) lies in LDS as it lies in memory: 32 rows of k, each holding the
+// tile's 128 or 256 columns (chunk c of k-row r in slot
 // c ^ 4 (r & 3)).  Its MFMA fragment (one column, 8 consecutive k per lane) takes two
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives the (i % 4)-th 16-bit
 // element of the 8 bytes that lane 4j + i / 4 of the group addresses, for j = 0..3.  So
@@ -247,18 +247,30 @@ __global__ __launch_bounds__(kBwdThreads, 2) void grouped_gemm_bwd_kernel(BwdArg
 // ------------------------------------------------------------------------------------
 namespace wide {
 
-constexpr int kTM = 128, kTN = 256, kKS = 64;
-constexpr int kABytes = kTM * kKS * 2;               // 16 KB
-constexpr int kBBytes = kTN * kKS * 2;               // 32 KB
-constexpr int kStage = kABytes + kBBytes;            // 48 KB
+constexpr int kTM = 128, kTN = 256;
 constexpr int kSlots = 3;
-constexpr int kAOps = kABytes / 1024 / 4;            // 1 KB loads per wave and stage (4)
-constexpr int kBOps = kBBytes / 1024 / 4;            // (8)
-constexpr int kOps = kAOps + kBOps;
+constexpr int kKSMin = 32;   // the smallest k per stage (a stage of 64 needs K % 64 == 0)
+
+// sizes of a stage of KS k (KS = 64: 48 KB, one workgroup per CU; KS = 32: 24 KB, two)
+template <int KS>
+struct Cfg {
+  static constexpr int kABytes = kTM * KS * 2;
+  static constexpr int kBBytes = kTN * KS * 2;
+  static constexpr int kStage = kABytes + kBBytes;
+  static constexpr int kAOps = kABytes / 1024 / 4;   // 1 KB loads per wave and stage
+  static constexpr int kBOps = kBBytes / 1024 / 4;
+  static constexpr int kOps = kAOps + kBOps;
+  static constexpr int kChunks = KS / 8;              // 16-byte chunks of a k-contiguous row
+  static constexpr int kOcc = KS == 32 ? 2 : 1;       // workgroups per CU
+  // slot of chunk c of k-contiguous row r: c ^ key(r) (a fragment read of 32 rows and an
+  // 8- or 16-row load both spread over the 64 banks)
+  __device__ static __forceinline__ int kc_key(int r) {
+    return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
+  }
+};
 
 __device__ __attribute__((aligned(16))) uint8_t g_zero_page[kTM * 2];
 
-__device__ __forceinline__ int kc_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int mc_key(int k) { return 4 * (k & 3); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -280,8 +292,11 @@ __device__ __forceinline__ uint4 tr_frag(uint32_t base, int pitch, int s, int co
   return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_bwd_wide_kernel(BwdArgs p) {
+template <int MODE, int KS>
+__global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kernel(BwdArgs p) {
+  using C = Cfg<KS>;
+  constexpr int kKS = KS, kABytes = C::kABytes, kStage = C::kStage, kAOps = C::kAOps, kBOps = C::kBOps;
+  constexpr int kOps = C::kOps, kChunks = C::kChunks;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kStage];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -338,9 +353,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bwd_wide_kernel(BwdArgs p
     if (j < kAOps) {
       const int g = wave + 4 * j;
       dst = lds0 + sl * kStage + g * 1024;
-      if (MODE == BWD_DGRAD) {   // 8 rows of 128 bytes
-        int r = 8 * g + (lane >> 3);
-        const int c = (lane & 7) ^ kc_key(r);
+      if (MODE == BWD_DGRAD) {   // 1024 / (2 KS) rows of 2 KS bytes
+        int r = (1024 / (2 * kKS)) * g + lane / kChunks;
+        const int c = (lane % kChunks) ^ C::kc_key(r);
         r = r < mcount ? r : mcount - 1;
         src = reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(m0 + r) * p.K + k0) * 2 + c * 16;
       } else {                   // 4 k-rows of 256 bytes (128 m)
@@ -393,14 +408,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bwd_wide_kernel(BwdArgs p
         for (int j = 0; j < kOps; ++j) issue(ks + 2, sl2, j);
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < kKS / 16; ++s) {
         uint4 fa[2], fb[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           if (MODE == BWD_DGRAD) {
             const int row = wm * 64 + i * 32 + (lane & 31);
-            const int c = (2 * s + (lane >> 5)) ^ kc_key(row);
-            fa[i] = *reinterpret_cast<const uint4*>(lds + (abase - lds0) + row * 128 + c * 16);
+            const int c = (2 * s + (lane >> 5)) ^ C::kc_key(row);
+            fa[i] = *reinterpret_cast<const uint4*>(lds + (abase - lds0) + row * (2 * kKS) + c * 16);
           } else {
             fa[i] = tr_frag(abase, kTM * 2, s, wm * 64 + i * 32, lane);
           }
@@ -451,6 +466,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bwd_wide_kernel(BwdArgs p
 
 }  // namespace wide
 
+// k per stage of the 128 x 256 kernels: 32, so that two workgroups share a CU (one
+// workgroup's first stages load while the other multiplies); stages of 64 with one
+// workgroup per CU measured 3-25% slower on every backward GEMM of the DeepSeek-V3 layer
+constexpr int kBwdStageK = 32;
+
 unsigned grid_for(long long tiles) {
   const long long per_xcd = (tiles + kNumXcd - 1) / kNumXcd;
   return static_cast<unsigned>(per_xcd * kNumXcd);
@@ -483,9 +503,9 @@ hipError_t launch_expert_dgrad(const void* dC, const int32_t* offsets, int E, in
   p.N = N;
   p.K = K;
   p.b_div = 1;
-  if (N % wide::kTN == 0 && K % wide::kKS == 0)
-    hipLaunchKernelGGL(wide::grouped_gemm_bwd_wide_kernel<BWD_DGRAD>,
-                       dim3(grid_for(static_cast<long long>(cap) * (N / wide::kTN))), dim3(256), 0, s, p);
+  const dim3 wgrid(grid_for(static_cast<long long>(cap) * (N / wide::kTN)));
+  if (N % wide::kTN == 0 && K % kBwdStageK == 0)
+    hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_DGRAD, kBwdStageK>), wgrid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_DGRAD>, dim3(grid_for(static_cast<long long>(cap) * (N / kBT))),
                        dim3(kBwdThreads), 0, s, p);
@@ -510,7 +530,8 @@ hipError_t launch_expert_wgrad(const void* a, const void* b, const int32_t* b_ro
   p.out_f32 = dw_f32 ? 1 : 0;
   if (b_rows == nullptr && N % wide::kTN == 0) {
     const long long tiles = static_cast<long long>(E) * (M / wide::kTM) * (N / wide::kTN);
-    hipLaunchKernelGGL(wide::grouped_gemm_bwd_wide_kernel<BWD_WGRAD>, dim3(grid_for(tiles)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_WGRAD, kBwdStageK>), dim3(grid_for(tiles)), dim3(256), 0,
+                       s, p);
   } else {
     const long long tiles = static_cast<long long>(E) * (M / kBT) * (N / kBT);
     hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_WGRAD>, dim3(grid_for(tiles)), dim3(kBwdThreads), 0, s, p);
