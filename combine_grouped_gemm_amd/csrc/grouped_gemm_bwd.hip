@@ -437,30 +437,55 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
   }
 
   // ---- epilogue: lane l holds tile row wm*64 + i*32 + l % 32 and, in registers 4q .. 4q+3
-  // of block j, columns wn*128 + j*32 + 8q + 4 (l / 32) + 0..3
+  // of block j, columns wn*128 + j*32 + 8q + 4 (l / 32) + 0..3.  bf16 tiles go through LDS
+  // (16-byte chunk c of row r in slot c ^ (r % 32)), so that each store instruction writes two
+  // whole 512-byte rows; fp32 tiles are stored from the registers, 16 bytes per lane.
+  const bool staged = MODE == BWD_DGRAD || !p.out_f32;
+  if (staged) {
+    static_assert(kTM * kTN * 2 <= kSlots * kStage, "a bf16 tile fits the ring");
+    wait_lgkmcnt_all();
+    block_barrier();   // every wave is past its last fragment reads
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wm * 64 + i * 32 + (lane & 31);
-    if (MODE == BWD_DGRAD && r >= mcount) continue;
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + i * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-        const f32x16_t& a = acc[i][j];
-        if (MODE == BWD_DGRAD) {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(m0 + r) * p.N + col) =
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+          const int chunk = (col >> 3) ^ (r & 31);
+          const f32x16_t& a = acc[i][j];
+          *reinterpret_cast<uint2*>(lds + r * (kTN * 2) + chunk * 16 + (col & 7) * 2) =
               make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
-        } else {
-          const size_t o = (static_cast<size_t>(e) * p.M + m0 + r) * p.N + col;
-          if (p.out_f32)
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) =
-                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-          else
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) =
-                make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
         }
-      }
+    }
+    wait_lgkmcnt_all();
+    block_barrier();
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+    const size_t row0 = MODE == BWD_DGRAD ? static_cast<size_t>(m0) : static_cast<size_t>(e) * p.M + m0;
+#pragma unroll
+    for (int t = 0; t < kTM * kTN * 2 / 16 / 256; ++t) {
+      const int c = t * 256 + tid;
+      const int r = c >> 5, chunk = c & 31;
+      if (MODE == BWD_DGRAD && r >= mcount) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (kTN * 2) + ((chunk ^ (r & 31)) << 4));
+      *reinterpret_cast<uint4*>(out + (row0 + r) * p.N + n0 + chunk * 8) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+          const f32x16_t& a = acc[i][j];
+          const size_t o = (static_cast<size_t>(e) * p.M + m0 + r) * p.N + col;
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }
+    }
   }
 }
 
