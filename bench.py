@@ -228,6 +228,8 @@ def main():
             raise SystemExit("--train runs the layer on one stream (no --overlap)")
         dy = workload.normal((cfg.N, cfg.H), workload.stream_key(cfg.seed, workload.T_EO, 5), dev, torch.bfloat16,
                              std=1.0)
+        # the training forward keeps the gate/up pre-activations for the backward
+        layer.forward(x, save_for_backward=True)
         stages += layer.backward_steps(x, dy)
 
     def step(ev=None):

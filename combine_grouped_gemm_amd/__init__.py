@@ -60,7 +60,7 @@ _SIGS = {
     "moe_expert_gate_up": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
     "moe_expert_gate_up_gathered": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
     "moe_expert_down": [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _SZ, _P],
-    "moe_expert_gate_up_gathered_shared": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
+    "moe_expert_gate_up_gathered_shared": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_expert_down_shared": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
@@ -271,9 +271,11 @@ def moe_expert_gate_up_gathered(x: torch.Tensor, src_slot: torch.Tensor, k: int,
 
 def moe_expert_gate_up_gathered_shared(x: torch.Tensor, src_slot: torch.Tensor, k: int, offsets: torch.Tensor,
                                        w13: torch.Tensor, shared_w13: torch.Tensor, rows: Optional[int] = None,
-                                       h: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+                                       h: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                                       au: Optional[torch.Tensor] = None):
     """Routed gate/up (rows gathered from x) plus the shared expert on all N tokens in one
-    launch: h [rows + N, I], the shared expert's rows last."""
+    launch: h [rows + N, I], the shared expert's rows last (and the pre-activations into au
+    [rows + N, 2I] when given)."""
     N, H = x.shape
     E, I2, _ = w13.shape
     I = I2 // 2
@@ -285,7 +287,7 @@ def moe_expert_gate_up_gathered_shared(x: torch.Tensor, src_slot: torch.Tensor, 
         ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, MOE_BF16), x.device)
     _check("moe_expert_gate_up_gathered_shared", lib().moe_expert_gate_up_gathered_shared(
         _ptr(x), _dt(x), N, _ptr(src_slot), k, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(shared_w13),
-        _ptr(h), _ptr(ws), ws.numel(), _stream(x)))
+        _ptr(h), _ptr(au), _ptr(ws), ws.numel(), _stream(x)))
     return h
 
 

@@ -33,6 +33,8 @@ struct GemmArgs {
   const float* row_gate;       //   (slots clamped into [0, rows)), or both null
   int k_split;                 // router: K is cut into k_split equal parts; part s of every
                                // output goes to out + s * rows * n_out (fp32)
+  void* au;                    // gate/up (256 x 256 kernel): also the pre-activations [rows, 2I]
+                               // bf16 (gate in columns 0..I-1, up in I..2I-1), or null
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot

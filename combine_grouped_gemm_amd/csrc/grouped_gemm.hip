@@ -757,7 +757,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,
                                long long b_rows, void* sched, hipStream_t s, const int32_t* a_rows,
                                int a_div, int a_nrows, const void* shared_b, int shared_rows,
-                               const int32_t* row_slot, const float* row_gate) {
+                               const int32_t* row_slot, const float* row_gate, void* au) {
   // with a shared segment the schedule covers E + 1 segments and rows + shared_rows rows
   const int n_seg = E + (shared_rows > 0 ? 1 : 0);
   int32_t* prefix = reinterpret_cast<int32_t*>(sched);
@@ -776,9 +776,9 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const bool wide_ok = dma && K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 &&
                        b_rows * rbytes < (1LL << 32) &&
                        (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
-  if ((shared_rows > 0 || row_gate != nullptr) && (!wide_ok || stream))
+  if ((shared_rows > 0 || row_gate != nullptr || au != nullptr) && (!wide_ok || stream))
     return hipErrorNotSupported;   // (callers check first)
-  const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr ||
+  const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr || au != nullptr ||
                                 (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= (E > 1 ? 2 : 3)));
   const int tile_rows = stream ? kStreamTileRows : (wide ? kWideTileRows : (dma ? kDM : GBM));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
@@ -809,6 +809,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.row_slot = row_gate != nullptr ? row_slot : nullptr;
   p.row_gate = row_slot != nullptr ? row_gate : nullptr;
   p.k_split = 1;
+  p.au = au;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
   if (wide) {
     p.tile_counter = kWideDynamic ? tile_counter : nullptr;

@@ -360,6 +360,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
               const float up = acc[mb][nb + 2][4 * q + u];
               hv[u] = g / (1.0f + expf(-g)) * up;
             }
+            if (p.au != nullptr) {   // the pre-activations, for the backward pass
+              const f32x16_t& ga = acc[mb][nb];
+              const f32x16_t& ua = acc[mb][nb + 2];
+              uint16_t* arow = reinterpret_cast<uint16_t*>(p.au) + static_cast<size_t>(r) * 2 * p.I;
+              *reinterpret_cast<uint2*>(arow + col) =
+                  make_uint2(pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3]));
+              *reinterpret_cast<uint2*>(arow + p.I + col) =
+                  make_uint2(pack_bf16x2(ua[4 * q], ua[4 * q + 1]), pack_bf16x2(ua[4 * q + 2], ua[4 * q + 3]));
+            }
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.I + col) =
                 make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           }

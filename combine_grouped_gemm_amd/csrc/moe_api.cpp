@@ -202,8 +202,8 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
 
 moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
                                               int k, const int32_t* offsets, int E, int rows, int H, int I,
-                                              const void* w13, const void* shared_w13, void* h, void* ws,
-                                              size_t ws_bytes, hipStream_t stream) {
+                                              const void* w13, const void* shared_w13, void* h, void* au,
+                                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (x_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (E < 1 || rows < 0 || N < 0 || H <= 0 || I <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
   if (k < 1 || k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
@@ -214,11 +214,12 @@ moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int
   if (x == nullptr || shared_w13 == nullptr || h == nullptr || (rows > 0 && (w13 == nullptr || src_slot == nullptr)))
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(shared_w13) || (w13 != nullptr && !aligned16(w13))) return MOE_ERR_INVALID_ARG;
+  if (au != nullptr && !aligned16(au)) return MOE_ERR_INVALID_ARG;
   if (static_cast<long long>(N) * H * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
   if (!moe::grouped_gemm_shared_supported(0, H, I, I, 2ll * I, N, true)) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_grouped_gemm(1, false, 0, x, nullptr, w13, nullptr, h, false, offsets,
                                              E, rows, H, I, I, 2ll * I, ws, stream, src_slot, k, N,
-                                             shared_w13, N));
+                                             shared_w13, N, nullptr, nullptr, au));
 }
 
 moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,

@@ -58,7 +58,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                                long long b_rows, void* sched, hipStream_t s,
                                const int32_t* a_rows = nullptr, int a_div = 1, int a_nrows = 0,
                                const void* shared_b = nullptr, int shared_rows = 0,
-                               const int32_t* row_slot = nullptr, const float* row_gate = nullptr);
+                               const int32_t* row_slot = nullptr, const float* row_gate = nullptr,
+                               void* au = nullptr);
 // whether launch_grouped_gemm accepts a shared segment for these bf16 shapes
 bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long b_rows, int a_nrows,
                                    bool gathered);

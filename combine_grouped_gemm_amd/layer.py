@@ -109,6 +109,9 @@ class MoELayer:
         self.side = torch.cuda.Stream(device=dev) if self.shared and overlap_shared and not self.fuse else None
         self.shared_done = torch.cuda.Event() if self.side is not None else None
         self.y = torch.empty((N, H), dtype=act, device=dev)
+        self.save_au = False     # the next forward keeps the gate/up pre-activations (training)
+        self.au_saved = False    # the last forward kept them
+        self.au_all = None
 
     @property
     def expert_out(self) -> torch.Tensor:
@@ -155,7 +158,8 @@ class MoELayer:
         layers also compute the shared expert's rows)."""
         if self.fuse:
             return moe_expert_gate_up_gathered_shared(x, self.layout[3], self.k, self.layout[1], self.w13,
-                                                      self.sw13, h=self.h_all, ws=self.fused_ws)
+                                                      self.sw13, h=self.h_all, ws=self.fused_ws,
+                                                      au=self.au_all if self.save_au else None)
         if self.gather:
             return moe_expert_gate_up_gathered(x, self.layout[3], self.k, self.layout[1], self.w13,
                                                h=self.h, ws=self.ffn_ws)
@@ -200,7 +204,16 @@ class MoELayer:
             self.shared_expert(x)
             self.shared_done.record(self.side)
 
-    def forward(self, x: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, z: Optional[torch.Tensor] = None, save_for_backward: bool = False) -> torch.Tensor:
+        """y for tokens x; z: the router logits (computed from W_r when None).  With
+        save_for_backward a bf16 layer that runs the shared expert inside the routed launches
+        also keeps the gate/up pre-activations, which backward then reads instead of
+        recomputing them."""
+        self.save_au = bool(save_for_backward and self.fuse)
+        if self.save_au and self.au_all is None:
+            self.au_all = torch.empty((self.N * self.k + self.N, 2 * self.I), dtype=torch.bfloat16,
+                                      device=self.device)
+        self.au_saved = self.save_au
         if self.side is not None:
             self.launch_shared_side(x)
         if z is None:
@@ -269,13 +282,20 @@ class MoELayer:
         k, N = self.k, self.N
         rows = N * k
         offsets, send_pos, src_slot = self.layout[1], self.layout[2], self.layout[3]
+        # the pre-activations: kept by the forward, or recomputed here
+        saved = self.au_saved
+        au = self.au_all[:rows] if saved else b["au"]
+        au_s = self.au_all[rows:] if saved else b.get("au_s")
         st = [
             ("combine_bwd", lambda: moe_combine_backward(dy, send_pos, self.topk_gate, self.expert_out, b["d_eo"],
                                                          b["dg"])),
-            ("gate_up_preact", lambda: moe_expert_gate_up_preact(x, offsets, self.w13, rows, src_slot, k, b["au"],
-                                                                 b["gemm_ws"])),
+        ]
+        if not saved:
+            st.append(("gate_up_preact", lambda: moe_expert_gate_up_preact(x, offsets, self.w13, rows, src_slot, k,
+                                                                           b["au"], b["gemm_ws"])))
+        st += [
             ("down_dgrad", lambda: moe_expert_dgrad(b["d_eo"], offsets, self.w2, b["dh"], b["dgrad_ws"])),
-            ("swiglu_bwd", lambda: moe_swiglu_backward(b["au"], b["dh"], b["d_au"], b["h"])),
+            ("swiglu_bwd", lambda: moe_swiglu_backward(au, b["dh"], b["d_au"], b["h"])),
             ("down_wgrad", lambda: moe_expert_wgrad(b["d_eo"], b["h"], offsets, dw=b["dw2"], rows=rows)),
             # the weight gradient of W13 reads the expert-ordered rows of x (a permuted copy:
             # the wgrad kernel streams its B operand in layout order)
@@ -286,11 +306,12 @@ class MoELayer:
         rest = None
         if self.shared:
             so = b["shared_offsets"]
+            if not saved:
+                st.append(("shared_preact", lambda: moe_expert_gate_up_preact(x, so, self.sw13, N, None, 1,
+                                                                              b["au_s"], b["gemm_ws"])))
             st += [
-                ("shared_preact", lambda: moe_expert_gate_up_preact(x, so, self.sw13, N, None, 1, b["au_s"],
-                                                                    b["gemm_ws"])),
                 ("shared_down_dgrad", lambda: moe_expert_dgrad(dy, so, self.sw2, b["dh_s"], b["dgrad_ws"])),
-                ("shared_swiglu_bwd", lambda: moe_swiglu_backward(b["au_s"], b["dh_s"], b["d_au_s"], b["h_s"])),
+                ("shared_swiglu_bwd", lambda: moe_swiglu_backward(au_s, b["dh_s"], b["d_au_s"], b["h_s"])),
                 ("shared_down_wgrad", lambda: moe_expert_wgrad(dy, b["h_s"], so, dw=b["dsw2"], rows=N)),
                 ("shared_gate_up_wgrad", lambda: moe_expert_wgrad(b["d_au_s"], x, so, dw=b["dsw13"], rows=N)),
                 ("shared_gate_up_dgrad", lambda: moe_expert_dgrad(b["d_au_s"], so, self.sw13, b["dx_s"],

@@ -263,6 +263,9 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
  *   gate/up:  x [N, H] bf16; src_slot, k, offsets, E, rows, H, I, w13 as for
  *             moe_expert_gate_up_gathered; shared_w13 [2*I, H] bf16 (W_gate rows, then
  *             W_up rows); h [rows + N, I] bf16 (shared rows last); n = N.
+             au [rows + N, 2I] bf16, or NULL: when given, the gate and up pre-activations of
+             every row as well (gate in columns 0..I-1, up in I..2I-1; the training forward
+             keeps them for moe_swiglu_backward instead of moe_expert_gate_up_preact).
  *   down:     h [rows + n_shared, I] bf16; w2 [E, H, I] and shared_w2 [H, I] bf16;
  *             out [rows + n_shared, H] bf16 (the shared rows last: pass out + rows * H to
  *             moe_combine as shared_out).
@@ -279,8 +282,8 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
  */
 moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
                                               int k, const int32_t* offsets, int E, int rows, int H, int I,
-                                              const void* w13, const void* shared_w13, void* h, void* ws,
-                                              size_t ws_bytes, hipStream_t stream);
+                                              const void* w13, const void* shared_w13, void* h, void* au,
+                                              void* ws, size_t ws_bytes, hipStream_t stream);
 moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                                   int n_shared, int I, int H, const void* w2, const void* shared_w2,
                                   const int32_t* src_slot, const float* topk_gate, void* out,

@@ -157,7 +157,7 @@ def test_shared_segment_validation(L):
     assert sched > moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16)
     f = L.moe_expert_gate_up_gathered_shared
     args = lambda **kw: dict(dict(x=FAKE, x_dt=MOE_BF16, N=N, src_slot=FAKE, k=k, offsets=FAKE, E=E,
-                                  rows=rows, H=H, I=I, w13=FAKE, sw13=FAKE, h=FAKE, ws=FAKE, ws_bytes=sched,
+                                  rows=rows, H=H, I=I, w13=FAKE, sw13=FAKE, h=FAKE, au=None, ws=FAKE, ws_bytes=sched,
                                   s=None), **kw)
     call = lambda **kw: f(*args(**kw).values())
     assert call(x_dt=MOE_F32) == MOE_ERR_UNSUPPORTED
@@ -165,6 +165,7 @@ def test_shared_segment_validation(L):
     assert call(sw13=None) == MOE_ERR_INVALID_ARG
     assert call(src_slot=None) == MOE_ERR_INVALID_ARG
     assert call(k=0) == MOE_ERR_INVALID_ARG
+    assert call(au=FAKE + 8) == MOE_ERR_INVALID_ARG      # misaligned pre-activation output
     assert call(E=1024) == MOE_ERR_UNSUPPORTED            # E + 1 segments must fit the schedule
     assert call(I=2000) == MOE_ERR_UNSUPPORTED
     assert call(N=300000, ws_bytes=1 << 40) == MOE_ERR_UNSUPPORTED   # N * H * 2 >= 2^32

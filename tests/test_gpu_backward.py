@@ -211,20 +211,24 @@ SMALL = {
 }
 
 
-def _layer_for_backward(cfg):
+def _layer_for_backward(cfg, save=False):
     inp = with_logits(w.make_layer_inputs(cfg, DEV))
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"], inp.get("sw13"),
                      inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"], w_r=inp["w_r"])
-    layer.forward(inp["x"], inp["z"])
+    layer.forward(inp["x"], inp["z"], save_for_backward=save)
     dy = w.normal((cfg.N, cfg.H), w.stream_key(cfg.seed, w.T_EO, 5), DEV, torch.bfloat16, std=1.0)
     return inp, layer, dy
 
 
+@pytest.mark.parametrize("save", [False, True], ids=["recomputed", "saved"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_layer_backward_small(name):
+def test_layer_backward_small(name, save):
+    """The layer's gradients against the oracle's, with the gate/up pre-activations
+    recomputed by the backward or kept by the forward (layers that fuse the shared expert)."""
     cfg = SMALL[name]
-    say(f"layer backward {name} N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}")
-    inp, layer, dy = _layer_for_backward(cfg)
+    say(f"layer backward {name} N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} saved={save}")
+    inp, layer, dy = _layer_for_backward(cfg, save)
+    assert layer.au_saved == (save and layer.fuse)
     gr = layer.backward(inp["x"], dy, dw_dtype=torch.float32)
     sync()
     b = inp["bias_cpu"]
@@ -259,7 +263,7 @@ def test_layer_backward_full_size_sampled():
     or that token alone."""
     cfg = w.CONFIGS["dsv3_bf16"]
     say("layer backward dsv3_bf16 full size")
-    inp, layer, dy = _layer_for_backward(cfg)
+    inp, layer, dy = _layer_for_backward(cfg, save=True)
     gr = layer.backward(inp["x"], dy)
     sync()
     k = cfg.k
@@ -300,3 +304,21 @@ def test_layer_backward_full_size_sampled():
         err = float(np.abs(f64(gr["dx"][t]) - dx).max() / np.abs(dx).max())
         say(f"  token {t}: dx relative error {err:.2e}")
         assert err <= GRAD_BAR
+
+
+def test_saved_preactivations_equal_recomputed():
+    """The forward's kept pre-activations of the routed rows equal the backward's recomputed
+    ones bit for bit (the same tile kernel and k order); the gradients agree."""
+    cfg = SMALL["dsv3_small"]
+    say("saved vs recomputed pre-activations")
+    inp, layer, dy = _layer_for_backward(cfg, save=True)
+    rows = cfg.N * cfg.k
+    au_saved = layer.au_all[:rows].clone()
+    g1 = {n: layer.backward(inp["x"], dy)[n].clone() for n in ("dx", "dw13", "dw2", "dsw13", "dw_r")}
+    layer.forward(inp["x"], inp["z"], save_for_backward=False)
+    assert not layer.au_saved
+    g2 = layer.backward(inp["x"], dy)
+    sync()
+    assert torch.equal(au_saved.view(torch.int16), layer.grads["au"].view(torch.int16))
+    for n, v in g1.items():
+        assert mat_rel_err(f64(g2[n]), f64(v)) <= 1e-2, n
