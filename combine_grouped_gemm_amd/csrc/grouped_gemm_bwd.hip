@@ -247,37 +247,41 @@ __global__ __launch_bounds__(kBwdThreads, 2) void grouped_gemm_bwd_kernel(BwdArg
 // ------------------------------------------------------------------------------------
 namespace wide {
 
-constexpr int kTM = 128, kTN = 256;
+constexpr int kTN = 256;     // tile columns
+constexpr int kKS = 32;      // k per stage
 constexpr int kSlots = 3;
-constexpr int kKSMin = 32;   // the smallest k per stage (a stage of 64 needs K % 64 == 0)
 
-// sizes of a stage of KS k (KS = 64: 48 KB, one workgroup per CU; KS = 32: 24 KB, two)
-template <int KS>
+// A tile of TM rows (128: 4 waves, dgrad and wgrad; 256: 8 waves, wgrad) x 256 columns; a
+// wave computes 64 rows x 128 columns.  A stage of 32 k is (TM + 256) x 64 bytes: 24 KB (two
+// workgroups per CU) or 32 KB (one workgroup of 8 waves per CU).
+template <int TM>
 struct Cfg {
-  static constexpr int kABytes = kTM * KS * 2;
-  static constexpr int kBBytes = kTN * KS * 2;
+  static constexpr int kWM = TM / 64;                  // waves along the rows
+  static constexpr int kWaves = 2 * kWM;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kABytes = TM * kKS * 2;
+  static constexpr int kBBytes = kTN * kKS * 2;
   static constexpr int kStage = kABytes + kBBytes;
-  static constexpr int kAOps = kABytes / 1024 / 4;   // 1 KB loads per wave and stage
-  static constexpr int kBOps = kBBytes / 1024 / 4;
+  static constexpr int kAOps = kABytes / 1024 / kWaves;   // 1 KB loads per wave and stage
+  static constexpr int kBOps = kBBytes / 1024 / kWaves;
   static constexpr int kOps = kAOps + kBOps;
-  static constexpr int kChunks = KS / 8;              // 16-byte chunks of a k-contiguous row
-  static constexpr int kOcc = KS == 32 ? 2 : 1;       // workgroups per CU
-  // slot of chunk c of k-contiguous row r: c ^ key(r) (a fragment read of 32 rows and an
-  // 8- or 16-row load both spread over the 64 banks)
-  __device__ static __forceinline__ int kc_key(int r) {
-    return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
-  }
+  static constexpr int kOcc = TM == 128 ? 2 : 1;         // workgroups per CU
+  static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "loads spread evenly");
 };
 
-__device__ __attribute__((aligned(16))) uint8_t g_zero_page[kTM * 2];
-
+// k-contiguous rows of 64 bytes: chunk c of row r in slot c ^ ((r >> 2) & 3) (a fragment read
+// of 32 rows and a 16-row load both spread over the 64 banks)
+__device__ __forceinline__ int kc_key(int r) { return (r >> 2) & 3; }
+// k-rows of the strided operands: chunk c of k-row r in slot c ^ 4 (r & 3)
 __device__ __forceinline__ int mc_key(int k) { return 4 * (k & 3); }
+
+__device__ __attribute__((aligned(16))) uint8_t g_zero_page[256 * 2];
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// MFMA fragment of a k-strided operand: column `col` of the tile, k-rows 16 s + 8 (l / 32)
-// + 0..7, from a slot whose k-rows are `pitch` bytes long
+// MFMA fragment of a k-strided operand: column `col0 + l % 32` of the tile, k-rows 16 s +
+// 8 (l / 32) + 0..7, from a slot whose k-rows are `pitch` bytes long
 __device__ __forceinline__ uint4 tr_frag(uint32_t base, int pitch, int s, int col0, int lane) {
   const int g = lane >> 4, i = lane & 15;
   uint2 h[2];
@@ -292,21 +296,22 @@ __device__ __forceinline__ uint4 tr_frag(uint32_t base, int pitch, int s, int co
   return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
 }
 
-template <int MODE, int KS>
-__global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kernel(BwdArgs p) {
-  using C = Cfg<KS>;
-  constexpr int kKS = KS, kABytes = C::kABytes, kStage = C::kStage, kAOps = C::kAOps, kBOps = C::kBOps;
-  constexpr int kOps = C::kOps, kChunks = C::kChunks;
+template <int MODE, int TM>
+__global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm_bwd_wide_kernel(BwdArgs p) {
+  using C = Cfg<TM>;
+  constexpr int kWaves = C::kWaves, kABytes = C::kABytes, kStage = C::kStage, kAOps = C::kAOps;
+  constexpr int kOps = C::kOps, kThreads = C::kThreads;
+  static_assert(MODE == BWD_WGRAD || TM == 128, "dgrad tiles have 128 rows");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kStage];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- the tile (as the 128 x 128 kernel, with 256-column n-blocks)
+  // ---- the tile
   const int nN = p.N / kTN;
   long long total;
   if (MODE == BWD_DGRAD) total = static_cast<long long>(p.tile_prefix[p.E]) * nN;
-  else total = static_cast<long long>(p.E) * (p.M / kTM) * nN;
+  else total = static_cast<long long>(p.E) * (p.M / TM) * nN;
   const int xcd = blockIdx.x % kNumXcd;
   const long long slot = blockIdx.x / kNumXcd;
   const long long per_xcd = (total + kNumXcd - 1) / kNumXcd;
@@ -314,6 +319,8 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
   if (slot >= per_xcd || L >= total) return;
   int e, m0, mcount, n0, klo, kcount;
   if (MODE == BWD_DGRAD) {
+    // expert -> n-block -> m-tile: expert e owns logical tiles [prefix[e] nN, prefix[e+1] nN);
+    // the last expert whose range starts at or before L (an empty expert's range is empty)
     int lo_e = 0, hi_e = p.E - 1;
     while (lo_e < hi_e) {
       const int mid = (lo_e + hi_e + 1) >> 1;
@@ -325,18 +332,18 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
     const long long local = L - static_cast<long long>(p.tile_prefix[e]) * nN;
     int lo, hi;
     seg_of(p, e, lo, hi);
-    m0 = lo + static_cast<int>(local % mt_e) * kTM;
-    mcount = hi - m0 < kTM ? hi - m0 : kTM;
+    m0 = lo + static_cast<int>(local % mt_e) * TM;
+    mcount = hi - m0 < TM ? hi - m0 : TM;
     n0 = static_cast<int>(local / mt_e) * kTN;
     klo = 0;
     kcount = p.K;
   } else {
-    const int mB = p.M / kTM;
+    const int mB = p.M / TM;
     e = static_cast<int>(L / (static_cast<long long>(mB) * nN));
     const int local = static_cast<int>(L - static_cast<long long>(e) * mB * nN);
-    m0 = (local / nN) * kTM;
+    m0 = (local / nN) * TM;
     n0 = (local % nN) * kTN;
-    mcount = kTM;
+    mcount = TM;
     int lo, hi;
     seg_of(p, e, lo, hi);
     klo = lo;
@@ -344,29 +351,30 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
   }
   const int nk = (kcount + kKS - 1) / kKS;
 
-  // ---- loads of stage ks into ring slot sl: op j < kAOps fills A's 1 KB group wave + 4 j,
-  // op kAOps + j fills B's group wave + 4 j
+  // ---- loads of stage ks into ring slot sl: op j < kAOps fills A's 1 KB group wave +
+  // kWaves j, op kAOps + j fills B's group wave + kWaves j
   auto issue = [&](int ks, int sl, int j) __attribute__((always_inline)) {
     const int k0 = ks * kKS;
     const uint8_t* src;
     uint32_t dst;
     if (j < kAOps) {
-      const int g = wave + 4 * j;
+      const int g = wave + kWaves * j;
       dst = lds0 + sl * kStage + g * 1024;
-      if (MODE == BWD_DGRAD) {   // 1024 / (2 KS) rows of 2 KS bytes
-        int r = (1024 / (2 * kKS)) * g + lane / kChunks;
-        const int c = (lane % kChunks) ^ C::kc_key(r);
+      if (MODE == BWD_DGRAD) {   // 16 rows of 64 bytes
+        int r = 16 * g + (lane >> 2);
+        const int c = (lane & 3) ^ kc_key(r);
         r = r < mcount ? r : mcount - 1;
         src = reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(m0 + r) * p.K + k0) * 2 + c * 16;
-      } else {                   // 4 k-rows of 256 bytes (128 m)
-        const int kr = 4 * g + (lane >> 4);
-        const int c = (lane & 15) ^ mc_key(kr);
+      } else {                   // 1024 / (2 TM) k-rows of 2 TM bytes
+        constexpr int kPer = 1024 / (2 * TM), kCh = 2 * TM / 16;
+        const int kr = kPer * g + lane / kCh;
+        const int c = (lane % kCh) ^ mc_key(kr);
         src = k0 + kr < kcount
                   ? reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(klo + k0 + kr) * p.M + m0) * 2 + c * 16
                   : g_zero_page + c * 16;
       }
     } else {                     // 2 k-rows of 512 bytes (256 n)
-      const int g = wave + 4 * (j - kAOps);
+      const int g = wave + kWaves * (j - kAOps);
       dst = lds0 + sl * kStage + kABytes + g * 1024;
       const int kr = 2 * g + (lane >> 5);
       const int c = (lane & 31) ^ mc_key(kr);
@@ -414,10 +422,10 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
         for (int i = 0; i < 2; ++i) {
           if (MODE == BWD_DGRAD) {
             const int row = wm * 64 + i * 32 + (lane & 31);
-            const int c = (2 * s + (lane >> 5)) ^ C::kc_key(row);
+            const int c = (2 * s + (lane >> 5)) ^ kc_key(row);
             fa[i] = *reinterpret_cast<const uint4*>(lds + (abase - lds0) + row * (2 * kKS) + c * 16);
           } else {
-            fa[i] = tr_frag(abase, kTM * 2, s, wm * 64 + i * 32, lane);
+            fa[i] = tr_frag(abase, TM * 2, s, wm * 64 + i * 32, lane);
           }
         }
 #pragma unroll
@@ -438,38 +446,44 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
 
   // ---- epilogue: lane l holds tile row wm*64 + i*32 + l % 32 and, in registers 4q .. 4q+3
   // of block j, columns wn*128 + j*32 + 8q + 4 (l / 32) + 0..3.  bf16 tiles go through LDS
-  // (16-byte chunk c of row r in slot c ^ (r % 32)), so that each store instruction writes two
-  // whole 512-byte rows; fp32 tiles are stored from the registers, 16 bytes per lane.
+  // 128 rows at a time (16-byte chunk c of row r in slot c ^ (r % 32)), so that each store
+  // instruction writes whole 512-byte rows; fp32 tiles are stored from the registers.
   const bool staged = MODE == BWD_DGRAD || !p.out_f32;
   if (staged) {
-    static_assert(kTM * kTN * 2 <= kSlots * kStage, "a bf16 tile fits the ring");
-    wait_lgkmcnt_all();
-    block_barrier();   // every wave is past its last fragment reads
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wm * 64 + i * 32 + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-          const int chunk = (col >> 3) ^ (r & 31);
-          const f32x16_t& a = acc[i][j];
-          *reinterpret_cast<uint2*>(lds + r * (kTN * 2) + chunk * 16 + (col & 7) * 2) =
-              make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
-        }
-    }
-    wait_lgkmcnt_all();
-    block_barrier();
+    static_assert(128 * kTN * 2 <= kSlots * kStage, "128 rows of a bf16 tile fit the ring");
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     const size_t row0 = MODE == BWD_DGRAD ? static_cast<size_t>(m0) : static_cast<size_t>(e) * p.M + m0;
 #pragma unroll
-    for (int t = 0; t < kTM * kTN * 2 / 16 / 256; ++t) {
-      const int c = t * 256 + tid;
-      const int r = c >> 5, chunk = c & 31;
-      if (MODE == BWD_DGRAD && r >= mcount) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (kTN * 2) + ((chunk ^ (r & 31)) << 4));
-      *reinterpret_cast<uint4*>(out + (row0 + r) * p.N + n0 + chunk * 8) = v;
+    for (int half = 0; half < TM / 128; ++half) {
+      wait_lgkmcnt_all();
+      block_barrier();   // every wave is past its last fragment reads (or the previous half's stores)
+      if ((wm >> 1) == half) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = (wm & 1) * 64 + i * 32 + (lane & 31);   // row within the half
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+              const int chunk = (col >> 3) ^ (r & 31);
+              const f32x16_t& a = acc[i][j];
+              *reinterpret_cast<uint2*>(lds + r * (kTN * 2) + chunk * 16 + (col & 7) * 2) =
+                  make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+            }
+        }
+      }
+      wait_lgkmcnt_all();
+      block_barrier();
+#pragma unroll
+      for (int t = 0; t < 128 * kTN * 2 / 16 / kThreads; ++t) {
+        const int c = t * kThreads + tid;
+        const int r = c >> 5, chunk = c & 31;
+        const int rt = half * 128 + r;   // row within the tile
+        if (MODE == BWD_DGRAD && rt >= mcount) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (kTN * 2) + ((chunk ^ (r & 31)) << 4));
+        *reinterpret_cast<uint4*>(out + (row0 + rt) * p.N + n0 + chunk * 8) = v;
+      }
     }
   } else {
 #pragma unroll
@@ -491,10 +505,6 @@ __global__ __launch_bounds__(256, Cfg<KS>::kOcc) void grouped_gemm_bwd_wide_kern
 
 }  // namespace wide
 
-// k per stage of the 128 x 256 kernels: 32, so that two workgroups share a CU (one
-// workgroup's first stages load while the other multiplies); stages of 64 with one
-// workgroup per CU measured 3-25% slower on every backward GEMM of the DeepSeek-V3 layer
-constexpr int kBwdStageK = 32;
 
 unsigned grid_for(long long tiles) {
   const long long per_xcd = (tiles + kNumXcd - 1) / kNumXcd;
@@ -529,8 +539,9 @@ hipError_t launch_expert_dgrad(const void* dC, const int32_t* offsets, int E, in
   p.K = K;
   p.b_div = 1;
   const dim3 wgrid(grid_for(static_cast<long long>(cap) * (N / wide::kTN)));
-  if (N % wide::kTN == 0 && K % kBwdStageK == 0)
-    hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_DGRAD, kBwdStageK>), wgrid, dim3(256), 0, s, p);
+  if (N % wide::kTN == 0 && K % wide::kKS == 0)
+    hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_DGRAD, 128>), wgrid, dim3(wide::Cfg<128>::kThreads), 0,
+                       s, p);
   else
     hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_DGRAD>, dim3(grid_for(static_cast<long long>(cap) * (N / kBT))),
                        dim3(kBwdThreads), 0, s, p);
@@ -553,10 +564,14 @@ hipError_t launch_expert_wgrad(const void* a, const void* b, const int32_t* b_ro
   p.M = M;
   p.N = N;
   p.out_f32 = dw_f32 ? 1 : 0;
+  // (256-row tiles of 8 waves, one workgroup per CU, measured 20-30% slower on the
+  // DeepSeek-V3 weight gradients: with ~256 rows of K per expert a tile is 8 stages, and a
+  // second workgroup on the CU hides one tile's first loads and last stores behind the
+  // other's multiplies)
   if (b_rows == nullptr && N % wide::kTN == 0) {
-    const long long tiles = static_cast<long long>(E) * (M / wide::kTM) * (N / wide::kTN);
-    hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_WGRAD, kBwdStageK>), dim3(grid_for(tiles)), dim3(256), 0,
-                       s, p);
+    const long long tiles = static_cast<long long>(E) * (M / 128) * (N / wide::kTN);
+    hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_WGRAD, 128>), dim3(grid_for(tiles)),
+                       dim3(wide::Cfg<128>::kThreads), 0, s, p);
   } else {
     const long long tiles = static_cast<long long>(E) * (M / kBT) * (N / kBT);
     hipLaunchKernelGGL(grouped_gemm_bwd_kernel<BWD_WGRAD>, dim3(grid_for(tiles)), dim3(kBwdThreads), 0, s, p);

@@ -141,6 +141,7 @@ WGRAD_CASES = [
     # name, N, k, E, M, Nout, gathered, out dtype, empty experts (ungathered with Nout % 256
     # == 0: the 128 x 256 tile kernel; otherwise the 128 x 128 one)
     ("wide_ragged_f32", 400, 3, 8, 256, 512, False, torch.float32, (1,)),
+    ("wide_bf16_m512", 300, 2, 8, 512, 256, False, torch.bfloat16, (2,)),
     ("wide_bf16_long", 700, 1, 2, 128, 256, False, torch.bfloat16, ()),
     ("wide_many_small", 150, 2, 64, 384, 256, False, torch.float32, (0, 5)),
     ("ragged_f32", 400, 3, 8, 256, 384, False, torch.float32, (1,)),
