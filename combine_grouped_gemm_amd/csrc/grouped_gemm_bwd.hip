@@ -6,18 +6,21 @@
 //   wgrad:  dW_e[m, n] = sum_{r in segment e} A[r, m] B[r', n]              (r' = r, or gathered)
 //
 // The forward kernels read both operands with k contiguous.  Here one (dgrad: W_e) or both
-// (wgrad: A and B, k being the row index) have k as the slow index, so those operands are
-// transposed on their way into LDS: a lane loads 8 consecutive m (or n) at one k and stores
-// them into 8 LDS rows.  In LDS every operand is 128 rows (the tile's m or n) of 32 k,
-// rows padded from 64 to 80 bytes so that the MFMA fragment reads (32 rows x 16 bytes) hit
-// distinct banks.
+// (wgrad: A and B, k being the row index) have k as the slow index.  Two kernels:
 //
-// Tiles are 128 x 128, 256 threads in 2 x 2 waves of 64 x 64 (2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16), K in stages of 32 double-buffered through registers: stage
-// ks+1 is loaded from memory while stage ks is multiplied.  Logical tiles are dealt to the
-// XCDs in contiguous ranges (workgroup i runs on XCD i mod 8): dgrad orders them expert ->
-// n-block -> m-tile, so the m-tiles sharing a weight slice run together; wgrad expert ->
-// m-block -> n-block, so an expert's rows are read by one XCD.
+//   - the main one (namespace `wide` below): 128 x 256 tiles, direct-to-LDS loads of the
+//     operands as they lie in memory, and gfx950's transposing LDS read to form the MFMA
+//     fragments of the k-strided operands.  Used for N % 256 == 0 (and K % 32 == 0 for
+//     dgrad), with B not gathered for wgrad: every GEMM of the bf16 layer's backward.
+//   - a general one for the other shapes (N % 128 == 0, gathered B): 128 x 128 tiles whose
+//     k-strided operands are transposed on their way into LDS (a lane loads 8 consecutive m
+//     or n at one k and stores them into 8 LDS rows; rows padded from 64 to 80 bytes so that
+//     the fragment reads hit distinct banks), K in stages of 32 double-buffered through
+//     registers.
+//
+// Both deal logical tiles to the XCDs in contiguous ranges (workgroup i runs on XCD i mod
+// 8): dgrad orders them expert -> n-block -> m-tile, so the m-tiles sharing a weight slice run
+// together; wgrad expert -> m-block -> n-block, so an expert's rows are read by one XCD.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
