@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--train", action="store_true",
                    help="time a training step instead: the forward, then the backward pass for a fixed "
                         "upstream gradient (bf16 layers; weight gradients in bf16)")
+    p.add_argument("--graph", action="store_true",
+                   help="also capture one step in a HIP graph and time its replays; value is then the "
+                        "replayed throughput (the per-kernel figures stay those of the eager steps)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -284,6 +287,33 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = cfg.N / (ms_per_step / 1e3)
 
+    graph = None
+    if args.graph:
+        # one step captured in a HIP graph (the library allocates, clears and synchronises
+        # nothing inside a call), replayed `steps` times between synchronisations
+        if side is not None:
+            raise SystemExit("--graph runs the layer on one stream (no --overlap)")
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph = {"ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(ms_per_step, 4)}
+        ms_per_step = graph_ms
+        value = cfg.N / (ms_per_step / 1e3)
+
     if layer.gather:
         # the layer folds the permute into gate/up; the permute kernel (the standalone
         # moe_permute, same rows) is timed on its own after the layer, outside `value`
@@ -391,6 +421,7 @@ def main():
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,
         "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+        "hip_graph": graph,
     }
     if args.train:
         fwd_names = [n for n, _ in stages[:len(stages) - len(layer.backward_steps(x, dy))]]

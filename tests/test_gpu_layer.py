@@ -313,3 +313,37 @@ def test_layer_full_size_sampled(name):
     say(f"  y on tokens {toks.tolist()}: max per-token relative error {err:.3e}")
     assert err <= Y_BAR[cfg.dtype]
     assert err <= Y_EXPECT[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv3_small"])
+def test_layer_forward_graph_replay(name):
+    """A whole forward (router logits through combine) captured in a HIP graph: the library
+    allocates, clears and synchronises nothing inside a call, so every replay equals the eager
+    forward bit for bit, with eager work on the same buffers between the replays."""
+    cfg = SMALL[name]
+    say(f"graph replay {name}")
+    inp = w.make_layer_inputs(cfg, DEV)
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"], w_r=inp["w_r"])
+    x = inp["x"]
+    ref = layer.forward(x).clone()
+    view = torch.int32 if cfg.dtype == "f32" else torch.int16
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x)
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x)
+    for _ in range(3):
+        layer.y.zero_()
+        layer.topk_idx.fill_(-1)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(layer.y.view(view), ref.view(view))
+        eager = layer.forward(x)   # eager work between the replays
+        sync()
+        assert torch.equal(eager.view(view), ref.view(view))
