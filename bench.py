@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--train", action="store_true",
                    help="time a training step instead: the forward, then the backward pass for a fixed "
                         "upstream gradient (bf16 layers; weight gradients in bf16)")
+    p.add_argument("--overlap-backward", action="store_true",
+                   help="--train: run the shared expert's backward on a second stream beside the routed "
+                        "backward (the backward is then one timed stage)")
     p.add_argument("--graph", action="store_true",
                    help="also capture one step in a HIP graph and time its replays; value is then the "
                         "replayed throughput (the per-kernel figures stay those of the eager steps)")
@@ -233,7 +236,11 @@ def main():
                              std=1.0)
         # the training forward keeps the gate/up pre-activations for the backward
         layer.forward(x, save_for_backward=True)
-        stages += layer.backward_steps(x, dy)
+        if args.overlap_backward:
+            layer.backward_steps(x, dy)   # (allocates the gradients)
+            stages.append(("backward", lambda: layer.backward(x, dy, overlap_shared=True)))
+        else:
+            stages += layer.backward_steps(x, dy)
 
     def step(ev=None):
         """One forward; ev: per-stage (start, end) event pairs to record, or None."""
@@ -424,20 +431,24 @@ def main():
         "hip_graph": graph,
     }
     if args.train:
-        fwd_names = [n for n, _ in stages[:len(stages) - len(layer.backward_steps(x, dy))]]
+        nb = 1 if args.overlap_backward else len(layer.backward_steps(x, dy))
+        fwd_names = [n for n, _ in stages[:len(stages) - nb]]
         bwd_names = [n for n, _ in stages if n not in fwd_names]
-        slow = max((n for n in bwd_names if n in alg), key=lambda n: kernels[n]["avg_ms"])
-        a = alg[slow]
-        t = kernels[slow]["avg_ms"] * 1e-3
-        if "flops" in a and a["flops"] / PEAK_MFMA[cfg.dtype] > a["bytes"] / PEAK_HBM:
-            broof = {"bound": "mfma", "achieved": round(a["flops"] / t / 1e12, 1),
-                     "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
-        else:
-            broof = {"bound": "hbm", "achieved": round(a["bytes"] / t / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                     "unit": "GB/s"}
-        broof["frac"] = round(broof["achieved"] / broof["peak"], 4)
-        broof["traffic"] = None
-        broof["kernel"] = f"backward step '{slow}' (the slowest of the backward pass)"
+        cands = [n for n in bwd_names if n in alg]
+        broof = None
+        if cands:   # (per-step figures exist when the backward's steps are timed one by one)
+            slow = max(cands, key=lambda n: kernels[n]["avg_ms"])
+            a = alg[slow]
+            t = kernels[slow]["avg_ms"] * 1e-3
+            if "flops" in a and a["flops"] / PEAK_MFMA[cfg.dtype] > a["bytes"] / PEAK_HBM:
+                broof = {"bound": "mfma", "achieved": round(a["flops"] / t / 1e12, 1),
+                         "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
+            else:
+                broof = {"bound": "hbm", "achieved": round(a["bytes"] / t / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s"}
+            broof["frac"] = round(broof["achieved"] / broof["peak"], 4)
+            broof["traffic"] = None
+            broof["kernel"] = f"backward step '{slow}' (the slowest of the backward pass)"
         out.update({
             "metric": "MoE-layer training step tokens/s (router logits, forward and backward; bf16 weight "
                       "gradients)",

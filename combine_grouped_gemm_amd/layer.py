@@ -254,6 +254,12 @@ class MoELayer:
         b["dgrad_ws"] = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_DGRAD, max(rows, N), 0, 0, E, 0, 0), 256),
                                     dtype=torch.uint8, device=dev)
         if self.shared:
+            # (the shared expert's steps have workspaces of their own: they may run on a
+            # second stream beside the routed ones)
+            b["gemm_ws_s"] = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, N, H, I, 1, 1, MOE_BF16), 256),
+                                         dtype=torch.uint8, device=dev)
+            b["dgrad_ws_s"] = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_DGRAD, N, 0, 0, 1, 0, 0), 256),
+                                          dtype=torch.uint8, device=dev)
             b["shared_offsets"] = torch.tensor([0, N], dtype=torch.int32, device=dev)
             b["au_s"] = torch.empty((N, 2 * I), dtype=bf, device=dev)
             b["dh_s"] = torch.empty((N, I), dtype=bf, device=dev)
@@ -308,14 +314,14 @@ class MoELayer:
             so = b["shared_offsets"]
             if not saved:
                 st.append(("shared_preact", lambda: moe_expert_gate_up_preact(x, so, self.sw13, N, None, 1,
-                                                                              b["au_s"], b["gemm_ws"])))
+                                                                              b["au_s"], b["gemm_ws_s"])))
             st += [
-                ("shared_down_dgrad", lambda: moe_expert_dgrad(dy, so, self.sw2, b["dh_s"], b["dgrad_ws"])),
+                ("shared_down_dgrad", lambda: moe_expert_dgrad(dy, so, self.sw2, b["dh_s"], b["dgrad_ws_s"])),
                 ("shared_swiglu_bwd", lambda: moe_swiglu_backward(au_s, b["dh_s"], b["d_au_s"], b["h_s"])),
                 ("shared_down_wgrad", lambda: moe_expert_wgrad(dy, b["h_s"], so, dw=b["dsw2"], rows=N)),
                 ("shared_gate_up_wgrad", lambda: moe_expert_wgrad(b["d_au_s"], x, so, dw=b["dsw13"], rows=N)),
                 ("shared_gate_up_dgrad", lambda: moe_expert_dgrad(b["d_au_s"], so, self.sw13, b["dx_s"],
-                                                                  b["dgrad_ws"])),
+                                                                  b["dgrad_ws_s"])),
             ]
             rest = b["dx_s"]
         if self.w_r is not None:
@@ -331,7 +337,8 @@ class MoELayer:
         st.append(("dx", lambda: moe_combine(b["d_perm"], send_pos, None, rest_x, b["dx"], k=k)))
         return st
 
-    def backward(self, x: torch.Tensor, dy: torch.Tensor, dw_dtype: torch.dtype = torch.bfloat16) -> dict:
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, dw_dtype: torch.dtype = torch.bfloat16,
+                 overlap_shared: bool = False) -> dict:
         """Gradients of the last forward for the upstream gradient dy [N, H] (bf16).
 
         The backward mirrors the forward ("DeepSeek MoE: EP and FSDP guide": dispatch's
@@ -342,7 +349,34 @@ class MoELayer:
         and router's gradients; dx = the slots' gradients summed back to their tokens plus
         the shared expert's and the router's.  Buffers are allocated on the first call.
         Returns the dict of gradient tensors ('dx', 'dw13', 'dw2', 'dsw13', 'dsw2', 'dw_r', ...).
+        With overlap_shared the shared expert's steps (which need only x, dy and its
+        pre-activations) run on a second stream (default priority) beside the routed ones, and
+        the input-gradient sum waits for them.
         """
-        for _, f in self.backward_steps(x, dy, dw_dtype):
+        steps = self.backward_steps(x, dy, dw_dtype)
+        if not (overlap_shared and self.shared):
+            for _, f in steps:
+                f()
+            return self.grads
+        main = torch.cuda.current_stream(self.device)
+        if getattr(self, "bwd_side", None) is None:
+            self.bwd_side = torch.cuda.Stream(device=self.device)
+            self.bwd_side_done = torch.cuda.Event()
+        side = self.bwd_side
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            for name, f in steps:
+                if name.startswith("shared_"):
+                    f()
+            self.bwd_side_done.record(side)
+        for name, f in steps:
+            if name.startswith("shared_"):
+                continue
+            if name in ("router_dx", "dx") and not getattr(self, "_waited", False):
+                main.wait_event(self.bwd_side_done)   # the shared expert's dx joins here
+                self._waited = True
             f()
+        self._waited = False
+        for t in (x, dy):
+            t.record_stream(side)
         return self.grads

@@ -323,3 +323,18 @@ def test_saved_preactivations_equal_recomputed():
     assert torch.equal(au_saved.view(torch.int16), layer.grads["au"].view(torch.int16))
     for n, v in g1.items():
         assert mat_rel_err(f64(g2[n]), f64(v)) <= 1e-2, n
+
+
+def test_backward_shared_on_side_stream_equals_serial():
+    """The shared expert's backward on a second stream == all on one stream, bit for bit,
+    over several steps in a row."""
+    cfg = SMALL["dsv3_small"]
+    say("backward with the shared expert on a side stream")
+    inp, layer, dy = _layer_for_backward(cfg, save=True)
+    names = ("dx", "dw13", "dw2", "dsw13", "dsw2", "dw_r")
+    ref = {n: layer.backward(inp["x"], dy)[n].clone() for n in names}
+    for _ in range(3):
+        got = layer.backward(inp["x"], dy, overlap_shared=True)
+    sync()
+    for n in names:
+        assert torch.equal(got[n], ref[n]), n
