@@ -8,7 +8,10 @@ weights are resident in HBM before timing starts.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dsv3_bf16]
 
 Prints one JSON line.  Kernel durations come from HIP events recorded on the
-stream the kernels run on, around every call of every timed step.
+stream the kernels run on, around every call of every timed step.  `kernels` holds
+the warm figures of the back-to-back steps that `value` is taken from;
+`kernels_cold` the same stages timed again with L2 and the MALL flushed before
+each one (their GB/s then count HBM reads, not cache hits).
 """
 from __future__ import annotations
 
@@ -57,6 +60,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="also capture one step in a HIP graph and time its replays; value is then the "
                         "replayed throughput (the per-kernel figures stay those of the eager steps)")
+    p.add_argument("--cold-steps", type=int, default=5,
+                   help="extra steps timed with L2 and the 256 MB MALL flushed (1 GiB written) before "
+                        "every stage, so each stage reads its inputs from HBM (0 = skip)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -321,6 +327,35 @@ def main():
         ms_per_step = graph_ms
         value = cfg.N / (ms_per_step / 1e3)
 
+    cold = {}
+    fill_GBps = None
+    if args.cold_steps > 0:
+        # cold-cache figures: before each stage a 1 GiB write evicts L2 (4 MB per XCD) and the
+        # 256 MB MALL, so the stage reads its inputs (weights, activations) from HBM; the
+        # stages stay in order on one stream, so every stage still sees its true inputs
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush.fill_(0)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        cev_ = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for n, _ in stages} for _ in range(args.cold_steps)]
+        torch.cuda.synchronize()
+        for s in range(args.cold_steps):
+            for i, (name, f) in enumerate(stages):
+                if i == 0:
+                    fev[s][0].record(stream)
+                flush.fill_(s + i + 1)
+                if i == 0:
+                    fev[s][1].record(stream)
+                cev_[s][name][0].record(stream)
+                f()
+                cev_[s][name][1].record(stream)
+        torch.cuda.synchronize()
+        cold = {n: [cev_[s][n][0].elapsed_time(cev_[s][n][1]) for s in range(args.cold_steps)]
+                for n, _ in stages}
+        fill_GBps = round((1 << 30) / (sum(a.elapsed_time(b) for a, b in fev) / len(fev) * 1e-3) / 1e9, 1)
+        del flush
+
     if layer.gather:
         # the layer folds the permute into gate/up; the permute kernel (the standalone
         # moe_permute, same rows) is timed on its own after the layer, outside `value`
@@ -355,20 +390,25 @@ def main():
     alg["permute (standalone)"] = alg["permute"]
     if args.train:
         alg.update(algorithmic_backward(cfg, n_e))
-    kernels = {}
-    for name, times in per.items():
-        t = sorted(times)
-        avg = sum(t) / len(t)
-        k = {"avg_ms": round(avg, 4), "median_ms": round(t[len(t) // 2], 4),
-             "p99_ms": round(t[min(len(t) - 1, int(math.ceil(0.99 * len(t))) - 1)], 4)}
-        a = alg.get(name, {})
-        if "bytes" in a:
-            k["GB_per_s"] = round(a["bytes"] / (avg * 1e-3) / 1e9, 1)
-            k["hbm_frac"] = round(a["bytes"] / (avg * 1e-3) / PEAK_HBM, 4)
-        if "flops" in a:
-            k["TFLOP_per_s"] = round(a["flops"] / (avg * 1e-3) / 1e12, 1)
-            k["mfma_frac"] = round(a["flops"] / (avg * 1e-3) / PEAK_MFMA[cfg.dtype], 4)
-        kernels[name] = k
+    def summary(per):
+        kernels = {}
+        for name, times in per.items():
+            t = sorted(times)
+            avg = sum(t) / len(t)
+            k = {"avg_ms": round(avg, 4), "median_ms": round(t[len(t) // 2], 4),
+                 "p99_ms": round(t[min(len(t) - 1, int(math.ceil(0.99 * len(t))) - 1)], 4)}
+            a = alg.get(name, {})
+            if "bytes" in a:
+                k["GB_per_s"] = round(a["bytes"] / (avg * 1e-3) / 1e9, 1)
+                k["hbm_frac"] = round(a["bytes"] / (avg * 1e-3) / PEAK_HBM, 4)
+            if "flops" in a:
+                k["TFLOP_per_s"] = round(a["flops"] / (avg * 1e-3) / 1e12, 1)
+                k["mfma_frac"] = round(a["flops"] / (avg * 1e-3) / PEAK_MFMA[cfg.dtype], 4)
+            kernels[name] = k
+        return kernels
+
+    kernels = summary(per)
+    kernels_cold = summary(cold) if cold else None
 
     g = alg["gate_up"]
     g_avg = sum(per["gate_up"]) / len(per["gate_up"]) * 1e-3
@@ -427,6 +467,9 @@ def main():
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,
+        "device_fill_GBps": fill_GBps,
+        "kernels_cold": kernels_cold,
+        "cold_steps": args.cold_steps,
         "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
         "hip_graph": graph,
     }
