@@ -278,24 +278,53 @@ __device__ __forceinline__ int kc_key(int r) { return (r >> 2) & 3; }
 // k-rows of the strided operands: chunk c of k-row r in slot c ^ 4 (r & 3)
 __device__ __forceinline__ int mc_key(int k) { return 4 * (k & 3); }
 
-__device__ __attribute__((aligned(16))) uint8_t g_zero_page[256 * 2];
+// A buffer resource over `bytes` bytes from `base` (raw, stride 0): a load whose offset lies
+// past the end returns zeros instead of touching memory.
+__device__ __forceinline__ u32x4_t buffer_window(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from byte `voff` of a buffer window into LDS at lds_base + 16 * lane
+// (zeros for offsets past the window).  Inline assembly, like dma16, so that the compiler
+// adds no wait of its own before later LDS reads; M0 holds the LDS base, one wait state
+// after its write.
+__device__ __forceinline__ void dma16_window(u32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+  __asm__ volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
+      : "memory", "m0");
+}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-// MFMA fragment of a k-strided operand: column `col0 + l % 32` of the tile, k-rows 16 s +
-// 8 (l / 32) + 0..7, from a slot whose k-rows are `pitch` bytes long
-__device__ __forceinline__ uint4 tr_frag(uint32_t base, int pitch, int s, int col0, int lane) {
+// Byte offset, inside a slot whose k-rows are `pitch` bytes long, of lane `lane`'s first
+// transposing read for the MFMA fragment of tile columns col0 .. col0 + 31 at k-rows 0 .. 15:
+// in each 16-lane group lane i reads 8 bytes (4 columns) of k-row 8 (g / 2) + i / 4.  The
+// swizzle key of a k-row depends on k mod 4 only, so k-rows 16 s + 4 r further are the same
+// offset plus (16 s + 4 r) pitch.
+__device__ __forceinline__ uint32_t tr_off(int pitch, int col0, int lane) {
   const int g = lane >> 4, i = lane & 15;
+  const int row = 8 * (g >> 1) + (i >> 2);
+  const int byte = (col0 + 16 * (g & 1) + 4 * (i & 3)) * 2;
+  return static_cast<uint32_t>(row * pitch + ((((byte >> 4) ^ mc_key(row)) << 4) | (byte & 15)));
+}
+
+// MFMA fragment of a k-strided operand: two transposing reads at the lane's tr_off address
+// (absolute LDS byte address `addr`), k-rows 16 s + 0..3 and 16 s + 4..7 of each group;
+// lane l ends up with column col0 + l % 32, k-rows 16 s + 8 (l / 32) + 0..7
+template <int kPitchBytes>
+__device__ __forceinline__ uint4 tr_frag_at(uint32_t addr, int s) {
   uint2 h[2];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = 16 * s + 8 * (g >> 1) + 4 * r + (i >> 2);
-    const int byte = (col0 + 16 * (g & 1) + 4 * (i & 3)) * 2;
-    const uint32_t a = base + row * pitch + ((((byte >> 4) ^ mc_key(row)) << 4) | (byte & 15));
-    h[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                         reinterpret_cast<lds_v4i16*>(static_cast<uintptr_t>(a))));
-  }
+  for (int r = 0; r < 2; ++r)
+    h[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(
+                                         static_cast<uintptr_t>(addr + (16 * s + 4 * r) * kPitchBytes))));
   return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
 }
 
@@ -354,44 +383,67 @@ __global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm
   }
   const int nk = (kcount + kKS - 1) / kKS;
 
-  // ---- loads of stage ks into ring slot sl: op j < kAOps fills A's 1 KB group wave +
-  // kWaves j, op kAOps + j fills B's group wave + kWaves j
-  auto issue = [&](int ks, int sl, int j) __attribute__((always_inline)) {
-    const int k0 = ks * kKS;
-    const uint8_t* src;
-    uint32_t dst;
-    if (j < kAOps) {
-      const int g = wave + kWaves * j;
-      dst = lds0 + sl * kStage + g * 1024;
-      if (MODE == BWD_DGRAD) {   // 16 rows of 64 bytes
-        int r = 16 * g + (lane >> 2);
-        const int c = (lane & 3) ^ kc_key(r);
-        r = r < mcount ? r : mcount - 1;
-        src = reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(m0 + r) * p.K + k0) * 2 + c * 16;
-      } else {                   // 1024 / (2 TM) k-rows of 2 TM bytes
-        constexpr int kPer = 1024 / (2 * TM), kCh = 2 * TM / 16;
-        const int kr = kPer * g + lane / kCh;
-        const int c = (lane % kCh) ^ mc_key(kr);
-        src = k0 + kr < kcount
-                  ? reinterpret_cast<const uint8_t*>(p.a) + (static_cast<size_t>(klo + k0 + kr) * p.M + m0) * 2 + c * 16
-                  : g_zero_page + c * 16;
-      }
-    } else {                     // 2 k-rows of 512 bytes (256 n)
-      const int g = wave + kWaves * (j - kAOps);
-      dst = lds0 + sl * kStage + kABytes + g * 1024;
-      const int kr = 2 * g + (lane >> 5);
-      const int c = (lane & 31) ^ mc_key(kr);
-      size_t row;
-      if (MODE == BWD_DGRAD) {
-        row = static_cast<size_t>(e) * p.K + k0 + kr;
-      } else {
-        const int kk = k0 + kr < kcount ? k0 + kr : kcount - 1;
-        row = static_cast<size_t>(klo + kk);
-      }
-      src = reinterpret_cast<const uint8_t*>(p.b) + (row * p.N + n0) * 2 + c * 16;
+  // ---- loads.  Stage ks covers k-rows k0 = ks kKS .. k0 + 31 of both operands, each read
+  // through a buffer window that starts at the stage's first element and ends after the
+  // last valid row, so rows past the data (wgrad: past the segment; dgrad: tile rows past
+  // mcount) load zeros.  Op j of a wave fills its operand's 1 KB group wave + kWaves j; the
+  // lane's byte offset inside the window is fixed for the tile.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t voff_a[kAOps], voff_b[C::kBOps];
+#pragma unroll
+  for (int j = 0; j < kAOps; ++j) {
+    const int g = wave + kWaves * j;
+    if (MODE == BWD_DGRAD) {   // 16 rows of 64 bytes
+      const int r = 16 * g + (lane >> 2);
+      const int c = (lane & 3) ^ kc_key(r);
+      voff_a[j] = static_cast<uint32_t>(r * p.K * 2 + c * 16);
+    } else {                   // 1024 / (2 TM) k-rows of 2 TM bytes
+      constexpr int kPer = 1024 / (2 * TM), kCh = 2 * TM / 16;
+      const int kr = kPer * g + lane / kCh;
+      const int c = (lane % kCh) ^ mc_key(kr);
+      voff_a[j] = static_cast<uint32_t>(kr * p.M * 2 + c * 16);
     }
-    dma16(src, __builtin_amdgcn_readfirstlane(dst));
+  }
+#pragma unroll
+  for (int j = 0; j < C::kBOps; ++j) {   // 2 k-rows of 512 bytes (256 n)
+    const int kr = 2 * (wave + kWaves * j) + (lane >> 5);
+    const int c = (lane & 31) ^ mc_key(kr);
+    voff_b[j] = static_cast<uint32_t>(kr * p.N * 2 + c * 16);
+  }
+  auto windows = [&](int ks, u32x4_t& wa, u32x4_t& wb) __attribute__((always_inline)) {
+    const int k0 = ks * kKS;
+    if (MODE == BWD_DGRAD) {
+      wa = buffer_window(p.a + (static_cast<size_t>(m0) * p.K + k0),
+                         static_cast<uint32_t>(mcount - 1) * p.K * 2 + 2 * kKS);
+      wb = buffer_window(p.b + ((static_cast<size_t>(e) * p.K + k0) * p.N + n0),
+                         static_cast<uint32_t>(kKS - 1) * p.N * 2 + 2 * kTN);
+    } else {
+      const int left = kcount - k0 < kKS ? kcount - k0 : kKS;
+      wa = buffer_window(p.a + (static_cast<size_t>(klo + k0) * p.M + m0),
+                         static_cast<uint32_t>(left - 1) * p.M * 2 + 2 * TM);
+      wb = buffer_window(p.b + (static_cast<size_t>(klo + k0) * p.N + n0),
+                         static_cast<uint32_t>(left - 1) * p.N * 2 + 2 * kTN);
+    }
   };
+  auto issue = [&](const u32x4_t& wa, const u32x4_t& wb, int sl, int j) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + sl * kStage;
+    if (j < kAOps) dma16_window(wa, voff_a[j], base + (wave_u + kWaves * j) * 1024);
+    else dma16_window(wb, voff_b[j - kAOps], base + kABytes + (wave_u + kWaves * (j - kAOps)) * 1024);
+  };
+
+  // ---- fragment reads: per-lane byte offsets inside a slot, fixed for the tile
+  uint32_t fo_a[2], fo_b[4];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (MODE == BWD_DGRAD) {   // x = s: row wm 64 + l % 32 (+ 32 i), 16-byte chunk 2 s + l / 32
+      const int row = wm * 64 + (lane & 31);
+      fo_a[x] = static_cast<uint32_t>(row * (2 * kKS) + (((2 * x + (lane >> 5)) ^ kc_key(row)) << 4));
+    } else {                   // x = i: columns wm 64 + 32 i
+      fo_a[x] = tr_off(TM * 2, wm * 64 + x * 32, lane);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fo_b[j] = kABytes + tr_off(kTN * 2, wn * 128 + j * 32, lane);
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -400,39 +452,45 @@ __global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   if (nk > 0) {
+    u32x4_t wa, wb;
+    windows(0, wa, wb);
 #pragma unroll
-    for (int j = 0; j < kOps; ++j) issue(0, 0, j);
+    for (int j = 0; j < kOps; ++j) issue(wa, wb, 0, j);
     if (nk > 1) {
+      windows(1, wa, wb);
 #pragma unroll
-      for (int j = 0; j < kOps; ++j) issue(1, 1, j);
+      for (int j = 0; j < kOps; ++j) issue(wa, wb, 1, j);
       wait_vmcnt<kOps>();
     } else {
       wait_vmcnt<0>();
     }
     block_barrier();
+    int sl = 0, sl2 = 2;   // ring slots of stages ks and ks + 2
     for (int ks = 0; ks < nk; ++ks) {
-      const int sl = ks % kSlots;
-      const uint32_t abase = lds0 + sl * kStage, bbase = abase + kABytes;
       if (ks + 2 < nk) {
-        const int sl2 = (ks + 2) % kSlots;
+        windows(ks + 2, wa, wb);
 #pragma unroll
-        for (int j = 0; j < kOps; ++j) issue(ks + 2, sl2, j);
+        for (int j = 0; j < kOps; ++j) issue(wa, wb, sl2, j);
       }
+      const uint32_t sbase = lds0 + sl * kStage;
+      uint32_t ra[2], rb[4];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) ra[x] = sbase + fo_a[x];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rb[j] = sbase + fo_b[j];
 #pragma unroll
       for (int s = 0; s < kKS / 16; ++s) {
         uint4 fa[2], fb[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          if (MODE == BWD_DGRAD) {
-            const int row = wm * 64 + i * 32 + (lane & 31);
-            const int c = (2 * s + (lane >> 5)) ^ kc_key(row);
-            fa[i] = *reinterpret_cast<const uint4*>(lds + (abase - lds0) + row * (2 * kKS) + c * 16);
-          } else {
-            fa[i] = tr_frag(abase, TM * 2, s, wm * 64 + i * 32, lane);
-          }
+          if (MODE == BWD_DGRAD)
+            fa[i] = __builtin_bit_cast(
+                uint4, *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(ra[s] + i * 32 * (2 * kKS))));
+          else
+            fa[i] = tr_frag_at<TM * 2>(ra[i], s);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = tr_frag(bbase, kTN * 2, s, wn * 128 + j * 32, lane);
+        for (int j = 0; j < 4; ++j) fb[j] = tr_frag_at<kTN * 2>(rb[j], s);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -444,13 +502,17 @@ __global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm
         else wait_vmcnt<0>();
         block_barrier();
       }
+      sl = sl + 1 == kSlots ? 0 : sl + 1;
+      sl2 = sl2 + 1 == kSlots ? 0 : sl2 + 1;
     }
   }
 
   // ---- epilogue: lane l holds tile row wm*64 + i*32 + l % 32 and, in registers 4q .. 4q+3
   // of block j, columns wn*128 + j*32 + 8q + 4 (l / 32) + 0..3.  bf16 tiles go through LDS
-  // 128 rows at a time (16-byte chunk c of row r in slot c ^ (r % 32)), so that each store
-  // instruction writes whole 512-byte rows; fp32 tiles are stored from the registers.
+  // 128 rows at a time (16-byte chunk c of row r in slot c ^ (r % 32), its two 8-byte halves
+  // swapped when r % 32 >= 16, so that the 32 rows one write instruction covers hit distinct
+  // banks), and each store instruction writes whole 512-byte rows; fp32 tiles are stored
+  // from the registers.
   const bool staged = MODE == BWD_DGRAD || !p.out_f32;
   if (staged) {
     static_assert(128 * kTN * 2 <= kSlots * kStage, "128 rows of a bf16 tile fit the ring");
@@ -470,8 +532,9 @@ __global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm
             for (int q = 0; q < 4; ++q) {
               const int col = wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
               const int chunk = (col >> 3) ^ (r & 31);
+              const int half = ((col & 7) >> 2) ^ ((r >> 4) & 1);
               const f32x16_t& a = acc[i][j];
-              *reinterpret_cast<uint2*>(lds + r * (kTN * 2) + chunk * 16 + (col & 7) * 2) =
+              *reinterpret_cast<uint2*>(lds + r * (kTN * 2) + chunk * 16 + half * 8) =
                   make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
             }
         }
@@ -484,7 +547,8 @@ __global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm
         const int r = c >> 5, chunk = c & 31;
         const int rt = half * 128 + r;   // row within the tile
         if (MODE == BWD_DGRAD && rt >= mcount) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (kTN * 2) + ((chunk ^ (r & 31)) << 4));
+        uint4 v = *reinterpret_cast<const uint4*>(lds + r * (kTN * 2) + ((chunk ^ (r & 31)) << 4));
+        if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
         *reinterpret_cast<uint4*>(out + (row0 + rt) * p.N + n0 + chunk * 8) = v;
       }
     }
