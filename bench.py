@@ -83,7 +83,7 @@ def source_sha(*paths):
 # sources of the dominant kernel (the routed gate/up GEMM): a stored traffic figure is used
 # only while they are unchanged since its counters were taken
 GEMM_SOURCES = [os.path.join(ROOT, "combine_grouped_gemm_amd", "csrc", n)
-                for n in ("grouped_gemm_wide.hip", "gemm_device.h")]
+                for n in ("grouped_gemm_wide.hip", "gemm_device.h", "moe_common.h")]
 
 
 def algorithmic(cfg, n_e, gather=False, fused=False):

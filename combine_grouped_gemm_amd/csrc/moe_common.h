@@ -18,16 +18,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// fp32 -> bf16 with round-to-nearest-even, on gfx950's v_cvt_pk_bf16_f32 (one instruction
+// for two values; NaN stays NaN).
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_cvt_t{lo, hi}, bf16x2_cvt_t));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
 // OCP e4m3fn encode of a finite fp32 value: round to nearest even, saturate to +-448.
