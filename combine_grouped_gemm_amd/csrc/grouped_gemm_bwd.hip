@@ -541,15 +541,31 @@ __global__ __launch_bounds__(Cfg<TM>::kThreads, Cfg<TM>::kOcc) void grouped_gemm
       }
       wait_lgkmcnt_all();
       block_barrier();
+      // each thread takes 16-byte chunk tid % 32 of rows kRpt t + tid / 32: all its LDS reads
+      // first (the chunk's slot is (tid % 32) ^ (row % 32), and row % 32 = (kRpt t) % 32 +
+      // tid / 32, so a few per-lane bases serve every t), then the stores; weight gradients
+      // are not read again by the step, so they bypass the caches (non-temporal stores)
+      constexpr int kT = 128 * kTN * 2 / 16 / kThreads;
+      constexpr int kRpt = kThreads / 32;
+      const int w = tid >> 5, ch = tid & 31;
+      uint32_t rbase[32 / kRpt];
 #pragma unroll
-      for (int t = 0; t < 128 * kTN * 2 / 16 / kThreads; ++t) {
-        const int c = t * kThreads + tid;
-        const int r = c >> 5, chunk = c & 31;
-        const int rt = half * 128 + r;   // row within the tile
-        if (MODE == BWD_DGRAD && rt >= mcount) continue;
-        uint4 v = *reinterpret_cast<const uint4*>(lds + r * (kTN * 2) + ((chunk ^ (r & 31)) << 4));
-        if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-        *reinterpret_cast<uint4*>(out + (row0 + rt) * p.N + n0 + chunk * 8) = v;
+      for (int q = 0; q < 32 / kRpt; ++q)
+        rbase[q] = lds0 + static_cast<uint32_t>(w * (kTN * 2) + (((ch ^ w) ^ (q * kRpt)) << 4));
+      uint4 v[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+        v[t] = __builtin_bit_cast(uint4, *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(
+                                             rbase[((t * kRpt) & 31) / kRpt] + t * kRpt * (kTN * 2))));
+      uint16_t* o = out + (row0 + half * 128 + w) * p.N + n0 + ch * 8;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        if (MODE == BWD_DGRAD && half * 128 + kRpt * t + w >= mcount) continue;
+        uint4 x = v[t];
+        if (((t * kRpt) >> 4) & 1) x = make_uint4(x.z, x.w, x.x, x.y);   // the row's halves were swapped
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(o + static_cast<size_t>(t) * kRpt * p.N);
+        if (MODE == BWD_WGRAD) __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, x), dst);
+        else *dst = __builtin_bit_cast(u32x4_t, x);
       }
     }
   } else {
