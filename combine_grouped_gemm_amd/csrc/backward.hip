@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const uint16_t* __
     Vec<false>::load(dh, static_cast<size_t>(r) * cpr + c, d);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float sg = 1.0f / (1.0f + expf(-a[q]));
+      const float sg = sigmoid_f32(a[q]);
       da[q] = d[q] * u[q] * sg * (1.0f + a[q] * (1.0f - sg));
       du[q] = d[q] * a[q] * sg;
       hv[q] = a[q] * sg * u[q];

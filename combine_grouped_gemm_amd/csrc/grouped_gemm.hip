@@ -364,7 +364,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
           for (int nb = 0; nb < 2; ++nb) {
             const float g = acc[mb][nb][v];
             const float u = acc[mb][nb + 2][v];
-            const float hv = g / (1.0f + expf(-g)) * u;
+            const float hv = silu_f32(g) * u;
             const size_t o = static_cast<size_t>(r) * p.I + static_cast<size_t>(nblk) * (GBN / 2) + wn * 64 +
                              nb * 32 + (lane & 31);
             if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = hv;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(WM * WN * 64, MOE_DMA_OCC) void grouped_gemm_dma_ke
             if (col >= n_cols) continue;
             const float g = acc[mb][nb][v];
             const float u = acc[mb][nb + NB / 2][v];
-            const float hv = g / (1.0f + expf(-g)) * u;
+            const float hv = silu_f32(g) * u;
             reinterpret_cast<uint16_t*>(p.out)[static_cast<size_t>(r) * p.I + col] = f32_to_bf16(hv);
           }
         } else {

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
           for (int cb = 0; cb < 4; ++cb) {
             const float g = acc[cb][v];
             const float u = acc[cb + 4][v];
-            hrow[16 * cb] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+            hrow[16 * cb] = f32_to_bf16(silu_f32(g) * u);
           }
         } else if (p.out_f32) {
           float* orow = reinterpret_cast<float*>(p.out) + static_cast<size_t>(r) * p.n_out + t.row0 + c;

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
             for (int u = 0; u < 4; ++u) {
               const float g = acc[mb][nb][4 * q + u];
               const float up = acc[mb][nb + 2][4 * q + u];
-              hv[u] = g / (1.0f + expf(-g)) * up;
+              hv[u] = silu_f32(g) * up;
             }
             if (p.au != nullptr) {   // the pre-activations, for the backward pass
               const f32x16_t& ga = acc[mb][nb];

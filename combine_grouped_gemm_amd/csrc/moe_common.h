@@ -31,6 +31,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
+// logistic sigmoid 1 / (1 + e^-x), written as 1 / (1 + 2^(-x log2 e)) on the hardware
+// exp2 and reciprocal (each within about 1 ulp of fp32); SwiGLU's gate is silu(x) = x sigmoid(x)
+__device__ __forceinline__ float sigmoid_f32(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+__device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
+
 // OCP e4m3fn encode of a finite fp32 value: round to nearest even, saturate to +-448.
 // Normal range (|v| >= 2^-6): keep the 3 leading fraction bits of the fp32 significand
 // and round on the 20 dropped bits; a carry propagates into the exponent field.
