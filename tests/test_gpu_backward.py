@@ -178,6 +178,37 @@ def test_expert_wgrad(case):
     assert not got[list(empty)].any() if empty else True
 
 
+def test_expert_wgrad_chunked_deal_skewed():
+    """A weight-gradient launch of 2048 tiles (32 experts x 4 x 16 tiles of 128 x 256), large
+    enough that tiles go to the XCDs in chunks of 32, with one hot expert (~80% of the
+    tokens), an empty expert and ragged row counts: every expert's gradient within the fp32
+    sum bound plus one bf16 rounding."""
+    say("wgrad chunked deal, skewed")
+    N, k, E, M, Nout = 600, 2, 32, 512, 4096
+    rng = np.random.default_rng(31)
+    idx = np.zeros((N, k), np.int64)
+    for t in range(N):
+        first = 0 if rng.random() < 0.8 else int(rng.choice([c for c in range(1, E) if c != 5]))
+        pool = [c for c in range(E) if c != first and c != 5]
+        idx[t] = [first, pool[int(rng.integers(len(pool)))]]
+    n_e, off, sp, ss = oracle.dispatch_layout(idx, E)
+    assert n_e[5] == 0 and n_e[0] > 400
+    doff = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    rows = N * k
+    A = _n((rows, M), 16)
+    B = _n((rows, Nout), 17)
+    dw = moe.moe_expert_wgrad(A, B, doff, dw_dtype=torch.bfloat16)
+    sync()
+    got = f64(dw)
+    Af, Bf = f64(A), f64(B)
+    for e in range(E):
+        a, b = Af[off[e]:off[e + 1]], Bf[off[e]:off[e + 1]]
+        ref = a.T @ b
+        bound = 2 * (len(a) + 1) * U32 * (np.abs(a).T @ np.abs(b)) + bf16_ulp(ref)
+        assert np.all(np.abs(got[e] - ref) <= bound + 1e-30), f"expert {e} (n_e {n_e[e]})"
+    assert not got[5].any()
+
+
 def test_router_backward():
     N, H, E, k = 500, 256, 32, 6
     say("router backward")
