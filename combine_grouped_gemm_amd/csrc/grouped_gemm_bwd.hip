@@ -636,7 +636,9 @@ hipError_t launch_expert_dgrad(const void* dC, const int32_t* offsets, int E, in
   p.K = K;
   p.b_div = 1;
   const dim3 wgrid(grid_for(static_cast<long long>(cap) * (N / wide::kTN)));
-  if (N % wide::kTN == 0 && K % wide::kKS == 0)
+  // (the tile kernel's per-lane window offsets are 32-bit: up to 128 rows of K and 32 k-rows
+  // of N elements)
+  if (N % wide::kTN == 0 && K % wide::kKS == 0 && K <= (1 << 22) && N <= (1 << 22))
     hipLaunchKernelGGL((wide::grouped_gemm_bwd_wide_kernel<BWD_DGRAD, 128>), wgrid, dim3(wide::Cfg<128>::kThreads), 0,
                        s, p);
   else
@@ -665,7 +667,7 @@ hipError_t launch_expert_wgrad(const void* a, const void* b, const int32_t* b_ro
   // DeepSeek-V3 weight gradients: with ~256 rows of K per expert a tile is 8 stages, and a
   // second workgroup on the CU hides one tile's first loads and last stores behind the
   // other's multiplies)
-  if (b_rows == nullptr && N % wide::kTN == 0) {
+  if (b_rows == nullptr && N % wide::kTN == 0 && M <= (1 << 22) && N <= (1 << 22)) {
     const long long tiles = static_cast<long long>(E) * (M / 128) * (N / wide::kTN);
     // chunks of 32 tiles dealt round-robin to the XCDs once each XCD gets 8 or more chunks
     // (the DeepSeek-V3 weight gradients under a Zipf skew: dW13 11.3 -> 6.5 ms; uniform
