@@ -247,8 +247,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void grouped_gemm_bwd_kernel(BwdArg
 // v_mfma_f32_32x32x16_bf16, the n-operand first, so a lane's accumulators hold one tile row
 // and runs of 4 adjacent columns).  While stage ks is multiplied, stage ks+2 is loaded into
 // the slot stage ks-1 used; at the end of stage ks each wave waits for its loads of stage
-// ks+1 and the workgroup synchronises.  wgrad rows past an expert's segment read a zero page
-// for the A operand (their B rows are clamped into the segment), so they add nothing.
+// ks+1 and the workgroup synchronises.  Each stage of each operand is read through a buffer
+// window ending after the stage's last valid row, so wgrad rows past an expert's segment
+// (and dgrad tile rows past the segment) load zeros and add nothing.
 // ------------------------------------------------------------------------------------
 namespace wide {
 
