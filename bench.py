@@ -385,6 +385,21 @@ def main():
     copy_GBps = round(2 * 5 * (1 << 30) / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9, 1)
     del csrc, cdst
 
+    # the machine's achievable dense bf16 matrix rate on this machine (context for the MFMA
+    # fractions): torch's library GEMM on 8192^3, flops over its event time
+    ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        gc = ga @ gb
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    gev[0].record(stream)
+    for _ in range(5):
+        gc = ga @ gb
+    gev[1].record(stream)
+    torch.cuda.synchronize()
+    gemm_TFLOPs = round(2.0 * 8192 ** 3 * 5 / (gev[0].elapsed_time(gev[1]) * 1e-3) / 1e12, 1)
+    del ga, gb, gc
+
     n_e = layer.layout[0].cpu().numpy()
     alg = algorithmic(cfg, n_e, layer.gather, layer.fuse)
     alg["permute (standalone)"] = alg["permute"]
@@ -468,6 +483,7 @@ def main():
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,
         "device_fill_GBps": fill_GBps,
+        "library_bf16_gemm_TFLOPs": gemm_TFLOPs,
         "kernels_cold": kernels_cold,
         "cold_steps": args.cold_steps,
         "event_ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
