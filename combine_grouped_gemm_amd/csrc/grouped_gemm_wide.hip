@@ -335,17 +335,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     // registers 4q .. 4q+3 of block nb, output columns nb * 32 + 8q + 4 (l / 32) + 0..3:
     // one 8-byte store per run (16 bytes for fp32 router sums; n_cols % 4 == 0, so a run is
     // all in or all out)
+    // down with gates: a routed row carries the gate of its slot (the shared rows gate 1).
+    // The gates are loaded first and waited for once: a load pending across the stores'
+    // row and column branches would make the compiler wait for every store before the next.
+    float gsv[kMB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
+      gsv[mb] = 1.0f;
+      if (MODE == MODE_DOWN && p.row_gate != nullptr && r < p.rows && r < t.mend) {
+        int sl = p.row_slot[r];
+        sl = sl < 0 ? 0 : (sl < p.rows ? sl : p.rows - 1);
+        gsv[mb] = p.row_gate[sl];
+      }
+    }
+    if (MODE == MODE_DOWN) wait_vmcnt<0>();
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
       if (r >= t.mend) continue;
-      // down with gates: a routed row carries the gate of its slot (the shared rows gate 1)
-      float gs = 1.0f;
-      if (MODE == MODE_DOWN && p.row_gate != nullptr && r < p.rows) {
-        int sl = p.row_slot[r];
-        sl = sl < 0 ? 0 : (sl < p.rows ? sl : p.rows - 1);
-        gs = p.row_gate[sl];
-      }
+      const float gs = gsv[mb];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (MODE == MODE_GATE_UP) {
