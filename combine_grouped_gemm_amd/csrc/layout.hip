@@ -54,11 +54,19 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
   const int e = threadIdx.x;
   int32_t run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      int32_t* p = counts + static_cast<size_t>(c) * E + e;
-      const int32_t v = *p;
-      *p = run;
-      run += v;
+    // 16 chunks' counts loaded before any is replaced by its exclusive prefix, so the loads
+    // are in flight together instead of one latency per chunk
+    constexpr int kBatch = 16;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int32_t v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < nchunks ? counts[static_cast<size_t>(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (c0 + j < nchunks) counts[static_cast<size_t>(c0 + j) * E + e] = run;
+        run += v[j];
+      }
     }
     n_e[e] = run;
   }
