@@ -14,6 +14,7 @@ import workload as w
 from combine_grouped_gemm_amd.layer import MoELayer
 from oracle import moe_oracle as oracle
 from tests.gpu_util import bf16_ulp, f64, say, sync, token_rel_err, with_logits
+from tests.test_gpu_layer import sampled_experts
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -290,14 +291,22 @@ def test_layer_backward_small(name, save):
 
 
 def test_layer_backward_full_size_sampled():
-    """DeepSeek-V3 size: the weight gradients of three experts (largest, smallest non-empty,
-    middle) and the input gradient of four tokens, each from the oracle on that expert's rows
-    or that token alone."""
+    """DeepSeek-V3 size: every gradient buffer starts as NaN and must be finite afterwards (no
+    row or expert left unwritten); the weight gradients of experts spread over the tile order
+    (and the largest, the smallest non-empty and split ones) and the input gradient of 16
+    tokens, each from the oracle on that expert's rows or that token alone."""
     cfg = w.CONFIGS["dsv3_bf16"]
     say("layer backward dsv3_bf16 full size")
     inp, layer, dy = _layer_for_backward(cfg, save=True)
+    layer.backward_steps(inp["x"], dy)   # (allocates the gradient buffers)
+    outs = ("d_eo", "dg", "dh", "d_au", "h", "d_perm", "x_perm", "dw13", "dw2", "dh_s", "d_au_s", "h_s",
+            "dx_s", "dsw13", "dsw2", "dz", "dw_r", "dx_r", "dx")
+    for n in outs:
+        layer.grads[n].fill_(float("nan"))
     gr = layer.backward(inp["x"], dy)
     sync()
+    for n in outs:
+        assert bool(torch.isfinite(gr[n]).all()), f"{n}: left unwritten"
     k = cfg.k
     n_e = layer.layout[0].cpu().numpy()
     off = layer.layout[1].cpu().numpy()
@@ -306,8 +315,7 @@ def test_layer_backward_full_size_sampled():
     gates = layer.topk_gate.cpu().numpy().astype(np.float64)
     xs = f64(inp["x"])
     dys = f64(dy)
-    nz = np.nonzero(n_e)[0]
-    experts = sorted({int(nz[np.argmax(n_e[nz])]), int(nz[np.argmin(n_e[nz])]), int(nz[len(nz) // 2])})
+    experts = sampled_experts(n_e, -(-cfg.I // 128), 8)
     for e in experts:
         slots = ss[off[e]:off[e + 1]]
         toks = slots // k
@@ -320,15 +328,15 @@ def test_layer_backward_full_size_sampled():
     # dx of sampled tokens: the slots' input gradients, the shared expert's, the router's
     w_r = f64(inp["w_r"])
     sw13, sw2 = f64(inp["sw13"][0]), f64(inp["sw2"][0])
-    for t in np.linspace(0, cfg.N - 1, 4).astype(np.int64):
+    for t in np.linspace(0, cfg.N - 1, 16).astype(np.int64):
         dx = np.zeros(cfg.H)
         dg = np.zeros(k)
         for j in range(k):
             e = int(idx[t, j])
-            _, o = oracle.expert_ffn(xs[t:t + 1], f64(inp["w13"][e]), f64(inp["w2"][e]))
+            w13e, w2e = f64(inp["w13"][e]), f64(inp["w2"][e])
+            _, o = oracle.expert_ffn(xs[t:t + 1], w13e, w2e)
             dg[j] = float(dys[t] @ o[0])
-            r = oracle.expert_ffn_backward(xs[t:t + 1], f64(inp["w13"][e]), f64(inp["w2"][e]),
-                                           gates[t, j] * dys[t:t + 1])
+            r = oracle.expert_ffn_backward(xs[t:t + 1], w13e, w2e, gates[t, j] * dys[t:t + 1])
             dx += r["d_in"][0]
         dx += oracle.expert_ffn_backward(xs[t:t + 1], sw13, sw2, dys[t:t + 1])["d_in"][0]
         dz = oracle.gates_backward(gates[t:t + 1], dg[None])[0]

@@ -1,0 +1,107 @@
+"""Grouped GEMMs sized so that every persistent workgroup runs several tiles, compared in
+full with the oracle.
+
+The bf16 expert GEMMs run one workgroup per CU (256) and hand tiles out from a counter per
+XCD, so a workgroup that finishes a tile takes the next index while its last stages run and
+loads that tile's first stages while its epilogue stores drain.  The small layer tests give
+few workgroups a second tile; here the routed segments and the shared segment make about
+four gate/up tiles and four down tiles per workgroup.  Every output row of every launch is
+compared with the oracle's expert FFN on the same rows, and every output buffer starts as
+NaN, so a tile that is skipped (or whose rows land elsewhere) cannot pass.
+
+"MoE part 4: DeepEP and GroupedGEMM", section 2: the grouped GEMM batches the expert GEMMs
+and does not change the mathematics, so each segment must equal its own dense expert FFN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_grouped_gemm_amd as moe
+import workload as w
+from oracle import moe_oracle as oracle
+from tests.gpu_util import f64, say, sync, token_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BAR = 1e-2          # per-row relative error of a bf16 GEMM output (rounding of h and of the output)
+WORKGROUPS = 256    # the persistent GEMMs' grid: one workgroup per CU
+TILE_ROWS = 256     # rows of an m-tile of the bf16 tile kernel
+
+H, I, K = 4096, 2048, 4
+CASES = {
+    # ragged experts (one split into up to five m-tiles, one of exactly 256 rows, one of 257,
+    # one empty)
+    "ragged": [420, 1260, 0, 717, 257, 896, 1078, 466, 1246, 256, 672, 840, 980, 532, 1148, 564],
+    # one expert takes every token, the others are small or empty
+    "hot": [2900, 33, 0, 300, 1, 700, 512, 31, 2900, 640, 260, 0, 900, 1333, 1050, 40],
+}
+
+
+def _tiles(seg_rows, cols_per_tile, n_cols):
+    n_blk = -(-n_cols // cols_per_tile)
+    return sum(-(-r // TILE_ROWS) for r in seg_rows) * n_blk
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_multitile_gate_up_down_every_row(case):
+    n_e = CASES[case]
+    E = len(n_e)
+    idx = w.counted_route(n_e, K, seed=5)
+    N = idx.shape[0]
+    rows = N * K
+    segs = [c for c in n_e] + [N]
+    gu_tiles = _tiles(segs, 128, I)      # gate/up: 128 h columns (256 weight rows) per tile
+    dn_tiles = _tiles(segs, 256, H)      # down: 256 output columns per tile
+    say(f"multitile {case}: N={N} rows={rows} E={E} H={H} I={I}; gate/up tiles {gu_tiles}, down tiles {dn_tiles}")
+    assert gu_tiles >= 3.5 * WORKGROUPS and dn_tiles >= 3.5 * WORKGROUPS
+
+    bf = torch.bfloat16
+    x = w.normal((N, H), w.stream_key(21, w.T_X, E), DEV, bf)
+    w13 = w.normal((E, 2 * I, H), w.stream_key(21, w.T_W13, E), DEV, bf)
+    w2 = w.normal((E, H, I), w.stream_key(21, w.T_W2, E), DEV, bf)
+    sw13 = w.normal((2 * I, H), w.stream_key(21, w.T_SW13, E), DEV, bf)
+    sw2 = w.normal((H, I), w.stream_key(21, w.T_SW2, E), DEV, bf)
+    gates = w.random_gates(N, K, seed=E).to(DEV)
+
+    ne_d, offs, sp, ss = moe.moe_dispatch_layout(idx.to(DEV), E)
+    nan = float("nan")
+    h = torch.full((rows + N, I), nan, dtype=bf, device=DEV)
+    moe.moe_expert_gate_up_gathered_shared(x, ss, K, offs, w13, sw13, h=h)
+    out = torch.full((rows + N, H), nan, dtype=bf, device=DEV)
+    moe.moe_expert_down_shared(h, offs, w2, sw2, rows, out=out)
+    out_g = torch.full((rows + N, H), nan, dtype=bf, device=DEV)
+    moe.moe_expert_down_shared(h, offs, w2, sw2, rows, out=out_g, src_slot=ss, topk_gate=gates)
+    # the routed launches without the shared segment (the layer's path without a shared expert)
+    h_r = torch.full((rows, I), nan, dtype=bf, device=DEV)
+    moe.moe_expert_gate_up_gathered(x, ss, K, offs, w13, h=h_r)
+    out_r = torch.full((rows, H), nan, dtype=bf, device=DEV)
+    moe.moe_expert_down(h_r, offs, w2, out=out_r)
+    sync()
+    for name, t in (("h", h), ("out", out), ("out_gated", out_g), ("h_routed", h_r), ("out_routed", out_r)):
+        assert bool(torch.isfinite(t).all()), f"{name}: rows left unwritten"
+
+    # the oracle's own layout of the same routes
+    ref_ne, ref_off, ref_sp, ref_ss = oracle.dispatch_layout(idx.numpy(), E)
+    assert np.array_equal(ne_d.cpu().numpy(), ref_ne) and np.array_equal(ss.cpu().numpy(), ref_ss)
+    xs = f64(x)
+    g_row = gates.cpu().numpy().astype(np.float64).reshape(-1)[ref_ss]
+    hh, oo, og, hr, orr = f64(h), f64(out), f64(out_g), f64(h_r), f64(out_r)
+    worst = 0.0
+    for e in range(E):
+        lo, hi = int(ref_off[e]), int(ref_off[e + 1])
+        if hi == lo:
+            continue
+        rh, ro = oracle.expert_ffn(xs[ref_ss[lo:hi] // K], f64(w13[e]), f64(w2[e]))
+        errs = [token_rel_err(hh[lo:hi], rh), token_rel_err(oo[lo:hi], ro),
+                token_rel_err(og[lo:hi], g_row[lo:hi, None] * ro),
+                token_rel_err(hr[lo:hi], rh), token_rel_err(orr[lo:hi], ro)]
+        worst = max(worst, max(errs))
+        assert max(errs) <= BAR, (e, errs)
+    rh, ro = oracle.expert_ffn(xs, f64(sw13), f64(sw2))
+    errs = [token_rel_err(hh[rows:], rh), token_rel_err(oo[rows:], ro), token_rel_err(og[rows:], ro)]
+    assert max(errs) <= BAR, ("shared", errs)
+    worst = max(worst, max(errs))
+    say(f"  every row of {E} segments + shared within {worst:.2e}")
+    # the routed rows do not depend on the shared segment being in the launch
+    assert torch.equal(h[:rows].view(torch.int16), h_r.view(torch.int16))
+    assert torch.equal(out[:rows].view(torch.int16), out_r.view(torch.int16))

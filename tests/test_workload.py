@@ -1,6 +1,8 @@
 """The seeded generator: device-independent definition and the workloads' distributions."""
 import math
 
+import pytest
+
 import numpy as np
 import torch
 
@@ -78,3 +80,15 @@ def test_batched_expert_generation_matches_per_expert_streams():
     b2 = w._normal_streams([w.stream_key(cfg.seed, w.T_W2, e) for e in range(5)], (256, 128), "cpu",
                            torch.bfloat16)
     assert torch.equal(a13, b13) and torch.equal(a2, b2)
+
+
+def test_counted_route_gives_the_requested_counts():
+    n_e = [5, 0, 8, 3, 8, 8]
+    idx = w.counted_route(n_e, 4, seed=3).numpy()
+    assert idx.shape == (8, 4) and idx.dtype == np.int32
+    assert all(len(set(row)) == 4 for row in idx.tolist())
+    assert np.array_equal(np.bincount(idx.reshape(-1), minlength=6), n_e)
+    with pytest.raises(ValueError):
+        w.counted_route([10, 2], 2)        # 10 rows for one expert but only 6 tokens
+    with pytest.raises(ValueError):
+        w.counted_route([3, 2], 2)         # 5 slots are not a multiple of k

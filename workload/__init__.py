@@ -316,6 +316,26 @@ def fixed_route(N: int, E: int, k: int, kind: str, seed: int = 0) -> torch.Tenso
     raise ValueError(kind)
 
 
+def counted_route(n_e, k: int, seed: int = 0) -> torch.Tensor:
+    """Routes [N, k] int32 in which expert e appears exactly n_e[e] times (distinct experts
+    per token); N = sum(n_e) / k, and every n_e[e] must be at most N.
+
+    The expert ids, listed in runs of n_e[e], are read column-wise: slot j of token t takes
+    entry j * N + t, so a token's k entries are N apart and fall in k different runs.  The
+    tokens are then shuffled by a seeded permutation.
+    """
+    n_e = [int(c) for c in n_e]
+    total = sum(n_e)
+    if total % k or any(c < 0 for c in n_e):
+        raise ValueError("sum(n_e) must be a multiple of k")
+    N = total // k
+    if any(c > N for c in n_e):
+        raise ValueError("an expert cannot take more rows than there are tokens")
+    ids = np.repeat(np.arange(len(n_e), dtype=np.int32), n_e)
+    idx = ids.reshape(k, N).T
+    return torch.from_numpy(np.ascontiguousarray(idx[random_permutation(N, stream_key(seed, T_IDX, 7))]))
+
+
 def random_gates(N: int, k: int, seed: int = 0) -> torch.Tensor:
     """Positive fp32 gates [N, k] (uniform in (0, 1]) for steps tested apart from the router."""
     bits = uniform_bits(N * k, stream_key(seed, T_GATE, k), "cpu")
