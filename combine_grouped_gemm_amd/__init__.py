@@ -20,7 +20,8 @@ __all__ = [
     "MoEError", "lib", "library_path", "declared_symbols",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
     "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM", "MOE_OP_ROUTER", "MOE_OP_EXPERT_DGRAD",
-    "moe_router_logits", "moe_route", "moe_dispatch_layout", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
+    "MOE_LAYOUT_SCRATCH_BYTES", "moe_router_logits", "moe_route", "moe_dispatch_layout",
+    "moe_dispatch_layout_noalloc", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
     "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
     "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
     "moe_version", "moe_combine_backward", "moe_expert_gate_up_preact", "moe_swiglu_backward", "moe_expert_dgrad",
@@ -33,6 +34,7 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_OP_DISPATCH_LAYOUT, MOE_OP_GROUPED_FFN, MOE_OP_EXPERT_GEMM, MOE_OP_ROUTER, MOE_OP_EXPERT_DGRAD = range(5)
+MOE_LAYOUT_SCRATCH_BYTES = 4 << 20   # the fixed count table of moe_dispatch_layout_noalloc
 
 
 class MoEError(RuntimeError):
@@ -54,6 +56,7 @@ _SIGS = {
     "moe_router_logits": [_P, _I, _I, _I, _P, _I, _P, _P, _SZ, _P],
     "moe_route": [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P],
     "moe_dispatch_layout": [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_dispatch_layout_noalloc": [_P, _I, _I, _I, _P, _P, _P, _P, _P],
     "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _I, _P, _P],
     "moe_quantize_fp8": [_P, _I, ctypes.c_int64, _I, _P, _P, _P],
     "moe_grouped_ffn": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
@@ -201,6 +204,22 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, out=None, ws: Optional[t
     _check("moe_dispatch_layout", lib().moe_dispatch_layout(
         _ptr(topk_idx), N, k, E, _ptr(n_e), _ptr(offsets), _ptr(send_pos), _ptr(src_slot),
         _ptr(ws), ws.numel(), _stream(topk_idx)))
+    return n_e, offsets, send_pos, src_slot
+
+
+def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, E: int, out=None):
+    """moe_dispatch_layout without a workspace: the counts go to the library's fixed device
+    scratch.  Returns (n_e, offsets, send_pos, src_slot) int32."""
+    N, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(N * k, dtype=torch.int32, device=dev),
+               torch.empty(N * k, dtype=torch.int32, device=dev))
+    n_e, offsets, send_pos, src_slot = out
+    _check("moe_dispatch_layout_noalloc", lib().moe_dispatch_layout_noalloc(
+        _ptr(topk_idx), N, k, E, _ptr(n_e), _ptr(offsets), _ptr(send_pos), _ptr(src_slot), _stream(topk_idx)))
     return n_e, offsets, send_pos, src_slot
 
 

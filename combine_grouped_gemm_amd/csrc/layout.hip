@@ -11,6 +11,8 @@
 //               steps of the wave) + (earlier lanes of the step).
 // LDS atomics only build counts, whose value does not depend on their order, so every
 // output is a pure function of topk_idx.
+#include <mutex>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -160,6 +162,39 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int nk, int E, int32_
                      4 * E * sizeof(int32_t), s, topk_idx, nk, E, chunk, counts, offsets, send_pos,
                      src_slot);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the per-chunk counts live in a fixed device
+// array instead of a caller's workspace.  Each device holds its own copy at its own address
+// for the life of the process.  The count launch writes every entry that the scan and the
+// scatter read, so no call needs the array cleared; calls that overlap on one device share
+// the array and race.
+// ------------------------------------------------------------------------------------
+
+constexpr size_t kScratchInts = MOE_LAYOUT_SCRATCH_BYTES / sizeof(int32_t);
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t layout_scratch(int32_t** out) {
+  // the device address of the current device's copy, looked up once per device (host code
+  // never passes the array's own name: on the host it is a stand-in, not a device address)
+  static std::mutex mu;
+  static int32_t* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe

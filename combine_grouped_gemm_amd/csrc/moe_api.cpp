@@ -133,6 +133,23 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int N, int k, int E, int
                                                 reinterpret_cast<int32_t*>(ws), stream));
 }
 
+moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int N, int k, int E, int32_t* n_e,
+                                       int32_t* offsets, int32_t* send_pos, int32_t* src_slot,
+                                       hipStream_t stream) {
+  if (N < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (topk_idx == nullptr || n_e == nullptr || offsets == nullptr || send_pos == nullptr ||
+      src_slot == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (layout_ws(N, k, E) > MOE_LAYOUT_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int32_t* counts = nullptr;
+  if (moe::layout_scratch(&counts) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_dispatch_layout(topk_idx, N * k, E, n_e, offsets, send_pos, src_slot, counts,
+                                                stream));
+}
+
 moe_status moe_permute(const void* x, moe_dtype x_dt, int N, int H, int k,
                        const int32_t* send_pos, void* x_perm, moe_dtype perm_dt, float* perm_scale,
                        hipStream_t stream) {

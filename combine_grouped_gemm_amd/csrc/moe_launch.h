@@ -16,6 +16,8 @@ int layout_num_chunks(long long nk);
 hipError_t launch_dispatch_layout(const int32_t* topk_idx, int nk, int E, int32_t* n_e,
                                   int32_t* offsets, int32_t* send_pos, int32_t* src_slot,
                                   int32_t* counts, hipStream_t s);
+// the device address of the current device's fixed layout scratch (MOE_LAYOUT_SCRATCH_BYTES)
+hipError_t layout_scratch(int32_t** out);
 
 hipError_t launch_permute_copy(const void* x, size_t row_bytes, int N, int k,
                                const int32_t* send_pos, void* out, hipStream_t s);

@@ -24,7 +24,9 @@
  *     bases must be 16-byte aligned (every row length below is a multiple of 16 bytes).
  *   - The caller owns every buffer, workspaces included.  The library never allocates
  *     or frees device memory and keeps no pointer after a call returns; it holds no
- *     state and may be called from several host threads.
+ *     state and may be called from several host threads.  (One exception, by design:
+ *     moe_dispatch_layout_noalloc keeps its counts in a fixed device array of the
+ *     library, see there.)
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream).  There is no
  *     host synchronisation and no device-to-host copy inside any call; stream order is
  *     the completion signal.  Buffers may be reused once later work on the stream runs.
@@ -144,6 +146,25 @@ moe_status moe_route(const float* z, int N, int E, int k, const float* bias, int
 moe_status moe_dispatch_layout(const int32_t* topk_idx, int N, int k, int E, int32_t* n_e,
                                int32_t* offsets, int32_t* send_pos, int32_t* src_slot, void* ws,
                                size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch_layout_noalloc -- moe_dispatch_layout with no workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus ws), outputs and determinism.
+ *
+ * The per-chunk expert counts go to a fixed array of MOE_LAYOUT_SCRATCH_BYTES in device
+ * memory that the library holds on each device it runs on until the process ends.  No HIP
+ * allocation is made.  Sizes whose count table exceeds it, i.e.
+ * moe_workspace_bytes(MOE_OP_DISPATCH_LAYOUT, N, 0, 0, E, k, 0) > MOE_LAYOUT_SCRATCH_BYTES
+ * (never for E <= 256; for E = 1024 once N * k exceeds 2^20), return MOE_ERR_WORKSPACE
+ * before anything is enqueued.  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (two streams, two threads) race and must be
+ * ordered by the caller.  Nothing has to be cleared between calls.
+ */
+#define MOE_LAYOUT_SCRATCH_BYTES (4u << 20)
+moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int N, int k, int E, int32_t* n_e,
+                                       int32_t* offsets, int32_t* send_pos, int32_t* src_slot,
+                                       hipStream_t stream);
 
 /*
  * moe_permute -- x_perm[send_pos[t * k + j]] = x[t] (the local stand-in of dispatch).
