@@ -38,8 +38,13 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="dsv3_bf16")
-    p.add_argument("--cpu-tokens", type=int, default=16,
-                   help="tokens of the batch the CPU oracle runs for the baseline (0 = skip)")
+    p.add_argument("--cpu-tokens", type=int, default=-1,
+                   help="tokens of the batch the CPU oracle runs for the baseline (-1 = the whole batch, "
+                        "0 = skip)")
+    p.add_argument("--other-configs", default="all",
+                   help="comma-separated workloads also timed (compactly) into other_configs, 'all' (every "
+                        "workload but --config) or 'none'")
+    p.add_argument("--other-steps", type=int, default=10, help="timed steps per other workload")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     p.add_argument("--gate-in-down", action="store_true",
@@ -153,77 +158,126 @@ def algorithmic_backward(cfg, n_e):
     return d
 
 
+class _StagedWeights:
+    """Weight source of the oracle: expert e's weights, held on the host in their storage
+    dtype, converted to float64 when the oracle asks for them.  The conversion is input
+    staging, not the oracle's arithmetic: its time is recorded and left out of the timing."""
+
+    def __init__(self, host):
+        self.host = host
+        self.spent = 0.0
+
+    def __call__(self, e):
+        import torch
+        t0 = time.perf_counter()
+        a = self.host[e].to(torch.float64).numpy()
+        self.spent += time.perf_counter() - t0
+        return a
+
+
 def cpu_baseline(cfg, inp, T):
-    """The oracle, as it stands, on the first T tokens of the batch (weights staged on the host)."""
+    """The oracle, as it stands, on the first T tokens of the batch (T < 0: all of it): router
+    logits, route, layout, permute, every expert's SwiGLU FFN on its rows (float64), the
+    shared expert and combine.  Weights are copied to the host before timing and converted
+    expert by expert as the oracle asks for them; that conversion is excluded."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle
 
-    T = min(T, cfg.N)
-    x = inp["x"][:T].detach().cpu()
+    T = cfg.N if T < 0 else min(T, cfg.N)
+    if cfg.dtype == "fp8":
+        return None   # (its weights would first be quantized by the oracle's codec, minutes of staging)
+    x = inp["x"][:T].detach().cpu().double().numpy()
     w_r = inp["w_r"].detach().cpu().double().numpy()
     b = inp["bias_cpu"]
-    # the experts the sample touches (to stage their weights on the host before timing)
-    z0 = moe_oracle.router_logits(x.double().numpy(), w_r)
-    idx, _ = moe_oracle.route(z0, cfg.k, None if b is None else b.numpy(), cfg.n_group, cfg.topk_group)
-    need = sorted(set(int(e) for e in idx.reshape(-1)))
-    w13 = {e: inp["w13"][e].detach().cpu() for e in need}   # staged on the host, not timed
-    w2 = {e: inp["w2"][e].detach().cpu() for e in need}
-    fp8 = cfg.dtype == "fp8"
+    w13 = _StagedWeights(inp["w13"].detach().cpu())
+    w2 = _StagedWeights(inp["w2"].detach().cpu())
+    kw = {}
     if cfg.shared:
-        sw13, sw2 = inp["sw13"][0].cpu(), inp["sw2"][0].cpu()
+        kw = dict(shared_w13=inp["sw13"][0].cpu().double().numpy(), shared_w2=inp["sw2"][0].cpu().double().numpy())
     t0 = time.perf_counter()
-    z = moe_oracle.router_logits(x.double().numpy(), w_r)
-    if fp8:
-        q13 = {e: moe_oracle.quantize_blocks(w13[e].float().numpy()) for e in need}
-        q2 = {e: moe_oracle.quantize_blocks(w2[e].float().numpy()) for e in need}
-        moe_oracle.moe_layer(x.float().numpy(), z, cfg.k, lambda e: q13[e][0], lambda e: q2[e][0],
-                             n_group=cfg.n_group, topk_group=cfg.topk_group, fp8=True,
-                             w13_scale=lambda e: q13[e][1], w2_scale=lambda e: q2[e][1])
-    else:
-        kw = {}
-        if cfg.shared:
-            kw = dict(shared_w13=sw13.double().numpy(), shared_w2=sw2.double().numpy())
-        moe_oracle.moe_layer(x.double().numpy(), z, cfg.k, lambda e: w13[e].double().numpy(),
-                             lambda e: w2[e].double().numpy(), bias=None if b is None else b.numpy(),
-                             n_group=cfg.n_group, topk_group=cfg.topk_group, **kw)
-    dt = time.perf_counter() - t0
+    z = moe_oracle.router_logits(x, w_r)
+    res = moe_oracle.moe_layer(x, z, cfg.k, w13, w2, bias=None if b is None else b.numpy(),
+                               n_group=cfg.n_group, topk_group=cfg.topk_group, **kw)
+    wall = time.perf_counter() - t0
+    dt = wall - w13.spent - w2.spent
+    touched = int((res["n_e"] > 0).sum())
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {T} of {cfg.N} tokens of the same batch through the whole oracle layer, "
-                      f"router logits included "
-                      f"({len(need)} experts touched; float64; weights staged on the host before timing); "
-                      f"{dt:.1f} s"}
+            "sample": f"{'the whole batch' if T == cfg.N else f'the first {T} tokens'} of {cfg.name} "
+                      f"({T} tokens, {touched} experts touched, max n_e {int(res['n_e'].max())}) through the "
+                      f"whole oracle layer in float64, router logits included; {dt:.1f} s timed "
+                      f"({w13.spent + w2.spent:.1f} s of bf16 -> float64 weight conversion left out)"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        sys.exit(2)
-    import numpy as np
-    import torch
+def summarize(per, alg, dtype):
+    kernels = {}
+    for name, times in per.items():
+        t = sorted(times)
+        avg = sum(t) / len(t)
+        k = {"avg_ms": round(avg, 4), "median_ms": round(t[len(t) // 2], 4),
+             "p99_ms": round(t[min(len(t) - 1, int(math.ceil(0.99 * len(t))) - 1)], 4)}
+        a = alg.get(name, {})
+        if "bytes" in a:
+            k["GB_per_s"] = round(a["bytes"] / (avg * 1e-3) / 1e9, 1)
+            k["hbm_frac"] = round(a["bytes"] / (avg * 1e-3) / PEAK_HBM, 4)
+        if "flops" in a:
+            k["TFLOP_per_s"] = round(a["flops"] / (avg * 1e-3) / 1e12, 1)
+            k["mfma_frac"] = round(a["flops"] / (avg * 1e-3) / PEAK_MFMA[dtype], 4)
+        kernels[name] = k
+    return kernels
 
+
+def roofline(cfg, alg, per, fused, gather, with_traffic=True):
+    """Roofline of the dominant kernel (the gate/up GEMM) from its average event time."""
+    g = alg["gate_up"]
+    g_avg = sum(per["gate_up"]) / len(per["gate_up"]) * 1e-3
+    t_mfma = g["flops"] / PEAK_MFMA[cfg.dtype]
+    t_hbm = g["bytes"] / PEAK_HBM
+    traffic = None
+    tf = TRAFFIC_FILE.format(cfg.name)
+    if with_traffic and os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_sha") == source_sha(*GEMM_SOURCES):
+            traffic = rec.get("bytes_per_launch")
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(g["bytes"] / g_avg / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(g["flops"] / g_avg / 1e12, 1),
+                "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU, routed rows gathered from x and the shared expert in the "
+                      "same launch (moe_expert_gate_up_gathered_shared)" if fused else
+                      "grouped gate/up GEMM + SwiGLU, rows gathered from x (moe_expert_gate_up_gathered)"
+                      if gather else "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)")
+    roof["algorithmic_bytes"] = int(g["bytes"])
+    roof["algorithmic_flops"] = g["flops"]
+    return roof
+
+
+def workload_name(cfg):
+    return (f"{cfg.name}: N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}"
+            + (f" groups {cfg.topk_group}/{cfg.n_group}" if cfg.n_group else "")
+            + (" +shared expert" if cfg.shared else "")
+            + (f" zipf bias s={cfg.zipf_s}" if cfg.zipf_s else ""))
+
+
+def build_layer(cfg, args, dev):
     import workload
-    import combine_grouped_gemm_amd as moe
     from combine_grouped_gemm_amd.layer import MoELayer
-
-    cfg = workload.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    moe.lib()
-    log(args, f"generating {cfg.name} inputs on the GPU")
     inp = workload.make_layer_inputs(cfg, dev)
     layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
                      inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"],
                      gather=not args.no_gather, overlap_shared=args.overlap,
                      fuse_shared=not args.no_fuse_shared, gate_in_down=args.gate_in_down, w_r=inp["w_r"])
-    x = inp["x"]
-    torch.cuda.synchronize()
+    return inp, layer
 
-    # the layer's own calls, one stage each, as MoELayer.forward issues them (bf16 layers fold
-    # the permute into gate/up; the shared expert runs on the layer's side stream)
-    stream = torch.cuda.current_stream()
+
+def layer_stages(cfg, layer, x):
+    """The layer's own calls, one stage each, as MoELayer.forward issues them (bf16 layers fold
+    the permute into gate/up; the shared expert runs on the layer's side stream)."""
     stages = [("router", lambda: layer.router(x)),
               ("route", lambda: layer.route(layer.z)),
               ("layout", layer.dispatch)]
@@ -234,22 +288,16 @@ def main():
     if cfg.shared and layer.side is None and not layer.fuse:
         stages.append(("shared", lambda: layer.shared_expert(x)))
     stages.append(("combine", layer.combine))
+    return stages
+
+
+def time_steps(stages, layer, x, steps, warmup, stream):
+    """Warm-up steps, then `steps` timed ones: (wall ms per step, per-stage event times,
+    per-step event times)."""
+    import torch
     side = layer.side
-    if args.train:
-        if side is not None:
-            raise SystemExit("--train runs the layer on one stream (no --overlap)")
-        dy = workload.normal((cfg.N, cfg.H), workload.stream_key(cfg.seed, workload.T_EO, 5), dev, torch.bfloat16,
-                             std=1.0)
-        # the training forward keeps the gate/up pre-activations for the backward
-        layer.forward(x, save_for_backward=True)
-        if args.overlap_backward:
-            layer.backward_steps(x, dy)   # (allocates the gradients)
-            stages.append(("backward", lambda: layer.backward(x, dy, overlap_shared=True)))
-        else:
-            stages += layer.backward_steps(x, dy)
 
     def step(ev=None):
-        """One forward; ev: per-stage (start, end) event pairs to record, or None."""
         if side is not None:
             side.wait_stream(stream)
             with torch.cuda.stream(side):
@@ -268,6 +316,87 @@ def main():
             if ev is not None:
                 ev[name][1].record(stream)
 
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    names = [n for n, _ in stages] + (["shared"] if side is not None else [])
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [ev[s_][n][0].elapsed_time(ev[s_][n][1]) for s_ in range(steps)] for n in names}
+    first = "shared" if side is not None else stages[0][0]
+    step_ms = [ev[s_][first][0].elapsed_time(ev[s_][stages[-1][0]][1]) for s_ in range(steps)]
+    return wall * 1e3 / steps, per, step_ms, step
+
+
+def other_config(name, args, dev):
+    """A compact measurement of another workload: ms per step, tokens/s, the dominant kernel's
+    roofline fraction, per-stage times and the routing imbalance."""
+    import torch
+    import workload
+    cfg = workload.CONFIGS[name]
+    log(args, f"other workload {name}")
+    inp, layer = build_layer(cfg, args, dev)
+    x = inp["x"]
+    stages = layer_stages(cfg, layer, x)
+    steps = args.other_steps * (10 if cfg.name == "tiny_f32" else 1)
+    ms, per, _, _ = time_steps(stages, layer, x, steps, 3, torch.cuda.current_stream())
+    n_e = layer.layout[0].cpu().numpy()
+    alg = algorithmic(cfg, n_e, layer.gather, layer.fuse)
+    kernels = summarize(per, alg, cfg.dtype)
+    roof = roofline(cfg, alg, per, layer.fuse, layer.gather)
+    del layer, inp, x, stages
+    torch.cuda.empty_cache()
+    return {"workload": workload_name(cfg), "dtype": cfg.dtype, "steps": steps, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(cfg.N / (ms / 1e3), 1), "imbalance": round(float(n_e.max() / n_e.mean()), 4),
+            "max_n_e": int(n_e.max()), "empty_experts": int((n_e == 0).sum()),
+            "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel")},
+            "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),
+                                       "down": kernels["down"].get("mfma_frac")},
+            "kernels": {n: {k: v for k, v in d.items() if k in ("avg_ms", "GB_per_s", "hbm_frac", "TFLOP_per_s",
+                                                                  "mfma_frac")} for n, d in kernels.items()}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workload
+    import combine_grouped_gemm_amd as moe
+
+    cfg = workload.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    moe.lib()
+    log(args, f"generating {cfg.name} inputs on the GPU")
+    inp, layer = build_layer(cfg, args, dev)
+    x = inp["x"]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    stages = layer_stages(cfg, layer, x)
+    side = layer.side
+    if args.train:
+        if side is not None:
+            raise SystemExit("--train runs the layer on one stream (no --overlap)")
+        dy = workload.normal((cfg.N, cfg.H), workload.stream_key(cfg.seed, workload.T_EO, 5), dev, torch.bfloat16,
+                             std=1.0)
+        # the training forward keeps the gate/up pre-activations for the backward
+        layer.forward(x, save_for_backward=True)
+        if args.overlap_backward:
+            layer.backward_steps(x, dy)   # (allocates the gradients)
+            stages.append(("backward", lambda: layer.backward(x, dy, overlap_shared=True)))
+        else:
+            stages += layer.backward_steps(x, dy)
+
     if args.copy_probe_mib > 0:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch scale the
         # byte counters read for the MoE kernels
@@ -279,25 +408,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    log(args, f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    names = [n for n, _ in stages] + (["shared"] if side is not None else [])
-    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-          for _ in range(args.steps)]
-    log(args, f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: [ev[s][n][0].elapsed_time(ev[s][n][1]) for s in range(args.steps)] for n in names}
-    first = "shared" if side is not None else stages[0][0]
-    step_ms = [ev[s][first][0].elapsed_time(ev[s][stages[-1][0]][1]) for s in range(args.steps)]
-    ms_per_step = wall * 1e3 / args.steps
+    log(args, f"warmup {args.warmup}, timing {args.steps} steps")
+    ms_per_step, per, step_ms, step = time_steps(stages, layer, x, args.steps, args.warmup, stream)
     value = cfg.N / (ms_per_step / 1e3)
 
     graph = None
@@ -340,18 +452,18 @@ def main():
         cev_ = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for n, _ in stages} for _ in range(args.cold_steps)]
         torch.cuda.synchronize()
-        for s in range(args.cold_steps):
+        for s_ in range(args.cold_steps):
             for i, (name, f) in enumerate(stages):
                 if i == 0:
-                    fev[s][0].record(stream)
-                flush.fill_(s + i + 1)
+                    fev[s_][0].record(stream)
+                flush.fill_(s_ + i + 1)
                 if i == 0:
-                    fev[s][1].record(stream)
-                cev_[s][name][0].record(stream)
+                    fev[s_][1].record(stream)
+                cev_[s_][name][0].record(stream)
                 f()
-                cev_[s][name][1].record(stream)
+                cev_[s_][name][1].record(stream)
         torch.cuda.synchronize()
-        cold = {n: [cev_[s][n][0].elapsed_time(cev_[s][n][1]) for s in range(args.cold_steps)]
+        cold = {n: [cev_[s_][n][0].elapsed_time(cev_[s_][n][1]) for s_ in range(args.cold_steps)]
                 for n, _ in stages}
         fill_GBps = round((1 << 30) / (sum(a.elapsed_time(b) for a, b in fev) / len(fev) * 1e-3) / 1e9, 1)
         del flush
@@ -364,11 +476,11 @@ def main():
         moe.moe_permute(x, layer.layout[2], cfg.k, None, xp)
         torch.cuda.synchronize()
         pev[0].record(stream)
-        for s in range(args.steps):
+        for s_ in range(args.steps):
             moe.moe_permute(x, layer.layout[2], cfg.k, None, xp)
-            pev[s + 1].record(stream)
+            pev[s_ + 1].record(stream)
         torch.cuda.synchronize()
-        per["permute (standalone)"] = [pev[s].elapsed_time(pev[s + 1]) for s in range(args.steps)]
+        per["permute (standalone)"] = [pev[s_].elapsed_time(pev[s_ + 1]) for s_ in range(args.steps)]
         del xp
 
     # the machine's practical copy rate (context for the HBM fractions): torch's device copy
@@ -384,6 +496,21 @@ def main():
     torch.cuda.synchronize()
     copy_GBps = round(2 * 5 * (1 << 30) / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9, 1)
     del csrc, cdst
+
+    # the ceiling of combine's access mix (about 9 rows read per row written, every access
+    # sequential): the library's read-mostly streaming probe over 1 GiB read
+    n16 = (1 << 30) // (9 * 16)
+    psrc = torch.zeros(9 * n16 * 16, dtype=torch.uint8, device=dev)
+    pdst = torch.empty(n16 * 16, dtype=torch.uint8, device=dev)
+    moe.moe_stream_probe(psrc, 9, pdst)
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    pev[0].record(stream)
+    for _ in range(5):
+        moe.moe_stream_probe(psrc, 9, pdst)
+    pev[1].record(stream)
+    torch.cuda.synchronize()
+    probe_GBps = round(10 * n16 * 16 * 5 / (pev[0].elapsed_time(pev[1]) * 1e-3) / 1e9, 1)
+    del psrc, pdst
 
     # the machine's achievable dense bf16 matrix rate on this machine (context for the MFMA
     # fractions): torch's library GEMM on 8192^3, flops over its event time
@@ -405,54 +532,13 @@ def main():
     alg["permute (standalone)"] = alg["permute"]
     if args.train:
         alg.update(algorithmic_backward(cfg, n_e))
-    def summary(per):
-        kernels = {}
-        for name, times in per.items():
-            t = sorted(times)
-            avg = sum(t) / len(t)
-            k = {"avg_ms": round(avg, 4), "median_ms": round(t[len(t) // 2], 4),
-                 "p99_ms": round(t[min(len(t) - 1, int(math.ceil(0.99 * len(t))) - 1)], 4)}
-            a = alg.get(name, {})
-            if "bytes" in a:
-                k["GB_per_s"] = round(a["bytes"] / (avg * 1e-3) / 1e9, 1)
-                k["hbm_frac"] = round(a["bytes"] / (avg * 1e-3) / PEAK_HBM, 4)
-            if "flops" in a:
-                k["TFLOP_per_s"] = round(a["flops"] / (avg * 1e-3) / 1e12, 1)
-                k["mfma_frac"] = round(a["flops"] / (avg * 1e-3) / PEAK_MFMA[cfg.dtype], 4)
-            kernels[name] = k
-        return kernels
-
-    kernels = summary(per)
-    kernels_cold = summary(cold) if cold else None
-
-    g = alg["gate_up"]
-    g_avg = sum(per["gate_up"]) / len(per["gate_up"]) * 1e-3
-    t_mfma = g["flops"] / PEAK_MFMA[cfg.dtype]
-    t_hbm = g["bytes"] / PEAK_HBM
-    traffic = None
-    tf = TRAFFIC_FILE.format(cfg.name)
-    if os.path.exists(tf):
-        rec = json.load(open(tf))
-        if rec.get("source_sha") == source_sha(*GEMM_SOURCES):
-            traffic = rec.get("bytes_per_launch")
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": round(g["bytes"] / g_avg / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(g["flops"] / g_avg / 1e12, 1),
-                "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = traffic
-    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU, routed rows gathered from x and the shared expert in the "
-                      "same launch (moe_expert_gate_up_gathered_shared)" if layer.fuse else
-                      "grouped gate/up GEMM + SwiGLU, rows gathered from x (moe_expert_gate_up_gathered)"
-                      if layer.gather else "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)")
-    roof["algorithmic_bytes"] = int(g["bytes"])
-    roof["algorithmic_flops"] = g["flops"]
+    kernels = summarize(per, alg, cfg.dtype)
+    kernels_cold = summarize(cold, alg, cfg.dtype) if cold else None
+    roof = roofline(cfg, alg, per, layer.fuse, layer.gather)
 
     cpu = None
-    if args.cpu_tokens > 0 and not args.train:
-        log(args, f"CPU oracle baseline on {args.cpu_tokens} tokens")
+    if args.cpu_tokens != 0 and not args.train:
+        log(args, f"CPU oracle baseline ({'whole batch' if args.cpu_tokens < 0 else args.cpu_tokens} tokens)")
         cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
 
     out = {
@@ -460,11 +546,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8" if cfg.dtype == "fp8" else cfg.dtype, "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: N={cfg.N} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}"
-                               + (f" groups {cfg.topk_group}/{cfg.n_group}" if cfg.n_group else "")
-                               + (" +shared expert" if cfg.shared else "")
-                               + (f" zipf bias s={cfg.zipf_s}" if cfg.zipf_s else ""),
-                   "global_batch": cfg.N, "parallelism": "single GPU"},
+        "config": {"workload": workload_name(cfg), "global_batch": cfg.N, "parallelism": "single GPU"},
         "roofline": roof,
         "router_logits_in_step": True,
         "ms_per_step_without_router": round(ms_per_step - kernels["router"]["avg_ms"], 4),
@@ -482,6 +564,8 @@ def main():
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
         "device_copy_GBps": copy_GBps,
+        "read_mostly_probe_GBps": probe_GBps,
+        "combine_vs_read_mostly_probe": round(kernels["combine"]["GB_per_s"] / probe_GBps, 4),
         "device_fill_GBps": fill_GBps,
         "library_bf16_gemm_TFLOPs": gemm_TFLOPs,
         "kernels_cold": kernels_cold,
@@ -516,6 +600,16 @@ def main():
             "backward_roofline": broof,
             "cpu_baseline": None,
         })
+
+    # the other workloads, each on its own after this one's buffers are released
+    others = None
+    if args.other_configs != "none" and not args.train:
+        names = ([n for n in workload.CONFIG_ORDER if n != cfg.name] if args.other_configs == "all"
+                 else [n for n in args.other_configs.split(",") if n])
+        del layer, inp, x, stages, step
+        torch.cuda.empty_cache()
+        others = {n: other_config(n, args, dev) for n in names}
+    out["other_configs"] = others
     print(json.dumps(out), flush=True)
 
 

@@ -25,7 +25,7 @@ __all__ = [
     "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
     "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
     "moe_version", "moe_combine_backward", "moe_expert_gate_up_preact", "moe_swiglu_backward", "moe_expert_dgrad",
-    "moe_expert_wgrad", "moe_router_backward",
+    "moe_expert_wgrad", "moe_router_backward", "moe_stream_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +73,7 @@ _SIGS = {
     "moe_expert_dgrad": [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
     "moe_expert_wgrad": [_P, _I, _P, _I, _P, _I, _I, _P, _I, _I, _P, _I, _P],
     "moe_router_backward": [_P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I, _P],
+    "moe_stream_probe": [_P, _SZ, _I, _P, _P],
     "moe_status_str": [_I],
     "moe_version": [],
 }
@@ -484,3 +485,16 @@ def moe_router_backward(topk_gate: torch.Tensor, d_gate: torch.Tensor, offsets: 
         _ptr(topk_gate), _ptr(d_gate), N, k, _ptr(offsets), _ptr(src_slot), E, rows, _ptr(x), _dt(x), H, _ptr(dz),
         _ptr(dw_r), _dt(dw_r), _stream(x)))
     return dz, dw_r
+
+
+def moe_stream_probe(src: torch.Tensor, ratio: int, dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read-mostly streaming probe: src holds ratio * n 16-byte words, dst n words (uint8
+    tensors); dst[i] = the integer sum of src[j * n + i] over j."""
+    nbytes = src.numel() * src.element_size()
+    if nbytes % (16 * ratio):
+        raise ValueError("src must hold ratio * n 16-byte words")
+    n16 = nbytes // (16 * ratio)
+    if dst is None:
+        dst = torch.empty(n16 * 16, dtype=torch.uint8, device=src.device)
+    _check("moe_stream_probe", lib().moe_stream_probe(_ptr(src), n16, ratio, _ptr(dst), _stream(src)))
+    return dst

@@ -318,6 +318,13 @@ moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, in
                                         shared_out, y, y_dt == MOE_F32, stream));
 }
 
+moe_status moe_stream_probe(const void* src, size_t n16, int ratio, void* dst, hipStream_t stream) {
+  if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 9 && ratio != 16) return MOE_ERR_UNSUPPORTED;
+  if (n16 == 0) return MOE_OK;
+  if (src == nullptr || dst == nullptr || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_stream_probe(src, n16, ratio, dst, stream));
+}
+
 // ---- backward pass
 
 moe_status moe_combine_backward(const void* dy, moe_dtype dt, int N, int H, int k, const int32_t* send_pos,

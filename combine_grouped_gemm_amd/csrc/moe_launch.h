@@ -33,6 +33,8 @@ hipError_t launch_router_logits(const void* x, bool bf16, int N, int H, const vo
 
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
                           const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s);
+// read-mostly streaming probe: ratio in {1, 2, 4, 8, 9, 16}
+hipError_t launch_stream_probe(const void* src, size_t n16, int ratio, void* dst, hipStream_t s);
 
 // backward pass (backward.hip, grouped_gemm_bwd.hip)
 hipError_t launch_combine_backward(const void* dy, bool f32, int N, int H, int k, const int32_t* send_pos,

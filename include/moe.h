@@ -330,6 +330,19 @@ moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, in
                        const int32_t* send_pos, const float* topk_gate, const void* shared_out,
                        void* y, moe_dtype y_dt, hipStream_t stream);
 
+/*
+ * moe_stream_probe -- a measurement utility, not a step of the layer: the achievable HBM
+ * rate of combine's access mix.  dst[i] = sum over j < ratio of src[j * n16 + i], each
+ * 16-byte word added as four 32-bit integers (wrapping).
+ *
+ *   src   [ratio * n16] 16-byte words, dst [n16] 16-byte words (16-byte aligned).
+ *   ratio in {1, 2, 4, 8, 9, 16} (MOE_ERR_UNSUPPORTED otherwise); 9 is the DeepSeek-V3-shaped
+ *         combine's mix: 8 expert rows and the shared expert's row read per row written.
+ * Every access is sequential, so the rate (ratio + 1) * n16 * 16 bytes over the kernel time is
+ * the ceiling for a kernel that reads ratio rows per row it writes.
+ */
+moe_status moe_stream_probe(const void* src, size_t n16, int ratio, void* dst, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * Backward pass (training).  "DeepSeek MoE: EP and FSDP guide": the backward of the layer
  * mirrors its forward -- the backward of dispatch is combine (and that of combine a

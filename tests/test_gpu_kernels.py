@@ -468,6 +468,10 @@ COMBINE_CASES = [
     ("f32", 256, 128, 8, 2, torch.float32, False),
     ("k3", 100, 64, 8, 3, torch.bfloat16, True),
     ("k32", 50, 256, 64, 32, torch.bfloat16, False),
+    ("k5_f32_shared", 64, 512, 16, 5, torch.float32, True),
+    ("k1", 77, 8, 4, 1, torch.bfloat16, False),
+    ("k8_spans", 3, 7168, 256, 8, torch.bfloat16, True),     # a few tokens: rows split into spans
+    ("k12", 40, 1024, 32, 12, torch.bfloat16, True),
 ]
 
 
@@ -505,3 +509,17 @@ def test_generator_device_matches_host():
     c13, c2 = w.all_expert_weights(cfg, "cpu")
     assert torch.equal(g13.cpu(), c13) and torch.equal(g2.cpu(), c2)
     assert torch.equal(w.hidden_states(cfg, DEV).cpu(), w.hidden_states(cfg, "cpu"))
+
+
+@pytest.mark.parametrize("ratio", [1, 9, 16])
+def test_stream_probe_sums(ratio):
+    """The read-mostly streaming probe (a measurement utility): dst[i] = the 32-bit integer
+    sum of src[j * n + i] over j, lane by lane."""
+    n16 = 3000
+    src = (torch.arange(ratio * n16 * 4, dtype=torch.int64) * 2654435761 % (1 << 32)).to(torch.int64)
+    src32 = (src - (src >= (1 << 31)).to(torch.int64) * (1 << 32)).to(torch.int32)
+    dst = moe.moe_stream_probe(src32.to(DEV).view(torch.uint8), ratio)
+    sync()
+    ref = src.reshape(ratio, n16 * 4).sum(0) % (1 << 32)
+    got = dst.cpu().view(torch.int32).to(torch.int64) % (1 << 32)
+    assert torch.equal(got, ref)
