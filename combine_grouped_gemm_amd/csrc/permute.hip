@@ -14,17 +14,36 @@ namespace moe {
 
 constexpr int kPermThreads = 256;
 
+// a lane's (up to) four 16-byte chunks of the row are loaded together, then written to the
+// token's k rows with non-temporal stores (the rows are written once, not read back here)
+typedef uint32_t perm_word_t __attribute__((ext_vector_type(4)));
+constexpr int kPermUnroll = 4;
+
 __global__ __launch_bounds__(kPermThreads) void permute_copy_kernel(
     const uint4* __restrict__ x, int row_chunks, int k, const int32_t* __restrict__ send_pos,
     uint4* __restrict__ out) {
   const int t = blockIdx.x;
   const uint4* src = x + static_cast<size_t>(t) * row_chunks;
   const int32_t* sp = send_pos + static_cast<size_t>(t) * k;
-  for (int c = threadIdx.x; c < row_chunks; c += kPermThreads) {
-    const uint4 v = src[c];
+  for (int c0 = threadIdx.x; c0 < row_chunks; c0 += kPermUnroll * kPermThreads) {
+    perm_word_t v[kPermUnroll];
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int c = c0 + u * kPermThreads;
+      if (c < row_chunks) {
+        const uint4 a = src[c];
+        v[u] = perm_word_t{a.x, a.y, a.z, a.w};
+      }
+    }
     for (int j = 0; j < k; ++j) {
       const int r = sp[j];
-      if (r >= 0) out[static_cast<size_t>(r) * row_chunks + c] = v;
+      if (r < 0) continue;
+      perm_word_t* dst = reinterpret_cast<perm_word_t*>(out + static_cast<size_t>(r) * row_chunks);
+#pragma unroll
+      for (int u = 0; u < kPermUnroll; ++u) {
+        const int c = c0 + u * kPermThreads;
+        if (c < row_chunks) __builtin_nontemporal_store(v[u], dst + c);
+      }
     }
   }
 }
