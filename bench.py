@@ -45,6 +45,9 @@ def parse():
                    help="comma-separated workloads also timed (compactly) into other_configs, 'all' (every "
                         "workload but --config) or 'none'")
     p.add_argument("--other-steps", type=int, default=10, help="timed steps per other workload")
+    p.add_argument("--chunks", type=int, default=2,
+                   help="also time the layer cut into this many chunks of tokens, each chunk's combine on a "
+                        "second stream beside the next chunk's GEMMs (A/B against the unchunked layer; 1 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     p.add_argument("--gate-in-down", action="store_true",
@@ -600,6 +603,27 @@ def main():
             "backward_roofline": broof,
             "cpu_baseline": None,
         })
+
+    # A/B: the same batch cut into chunks, one chunk's combine beside the next chunk's GEMMs
+    # (bf16 layers; the batch must split into equal chunks)
+    if args.chunks > 1 and not args.train and cfg.dtype == "bf16" and cfg.N % args.chunks == 0:
+        from combine_grouped_gemm_amd.layer import PipelinedMoE
+        log(args, f"chunked pipeline, {args.chunks} chunks")
+        pipe = PipelinedMoE(args.chunks, cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, inp["w13"], inp["w2"], inp.get("sw13"),
+                            inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"], w_r=inp["w_r"])
+        for _ in range(args.warmup):
+            pipe.forward(x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            pipe.forward(x)
+        torch.cuda.synchronize()
+        chunk_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        out["chunked_pipeline"] = {"chunks": args.chunks, "ms_per_step": round(chunk_ms, 4),
+                                   "tokens_per_s": round(cfg.N / (chunk_ms / 1e3), 1),
+                                   "vs_unchunked": round(ms_per_step / chunk_ms, 4)}
+        del pipe
+        torch.cuda.empty_cache()
 
     # the other workloads, each on its own after this one's buffers are released
     others = None

@@ -400,15 +400,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
 // s_barrier, which keeps the later stages in flight across the barrier.
 // ------------------------------------------------------------------------------------
 
-#ifndef MOE_DMA_OCC
-#define MOE_DMA_OCC 1   // workgroups per CU
-#endif
+constexpr int kDmaOcc = 1;   // workgroups per CU
 
 
-#ifndef MOE_DMA_DM
-#define MOE_DMA_DM 128  // rows of a tile
-#endif
-constexpr int kDM = MOE_DMA_DM;
+constexpr int kDM = 128;    // rows of a tile
 constexpr int kDGroup = 1024;                           // bytes of one DMA wave instruction
 template <int BN, int ROWB, int STAGES, int WM, int WN>
 struct DmaCfg {
@@ -434,7 +429,7 @@ struct DmaCfg {
 };
 
 template <int MODE, int BN, int ROWB, int STAGES, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64, MOE_DMA_OCC) void grouped_gemm_dma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(WM * WN * 64, kDmaOcc) void grouped_gemm_dma_kernel(GemmArgs p) {
   using C = DmaCfg<BN, ROWB, STAGES, WM, WN>;
   constexpr int KSTEPS = C::kKSteps;
   constexpr int NB = C::kNB;
@@ -444,7 +439,7 @@ __global__ __launch_bounds__(WM * WN * 64, MOE_DMA_OCC) void grouped_gemm_dma_ke
   static_assert(KSTEPS % 2 == 0, "a stage must end in fragment set 1 so the next starts in set 0");
   static_assert(MODE != MODE_GATE_UP || NB % 2 == 0, "gate/up pairs");
 
-  static_assert(STAGES * C::kStageBytes * MOE_DMA_OCC <= 160 * 1024, "LDS of the resident workgroups");
+  static_assert(STAGES * C::kStageBytes * kDmaOcc <= 160 * 1024, "LDS of the resident workgroups");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStageBytes];
   const uint32_t lds_addr0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
 
@@ -696,21 +691,9 @@ __global__ __launch_bounds__(WM * WN * 64, MOE_DMA_OCC) void grouped_gemm_dma_ke
   }
 }
 
-#ifndef MOE_DMA_BN
-#define MOE_DMA_BN 256
-#endif
-#ifndef MOE_DMA_ROWB
-#define MOE_DMA_ROWB 128
-#endif
-#ifndef MOE_DMA_STAGES
-#define MOE_DMA_STAGES 3
-#endif
-#ifndef MOE_DMA_WM
-#define MOE_DMA_WM 2
-#endif
-#ifndef MOE_DMA_WN
-#define MOE_DMA_WN 4
-#endif
+// the 128-row direct-to-LDS kernel's shape: 256 weight rows, stages of 128 bytes per row,
+// three stages in LDS, 2 x 4 waves
+constexpr int kDmaBN = 256, kDmaRowB = 128, kDmaStages = 3, kDmaWM = 2, kDmaWN = 4;
 
 // m-tiles at the finest granularity any kernel uses (16 rows)
 size_t gemm_tile_cap(int rows, int E) {
@@ -736,16 +719,10 @@ size_t gemm_schedule_bytes(int rows, int E) {
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 
-// 256 x 256 tiles for: 0 no GEMM, 1 gate/up, 2 gate/up and routed down (E > 1), 3 every
-// bf16 GEMM.  A single dense down GEMM (the shared expert: 8192 x 7168 outputs) makes 3.5
-// wide tiles per CU but exactly 7 of 128 x 256, so it keeps the smaller tiles.
-#ifndef MOE_GEMM_WIDE
-#define MOE_GEMM_WIDE 2
-#endif
-#ifndef MOE_WIDE_DYNAMIC
-#define MOE_WIDE_DYNAMIC 1
-#endif
-constexpr bool kWideDynamic = MOE_WIDE_DYNAMIC != 0;
+// bf16 GEMMs on 256 x 256 tiles: every gate/up and every routed down (E > 1).  A single
+// dense down GEMM (the shared expert on its own: 8192 x 7168 outputs) makes 3.5 wide tiles
+// per CU but exactly 7 of 128 x 256, so it keeps the smaller tiles.  The wide kernel takes
+// its tiles from a counter per XCD.
 
 static int persistent_grid() {
   // one workgroup per CU (256 CUs); a multiple of the 8 XCDs
@@ -779,7 +756,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   if ((shared_rows > 0 || row_gate != nullptr || au != nullptr) && (!wide_ok || stream))
     return hipErrorNotSupported;   // (callers check first)
   const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr || au != nullptr ||
-                                (mode == MODE_GATE_UP ? MOE_GEMM_WIDE >= 1 : MOE_GEMM_WIDE >= (E > 1 ? 2 : 3)));
+                                mode == MODE_GATE_UP || E > 1);
   const int tile_rows = stream ? kStreamTileRows : (wide ? kWideTileRows : (dma ? kDM : GBM));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert, tile_counter, shared_rows);
@@ -812,17 +789,17 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.au = au;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
   if (wide) {
-    p.tile_counter = kWideDynamic ? tile_counter : nullptr;
+    p.tile_counter = tile_counter;
     return launch_grouped_gemm_wide(mode, p, s);
   }
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \
   hipLaunchKernelGGL((grouped_gemm_kernel<CT_, B8_, MODE_>), grid, block, 0, s, p)
 #define MOE_LAUNCH_DMA(MODE_) \
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM, \
-                                              MOE_DMA_WN>), \
-                     dim3(persistent_grid() * MOE_DMA_OCC), \
-                     dim3(DmaCfg<MOE_DMA_BN, MOE_DMA_ROWB, MOE_DMA_STAGES, MOE_DMA_WM, MOE_DMA_WN>::kThreads), 0, s, p)
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE_, kDmaBN, kDmaRowB, kDmaStages, kDmaWM, \
+                                              kDmaWN>), \
+                     dim3(persistent_grid() * kDmaOcc), \
+                     dim3(DmaCfg<kDmaBN, kDmaRowB, kDmaStages, kDmaWM, kDmaWN>::kThreads), 0, s, p)
   if (mode == MODE_GATE_UP) {
     if (ct == CT_F32) MOE_LAUNCH(CT_F32, false, MODE_GATE_UP);
     else if (ct == CT_BF16) MOE_LAUNCH_DMA(MODE_GATE_UP);

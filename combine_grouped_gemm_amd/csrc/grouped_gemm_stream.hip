@@ -39,12 +39,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kSCB = 8;      // 16-row weight blocks of a panel (128 weight rows)
 constexpr int kSWaves = 4;   // waves per workgroup
 
-#ifndef MOE_STREAM_STAGES
-#define MOE_STREAM_STAGES 3
-#endif
-#ifndef MOE_STREAM_WG_PER_CU
-#define MOE_STREAM_WG_PER_CU 1
-#endif
+constexpr int kStreamStages = 3;     // K blocks each wave keeps in flight
+constexpr int kStreamWgPerCu = 1;    // workgroups per CU
 
 template <int MODE>
 struct StreamStage {
@@ -316,10 +312,10 @@ __global__ __launch_bounds__(kSWaves * 64, WG_PER_CU) void grouped_gemm_stream_k
 }
 
 hipError_t launch_grouped_gemm_stream(int mode, const GemmArgs& p, hipStream_t s) {
-  const dim3 grid(256 * MOE_STREAM_WG_PER_CU), block(kSWaves * 64);
+  const dim3 grid(256 * kStreamWgPerCu), block(kSWaves * 64);
   const bool vec = (p.K / 128) % 4 == 0;
 #define MOE_LAUNCH_STREAM(MODE_, VEC_)                                                                      \
-  hipLaunchKernelGGL((grouped_gemm_stream_kernel<MODE_, MOE_STREAM_STAGES, MOE_STREAM_WG_PER_CU, VEC_>), grid, \
+  hipLaunchKernelGGL((grouped_gemm_stream_kernel<MODE_, kStreamStages, kStreamWgPerCu, VEC_>), grid, \
                      block, 0, s, p)
   if (mode == MODE_GATE_UP) {
     if (vec) MOE_LAUNCH_STREAM(MODE_GATE_UP, true);

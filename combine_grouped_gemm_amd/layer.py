@@ -380,3 +380,60 @@ class MoELayer:
         for t in (x, dy):
             t.record_stream(side)
         return self.grads
+
+
+class PipelinedMoE:
+    """The layer over C chunks of tokens with one chunk's combine beside the next chunk's GEMMs.
+
+    "EP / DeepEP explanation" page, section 7: cut the batch into chunks so that the dispatch
+    and combine of one chunk overlap the expert computation of another (the pipelined time is
+    about T_warm + sum over chunks of max(T_dispatch, T_experts, T_combine) + T_drain).  Here
+    chunk c's router logits, route, layout and grouped GEMMs run on the caller's stream, and
+    its combine on a second stream (default priority) once chunk c's down GEMM is done, while
+    chunk c + 1's work starts on the first stream.  Each chunk is a MoELayer of N / C tokens
+    over the same weights (bf16 layers); y is one [N, H] buffer, chunk c writing its rows.
+    Routing is per token, so the result equals the unchunked layer's up to the tiles' row
+    split (the same arithmetic per row).
+    """
+
+    def __init__(self, chunks: int, N: int, H: int, E: int, k: int, I: int, w13: torch.Tensor, w2: torch.Tensor,
+                 shared_w13: Optional[torch.Tensor] = None, shared_w2: Optional[torch.Tensor] = None,
+                 n_group: int = 0, topk_group: int = 0, bias: Optional[torch.Tensor] = None,
+                 w_r: Optional[torch.Tensor] = None):
+        if chunks < 1 or N % chunks:
+            raise ValueError("N must split into equal chunks")
+        self.N, self.H, self.chunks = N, H, chunks
+        n = N // chunks
+        dev = w13.device
+        self.y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+        self.parts = []
+        for c in range(chunks):
+            lay = MoELayer(n, H, E, k, I, "bf16", w13, w2, shared_w13, shared_w2, n_group, topk_group, bias,
+                           w_r=w_r)
+            lay.y = self.y[c * n:(c + 1) * n]   # (a contiguous block of rows)
+            self.parts.append(lay)
+        self.side = torch.cuda.Stream(device=dev)
+        self.ready = [torch.cuda.Event() for _ in range(chunks)]
+        self.done = torch.cuda.Event()
+
+    def forward(self, x: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:
+        main = torch.cuda.current_stream(x.device)
+        n = self.N // self.chunks
+        self.side.wait_stream(main)
+        for c, lay in enumerate(self.parts):
+            xc = x[c * n:(c + 1) * n]
+            zc = None if z is None else z[c * n:(c + 1) * n]
+            if zc is None:
+                zc = lay.router(xc)
+            lay.route(zc)
+            lay.dispatch()
+            lay.permute(xc)
+            lay.experts(xc)
+            self.ready[c].record(main)
+            self.side.wait_event(self.ready[c])
+            with torch.cuda.stream(self.side):
+                lay.combine()
+        self.done.record(self.side)
+        main.wait_event(self.done)
+        x.record_stream(self.side)
+        return self.y

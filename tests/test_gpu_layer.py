@@ -13,7 +13,7 @@ import torch
 
 import combine_grouped_gemm_amd as moe
 import workload as w
-from combine_grouped_gemm_amd.layer import MoELayer
+from combine_grouped_gemm_amd.layer import MoELayer, PipelinedMoE
 from oracle import moe_oracle as oracle
 from tests.gpu_util import decision_margin, f64, router_bound, say, sync, token_rel_err, with_logits
 
@@ -407,3 +407,33 @@ def test_layer_forward_graph_replay(name):
         eager = layer.forward(x)   # eager work between the replays
         sync()
         assert torch.equal(eager.view(view), ref.view(view))
+
+
+@pytest.mark.parametrize("chunks", [2, 4])
+def test_pipelined_chunks_match_oracle(chunks):
+    """The layer cut into chunks of tokens, each chunk's combine on a second stream beside the
+    next chunk's GEMMs: y on every token against the oracle's unchunked layer (routing is per
+    token), over three forwards in a row; and equal to the unchunked layer's y within the bar."""
+    cfg = SMALL["dsv3_small"]
+    say(f"pipelined layer, {chunks} chunks")
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
+    pipe = PipelinedMoE(chunks, cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, inp["w13"], inp["w2"], inp["sw13"], inp["sw2"],
+                        cfg.n_group, cfg.topk_group, inp["bias"])
+    for _ in range(3):
+        y = pipe.forward(inp["x"], inp["z"])
+    sync()
+    ow = OracleWeights(inp["w13"], inp["w2"], False)
+    ref = oracle.moe_layer(f64(inp["x"]), inp["z_cpu"].numpy(), cfg.k, ow.g13, ow.g2, n_group=cfg.n_group,
+                           topk_group=cfg.topk_group, shared_w13=f64(inp["sw13"][0]), shared_w2=f64(inp["sw2"][0]))
+    n = cfg.N // chunks
+    got_idx = np.concatenate([lay.topk_idx.cpu().numpy() for lay in pipe.parts])
+    assert np.array_equal(got_idx, ref["topk_idx"])
+    err = token_rel_err(f64(y), ref["y"])
+    say(f"  y max per-token relative error {err:.3e}")
+    assert err <= Y_BAR["bf16"] and err <= Y_EXPECT["bf16"]
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"], inp["sw13"], inp["sw2"],
+                     cfg.n_group, cfg.topk_group, inp["bias"])
+    y1 = layer.forward(inp["x"], inp["z"])
+    sync()
+    assert token_rel_err(f64(y), f64(y1)) <= 1e-2
+    assert n * chunks == cfg.N
