@@ -71,6 +71,10 @@ def parse():
     p.add_argument("--cold-steps", type=int, default=5,
                    help="extra steps timed with L2 and the 256 MB MALL flushed (1 GiB written) before "
                         "every stage, so each stage reads its inputs from HBM (0 = skip)")
+    p.add_argument("--rows-per-expert", type=int, default=0,
+                   help="diagnostic: replace the router's routes by fixed ones giving exactly this many rows to "
+                        "each of as many experts as the batch fills (the batch shrinks to a multiple that fits); "
+                        "the step is then layout, GEMMs and combine")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -377,6 +381,18 @@ def main():
     import combine_grouped_gemm_amd as moe
 
     cfg = workload.CONFIGS[args.config]
+    fixed = None
+    if args.rows_per_expert > 0:
+        # E' experts of R rows each, with E' R a multiple of k and at most the batch's N k rows
+        R = args.rows_per_expert
+        e_used = min(cfg.E, cfg.N * cfg.k // R)
+        while e_used > 0 and (e_used * R) % cfg.k:
+            e_used -= 1
+        if e_used == 0 or R > e_used * R // cfg.k:
+            raise SystemExit("--rows-per-expert does not fit this workload")
+        fixed = workload.counted_route([R] * e_used + [0] * (cfg.E - e_used), cfg.k, seed=1)
+        cfg = cfg.scaled(name=f"{cfg.name}_fixed{R}", N=e_used * R // cfg.k, n_group=0, topk_group=0, zipf_s=0.0)
+        args.cpu_tokens, args.chunks = 0, 1   # (the oracle and the chunked layer route by themselves)
     dev = torch.device("cuda:0")
     moe.lib()
     log(args, f"generating {cfg.name} inputs on the GPU")
@@ -386,6 +402,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     stages = layer_stages(cfg, layer, x)
+    if fixed is not None:
+        layer.topk_idx.copy_(fixed.to(dev))
+        stages = [st for st in stages if st[0] not in ("router", "route")]
     side = layer.side
     if args.train:
         if side is not None:
@@ -551,9 +570,11 @@ def main():
         "dtype": "fp8" if cfg.dtype == "fp8" else cfg.dtype, "data": "synthetic",
         "config": {"workload": workload_name(cfg), "global_batch": cfg.N, "parallelism": "single GPU"},
         "roofline": roof,
-        "router_logits_in_step": True,
-        "ms_per_step_without_router": round(ms_per_step - kernels["router"]["avg_ms"], 4),
-        "tokens_per_s_without_router": round(cfg.N / ((ms_per_step - kernels["router"]["avg_ms"]) / 1e3), 1),
+        "router_logits_in_step": fixed is None,
+        "ms_per_step_without_router": round(ms_per_step - kernels.get("router", {}).get("avg_ms", 0.0), 4),
+        "tokens_per_s_without_router": round(cfg.N / ((ms_per_step - kernels.get("router", {}).get("avg_ms", 0.0))
+                                                      / 1e3), 1),
+        "fixed_rows_per_expert": args.rows_per_expert or None,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),
