@@ -25,7 +25,7 @@ __all__ = [
     "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
     "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
     "moe_version", "moe_combine_backward", "moe_expert_gate_up_preact", "moe_swiglu_backward", "moe_expert_dgrad",
-    "moe_expert_wgrad", "moe_router_backward", "moe_stream_probe",
+    "moe_expert_wgrad", "moe_router_backward", "moe_router_input_grad", "moe_stream_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,7 @@ _SIGS = {
     "moe_expert_wgrad": [_P, _I, _P, _I, _P, _I, _I, _P, _I, _I, _P, _I, _P],
     "moe_router_backward": [_P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I, _P],
     "moe_stream_probe": [_P, _SZ, _I, _P, _P],
+    "moe_router_input_grad": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_status_str": [_I],
     "moe_version": [],
 }
@@ -485,6 +486,18 @@ def moe_router_backward(topk_gate: torch.Tensor, d_gate: torch.Tensor, offsets: 
         _ptr(topk_gate), _ptr(d_gate), N, k, _ptr(offsets), _ptr(src_slot), E, rows, _ptr(x), _dt(x), H, _ptr(dz),
         _ptr(dw_r), _dt(dw_r), _stream(x)))
     return dz, dw_r
+
+
+def moe_router_input_grad(w_r: torch.Tensor, topk_idx: torch.Tensor, dz: torch.Tensor,
+                          rest: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None):
+    """dx [N, H] = sum_j dz[t, j] W_r[topk_idx[t, j]] (+ rest): the router's input gradient."""
+    E, H = w_r.shape
+    N, k = topk_idx.shape
+    if dx is None:
+        dx = torch.empty((N, H), dtype=w_r.dtype, device=w_r.device)
+    _check("moe_router_input_grad", lib().moe_router_input_grad(
+        _ptr(w_r), _dt(w_r), N, E, H, k, _ptr(topk_idx), _ptr(dz), _ptr(rest), _ptr(dx), _dt(dx), _stream(w_r)))
+    return dx
 
 
 def moe_stream_probe(src: torch.Tensor, ratio: int, dst: Optional[torch.Tensor] = None) -> torch.Tensor:

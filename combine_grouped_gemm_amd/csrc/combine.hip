@@ -125,14 +125,22 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <bool kEoF32>
+// NT: the non-temporal hint (rows read once); otherwise plain loads (rows read by many
+// tokens, such as the router weight's rows in the router's input gradient)
+template <bool NT>
+__device__ __forceinline__ uint4 load_row16(const uint4* p) {
+  if (NT) return load_stream(p);
+  return *p;
+}
+
+template <bool kEoF32, bool NT>
 __device__ __forceinline__ void raw_load(const void* base, size_t row, int H, int c, Raw8<kEoF32>& r) {
   if (kEoF32) {
     const uint4* p = reinterpret_cast<const uint4*>(base) + (row * H) / 4 + 2 * c;
-    r.w[0] = load_stream(p);
-    r.w[kEoF32 ? 1 : 0] = load_stream(p + 1);
+    r.w[0] = load_row16<NT>(p);
+    r.w[kEoF32 ? 1 : 0] = load_row16<NT>(p + 1);
   } else {
-    r.w[0] = load_stream(reinterpret_cast<const uint4*>(base) + (row * H) / 8 + c);
+    r.w[0] = load_row16<NT>(reinterpret_cast<const uint4*>(base) + (row * H) / 8 + c);
   }
 }
 
@@ -155,7 +163,7 @@ __device__ __forceinline__ void raw_values(const Raw8<kEoF32>& r, float (&v)[8])
 
 // k <= KMAX <= 8: one pass = the k rows and the shared row of 8 columns, loaded together;
 // the next pass is loaded before this one is summed
-template <int KMAX, bool kEoF32, bool kYF32, bool kGated, bool kShared>
+template <int KMAX, bool kEoF32, bool kYF32, bool kGated, bool kShared, bool NT>
 __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel_small_k(
     const void* __restrict__ eo, int H, int k, const int32_t* __restrict__ send_pos,
     const float* __restrict__ gate, const void* __restrict__ shared, void* __restrict__ y, int spans) {
@@ -175,8 +183,8 @@ __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel_small_k(
   auto issue = [&](int c, Raw8<kEoF32> (&b)[NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (r[j] >= 0) raw_load<kEoF32>(eo, static_cast<size_t>(r[j]), H, c, b[j]);
-    if (kShared) raw_load<kEoF32>(shared, static_cast<size_t>(t), H, c, b[NB - 1]);
+      if (r[j] >= 0) raw_load<kEoF32, NT>(eo, static_cast<size_t>(r[j]), H, c, b[j]);
+    if (kShared) raw_load<kEoF32, true>(shared, static_cast<size_t>(t), H, c, b[NB - 1]);
   };
   auto finish = [&](int c, const Raw8<kEoF32> (&b)[NB]) __attribute__((always_inline)) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -225,7 +233,8 @@ __global__ __launch_bounds__(kCombMaxThreads) void combine_kernel_small_k(
 }
 
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
-                          const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s) {
+                          const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s,
+                          bool rows_once) {
   const int groups8 = H / 8;
   const int threads = groups8 % 256 == 0 || groups8 % 128 != 0 ? 256 : 128;
   // small batches: split each row into up to one span per workgroup pass, for ~8
@@ -242,12 +251,18 @@ hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, cons
     constexpr bool A = decltype(eo32)::value, B = decltype(y32)::value, G = decltype(gated)::value;
     auto small = [&](auto kmax) {
       constexpr int KM = decltype(kmax)::value;
-      if (shared != nullptr)
-        hipLaunchKernelGGL((combine_kernel_small_k<KM, A, B, G, true>), grid, block, 0, s, eo, H, k, send_pos, gate,
-                           shared, y, spans);
-      else
-        hipLaunchKernelGGL((combine_kernel_small_k<KM, A, B, G, false>), grid, block, 0, s, eo, H, k, send_pos,
+      if (shared != nullptr && rows_once)
+        hipLaunchKernelGGL((combine_kernel_small_k<KM, A, B, G, true, true>), grid, block, 0, s, eo, H, k, send_pos,
                            gate, shared, y, spans);
+      else if (shared != nullptr)
+        hipLaunchKernelGGL((combine_kernel_small_k<KM, A, B, G, true, false>), grid, block, 0, s, eo, H, k, send_pos,
+                           gate, shared, y, spans);
+      else if (rows_once)
+        hipLaunchKernelGGL((combine_kernel_small_k<KM, A, B, G, false, true>), grid, block, 0, s, eo, H, k, send_pos,
+                           gate, shared, y, spans);
+      else
+        hipLaunchKernelGGL((combine_kernel_small_k<KM, A, B, G, false, false>), grid, block, 0, s, eo, H, k,
+                           send_pos, gate, shared, y, spans);
     };
     if (k <= 2) small(std::integral_constant<int, 2>{});
     else if (k <= 4) small(std::integral_constant<int, 4>{});

@@ -318,6 +318,20 @@ moe_status moe_combine(const void* expert_out, moe_dtype eo_dt, int N, int H, in
                                         shared_out, y, y_dt == MOE_F32, stream));
 }
 
+moe_status moe_router_input_grad(const void* w_r, moe_dtype w_dt, int N, int E, int H, int k,
+                                 const int32_t* topk_idx, const float* dz, const void* rest, void* dx,
+                                 moe_dtype dx_dt, hipStream_t stream) {
+  if (N < 0 || E < 1 || H <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if ((w_dt != MOE_F32 && w_dt != MOE_BF16) || (dx_dt != MOE_F32 && dx_dt != MOE_BF16)) return MOE_ERR_UNSUPPORTED;
+  if (k > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS || N >= kMaxRowsPerLaunch || H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(N) * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  if (w_r == nullptr || topk_idx == nullptr || dz == nullptr || dx == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w_r) || !aligned16(dx) || (rest != nullptr && !aligned16(rest))) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(w_r, w_dt == MOE_F32, N, H, k, topk_idx, dz, rest, dx, dx_dt == MOE_F32,
+                                        stream, /*rows_once=*/false));
+}
+
 moe_status moe_stream_probe(const void* src, size_t n16, int ratio, void* dst, hipStream_t stream) {
   if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 9 && ratio != 16) return MOE_ERR_UNSUPPORTED;
   if (n16 == 0) return MOE_OK;

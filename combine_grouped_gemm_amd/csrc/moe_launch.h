@@ -31,8 +31,11 @@ size_t router_ws_bytes(int N, int H, int E, bool bf16);
 hipError_t launch_router_logits(const void* x, bool bf16, int N, int H, const void* w_r, int E, float* z,
                                 void* ws, hipStream_t s);
 
+// rows_once: every row of eo is named by at most one slot (the layer's expert outputs), so
+// its loads carry the non-temporal hint; false keeps them in the caches (rows re-read)
 hipError_t launch_combine(const void* eo, bool eo_f32, int N, int H, int k, const int32_t* send_pos,
-                          const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s);
+                          const float* gate, const void* shared, void* y, bool y_f32, hipStream_t s,
+                          bool rows_once = true);
 // read-mostly streaming probe: ratio in {1, 2, 4, 8, 9, 16}
 hipError_t launch_stream_probe(const void* src, size_t n16, int ratio, void* dst, hipStream_t s);
 

@@ -27,7 +27,7 @@ from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_E
                moe_expert_dgrad, moe_expert_down, moe_expert_down_shared, moe_expert_gate_up,
                moe_expert_gate_up_gathered, moe_expert_gate_up_gathered_shared, moe_expert_gate_up_preact,
                moe_expert_wgrad, moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route, moe_router_backward,
-               moe_router_logits, moe_swiglu_backward, moe_workspace_bytes)
+               moe_router_input_grad, moe_router_logits, moe_swiglu_backward, moe_workspace_bytes)
 
 
 class MoELayer:
@@ -330,7 +330,7 @@ class MoELayer:
             st += [
                 ("router_bwd", lambda: moe_router_backward(self.topk_gate, b["dg"], offsets, src_slot, x, b["dz"],
                                                            b["dw_r"])),
-                ("router_dx", lambda: moe_combine(self.w_r, self.topk_idx, b["dz"], rest_r, b["dx_r"])),
+                ("router_dx", lambda: moe_router_input_grad(self.w_r, self.topk_idx, b["dz"], rest_r, b["dx_r"])),
             ]
             rest = b["dx_r"]
         rest_x = rest

@@ -357,8 +357,9 @@ moe_status moe_stream_probe(const void* src, size_t n16, int ratio, void* dst, h
  *   moe_expert_wgrad            dW_down,e = d_expert_out_e^T h_e,  dW13_e = d_au_e^T x_e
  *   moe_expert_dgrad            d_perm = d_au W13_e
  *   moe_router_backward         dz on the selected logits, dW_r
- *   moe_combine (gates = dz, rows of W_r)  and  moe_combine (gates = NULL, rows of d_perm)
- *                               dx = sum_j dz_tj W_r[e_tj] + sum_j d_perm[send_pos[t,j]]
+ *   moe_router_input_grad       dx_r = sum_j dz_tj W_r[e_tj] (+ the shared expert's input gradient)
+ *   moe_combine (gates = NULL, rows of d_perm, + dx_r)
+ *                               dx = dx_r + sum_j d_perm[send_pos[t,j]]
  * (the shared expert: the same GEMMs with E = 1 on all N tokens and d_out = dy).
  * ------------------------------------------------------------------------------------ */
 
@@ -417,6 +418,23 @@ moe_status moe_expert_dgrad(const void* dC, const int32_t* offsets, int E, int r
 moe_status moe_expert_wgrad(const void* a, int M, const void* b, int N, const int32_t* b_rows, int b_div,
                             int b_nrows, const int32_t* offsets, int E, int rows, void* dw, moe_dtype dw_dt,
                             hipStream_t stream);
+
+/*
+ * moe_router_input_grad -- the router's share of the input gradient, through z = x W_r^T.
+ *
+ * Definition: "EP / DeepEP explanation" page, section 2 (z = the router's logits of x) and
+ * the chain rule: dx_t = sum_{j<k} dz_tj W_r[topk_idx[t,j]] (+ rest_t), fp32 sum in slot order
+ * then rest, one rounding to dx_dt.  The same gather-sum as moe_combine over the E rows of
+ * W_r, each row read by about N k / E slots, so its loads stay in the caches (moe_combine
+ * marks its loads as read once).
+ *   w_r [E, H] of w_dt (MOE_BF16 or MOE_F32); topk_idx [N, k] int32 in [0, E) (from
+ *   moe_route; negative ids are skipped, ids >= E are undefined behaviour); dz [N, k] fp32
+ *   (from moe_router_backward); rest [N, H] of w_dt or NULL; dx [N, H] of dx_dt out.
+ * Requires H % 8 == 0 and H * sizeof(w_dt) % 16 == 0; 16-byte aligned w_r, rest and dx.
+ */
+moe_status moe_router_input_grad(const void* w_r, moe_dtype w_dt, int N, int E, int H, int k,
+                                 const int32_t* topk_idx, const float* dz, const void* rest, void* dx,
+                                 moe_dtype dx_dt, hipStream_t stream);
 
 /*
  * moe_router_backward -- gradients through the renormalised gates into the router.

@@ -229,3 +229,19 @@ def test_backward_validation_and_workspace(L):
     assert f(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 8, FAKE, MOE_BF16, 100, FAKE, FAKE, MOE_F32, None) == \
         MOE_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, 4, 2, None, FAKE, 8, 8, FAKE, MOE_BF16, 256, FAKE, FAKE, MOE_F32, None) == MOE_ERR_INVALID_ARG
+
+
+def test_router_input_grad_validation(L):
+    f = L.moe_router_input_grad
+    ok = (FAKE, MOE_BF16, 8, 16, 256, 4, FAKE, FAKE, None, FAKE, MOE_BF16, None)
+    assert f(*ok[:1], MOE_BF16, 0, 16, 256, 4, None, None, None, None, MOE_BF16, None) == MOE_OK   # N = 0
+    assert f(FAKE, MOE_BF16, 8, 16, 256, 17, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG  # k > E
+    assert f(FAKE, MOE_BF16, -1, 16, 256, 4, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_FP8_E4M3, 8, 16, 256, 4, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_UNSUPPORTED
+    assert f(FAKE, MOE_BF16, 8, 16, 260, 4, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_UNSUPPORTED  # H % 8
+    assert f(FAKE, MOE_BF16, 8, 16, 256, 33, FAKE, FAKE, None, FAKE, MOE_BF16, None) in (MOE_ERR_UNSUPPORTED,
+                                                                                          MOE_ERR_INVALID_ARG)
+    assert f(None, MOE_BF16, 8, 16, 256, 4, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8, 16, 256, 4, None, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE + 8, MOE_BF16, 8, 16, 256, 4, FAKE, FAKE, None, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG
+    assert f(FAKE, MOE_BF16, 8, 16, 256, 4, FAKE, FAKE, FAKE + 8, FAKE, MOE_BF16, None) == MOE_ERR_INVALID_ARG

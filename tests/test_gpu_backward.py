@@ -237,6 +237,34 @@ def test_router_backward():
     assert not f64(dw_r[4]).any()
 
 
+@pytest.mark.parametrize("E,k,shared", [(256, 8, True), (8, 2, False), (64, 6, True)])
+def test_router_input_grad(E, k, shared):
+    """The router's input gradient dx_t = sum_j dz_tj W_r[e_tj] (+ rest): equal to moe_combine's
+    gather-sum over the rows of W_r bit for bit (the same arithmetic; only the loads' cache hint
+    differs), and within one bf16 step plus the fp32 sum bound of the exactly rounded sum."""
+    N, H = 300, 1024
+    say(f"router input gradient E={E} k={k}")
+    w_r = _n((E, H), 21)
+    idx = w.fixed_route(N, E, k, "random", seed=E + k)
+    dz = w.normal((N, k), w.stream_key(22, w.T_GATE, E), "cpu", torch.float32, std=1.0)
+    rest = _n((N, H), 23) if shared else None
+    got = moe.moe_router_input_grad(w_r, idx.to(DEV), dz.to(DEV), rest)
+    ref_c = moe.moe_combine(w_r, idx.to(DEV), dz.to(DEV), rest)
+    sync()
+    assert torch.equal(got.view(torch.int16), ref_c.view(torch.int16))
+    wr, d = f64(w_r), dz.numpy().astype(np.float64)
+    ref = np.zeros((N, H))
+    mag = np.zeros((N, H))
+    for j in range(k):
+        ref += d[:, j:j + 1] * wr[idx[:, j].numpy()]
+        mag += np.abs(d[:, j:j + 1] * wr[idx[:, j].numpy()])
+    if shared:
+        ref += f64(rest)
+        mag += np.abs(f64(rest))
+    tol = bf16_ulp(ref) * 1.0001 + (k + 1) * U32 * mag
+    assert np.all(np.abs(f64(got) - ref) <= tol + bf16_ulp(ref))
+
+
 SMALL = {
     "dsv3_small": w.CONFIGS["dsv3_bf16"].scaled(N=512, H=1024, E=64, I=256),
     "dsv3_zipf_small": w.CONFIGS["dsv3_zipf_bf16"].scaled(N=512, H=1024, E=64, I=256),
