@@ -357,11 +357,12 @@ def other_config(name, args, dev):
     alg = algorithmic(cfg, n_e, layer.gather, layer.fuse)
     kernels = summarize(per, alg, cfg.dtype)
     roof = roofline(cfg, alg, per, layer.fuse, layer.gather)
+    mem = {**layer.device_bytes(), "input_x": x.nbytes}
     del layer, inp, x, stages
     torch.cuda.empty_cache()
     return {"workload": workload_name(cfg), "dtype": cfg.dtype, "steps": steps, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(cfg.N / (ms / 1e3), 1), "imbalance": round(float(n_e.max() / n_e.mean()), 4),
-            "max_n_e": int(n_e.max()), "empty_experts": int((n_e == 0).sum()),
+            "max_n_e": int(n_e.max()), "empty_experts": int((n_e == 0).sum()), "device_bytes": mem,
             "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel")},
             "grouped_gemm_mfma_util": {"gate_up": kernels["gate_up"].get("mfma_frac"),
                                        "down": kernels["down"].get("mfma_frac")},
@@ -587,6 +588,7 @@ def main():
         "gates_in_down_epilogue": layer.gate_in_down,
         "combine_hbm_GBps": kernels["combine"]["GB_per_s"],
         "imbalance": round(float(n_e.max() / n_e.mean()), 4),
+        "device_bytes": {**layer.device_bytes(), "input_x": inp["x"].nbytes},
         "device_copy_GBps": copy_GBps,
         "read_mostly_probe_GBps": probe_GBps,
         "combine_vs_read_mostly_probe": round(kernels["combine"]["GB_per_s"] / probe_GBps, 4),

@@ -37,6 +37,31 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
       : "memory", "m0");
 }
 
+// The same load with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
+// (address = sbase + voff: no 64-bit address arithmetic per lane), into LDS at lds_part +
+// LDS_OFF (a constant added in the instruction stream, so the compiler keeps one LDS base
+// per buffer live instead of one per load).  The add writes SCC, which is declared.
+template <uint32_t LDS_OFF>
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_part) {
+  __asm__ volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_part), "n"(LDS_OFF)
+      : "memory", "m0", "scc");
+}
+
+// The lane index, computed where it is used (v_mbcnt in volatile assembly): a value the
+// compiler can neither hoist nor keep live, so it is never spilled and reloaded.  A reload
+// is a memory load the compiler waits for with vmcnt, and that count includes the
+// direct-to-LDS loads in flight.
+__device__ __forceinline__ uint32_t opaque_lane() {
+  uint32_t l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // D += A * B^T on one 32x32 block over 16 k: lane l supplies row l % 32, k 8 * (l / 32) ..
 // + 7 of both operands (any permutation of k applied to both operands alike is allowed)
 __device__ __forceinline__ f32x16_t mma_bf16(uint4 a, uint4 b, f32x16_t c) {

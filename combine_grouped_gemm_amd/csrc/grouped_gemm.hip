@@ -700,6 +700,13 @@ size_t gemm_tile_cap(int rows, int E) {
   return static_cast<size_t>((rows + kStreamTileRows - 1) / kStreamTileRows) + E;
 }
 
+// the 256 x 256 kernel numbers its tiles in 32 bits and splits them over the 8 XCDs by
+// multiplying the count by the XCD index: 8 x an upper bound of the tile count stays below 2^31
+static bool wide_tiles_fit(int mode, int rows, int n_seg, int I, int n_out) {
+  const long long n_blocks = mode == MODE_GATE_UP ? (I + 127) / 128 : (n_out + 255) / 256;
+  return static_cast<long long>(gemm_tile_cap(rows, n_seg)) * n_blocks * kNumXcd < (1LL << 31);
+}
+
 bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long b_rows, int a_nrows,
                                    bool gathered) {
   const long long rbytes = 2LL * K;
@@ -752,7 +759,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const long long rbytes = 2LL * K;
   const bool wide_ok = dma && K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 4 == 0 &&
                        b_rows * rbytes < (1LL << 32) &&
-                       (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
+                       (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32) &&
+                       wide_tiles_fit(mode, rows + shared_rows, n_seg, I, n_out);
   if ((shared_rows > 0 || row_gate != nullptr || au != nullptr) && (!wide_ok || stream))
     return hipErrorNotSupported;   // (callers check first)
   const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr || au != nullptr ||

@@ -33,8 +33,13 @@
 // row and runs of 4 adjacent output columns: the epilogue stores 8 bytes per lane.
 //
 // Ragged tiles: an expert's n_e rows are split into ceil(n_e / 256) tiles of equal size
-// (a multiple of 32 rows).  32-row blocks are dealt to the two row waves in turn, and a
-// wave skips the MFMAs and fragment reads of blocks without rows.
+// (a multiple of 32 rows).  A tile with an even number R of 32-row blocks deals them to the
+// two row waves in turn, and a wave skips the MFMAs and fragment reads of blocks without
+// rows: R / 2 row blocks x 4 column blocks per wave.  With R odd that layout leaves one row
+// wave a block short, so a tile with R = 1, 3 or 5 runs 1 x 4 instead: each wave takes all
+// R row blocks and 64 of the 256 weight rows (gate/up: 32 W_gate rows and the same 32 W_up
+// rows), 2 R MFMAs per k-step against (R + 1) / 2 x 4.  The accumulators are the same 16
+// blocks in both layouts; only the epilogue's row and column of each block differ.
 #include <utility>
 
 #include "gemm_device.h"
@@ -51,20 +56,31 @@ constexpr int kPart = kTM * kRowB;     // one stage of activation or weight rows
 constexpr int kWBase = 2 * kPart;      // weight ring after the two activation buffers
 constexpr int kLdsBytes = 5 * kPart;   // 160 KB
 constexpr int kThreads = 256;
-constexpr int kMB = 4, kNB = 4;        // 32 x 32 blocks per wave
+constexpr int kMB = 4, kNB = 4;        // 32 x 32 blocks per wave (2 x 2 layout)
+constexpr int kMB1 = 5, kNB1 = 2;      // at most 5 row blocks x 2 column blocks (1 x 4 layout)
 constexpr int kLd = kPart / 1024 / 4;  // 1 KB loads per wave and part (8)
 static_assert(kTM == kTN, "activation and weight parts have the same shape");
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f(std::integral_constant<int, I>{}), ...); }(
+      std::make_integer_sequence<int, N>{});
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
 
+  // the 1 x 4 layout for gate/up tiles only: the down GEMM's epilogue would need the gates of
+  // twice the rows per lane, and the extra registers cost its K loop more than the layout saves
+  constexpr bool kLay1 = MODE == MODE_GATE_UP;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
   const int wm = wave >> 1, wn = wave & 1;
   // loads: wave w moves the 8-row groups w, w + 4, ... of a part; lane l fills LDS slot l % 8
   // of row l / 8 of the group, so it loads chunk (l % 8) ^ key(row).  Bit 3 of every row of
@@ -79,20 +95,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // so with k_split = 8 each XCD's range is one column part (its slice of W_r stays in L2)
   const int mt_r = MODE == MODE_ROUTER ? (p.rows + kTM - 1) / kTM : 0;
   // routed tiles (expert -> n-block -> m-tile), then the shared segment's (m-tile -> n-block)
-  const long long n_r = MODE == MODE_ROUTER ? static_cast<long long>(p.k_split) * mt_r * nN
-                                            : static_cast<long long>(p.tile_prefix[p.E]) * nN;
-  const long long n_s = MODE != MODE_ROUTER && p.shared_rows > 0
-                            ? static_cast<long long>(p.tile_prefix[p.E + 1] - p.tile_prefix[p.E]) * nN
+  // (tile numbers are 32-bit: the launcher keeps 8 x the tile count below 2^31)
+  const int n_r = MODE == MODE_ROUTER ? p.k_split * mt_r * nN : p.tile_prefix[p.E] * nN;
+  const int n_s = MODE != MODE_ROUTER && p.shared_rows > 0
+                            ? (p.tile_prefix[p.E + 1] - p.tile_prefix[p.E]) * nN
                             : 0;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
   // each XCD takes a contiguous range of the routed tiles and one of the shared segment's
   // (4 m-tiles x all n-blocks for an 8192-row shared expert: its rows are read once per XCD)
-  const long long r_beg = n_r * xcd / kNumXcd, r_cnt = n_r * (xcd + 1) / kNumXcd - r_beg;
-  const long long s_beg = n_s * xcd / kNumXcd, s_cnt = n_s * (xcd + 1) / kNumXcd - s_beg;
-  const long long v_end = r_cnt + s_cnt;   // this XCD's tiles, numbered 0 .. v_end - 1
-  auto tile_of = [&](long long v) __attribute__((always_inline)) {
+  const int r_beg = n_r * xcd / kNumXcd, r_cnt = n_r * (xcd + 1) / kNumXcd - r_beg;
+  const int s_beg = n_s * xcd / kNumXcd, s_cnt = n_s * (xcd + 1) / kNumXcd - s_beg;
+  const int v_end = r_cnt + s_cnt;   // this XCD's tiles, numbered 0 .. v_end - 1
+  auto tile_of = [&](int v) __attribute__((always_inline)) {
     return v < r_cnt ? r_beg + v : n_r + s_beg + (v - r_cnt);
   };
   const int kspan = MODE == MODE_ROUTER ? p.K / p.k_split : p.K;   // K of one tile
@@ -100,20 +116,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   const uint32_t rb = static_cast<uint32_t>(p.K) * 2;       // row bytes of both operands
 
   const int hk = lane >> 5;
-  const int fkey = slot_key(lane & 31);
-  int koff[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) koff[s] = ((2 * s + hk) ^ fkey) * 16;
-  int a_frag[kMB], b_frag[kNB];
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) a_frag[mb] = ((mb * 2 + wm) * 32 + (lane & 31)) * kRowB;
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    // gate/up: blocks 0-1 are W_gate rows, blocks 2-3 the same W_up rows
-    const int r = MODE == MODE_GATE_UP ? (nb >> 1) * (kTN / 2) + wn * 64 + (nb & 1) * 32 + (lane & 31)
-                                       : wn * 128 + nb * 32 + (lane & 31);
-    b_frag[nb] = r * kRowB;
-  }
+  // first row of the wave's activation block m and weight block n, per layout (gate/up in
+  // the 2 x 2 layout: weight blocks 0-1 are W_gate rows, 2-3 the same W_up rows; in the
+  // 1 x 4 layout wave w holds weight rows 64 w .. 64 w + 63, gate/up: W_gate rows 32 w ..
+  // 32 w + 31 and the same W_up rows)
+  auto a_row = [&](int lay, int m) __attribute__((always_inline)) { return lay ? m * 32 : (2 * m + wm) * 32; };
+  auto b_row = [&](int lay, int n) __attribute__((always_inline)) {
+    if (MODE == MODE_GATE_UP)
+      return lay ? n * (kTN / 2) + wave * 32 : (n >> 1) * (kTN / 2) + wn * 64 + (n & 1) * 32;
+    return lay ? wave * 64 + n * 32 : wn * 128 + n * 32;
+  };
 
   // Tiles: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.  With
   // the counter, tiles adjacent in the order (the m-tiles sharing a weight panel, the
@@ -125,11 +137,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes - 4);
   const bool dynamic = p.tile_counter != nullptr;
   int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
-  long long v = slot;
+  int v = slot;
   if (dynamic) {
     if (tid == 0) *tile_word = atomicAdd(p.tile_counter + xcd, 1);
     __syncthreads();
-    v = *tile_word;
+    v = __builtin_amdgcn_readfirstlane(*tile_word);
   }
   if (v >= v_end) return;
 
@@ -139,14 +151,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     const uint8_t* b;
     uint32_t a_src[kLd], b_src[kLd];
   };
-  auto setup = [&](long long L, Tile& t) __attribute__((always_inline)) {
+  auto setup = [&](int L, Tile& t) __attribute__((always_inline)) {
     int e, mt_e, nblk, mtile, seg_lo, seg_hi, kp = 0;
     if (MODE == MODE_ROUTER) {
       e = 0;
       mt_e = mt_r;
-      const long long per = static_cast<long long>(mt_r) * nN;
+      const int per = mt_r * nN;
       kp = static_cast<int>(L / per);
-      const int local = static_cast<int>(L - kp * per);
+      const int local = L - kp * per;
       nblk = local / mt_r;
       mtile = local % mt_r;
       seg_lo = 0;
@@ -155,16 +167,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       e = p.tile_expert[L / nN];
       const int pe = p.tile_prefix[e];
       mt_e = p.tile_prefix[e + 1] - pe;
-      const long long local = L - static_cast<long long>(pe) * nN;
-      nblk = static_cast<int>(local / mt_e);
-      mtile = static_cast<int>(local % mt_e);
+      const int local = L - pe * nN;
+      nblk = local / mt_e;
+      mtile = local % mt_e;
       expert_segment(p, e, seg_lo, seg_hi);
     } else {   // the shared segment [rows, rows + shared_rows), weights shared_b
       e = p.E;
       mt_e = p.tile_prefix[p.E + 1] - p.tile_prefix[p.E];
-      const long long local = L - n_r;
-      mtile = static_cast<int>(local / nN);
-      nblk = static_cast<int>(local % nN);
+      const int local = L - n_r;
+      mtile = local / nN;
+      nblk = local % nN;
       seg_lo = p.rows;
       seg_hi = p.rows + p.shared_rows;
     }
@@ -204,31 +216,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       t.b_src[j] = wr * rb + lchunk * 16;
     }
   };
-  // activation rows of stage ks into buffer buf; weight rows of stage ks into ring slot ws
-  auto load_a = [&](const Tile& t, int ks, int buf, int j) __attribute__((always_inline)) {
-    const uint32_t base =
-        __builtin_amdgcn_readfirstlane(lds0 + static_cast<uint32_t>(buf * kPart + (wave + 4 * j) * 1024));
-    dma16(t.a + static_cast<size_t>(ks) * kRowB + t.a_src[j], base);
+  // activation rows of stage ks into buffer buf; weight rows of stage ks into ring slot ws.
+  // Load J of a part fills its 8-row group wave + 4 J: LDS part base + wave * 1 KB, plus J * 4 KB
+  // as a constant of the instruction.
+  const uint32_t lds_wave = lds0 + static_cast<uint32_t>(wave) * 1024;
+  auto load_a = [&]<int J>(const Tile& t, int ks, int buf) __attribute__((always_inline)) {
+    dma16s<J * 4096>(t.a + static_cast<size_t>(ks) * kRowB, t.a_src[J], lds_wave + buf * kPart);
   };
-  auto load_w = [&](const Tile& t, int ks, int ws, int j) __attribute__((always_inline)) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(
-        lds0 + static_cast<uint32_t>(kWBase + ws * kPart + (wave + 4 * j) * 1024));
-    dma16(t.b + static_cast<size_t>(ks) * kRowB + t.b_src[j], base);
+  auto load_w = [&]<int J>(const Tile& t, int ks, int ws) __attribute__((always_inline)) {
+    dma16s<J * 4096>(t.b + static_cast<size_t>(ks) * kRowB, t.b_src[J], lds_wave + kWBase + ws * kPart);
   };
   // prologue loads of a tile (stage 0 and 1); the caller waits for stage 0 and synchronises
   auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_a(t, 0, 0, j);
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_w(t, 0, 0, j);
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_w(t, 1, 1, j);
-#pragma unroll
-    for (int j = 0; j < kLd; ++j) load_a(t, 1, 1, j);
+    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
+    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 0, 0); });
+    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 1, 1); });
+    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 1, 1); });
   };
 
   Tile cur;
-  long long L = tile_of(v);
+  int L = tile_of(v);
   setup(L, cur);
   prologue(cur);
   wait_vmcnt<2 * kLd>();   // stage 0 landed; stage 1 may be in flight
@@ -242,36 +249,58 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 #pragma unroll
       for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16_t{};
 
-    int act = ((t.mlast + 32) / 32 - wm + 1) / 2;   // 32-row blocks of this wave that hold rows
-    act = act < 0 ? 0 : (act > kMB ? kMB : act);
+    const int nblk = (t.mlast + 32) / 32;   // 32-row blocks that hold rows (1 .. 8)
+    const bool lay1 = kLay1 && (nblk & 1) != 0 && nblk <= kMB1;
+    int act = lay1 ? nblk : (nblk - wm + 1) / 2;   // row blocks of this wave that hold rows
+    act = lay1 ? act : (act < 0 ? 0 : (act > kMB ? kMB : act));
 
-    auto k_loop = [&](auto act_c) __attribute__((always_inline)) {
+    auto k_loop = [&](auto act_c, auto lay_c) __attribute__((always_inline)) {
       constexpr int ACT = decltype(act_c)::value;
-      constexpr int kReads = ACT > 0 ? ACT + kNB : 0;   // fragment reads per k-step
-      uint4 f0a[kMB], f0b[kNB], f1a[kMB], f1b[kNB];
-      // fragment read r of a k-step, in the order the MFMAs use them: a0, b0..b3, a1, a2, a3
-      auto read_frag = [&](int r, int aoff, int boff, int s, uint4(&fa)[kMB], uint4(&fb)[kNB])
-          __attribute__((always_inline)) {
-        if (r == 0) fa[0] = *reinterpret_cast<const uint4*>(lds + aoff + a_frag[0] + koff[s]);
-        else if (r <= kNB) fb[r - 1] = *reinterpret_cast<const uint4*>(lds + boff + b_frag[r - 1] + koff[s]);
-        else fa[r - kNB] = *reinterpret_cast<const uint4*>(lds + aoff + a_frag[r - kNB] + koff[s]);
-      };
-      // the 16 MFMAs of a k-step on (ca, cb).  After MFMA i come fragment read i / 2 of the
-      // next k-step (into na, nb, when READ) and then between(i), all held in place by
-      // scheduling fences: the wave never stalls on a burst of LDS or memory instructions
-      // while the matrix pipe has nothing queued.
-      auto mfma_step = [&]<bool READ>(uint4(&ca)[kMB], uint4(&cb)[kNB], uint4(&na)[kMB], uint4(&nb)[kNB],
-                                      int aoff, int boff, int s, auto&& between) __attribute__((always_inline)) {
+      constexpr int LAY = decltype(lay_c)::value;      // 1: the 1 x 4 layout
+      constexpr int MB = LAY ? kMB1 : kMB, NB = LAY ? kNB1 : kNB;
+      constexpr int kReads = ACT > 0 ? ACT + NB : 0;   // fragment reads per k-step
+      uint4 f0a[MB], f0b[NB], f1a[MB], f1b[NB];
+      // fragment reads: lane l reads row l % 32 of a 32-row block, chunk 2 s + l / 32 of k-step
+      // s (swizzled).  fb[s] is the lane's part of the LDS offset; the block's first row
+      // (uniform) is the rest.  Computed here from the lane index, so that they live only
+      // through the K loop: kept across the epilogue they would be spilled, and the reload's
+      // wait before their first use would sit inside the loop.
+      const uint32_t ln = opaque_lane();
+      uint32_t fb[4];
 #pragma unroll
-        for (int i = 0; i < kMB * kNB; ++i) {
-          if (i / kNB < ACT) acc[i / kNB][i % kNB] = mma_bf16(cb[i % kNB], ca[i / kNB], acc[i / kNB][i % kNB]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (READ && (i & 1) == 0 && i / 2 < kReads) read_frag(i / 2, aoff, boff, s, na, nb);
-          between(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int s = 0; s < 4; ++s) fb[s] = (ln & 31) * kRowB + ((2 * s + (ln >> 5)) ^ slot_key(ln & 31)) * 16;
+      // fragment read r of a k-step, in the order the MFMAs use them: a0, b0 .. b(NB-1), a1, ..
+      auto read_frag = [&](int r, int aoff, int boff, int s, uint4(&fa)[MB], uint4(&fw)[NB])
+          __attribute__((always_inline)) {
+        if (r == 0) fa[0] = *reinterpret_cast<const uint4*>(lds + fb[s] + (aoff + a_row(LAY, 0) * kRowB));
+        else if (r <= NB)
+          fw[r - 1] = *reinterpret_cast<const uint4*>(lds + fb[s] + (boff + b_row(LAY, r - 1) * kRowB));
+        else
+          fa[r - NB] = *reinterpret_cast<const uint4*>(lds + fb[s] + (aoff + a_row(LAY, r - NB) * kRowB));
       };
-      auto nothing = [](int) __attribute__((always_inline)) {};
+      // the MFMAs of a k-step on (ca, cb), 16 slots: MFMA i is row block i / NB and column
+      // block i % NB.  After slot i come a fragment read of the next k-step (into na, nb, when
+      // READ: read i / 2 after even slots in the 2 x 2 layout, read i in the 1 x 4 one) and
+      // then between(i), all held in place by scheduling fences: the wave never stalls on a
+      // burst of LDS or memory instructions while the matrix pipe has nothing queued.  In the
+      // 1 x 4 layout, row block m and column block n accumulate in acc[m / 2][m % 2 + 2 n].
+      auto mfma_step = [&]<bool READ>(uint4(&ca)[MB], uint4(&cb)[NB], uint4(&na)[MB], uint4(&nb)[NB],
+                                      int aoff, int boff, int s, auto&& between) __attribute__((always_inline)) {
+        static_for<kMB * kNB>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int m = i / NB, n = i % NB;
+          if constexpr (m < ACT) {
+            f32x16_t& c = LAY ? acc[m / 2][(m & 1) + 2 * n] : acc[m][n];
+            c = mma_bf16(cb[n], ca[m], c);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int rd = LAY ? i : ((i & 1) == 0 ? i / 2 : kReads);
+          if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
+          between(ic);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      auto nothing = [](auto) __attribute__((always_inline)) {};
 
 #pragma unroll
       for (int r = 0; r < kReads; ++r) read_frag(r, 0, kWBase, 0, f0a, f0b);
@@ -281,11 +310,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         constexpr int buf = PAR, nbuf = PAR ^ 1;
         const int ws1 = ws == 2 ? 0 : ws + 1, ws2 = ws1 == 2 ? 0 : ws1 + 1;
         const int aoff = buf * kPart, boff = kWBase + ws * kPart;
-        mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 1, [&](int i) __attribute__((always_inline)) {
-          if (FULL && (i & 3) == 1) load_w(t, ks + 2, ws2, i >> 2);
+        mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 1, [&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (FULL && (i & 3) == 1) load_w.template operator()<(i >> 2)>(t, ks + 2, ws2);
         });
-        mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, [&](int i) __attribute__((always_inline)) {
-          if (FULL && (i & 3) == 1) load_w(t, ks + 2, ws2, 4 + (i >> 2));
+        mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, [&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (FULL && (i & 3) == 1) load_w.template operator()<4 + (i >> 2)>(t, ks + 2, ws2);
         });
         mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 3, nothing);
         if constexpr (NEXT) {
@@ -298,10 +329,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         }
         __builtin_amdgcn_sched_barrier(0);
         mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPart, kWBase + ws1 * kPart, 0,
-                                            [&](int i) __attribute__((always_inline)) {
-          if (FULL && (i & 1) == 1) load_a(t, ks + 2, buf, i >> 1);
+                                            [&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (FULL && (i & 1) == 1) load_a.template operator()<(i >> 1)>(t, ks + 2, buf);
           // second-to-last stage (its wait for loads is behind it): take the next tile
-          if (!FULL && NEXT && i == 0 && dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
+          if constexpr (!FULL && NEXT && i == 0)
+            if (dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
         });
       };
       int ks = 0, ws = 0;
@@ -315,33 +348,46 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       ws = ws == 2 ? 0 : ws + 1;
       stage.template operator()<false, false, 1>(nk - 1, ws);
     };
-    [&]<int... A>(std::integer_sequence<int, A...>) {
-      ((act == A ? k_loop(std::integral_constant<int, A>{}) : void()), ...);
-    }(std::make_integer_sequence<int, kMB + 1>{});
+    if (kLay1 && lay1) {
+      [&]<int... A>(std::integer_sequence<int, A...>) {
+        ((act == 2 * A + 1 ? k_loop(std::integral_constant<int, 2 * A + 1>{}, std::integral_constant<int, 1>{})
+                           : void()),
+         ...);
+      }(std::make_integer_sequence<int, (kMB1 + 1) / 2>{});
+    } else {
+      [&]<int... A>(std::integer_sequence<int, A...>) {
+        ((act == A ? k_loop(std::integral_constant<int, A>{}, std::integral_constant<int, 0>{}) : void()), ...);
+      }(std::make_integer_sequence<int, kMB + 1>{});
+    }
 
     // ---- tile boundary: every wave is past its last LDS reads; the next tile is known
     block_barrier();
-    long long vn = v + per_xcd;
+    int vn = v + per_xcd;
     if (dynamic) {
       if (tid == 0) *tile_word = grabbed;
       wait_lgkmcnt_all();
       block_barrier();
-      vn = *tile_word;
+      vn = __builtin_amdgcn_readfirstlane(*tile_word);
     }
     const bool more = vn < v_end;
-    const long long Ln = more ? tile_of(vn) : 0;
+    const int Ln = more ? tile_of(vn) : 0;
 
-    // ---- epilogue: lane l holds token row (2 mb + wm) * 32 + l % 32 of the tile and, in
-    // registers 4q .. 4q+3 of block nb, output columns nb * 32 + 8q + 4 (l / 32) + 0..3:
-    // one 8-byte store per run (16 bytes for fp32 router sums; n_cols % 4 == 0, so a run is
-    // all in or all out)
+    // ---- epilogue: block acc[mb][nb] holds, in lane l, token row rblk * 32 + l % 32 of the
+    // tile and, in registers 4q .. 4q+3, output columns cblk + 8q + 4 (l / 32) + 0..3 (2 x 2:
+    // rblk = 2 mb + wm, cblk = 32 nb of the wave's 128 columns; 1 x 4: rblk = 2 mb + nb % 2,
+    // cblk = 32 (nb / 2) of the wave's 64): one 8-byte store per run (16 bytes for fp32
+    // router sums; n_cols % 4 == 0, so a run is all in or all out).  Gate/up pairs the gate
+    // block nb < 2 with the up block nb + 2 of the same rows and columns.
+    auto row_of = [&](int mb, int h) __attribute__((always_inline)) {
+      return t.m0 + (kLay1 && lay1 ? 2 * mb + h : 2 * mb + wm) * 32 + (lane & 31);
+    };
     // down with gates: a routed row carries the gate of its slot (the shared rows gate 1).
     // The gates are loaded first and waited for once: a load pending across the stores'
     // row and column branches would make the compiler wait for every store before the next.
-    float gsv[kMB];
+    float gsv[kMB];   // (only the down GEMM has gates, and it runs the 2 x 2 layout)
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
-      const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
+      const int r = row_of(mb, 0);
       gsv[mb] = 1.0f;
       if (MODE == MODE_DOWN && p.row_gate != nullptr && r < p.rows && r < t.mend) {
         int sl = p.row_slot[r];
@@ -352,16 +398,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     if (MODE == MODE_DOWN) wait_vmcnt<0>();
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
-      const int r = t.m0 + (mb * 2 + wm) * 32 + (lane & 31);
-      if (r >= t.mend) continue;
-      const float gs = gsv[mb];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (MODE == MODE_GATE_UP) {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            const int col = t.c0 + wn * 64 + nb * 32 + 8 * q + 4 * hk;
-            if (col >= n_cols) continue;
+            const int r = row_of(mb, nb);
+            const int col = t.c0 + (lay1 ? wave * 32 : wn * 64 + nb * 32) + 8 * q + 4 * hk;
+            if (r >= t.mend || col >= n_cols) continue;
             float hv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -384,8 +428,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         } else if (MODE == MODE_ROUTER) {
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int col = t.c0 + wn * 128 + nb * 32 + 8 * q + 4 * hk;
-            if (col >= n_cols) continue;
+            const int r = row_of(mb, nb & 1);
+            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * 128 + nb * 32) + 8 * q + 4 * hk;
+            if (r >= t.mend || col >= n_cols) continue;
             const f32x16_t& a = acc[mb][nb];
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) +
                                        (static_cast<size_t>(t.kp) * p.rows + r) * p.n_out + col) =
@@ -394,8 +439,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         } else {
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int col = t.c0 + wn * 128 + nb * 32 + 8 * q + 4 * hk;
-            if (col >= n_cols) continue;
+            const int r = row_of(mb, nb & 1);
+            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * 128 + nb * 32) + 8 * q + 4 * hk;
+            if (r >= t.mend || col >= n_cols) continue;
+            const float gs = gsv[mb];
             const f32x16_t& a = acc[mb][nb];
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.n_out + col) =
                 make_uint2(pack_bf16x2(a[4 * q] * gs, a[4 * q + 1] * gs),

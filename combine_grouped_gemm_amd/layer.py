@@ -113,6 +113,33 @@ class MoELayer:
         self.au_saved = False    # the last forward kept them
         self.au_all = None
 
+    _WEIGHTS = ("w13", "w2", "w13_scale", "w2_scale", "sw13", "sw2", "sw13_scale", "sw2_scale", "w_r", "bias")
+    _WEIGHT_GRADS = ("dw13", "dw2", "dsw13", "dsw2", "dw_r")
+
+    def device_bytes(self) -> dict:
+        """Bytes of device memory the layer holds, by kind (each allocation counted once).
+
+        weights: the routed, shared and router weights, fp8 scales included; workspace: the
+        library's scratch buffers; activations: the forward's other buffers (logits, routes,
+        layout, permuted rows, h, expert outputs, y; the kept pre-activations once a training
+        forward ran).  After a backward also weight_grads and backward (its intermediates and
+        workspaces).  The caller's input x is not the layer's and is not counted.
+        """
+        seen, out = set(), {"weights": 0, "activations": 0, "workspace": 0}
+
+        def add(kind, v):
+            for t in (v if isinstance(v, tuple) else (v,)):
+                if isinstance(t, torch.Tensor) and t.is_cuda and t.untyped_storage().data_ptr() not in seen:
+                    seen.add(t.untyped_storage().data_ptr())
+                    out[kind] = out.get(kind, 0) + t.untyped_storage().nbytes()
+
+        for name, v in vars(self).items():
+            if name != "grads":
+                add("weights" if name in self._WEIGHTS else "workspace" if name.endswith("_ws") else "activations", v)
+        for name, v in (getattr(self, "grads", None) or {}).items():
+            add("weight_grads" if name in self._WEIGHT_GRADS else "backward", v)
+        return out
+
     @property
     def expert_out(self) -> torch.Tensor:
         """The routed experts' outputs [N*k, H] of the last forward."""

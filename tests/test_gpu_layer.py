@@ -98,6 +98,34 @@ def _build(cfg, sentinel=False):
     return inp, layer, y
 
 
+@pytest.mark.parametrize("name", ["dsv3_small", "decode_fp8_small"])
+def test_device_bytes_accounts_for_every_allocation(name):
+    """The layer's device_bytes sums to what the allocator handed out while the layer was
+    built and ran (each block rounded up to 512 bytes), and the weights are the sizes of the
+    weight tensors."""
+    cfg = SMALL[name]
+    inp = with_logits(w.make_layer_inputs(cfg, DEV))
+    sync()
+    before = torch.cuda.memory_allocated(DEV)
+    layer = MoELayer(cfg.N, cfg.H, cfg.E, cfg.k, cfg.I, cfg.dtype, inp["w13"], inp["w2"],
+                     inp.get("sw13"), inp.get("sw2"), cfg.n_group, cfg.topk_group, inp["bias"])
+    layer.forward(inp["x"], inp["z"])
+    sync()
+    grown = torch.cuda.memory_allocated(DEV) - before
+    got = layer.device_bytes()
+    # the caller's tensors the layer keeps: the routing bias, and the weights unless fp8
+    # (then it holds quantized copies of its own)
+    callers = [inp["bias"]] + ([] if cfg.dtype == "fp8" else [inp["w13"], inp["w2"], inp.get("sw13"), inp.get("sw2")])
+    caller_bytes = sum(t.nbytes for t in callers if t is not None)
+    held = sum(got.values()) - caller_bytes
+    n_blocks = sum(1 for v in vars(layer).values() for t in (v if isinstance(v, tuple) else (v,))
+                   if isinstance(t, torch.Tensor))
+    assert held <= grown <= held + 512 * n_blocks
+    if cfg.dtype != "fp8":
+        assert got["weights"] == caller_bytes
+    assert got["activations"] >= layer.y.nbytes + layer.topk_idx.nbytes and got["workspace"] > 0
+
+
 def _check_routing(cfg, inp, layer):
     b = inp["bias_cpu"]
     ridx, rgate = oracle.route(inp["z_cpu"].numpy(), cfg.k, None if b is None else b.numpy(),
