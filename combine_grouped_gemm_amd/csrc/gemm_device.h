@@ -62,6 +62,19 @@ __device__ __forceinline__ uint32_t opaque_lane() {
   return l;
 }
 
+// 4 bytes per lane into LDS at lds_part + LDS_OFF + 4 * lane (a gather: each lane its own
+// address sbase + voff)
+template <uint32_t LDS_OFF>
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds_part) {
+  __asm__ volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_part), "n"(LDS_OFF)
+      : "memory", "m0", "scc");
+}
+
 // D += A * B^T on one 32x32 block over 16 k: lane l supplies row l % 32, k 8 * (l / 32) ..
 // + 7 of both operands (any permutation of k applied to both operands alike is allowed)
 __device__ __forceinline__ f32x16_t mma_bf16(uint4 a, uint4 b, f32x16_t c) {

@@ -58,6 +58,6 @@ constexpr int kWideTileRows = 256;
 // MODE_ROUTER (one segment [0, rows), no tile schedule, static tile order): tile
 // (part s, n-block, m-tile) multiplies columns [s K/k_split, (s+1) K/k_split) of a and b
 // (K / k_split a multiple of 128) and stores its fp32 sums, 16 bytes per run (n_out % 4 == 0).
-hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s);
+hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s, bool w8 = false);
 
 }  // namespace moe

@@ -25,8 +25,9 @@
 //
 // fp8 layers: the gate/up GEMM multiplies e4m3 codes on the fp8 MFMA, sums each 128-wide
 // K block in a separate fp32 accumulator and adds it scaled by a_scale[row] *
-// w_scale[col]; the down GEMM converts e4m3 W_down to bf16 (exactly) on its way to LDS,
-// multiplies against bf16 h, and scales each 128-wide K block by w_scale[col].
+// w_scale[col]; the down GEMM dequantizes e4m3 W_down on its way to LDS (code times its
+// 128-column block's scale, rounded once to bf16, as a bf16 weight is stored) and multiplies
+// it against bf16 h like a bf16 weight.
 #include <type_traits>
 #include <utility>
 
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int esz = CTraits<CT>::esz;
   constexpr int BK = GKB / esz;                 // K elements per stage
   constexpr int KSTEPS = BK / 16;               // 16-wide MFMA steps per stage
-  constexpr bool kScaled = (CT == CT_FP8) || B8;
+  constexpr bool kScaled = CT == CT_FP8;   // per-block scales on both operands: a second accumulator
   constexpr int kStagesPerBlock = 128 / BK;     // stages per 128-wide scale block
   constexpr int kAStage = GBM * GPITCH;
   constexpr int kBStage = GBN * GPITCH;
@@ -208,12 +209,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
     const uint8_t* b_tile = p.b + (static_cast<size_t>(e) * p.b_rows + b_row0) * b_rb;
     const int b_rows_left = MODE == MODE_GATE_UP ? GBN : static_cast<int>(p.n_out - b_row0);  // valid B tile rows
     const float* sa_tile = CT == CT_FP8 ? p.a_scale + static_cast<size_t>(m0) * kblocks : nullptr;
-    const float* sb_tile = kScaled ? p.b_scale + (static_cast<size_t>(e) * p.b_rows + b_row0) * kblocks : nullptr;
+    const float* sb_tile =
+        kScaled || B8 ? p.b_scale + (static_cast<size_t>(e) * p.b_rows + b_row0) * kblocks : nullptr;
 
     struct Regs {
       uint4 a[kAChunks];
       uint4 b[kBChunks];
       uint2 b8[kBChunks];
+      float s8[kBChunks];   // (B8) the scale of each e4m3 chunk's row and K block
       float sa, sb;
     };
 
@@ -238,6 +241,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
         if (B8) r.b8[i] = *reinterpret_cast<const uint2*>(bb + off);
         else r.b[i] = *reinterpret_cast<const uint4*>(bb + off);
       }
+      if (B8) {
+        const int kb = (ks * BK) / 128;
+#pragma unroll
+        for (int i = 0; i < kBChunks; ++i) r.s8[i] = sb_tile[static_cast<size_t>(b_tile_row(t_row + 32 * i)) * kblocks + kb];
+      }
       if (kScaled) {
         const int kb = (ks * BK) / 128;
         r.sa = 1.0f;
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
       for (int i = 0; i < kBChunks; ++i) {
         uint4 v;
         if (B8) {
-          const uint2 lo = e4m3x4_to_bf16x4(r.b8[i].x), hi = e4m3x4_to_bf16x4(r.b8[i].y);
+          const uint2 lo = e4m3x4_scaled_to_bf16x4(r.b8[i].x, r.s8[i]), hi = e4m3x4_scaled_to_bf16x4(r.b8[i].y, r.s8[i]);
           v = make_uint4(lo.x, lo.y, hi.x, hi.y);
         } else {
           v = r.b[i];
@@ -765,7 +773,13 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
     return hipErrorNotSupported;   // (callers check first)
   const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr || au != nullptr ||
                                 mode == MODE_GATE_UP || E > 1);
-  const int tile_rows = stream ? kStreamTileRows : (wide ? kWideTileRows : (dma ? kDM : GBM));
+  // e4m3 down weights at more than 16 rows per expert: the 256 x 256 kernel, which converts
+  // each weight fragment (code times its block's scale) as it reads it from LDS
+  const bool wide8 = mode == MODE_DOWN && ct == CT_BF16 && b8 && !stream && K % 128 == 0 && n_out % 4 == 0 &&
+                     b_rows * K < (1LL << 32) && b_rows * (K / 128) * 4 < (1LL << 32) &&
+                     static_cast<long long>(kWideTileRows) * rbytes < (1LL << 32) && shared_rows == 0 &&
+                     au == nullptr && a_rows == nullptr && wide_tiles_fit(mode, rows, n_seg, I, n_out);
+  const int tile_rows = stream ? kStreamTileRows : (wide || wide8 ? kWideTileRows : (dma ? kDM : GBM));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert, tile_counter, shared_rows);
   GemmArgs p;
@@ -796,9 +810,9 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.k_split = 1;
   p.au = au;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
-  if (wide) {
+  if (wide || wide8) {
     p.tile_counter = tile_counter;
-    return launch_grouped_gemm_wide(mode, p, s);
+    return launch_grouped_gemm_wide(mode, p, s, wide8);
   }
   const dim3 grid(persistent_grid()), block(GTHREADS);
 #define MOE_LAUNCH(CT_, B8_, MODE_) \

@@ -62,6 +62,9 @@ constexpr int kLd = kPart / 1024 / 4;  // 1 KB loads per wave and part (8)
 static_assert(kTM == kTN, "activation and weight parts have the same shape");
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// (W8) 64-byte weight rows: chunk c of row r sits in slot c ^ key4(r); a fragment read (32 rows,
+// 8 bytes of one chunk per lane) then spreads over 16 of the 32 eight-byte bank pairs
+__device__ __forceinline__ int key4(int r) { return (r >> 2) & 3; }
 
 // f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order
 template <int N, typename F>
@@ -70,9 +73,21 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
-template <int MODE>
+// W8: e4m3 weights with fp32 scales per 128-column block (the down GEMM of an fp8 layer).  A
+// stage then holds 64 codes (64 bytes) of each weight row, loaded direct to LDS, and the 256
+// rows' scales of the stage's block, gathered into a ring of their own; a weight fragment is
+// converted to bf16 (code times scale, rounded once) after it is read from LDS, and the MFMAs
+// are the bf16 ones.
+template <int MODE, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  static_assert(!W8 || MODE == MODE_DOWN, "e4m3 weights: the down GEMM");
+  constexpr int kWRowB = W8 ? 64 : kRowB;           // bytes of a weight row per stage
+  constexpr int kWPart = kTN * kWRowB;              // one stage of weight rows (32 KB; 16 KB)
+  constexpr int kLdW = kWPart / 1024 / 4;           // weight loads per wave and stage (8; 4)
+  constexpr int kStageLd = kLdW + (W8 ? 1 : 0);     // + the scale gather (W8)
+  constexpr int kSBase = kWBase + 3 * kWPart;       // (W8) scale ring: three slots of 1 KB
+  constexpr int kLdsTot = kSBase + (W8 ? 3 * 1024 : 0);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsTot];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
 
   // the 1 x 4 layout for gate/up tiles only: the down GEMM's epilogue would need the gates of
@@ -113,7 +128,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   };
   const int kspan = MODE == MODE_ROUTER ? p.K / p.k_split : p.K;   // K of one tile
   const int nk = kspan / 64;                                // even: kspan % 128 == 0
-  const uint32_t rb = static_cast<uint32_t>(p.K) * 2;       // row bytes of both operands
+  const uint32_t rb = static_cast<uint32_t>(p.K) * 2;       // row bytes of the activations
+  const uint32_t rbw = W8 ? static_cast<uint32_t>(p.K) : rb;   // row bytes of the weights
+  const uint32_t kblk = static_cast<uint32_t>(p.K) / 128;      // (W8) scale blocks per weight row
 
   const int hk = lane >> 5;
   // first row of the wave's activation block m and weight block n, per layout (gate/up in
@@ -133,8 +150,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // tiles cost.  Wave 0 takes the next index during the tile's second-to-last stage (late
   // enough that the take is still close to the start, early enough to hide its latency) and
   // hands it to the other waves at the tile boundary through the last word of ring slot 2
-  // (no load writes that slot between a boundary and the first stage).
-  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes - 4);
+  // (of the scale ring with W8; no load writes that slot between a boundary and the first
+  // stage).
+  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsTot - 4);
   const bool dynamic = p.tile_counter != nullptr;
   int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
   int v = slot;
@@ -149,7 +167,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     int m0, mend, mlast, c0, kp;   // (kp: the router's column part)
     const uint8_t* a;
     const uint8_t* b;
+    const uint8_t* sc;             // (W8) the expert's scales [n_out, K / 128]
     uint32_t a_src[kLd], b_src[kLd];
+    uint32_t s_src;                // (W8) this lane's scale row offset
   };
   auto setup = [&](int L, Tile& t) __attribute__((always_inline)) {
     int e, mt_e, nblk, mtile, seg_lo, seg_hi, kp = 0;
@@ -191,7 +211,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     // that a_nrows * rb fits in 32 bits); rows past the segment or the matrix re-read the
     // last valid one
     t.a = p.a_rows ? p.a : p.a + static_cast<size_t>(t.m0) * rb;
-    t.b = e < p.E ? p.b + static_cast<size_t>(e) * p.b_rows * rb : p.shared_b;
+    t.b = e < p.E ? p.b + static_cast<size_t>(e) * p.b_rows * rbw : p.shared_b;
+    if constexpr (W8) {   // (no shared segment with W8: the launcher checks)
+      t.sc = reinterpret_cast<const uint8_t*>(p.b_scale + static_cast<size_t>(e) * p.b_rows * kblk);
+      // scale gather: wave w's lane l fetches the scale of tile weight row 64 w + l
+      const int r = wave * 64 + lane;
+      t.s_src = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast)) * kblk * 4;
+    }
     if (MODE == MODE_ROUTER) {
       t.a += static_cast<size_t>(kp) * kspan * 2;
       t.b += static_cast<size_t>(kp) * kspan * 2;
@@ -214,6 +240,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         wr = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
       }
       t.b_src[j] = wr * rb + lchunk * 16;
+      if constexpr (W8) {
+        // 64-byte rows: load j fills the 16-row group wave + 4 j; lane l fills LDS slot l % 4
+        // of row l / 4 of the group, so it loads chunk (l % 4) ^ key4(row)
+        if (j < kLdW) {
+          const int r8 = (wave + 4 * j) * 16 + (lane >> 2);
+          const uint32_t w8 = static_cast<uint32_t>(t.c0 + (r8 < clast ? r8 : clast));
+          t.b_src[j] = w8 * rbw + static_cast<uint32_t>((lane & 3) ^ key4(r8)) * 16;
+        }
+      }
     }
   };
   // activation rows of stage ks into buffer buf; weight rows of stage ks into ring slot ws.
@@ -224,13 +259,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     dma16s<J * 4096>(t.a + static_cast<size_t>(ks) * kRowB, t.a_src[J], lds_wave + buf * kPart);
   };
   auto load_w = [&]<int J>(const Tile& t, int ks, int ws) __attribute__((always_inline)) {
-    dma16s<J * 4096>(t.b + static_cast<size_t>(ks) * kRowB, t.b_src[J], lds_wave + kWBase + ws * kPart);
+    dma16s<J * 4096>(t.b + static_cast<size_t>(ks) * kWRowB, t.b_src[J], lds_wave + kWBase + ws * kWPart);
+  };
+  // (W8) the scales of stage ks (block ks / 2) of the tile's 256 weight rows into scale slot ws
+  auto load_s = [&](const Tile& t, int ks, int ws) __attribute__((always_inline)) {
+    dma4s<0>(t.sc + static_cast<size_t>(ks >> 1) * 4, t.s_src,
+             lds0 + static_cast<uint32_t>(kSBase + ws * 1024 + wave * 256));
   };
   // prologue loads of a tile (stage 0 and 1); the caller waits for stage 0 and synchronises
   auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
     static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
-    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 0, 0); });
-    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 1, 1); });
+    static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 0, 0); });
+    if constexpr (W8) load_s(t, 0, 0);
+    static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 1, 1); });
+    if constexpr (W8) load_s(t, 1, 1);
     static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 1, 1); });
   };
 
@@ -238,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   int L = tile_of(v);
   setup(L, cur);
   prologue(cur);
-  wait_vmcnt<2 * kLd>();   // stage 0 landed; stage 1 may be in flight
+  wait_vmcnt<kStageLd + kLd>();   // stage 0 landed; stage 1 may be in flight
   block_barrier();
 
   for (;;) {
@@ -269,12 +311,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       uint32_t fb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) fb[s] = (ln & 31) * kRowB + ((2 * s + (ln >> 5)) ^ slot_key(ln & 31)) * 16;
+      // (W8) weight fragments: 8 codes at chunk s, half l / 32, of the 64-byte row; read raw,
+      // then converted with the row's block scale (sc_cur: this stage's, sc_nxt: the next one's)
+      uint32_t fbw[4];
+      uint2 wraw[NB];
+      float sc_cur[NB], sc_nxt[NB];
+      if constexpr (W8) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) fbw[s] = (ln & 31) * 64 + ((s ^ key4(ln & 31)) * 16) + (ln >> 5) * 8;
+      }
+      auto read_scales = [&](int ws, float(&sc)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+          sc[n] = *reinterpret_cast<const float*>(lds + kSBase + ws * 1024 + (b_row(0, n) + (ln & 31)) * 4);
+      };
       // fragment read r of a k-step, in the order the MFMAs use them: a0, b0 .. b(NB-1), a1, ..
       auto read_frag = [&](int r, int aoff, int boff, int s, uint4(&fa)[MB], uint4(&fw)[NB])
           __attribute__((always_inline)) {
         if (r == 0) fa[0] = *reinterpret_cast<const uint4*>(lds + fb[s] + (aoff + a_row(LAY, 0) * kRowB));
-        else if (r <= NB)
-          fw[r - 1] = *reinterpret_cast<const uint4*>(lds + fb[s] + (boff + b_row(LAY, r - 1) * kRowB));
+        else if (r <= NB) {
+          if constexpr (W8)
+            wraw[r - 1] = *reinterpret_cast<const uint2*>(lds + fbw[s] + (boff + b_row(LAY, r - 1) * kWRowB));
+          else
+            fw[r - 1] = *reinterpret_cast<const uint4*>(lds + fb[s] + (boff + b_row(LAY, r - 1) * kRowB));
+        }
         else
           fa[r - NB] = *reinterpret_cast<const uint4*>(lds + fb[s] + (aoff + a_row(LAY, r - NB) * kRowB));
       };
@@ -285,7 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       // burst of LDS or memory instructions while the matrix pipe has nothing queued.  In the
       // 1 x 4 layout, row block m and column block n accumulate in acc[m / 2][m % 2 + 2 n].
       auto mfma_step = [&]<bool READ>(uint4(&ca)[MB], uint4(&cb)[NB], uint4(&na)[MB], uint4(&nb)[NB],
-                                      int aoff, int boff, int s, auto&& between) __attribute__((always_inline)) {
+                                      int aoff, int boff, int s, const float(&scn)[NB], auto&& between)
+          __attribute__((always_inline)) {
         static_for<kMB * kNB>([&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
           constexpr int m = i / NB, n = i % NB;
@@ -296,6 +357,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
           __builtin_amdgcn_sched_barrier(0);
           constexpr int rd = LAY ? i : ((i & 1) == 0 ? i / 2 : kReads);
           if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
+          // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n, converted at 9 + 2 n
+          if constexpr (W8 && READ && ACT > 0 && i >= 9 && (i & 1) == 1)
+            nb[(i - 9) / 2] = e4m3x8_scaled_to_bf16x8(wraw[(i - 9) / 2], scn[(i - 9) / 2]);
           between(ic);
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -304,31 +368,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
 #pragma unroll
       for (int r = 0; r < kReads; ++r) read_frag(r, 0, kWBase, 0, f0a, f0b);
+      if constexpr (W8 && ACT > 0) {
+        read_scales(0, sc_cur);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) f0b[n] = e4m3x8_scaled_to_bf16x8(wraw[n], sc_cur[n]);
+      }
       // stage ks: activation rows in buffer PAR = ks & 1, weight rows in ring slot ws = ks % 3.
       // FULL: stage ks+2 exists; NEXT: stage ks+1 exists
       auto stage = [&]<bool FULL, bool NEXT, int PAR>(int ks, int ws) __attribute__((always_inline)) {
         constexpr int buf = PAR, nbuf = PAR ^ 1;
         const int ws1 = ws == 2 ? 0 : ws + 1, ws2 = ws1 == 2 ? 0 : ws1 + 1;
-        const int aoff = buf * kPart, boff = kWBase + ws * kPart;
-        mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 1, [&](auto ic) __attribute__((always_inline)) {
+        const int aoff = buf * kPart, boff = kWBase + ws * kWPart;
+        mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 1, sc_cur, [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (FULL && (i & 3) == 1) load_w.template operator()<(i >> 2)>(t, ks + 2, ws2);
+          if constexpr (FULL && (i & 3) == 1 && (i >> 2) < kLdW) load_w.template operator()<(i >> 2)>(t, ks + 2, ws2);
         });
-        mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, [&](auto ic) __attribute__((always_inline)) {
+        mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, sc_cur, [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (FULL && (i & 3) == 1) load_w.template operator()<4 + (i >> 2)>(t, ks + 2, ws2);
+          if constexpr (FULL && (i & 3) == 1 && 4 + (i >> 2) < kLdW) load_w.template operator()<4 + (i >> 2)>(t, ks + 2, ws2);
+          if constexpr (W8 && FULL && i == 1) load_s(t, ks + 2, ws2);
         });
-        mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 3, nothing);
+        mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 3, sc_cur, nothing);
         if constexpr (NEXT) {
-          // stage ks+1 (activation rows from k-step 3 of stage ks-1, weight rows from k-steps
-          // 0-1 of stage ks-1) has landed once at most this stage's weight loads remain
+          // stage ks+1 (activation rows from k-step 3 of stage ks-1, weight rows (and scales)
+          // from k-steps 0-1 of stage ks-1) has landed once at most this stage's weight-side
+          // loads remain
           wait_lgkmcnt_all();
-          if constexpr (FULL) wait_vmcnt<kLd>();
+          if constexpr (FULL) wait_vmcnt<kStageLd>();
           else wait_vmcnt<0>();
           block_barrier();
+          if constexpr (W8 && ACT > 0) read_scales(ws1, sc_nxt);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPart, kWBase + ws1 * kPart, 0,
+        mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPart, kWBase + ws1 * kWPart, 0, sc_nxt,
                                             [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
           if constexpr (FULL && (i & 1) == 1) load_a.template operator()<(i >> 1)>(t, ks + 2, buf);
@@ -336,6 +408,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
           if constexpr (!FULL && NEXT && i == 0)
             if (dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
         });
+        if constexpr (W8 && NEXT && ACT > 0) {
+#pragma unroll
+          for (int n = 0; n < NB; ++n) sc_cur[n] = sc_nxt[n];
+        }
       };
       int ks = 0, ws = 0;
       for (; ks < nk - 2; ks += 2) {
@@ -456,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     // stores (older) and stage 0, and leaves stage 1 in flight
     setup(Ln, cur);
     prologue(cur);
-    wait_vmcnt<2 * kLd>();
+    wait_vmcnt<kStageLd + kLd>();
     block_barrier();
     v = vn;
     L = Ln;
@@ -465,14 +541,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
 }  // namespace
 
-hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s) {
+hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s, bool w8) {
   const dim3 grid(256), block(kThreads);   // persistent: one workgroup per CU, a multiple of the 8 XCDs
+  if (w8 && mode != MODE_DOWN) return hipErrorNotSupported;
   if (mode == MODE_GATE_UP)
-    hipLaunchKernelGGL(grouped_gemm_wide_kernel<MODE_GATE_UP>, grid, block, 0, s, p);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_GATE_UP, false>), grid, block, 0, s, p);
+  else if (mode == MODE_DOWN && w8)
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_DOWN, true>), grid, block, 0, s, p);
   else if (mode == MODE_DOWN)
-    hipLaunchKernelGGL(grouped_gemm_wide_kernel<MODE_DOWN>, grid, block, 0, s, p);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_DOWN, false>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(grouped_gemm_wide_kernel<MODE_ROUTER>, grid, block, 0, s, p);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_ROUTER, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

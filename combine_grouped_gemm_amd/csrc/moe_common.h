@@ -82,6 +82,29 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Four e4m3 codes times one fp32 scale, rounded once to bf16 (the code's value is exact in
+// fp32, so the product rounds once)
+__device__ __forceinline__ uint2 e4m3x4_scaled_to_bf16x4(uint32_t w, float s) {
+  const uint2 b = e4m3x4_to_bf16x4(w);
+  auto val = [](uint32_t bits16) { return __uint_as_float(bits16 << 16); };
+  uint2 r;
+  r.x = pack_bf16x2(val(b.x & 0xFFFFu) * s, val(b.x >> 16) * s);
+  r.y = pack_bf16x2(val(b.y & 0xFFFFu) * s, val(b.y >> 16) * s);
+  return r;
+}
+
+// 8 e4m3 codes (one 8-byte fragment) times one fp32 scale, as 8 bf16 values: each code is
+// decoded exactly by the hardware conversion, multiplied in fp32 and rounded to bf16
+__device__ __forceinline__ uint4 e4m3x8_scaled_to_bf16x8(uint2 raw, float s) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), false);
+  const f32x2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), true);
+  const f32x2_t p2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), false);
+  const f32x2_t p3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), true);
+  return make_uint4(pack_bf16x2(p0.x * s, p0.y * s), pack_bf16x2(p1.x * s, p1.y * s),
+                    pack_bf16x2(p2.x * s, p2.y * s), pack_bf16x2(p3.x * s, p3.y * s));
+}
+
 // ------------------------------------------------------------------------------------
 // wave-level reductions (all lanes receive the result)
 // ------------------------------------------------------------------------------------

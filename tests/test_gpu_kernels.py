@@ -330,6 +330,9 @@ GEMM_CASES = [
     ("bf16_empty_tail", [64, 0, 0, 0], 256, 128, "bf16"),
     ("f32_ragged", [60, 0, 200, 1, 70], 256, 256, "f32"),
     ("fp8_ragged", [3, 0, 17, 128, 130, 1], 512, 256, "fp8"),
+    # fp8 with hundreds of rows per expert: the down GEMM on the 256 x 256 kernel with its e4m3
+    # weights converted as they are read (ragged tails, an empty expert, a one-row one)
+    ("fp8_wide_down", [300, 520, 0, 700, 129, 257, 1, 640], 1024, 1024, "fp8"),
     ("bf16_wide_K", [200, 90], 7168, 256, "bf16"),
     # at most 16 rows per expert on average with e4m3 weights: the weight-streaming kernels
     ("fp8_decode_ragged", [0, 1, 2, 5, 16, 17, 33, 0, 3, 0, 9, 1, 4, 0, 7, 12], 1024, 256, "fp8"),

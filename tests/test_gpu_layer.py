@@ -33,6 +33,9 @@ SMALL = {
     "dsv3_small": w.CONFIGS["dsv3_bf16"].scaled(N=512, H=1024, E=64, I=256),
     "dsv3_zipf_small": w.CONFIGS["dsv3_zipf_bf16"].scaled(N=512, H=1024, E=64, I=256),
     "decode_fp8_small": w.CONFIGS["decode_fp8"].scaled(N=64, H=1024, E=64, I=256),
+    # fp8 at a prefill batch (64 rows per expert: the tiled kernels, not the weight-streaming
+    # ones); routed experts only, the fp8 shared expert has a test of its own below
+    "dsv3_fp8_small": w.CONFIGS["dsv3_fp8"].scaled(N=512, H=1024, E=64, I=256, shared=False),
 }
 
 
@@ -188,6 +191,22 @@ def test_layer_small_all_intermediates(name):
     say(f"  y max per-token relative error {err:.3e}, imbalance {ref['imbalance']:.3f}")
     assert err <= Y_BAR[cfg.dtype]
     assert err <= Y_EXPECT[cfg.dtype]
+
+
+def test_layer_fp8_shared_expert():
+    """The shared expert of an fp8 layer runs on the fp8 path like the routed ones: x and its
+    weights quantized per row and 128 columns, SwiGLU FFN on the dequantized values.  Checked
+    against the oracle's codec and FFN composed the same way (quantize_blocks,
+    dequantize_blocks, expert_ffn), every token row."""
+    cfg = w.CONFIGS["dsv3_fp8"].scaled(N=512, H=1024, E=64, I=256)
+    inp, layer, y = _build(cfg)
+    x = inp["x"].cpu().to(torch.float32).numpy()
+    deq = lambda m: oracle.dequantize_blocks(*_quantize_rows(m))
+    a = deq(x)
+    w13 = deq(inp["sw13"][0].cpu().float().numpy())
+    w2 = deq(inp["sw2"][0].cpu().float().numpy())
+    _, ref = oracle.expert_ffn(a, w13, w2)
+    assert token_rel_err(f64(layer.shared_out), ref) <= GEMM_BAR["fp8"]
 
 
 def test_layer_gathered_equals_permuted():

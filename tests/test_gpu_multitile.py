@@ -105,3 +105,40 @@ def test_multitile_gate_up_down_every_row(case):
     # the routed rows do not depend on the shared segment being in the launch
     assert torch.equal(h[:rows].view(torch.int16), h_r.view(torch.int16))
     assert torch.equal(out[:rows].view(torch.int16), out_r.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_multitile_down_e4m3_every_row(case):
+    """The down GEMM on e4m3 weights with fp32 scales per 128-column block (an fp8 layer's),
+    at the same ragged counts: at least three tiles per workgroup, every row of NaN-filled output
+    compared with the oracle's dequantized product.  Codes (the NaN codes excluded) and scales
+    are seeded and uniform; the kernel converts each weight to bf16 (code times scale, rounded
+    once), so the bar is the bf16 GEMM's."""
+    n_e = CASES[case]
+    E, rows = len(n_e), sum(n_e)
+    dn_tiles = _tiles(n_e, 256, H)
+    say(f"multitile e4m3 down {case}: rows={rows} E={E} H={H} K={I}; tiles {dn_tiles}")
+    assert dn_tiles >= 3 * WORKGROUPS
+    h = w.normal((rows, I), w.stream_key(23, w.T_EO, E), DEV, torch.bfloat16, std=1.0)
+    bits = w.uniform_bits(E * H * I, w.stream_key(23, w.T_W2, E), "cpu")
+    codes = (np.asarray(bits) >> 24).astype(np.uint8).reshape(E, H, I)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    sbits = w.uniform_bits(E * H * (I // 128), w.stream_key(23, w.T_W2, E + 1), "cpu")
+    scales = (2.0 ** -8 * (1.0 + (np.asarray(sbits) >> 8) / 2.0 ** 24)).astype(np.float32).reshape(E, H, I // 128)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(n_e)]), dtype=torch.int32, device=DEV)
+    out = torch.full((rows, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_down(h, offs, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), out=out)
+    sync()
+    assert bool(torch.isfinite(out).all()), "rows left unwritten"
+    hh, oo = f64(h), f64(out)
+    off = np.concatenate([[0], np.cumsum(n_e)])
+    worst = 0.0
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        ref = hh[lo:hi] @ oracle.dequantize_blocks(codes[e], scales[e]).T
+        err = token_rel_err(oo[lo:hi], ref)
+        worst = max(worst, err)
+        assert err <= BAR, (e, err)
+    say(f"  every row of {E} segments within {worst:.2e}")

@@ -76,6 +76,10 @@ CONFIGS: Dict[str, MoEConfig] = {
                                 n_group=8, topk_group=4, shared=True, zipf_s=1.2),
     # decode-shaped fp8 layer
     "decode_fp8": MoEConfig("decode_fp8", N=128, H=7168, E=256, k=8, I=2048, dtype="fp8"),
+    # the DeepSeek-V3-shaped layer in fp8 at a prefill batch (measured on request: bench.py
+    # --config dsv3_fp8; not one of the default workloads)
+    "dsv3_fp8": MoEConfig("dsv3_fp8", N=8192, H=7168, E=256, k=8, I=2048, dtype="fp8",
+                          n_group=8, topk_group=4, shared=True),
 }
 CONFIG_ORDER = ["tiny_f32", "mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
 
