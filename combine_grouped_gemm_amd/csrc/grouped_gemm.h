@@ -35,6 +35,10 @@ struct GemmArgs {
                                // output goes to out + s * rows * n_out (fp32)
   void* au;                    // gate/up (256 x 256 kernel): also the pre-activations [rows, 2I]
                                // bf16 (gate in columns 0..I-1, up in I..2I-1), or null
+  const int32_t* tall_list = nullptr;   // (bf16 down, 256 x 256 kernel) [E + 1]: count T, then
+                               // the T experts with kWideTileRows < n_e <= kWideTallRows, which the
+                               // prefix gives no m-tiles and which run as one 320-row tile; or null
+  int32_t* tall_counter = nullptr;      // [kNumXcd] the counters of those tiles (zeroed by the prologue)
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot
@@ -55,6 +59,7 @@ hipError_t launch_grouped_gemm_stream(int mode, const GemmArgs& p, hipStream_t s
 // have been built with 256-row m-tiles, K must be a multiple of 128, and every operand
 // offset (b_rows * K * 2 per expert; a_nrows * K * 2 when gathered) must fit in 32 bits.
 constexpr int kWideTileRows = 256;
+constexpr int kWideTallRows = 320;   // an expert of 257..320 rows: one tile of 320 x 128
 // MODE_ROUTER (one segment [0, rows), no tile schedule, static tile order): tile
 // (part s, n-block, m-tile) multiplies columns [s K/k_split, (s+1) K/k_split) of a and b
 // (K / k_split a multiple of 128) and stores its fp32 sums, 16 bytes per run (n_out % 4 == 0).

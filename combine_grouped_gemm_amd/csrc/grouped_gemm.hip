@@ -53,29 +53,11 @@ template <> struct CTraits<CT_F32> { static constexpr int esz = 4; };
 template <> struct CTraits<CT_BF16> { static constexpr int esz = 2; };
 template <> struct CTraits<CT_FP8> { static constexpr int esz = 1; };
 
-// Tile schedule prologue: m-tiles (of tile_rows rows) of each expert, their prefix and the
-// m-tile -> expert table.  Offsets are clamped into [0, rows] so malformed input cannot
-// index out of range.  With shared_rows > 0 a last segment E of shared_rows rows (the
-// shared expert) follows, and prefix has E + 2 entries.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int rows, int tile_rows, int tile_cap,
-                                                           int32_t* __restrict__ prefix,
-                                                           int32_t* __restrict__ tile_expert,
-                                                           int32_t* __restrict__ tile_counter,
-                                                           int shared_rows) {
-  __shared__ int32_t tot[1024];
+// inclusive prefix sum over the 1024 threads of the block
+__device__ int32_t block_scan_1024(int32_t x, int32_t* tot) {
   const int e = threadIdx.x;
-  const int n_seg = E + (shared_rows > 0 ? 1 : 0);
-  int mt = 0;
-  if (e < E) {
-    int lo = offsets[e], hi = offsets[e + 1];
-    lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
-    hi = hi < lo ? lo : (hi > rows ? rows : hi);
-    mt = (hi - lo + tile_rows - 1) / tile_rows;
-  } else if (e < n_seg) {
-    mt = (shared_rows + tile_rows - 1) / tile_rows;
-  }
-  tot[e] = mt;
+  __syncthreads();
+  tot[e] = x;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int32_t v = e >= off ? tot[e - off] : 0;
@@ -83,13 +65,49 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     tot[e] += v;
     __syncthreads();
   }
-  const int start = tot[e] - mt;
+  return tot[e];
+}
+
+// Tile schedule prologue: m-tiles (of tile_rows rows) of each expert, their prefix and the
+// m-tile -> expert table.  Offsets are clamped into [0, rows] so malformed input cannot
+// index out of range.  With shared_rows > 0 a last segment E of shared_rows rows (the
+// shared expert) follows, and prefix has E + 2 entries.  With tall_list, the routed experts
+// of tile_rows < n_e <= tall_rows get no m-tiles and are listed instead (tall_list[0] = their
+// count, then the experts in order), and tall_list[E + 1 ..] holds kNumXcd zeroed counters.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
+                                                           int rows, int tile_rows, int tile_cap,
+                                                           int32_t* __restrict__ prefix,
+                                                           int32_t* __restrict__ tile_expert,
+                                                           int32_t* __restrict__ tile_counter,
+                                                           int shared_rows, int tall_rows,
+                                                           int32_t* __restrict__ tall_list) {
+  __shared__ int32_t tot[1024];
+  const int e = threadIdx.x;
+  const int n_seg = E + (shared_rows > 0 ? 1 : 0);
+  int mt = 0, tall = 0;
+  if (e < E) {
+    int lo = offsets[e], hi = offsets[e + 1];
+    lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+    hi = hi < lo ? lo : (hi > rows ? rows : hi);
+    tall = tall_list != nullptr && hi - lo > tile_rows && hi - lo <= tall_rows ? 1 : 0;
+    mt = tall ? 0 : (hi - lo + tile_rows - 1) / tile_rows;
+  } else if (e < n_seg) {
+    mt = (shared_rows + tile_rows - 1) / tile_rows;
+  }
+  const int32_t end = block_scan_1024(mt, tot);
+  const int start = end - mt;
   if (e < n_seg) {
     prefix[e] = start < tile_cap ? start : tile_cap;
     for (int i = 0; i < mt && start + i < tile_cap; ++i) tile_expert[start + i] = e;
   }
-  if (e == n_seg - 1) prefix[n_seg] = tot[e] < tile_cap ? tot[e] : tile_cap;
+  if (e == n_seg - 1) prefix[n_seg] = end < tile_cap ? end : tile_cap;
   if (e < kNumXcd) tile_counter[e] = 0;
+  if (tall_list != nullptr) {
+    const int32_t tend = block_scan_1024(tall, tot);
+    if (tall) tall_list[tend] = e;
+    if (e == 1023) tall_list[0] = tend;
+    if (e < kNumXcd) tall_list[E + 1 + e] = 0;
+  }
 }
 
 template <int CT>
@@ -710,8 +728,9 @@ size_t gemm_tile_cap(int rows, int E) {
 
 // the 256 x 256 kernel numbers its tiles in 32 bits and splits them over the 8 XCDs by
 // multiplying the count by the XCD index: 8 x an upper bound of the tile count stays below 2^31
+// (the 320 x 128 tiles: at most one per expert, with twice the n-blocks)
 static bool wide_tiles_fit(int mode, int rows, int n_seg, int I, int n_out) {
-  const long long n_blocks = mode == MODE_GATE_UP ? (I + 127) / 128 : (n_out + 255) / 256;
+  const long long n_blocks = mode == MODE_GATE_UP ? (I + 63) / 64 : (n_out + 127) / 128;
   return static_cast<long long>(gemm_tile_cap(rows, n_seg)) * n_blocks * kNumXcd < (1LL << 31);
 }
 
@@ -725,12 +744,14 @@ bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int rows, int tile_rows, int cap, int32_t* prefix,
                               int32_t* tile_expert, int32_t* tile_counter, hipStream_t s) {
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap, prefix,
-                     tile_expert, tile_counter, 0);
+                     tile_expert, tile_counter, 0, 0, nullptr);
   return hipGetLastError();
 }
 
+// prefix [E + 1], tile_expert [cap], counters [8], list of 320-row experts [E + 1] and its
+// counters [8]
 size_t gemm_schedule_bytes(int rows, int E) {
-  const size_t n = static_cast<size_t>(E) + 1 + gemm_tile_cap(rows, E) + kNumXcd;
+  const size_t n = 2 * (static_cast<size_t>(E) + 1 + kNumXcd) + gemm_tile_cap(rows, E);
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 
@@ -756,6 +777,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   int32_t* tile_expert = prefix + n_seg + 1;
   const int cap = static_cast<int>(gemm_tile_cap(rows + shared_rows, n_seg));
   int32_t* tile_counter = tile_expert + cap;
+  int32_t* tall_list = tile_counter + kNumXcd;   // [E + 1] + [kNumXcd] counters
   // few rows per expert and e4m3 weights: the weight-streaming kernel (16-row m-tiles)
   const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) &&
                       static_cast<long long>(rows) <= static_cast<long long>(kStreamTileRows) * E &&
@@ -780,8 +802,11 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                      static_cast<long long>(kWideTileRows) * rbytes < (1LL << 32) && shared_rows == 0 &&
                      au == nullptr && a_rows == nullptr && wide_tiles_fit(mode, rows, n_seg, I, n_out);
   const int tile_rows = stream ? kStreamTileRows : (wide || wide8 ? kWideTileRows : (dma ? kDM : GBM));
+  // bf16 down GEMM on the 256 x 256 kernel: experts of 257..320 rows as one 320 x 128 tile
+  const bool tall = wide && mode == MODE_DOWN;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
-                     prefix, tile_expert, tile_counter, shared_rows);
+                     prefix, tile_expert, tile_counter, shared_rows, kWideTallRows,
+                     tall ? tall_list : nullptr);
   GemmArgs p;
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.a_scale = a_scale;
@@ -812,6 +837,10 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
   if (wide || wide8) {
     p.tile_counter = tile_counter;
+    if (tall) {
+      p.tall_list = tall_list;
+      p.tall_counter = tall_list + E + 1;
+    }
     return launch_grouped_gemm_wide(mode, p, s, wide8);
   }
   const dim3 grid(persistent_grid()), block(GTHREADS);

@@ -40,6 +40,12 @@
 // R row blocks and 64 of the 256 weight rows (gate/up: 32 W_gate rows and the same 32 W_up
 // rows), 2 R MFMAs per k-step against (R + 1) / 2 x 4.  The accumulators are the same 16
 // blocks in both layouts; only the epilogue's row and column of each block differ.
+//
+// Down GEMM, experts of 257..320 rows: split in two, each half would stream the expert's whole
+// weight panel; instead the expert runs as one tile of 320 rows x 128 weight rows (5 x 2 blocks
+// per wave, 160 accumulators), whose LDS holds two 40 KB activation buffers and a five-slot
+// ring of 16 KB weight stages, so the weight rows load 3.25-3.75 stages ahead.  These tiles
+// come first, from counters of their own.
 #include <utility>
 
 #include "gemm_device.h"
@@ -49,17 +55,34 @@
 namespace moe {
 namespace {
 
-constexpr int kTM = kWideTileRows;     // rows of a tile (256)
-constexpr int kTN = 256;               // weight rows of a tile (gate/up: 128 W_gate + the same 128 W_up)
-constexpr int kRowB = 128;             // bytes of K per row and stage
-constexpr int kPart = kTM * kRowB;     // one stage of activation or weight rows (32 KB)
-constexpr int kWBase = 2 * kPart;      // weight ring after the two activation buffers
-constexpr int kLdsBytes = 5 * kPart;   // 160 KB
+constexpr int kRowB = 128;      // bytes of K per activation row and stage
 constexpr int kThreads = 256;
-constexpr int kMB = 4, kNB = 4;        // 32 x 32 blocks per wave (2 x 2 layout)
-constexpr int kMB1 = 5, kNB1 = 2;      // at most 5 row blocks x 2 column blocks (1 x 4 layout)
-constexpr int kLd = kPart / 1024 / 4;  // 1 KB loads per wave and part (8)
-static_assert(kTM == kTN, "activation and weight parts have the same shape");
+constexpr int kMB1 = 5, kNB1 = 2;   // at most 5 row blocks x 2 column blocks (1 x 4 layout)
+
+// Shape of a tile and of its LDS.  G = 0: 256 rows x 256 weight rows, two activation
+// buffers and a three-slot weight ring (5 x 32 KB).  G = 1 (an expert of 257-320 rows in one
+// tile): 320 rows x 128 weight rows, two activation buffers of 40 KB and a five-slot weight
+// ring of 16 KB slots, so the weight rows load 3.25-3.75 stages ahead.  W8: e4m3 weight
+// rows of 64 bytes per stage (G = 0 only).
+template <int G, bool W8>
+struct Geo {
+  static constexpr int TM = G ? kWideTallRows : kWideTileRows;
+  static constexpr int TN = G ? 128 : 256;
+  static constexpr int MB = TM / 64, NB = TN / 64;   // 32 x 32 blocks per wave (2 x 2 layout)
+  static constexpr int WRowB = W8 ? 64 : kRowB;      // bytes of a weight row per stage
+  static constexpr int PartA = TM * kRowB;           // one stage of activation rows
+  static constexpr int WPart = TN * WRowB;           // one stage of weight rows
+  static constexpr int WS = G ? 5 : 3;               // weight ring slots
+  static constexpr int LdA = PartA / 4096;           // 1 KB loads per wave and stage (8; 10)
+  static constexpr int LdW = WPart / 4096;           // (8, W8 4; 4)
+  static constexpr int StageLd = LdW + (W8 ? 1 : 0); // + the scale gather (W8)
+  static constexpr int WBase = 2 * PartA;            // weight ring after the activation buffers
+  static constexpr int SBase = WBase + WS * WPart;   // (W8) scale ring: three slots of 1 KB
+  static constexpr int LdsTot = SBase + (W8 ? 3 * 1024 : 0);
+  static_assert(!W8 || G == 0, "e4m3 weights: 256 x 256 tiles");
+  static_assert(TM % 64 == 0 && TN % 64 == 0 && (TN / 2) % 32 == 0, "2 x 2 waves of 32-row blocks");
+};
+static_assert(Geo<1, false>::LdsTot <= Geo<0, false>::LdsTot, "both shapes fit the kernel's LDS");
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // (W8) 64-byte weight rows: chunk c of row r sits in slot c ^ key4(r); a fragment read (32 rows,
@@ -73,26 +96,21 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
-// W8: e4m3 weights with fp32 scales per 128-column block (the down GEMM of an fp8 layer).  A
-// stage then holds 64 codes (64 bytes) of each weight row, loaded direct to LDS, and the 256
-// rows' scales of the stage's block, gathered into a ring of their own; a weight fragment is
-// converted to bf16 (code times scale, rounded once) after it is read from LDS, and the MFMAs
-// are the bf16 ones.
-template <int MODE, bool W8>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs p) {
-  static_assert(!W8 || MODE == MODE_DOWN, "e4m3 weights: the down GEMM");
-  constexpr int kWRowB = W8 ? 64 : kRowB;           // bytes of a weight row per stage
-  constexpr int kWPart = kTN * kWRowB;              // one stage of weight rows (32 KB; 16 KB)
-  constexpr int kLdW = kWPart / 1024 / 4;           // weight loads per wave and stage (8; 4)
-  constexpr int kStageLd = kLdW + (W8 ? 1 : 0);     // + the scale gather (W8)
-  constexpr int kSBase = kWBase + 3 * kWPart;       // (W8) scale ring: three slots of 1 KB
-  constexpr int kLdsTot = kSBase + (W8 ? 3 * 1024 : 0);
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsTot];
+// The tiles of one shape, from the XCD's counter: G = 0 the schedule's m-tiles (routed, then
+// the shared segment's), G = 1 one tile per listed expert.  lds is the kernel's LDS array.
+template <int MODE, bool W8, int G>
+__device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
+  using S = Geo<G, W8>;
+  constexpr int kTM = S::TM, kTN = S::TN, kMB = S::MB, kNB = S::NB;
+  constexpr int kWRowB = S::WRowB, kPartA = S::PartA, kWPart = S::WPart, kWS = S::WS;
+  constexpr int kLdA = S::LdA, kLdW = S::LdW, kStageLd = S::StageLd;
+  constexpr int kWBase = S::WBase, kSBase = S::SBase;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
 
-  // the 1 x 4 layout for gate/up tiles only: the down GEMM's epilogue would need the gates of
-  // twice the rows per lane, and the extra registers cost its K loop more than the layout saves
-  constexpr bool kLay1 = MODE == MODE_GATE_UP;
+  // the 1 x 4 layout for 256 x 256 gate/up tiles only: the down GEMM's epilogue would need the
+  // gates of twice the rows per lane, and the extra registers cost its K loop more than the
+  // layout saves
+  constexpr bool kLay1 = MODE == MODE_GATE_UP && G == 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
@@ -100,8 +118,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // loads: wave w moves the 8-row groups w, w + 4, ... of a part; lane l fills LDS slot l % 8
   // of row l / 8 of the group, so it loads chunk (l % 8) ^ key(row).  Bit 3 of every row of
   // such a group is the wave's parity.
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ slot_key(lrow + (wave & 1) * 8);
 
   const int n_cols = MODE == MODE_GATE_UP ? p.I : p.n_out;
   const int tile_cols = MODE == MODE_GATE_UP ? kTN / 2 : kTN;
@@ -109,12 +125,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // router: m-tiles of the single segment [0, rows); tiles ordered part -> n-block -> m-tile,
   // so with k_split = 8 each XCD's range is one column part (its slice of W_r stays in L2)
   const int mt_r = MODE == MODE_ROUTER ? (p.rows + kTM - 1) / kTM : 0;
-  // routed tiles (expert -> n-block -> m-tile), then the shared segment's (m-tile -> n-block)
+  // routed tiles (expert -> n-block -> m-tile), then the shared segment's (m-tile -> n-block);
+  // G = 1: listed expert -> n-block
   // (tile numbers are 32-bit: the launcher keeps 8 x the tile count below 2^31)
-  const int n_r = MODE == MODE_ROUTER ? p.k_split * mt_r * nN : p.tile_prefix[p.E] * nN;
-  const int n_s = MODE != MODE_ROUTER && p.shared_rows > 0
+  const int n_r = MODE == MODE_ROUTER ? p.k_split * mt_r * nN
+                  : G ? p.tall_list[0] * nN
+                      : p.tile_prefix[p.E] * nN;
+  const int n_s = G == 0 && MODE != MODE_ROUTER && p.shared_rows > 0
                             ? (p.tile_prefix[p.E + 1] - p.tile_prefix[p.E]) * nN
                             : 0;
+  int32_t* const counter = G ? p.tall_counter : p.tile_counter;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
@@ -134,14 +154,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
   const int hk = lane >> 5;
   // first row of the wave's activation block m and weight block n, per layout (gate/up in
-  // the 2 x 2 layout: weight blocks 0-1 are W_gate rows, 2-3 the same W_up rows; in the
-  // 1 x 4 layout wave w holds weight rows 64 w .. 64 w + 63, gate/up: W_gate rows 32 w ..
-  // 32 w + 31 and the same W_up rows)
+  // the 2 x 2 layout: the first NB / 2 weight blocks are W_gate rows, the rest the same W_up
+  // rows; in the 1 x 4 layout wave w holds weight rows 64 w .. 64 w + 63, gate/up: W_gate
+  // rows 32 w .. 32 w + 31 and the same W_up rows)
   auto a_row = [&](int lay, int m) __attribute__((always_inline)) { return lay ? m * 32 : (2 * m + wm) * 32; };
   auto b_row = [&](int lay, int n) __attribute__((always_inline)) {
     if (MODE == MODE_GATE_UP)
-      return lay ? n * (kTN / 2) + wave * 32 : (n >> 1) * (kTN / 2) + wn * 64 + (n & 1) * 32;
-    return lay ? wave * 64 + n * 32 : wn * 128 + n * 32;
+      return lay ? n * (kTN / 2) + wave * 32
+                 : (n / (kNB / 2)) * (kTN / 2) + wn * (kNB / 2) * 32 + (n % (kNB / 2)) * 32;
+    return lay ? wave * 64 + n * 32 : wn * kNB * 32 + n * 32;
   };
 
   // Tiles: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.  With
@@ -149,15 +170,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // n-blocks sharing activation rows) start close together in time whatever the earlier
   // tiles cost.  Wave 0 takes the next index during the tile's second-to-last stage (late
   // enough that the take is still close to the start, early enough to hide its latency) and
-  // hands it to the other waves at the tile boundary through the last word of ring slot 2
-  // (of the scale ring with W8; no load writes that slot between a boundary and the first
-  // stage).
-  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsTot - 4);
-  const bool dynamic = p.tile_counter != nullptr;
+  // hands it to the other waves at the tile boundary through the last word of the LDS array
+  // (in the last weight ring slot, or the last scale slot with W8; no load writes that slot
+  // between a boundary and the first stage).
+  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + S::LdsTot - 4);
+  const bool dynamic = counter != nullptr;
   int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
   int v = slot;
   if (dynamic) {
-    if (tid == 0) *tile_word = atomicAdd(p.tile_counter + xcd, 1);
+    __syncthreads();   // (after a previous shape's tiles: every wave has read the word)
+    if (tid == 0) *tile_word = atomicAdd(counter + xcd, 1);
     __syncthreads();
     v = __builtin_amdgcn_readfirstlane(*tile_word);
   }
@@ -168,10 +190,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     const uint8_t* a;
     const uint8_t* b;
     const uint8_t* sc;             // (W8) the expert's scales [n_out, K / 128]
-    uint32_t a_src[kLd], b_src[kLd];
+    uint32_t a_src[kLdA], b_src[kLdW];
     uint32_t s_src;                // (W8) this lane's scale row offset
   };
   auto setup = [&](int L, Tile& t) __attribute__((always_inline)) {
+    // the lane's load row and chunk, rebuilt here from the lane id: values kept across the
+    // tile loop are spilled, and their reloads' count waits would also wait for the
+    // epilogue's stores and the first loads of the tile
+    const uint32_t ln = opaque_lane();
+    const int lrow = static_cast<int>(ln >> 3);
+    const int lchunk = static_cast<int>(ln & 7) ^ slot_key(lrow + (wave & 1) * 8);
     int e, mt_e, nblk, mtile, seg_lo, seg_hi, kp = 0;
     if (MODE == MODE_ROUTER) {
       e = 0;
@@ -183,6 +211,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       mtile = local % mt_r;
       seg_lo = 0;
       seg_hi = p.rows;
+    } else if (G == 1) {   // one tile per listed expert: all of its rows
+      e = p.tall_list[1 + L / nN];
+      mt_e = 1;
+      nblk = L % nN;
+      mtile = 0;
+      expert_segment(p, e, seg_lo, seg_hi);
     } else if (L < n_r) {
       e = p.tile_expert[L / nN];
       const int pe = p.tile_prefix[e];
@@ -200,7 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       seg_lo = p.rows;
       seg_hi = p.rows + p.shared_rows;
     }
-    const int rpt = ((seg_hi - seg_lo + mt_e - 1) / mt_e + 31) / 32 * 32;
+    int rpt = ((seg_hi - seg_lo + mt_e - 1) / mt_e + 31) / 32 * 32;
+    rpt = rpt < kTM ? rpt : kTM;   // (G = 1: the list holds experts of at most kTM rows)
     t.m0 = seg_lo + mtile * rpt;
     t.mend = t.m0 + rpt < seg_hi ? t.m0 + rpt : seg_hi;
     t.mlast = t.mend - 1 - t.m0;
@@ -215,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     if constexpr (W8) {   // (no shared segment with W8: the launcher checks)
       t.sc = reinterpret_cast<const uint8_t*>(p.b_scale + static_cast<size_t>(e) * p.b_rows * kblk);
       // scale gather: wave w's lane l fetches the scale of tile weight row 64 w + l
-      const int r = wave * 64 + lane;
+      const int r = wave * 64 + static_cast<int>(ln);
       t.s_src = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast)) * kblk * 4;
     }
     if (MODE == MODE_ROUTER) {
@@ -223,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       t.b += static_cast<size_t>(kp) * kspan * 2;
     }
 #pragma unroll
-    for (int j = 0; j < kLd; ++j) {
+    for (int j = 0; j < kLdA; ++j) {
       const int r = (wave + 4 * j) * 8 + lrow;   // tile row of this lane's loads
       int ra = r < t.mlast ? r : t.mlast;
       if (p.a_rows) {   // (the shared segment's row r is token r - rows)
@@ -231,23 +266,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         ra = tok < 0 ? 0 : (tok < p.a_nrows ? tok : p.a_nrows - 1);
       }
       t.a_src[j] = static_cast<uint32_t>(ra) * rb + lchunk * 16;
-      uint32_t wr;
-      if (MODE == MODE_GATE_UP) {
-        const int c = r % (kTN / 2);
-        const int cc = c < clast ? c : clast;
-        wr = (r < kTN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(t.c0 + cc);
-      } else {
-        wr = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
-      }
-      t.b_src[j] = wr * rb + lchunk * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kLdW; ++j) {
       if constexpr (W8) {
         // 64-byte rows: load j fills the 16-row group wave + 4 j; lane l fills LDS slot l % 4
         // of row l / 4 of the group, so it loads chunk (l % 4) ^ key4(row)
-        if (j < kLdW) {
-          const int r8 = (wave + 4 * j) * 16 + (lane >> 2);
-          const uint32_t w8 = static_cast<uint32_t>(t.c0 + (r8 < clast ? r8 : clast));
-          t.b_src[j] = w8 * rbw + static_cast<uint32_t>((lane & 3) ^ key4(r8)) * 16;
+        const int r8 = (wave + 4 * j) * 16 + static_cast<int>(ln >> 2);
+        const uint32_t w8 = static_cast<uint32_t>(t.c0 + (r8 < clast ? r8 : clast));
+        t.b_src[j] = w8 * rbw + static_cast<uint32_t>((ln & 3) ^ key4(r8)) * 16;
+      } else {
+        const int r = (wave + 4 * j) * 8 + lrow;   // tile weight row of this lane's loads
+        uint32_t wr;
+        if (MODE == MODE_GATE_UP) {
+          const int c = r % (kTN / 2);
+          const int cc = c < clast ? c : clast;
+          wr = (r < kTN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(t.c0 + cc);
+        } else {
+          wr = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
         }
+        t.b_src[j] = wr * rb + lchunk * 16;
       }
     }
   };
@@ -256,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   // as a constant of the instruction.
   const uint32_t lds_wave = lds0 + static_cast<uint32_t>(wave) * 1024;
   auto load_a = [&]<int J>(const Tile& t, int ks, int buf) __attribute__((always_inline)) {
-    dma16s<J * 4096>(t.a + static_cast<size_t>(ks) * kRowB, t.a_src[J], lds_wave + buf * kPart);
+    dma16s<J * 4096>(t.a + static_cast<size_t>(ks) * kRowB, t.a_src[J], lds_wave + buf * kPartA);
   };
   auto load_w = [&]<int J>(const Tile& t, int ks, int ws) __attribute__((always_inline)) {
     dma16s<J * 4096>(t.b + static_cast<size_t>(ks) * kWRowB, t.b_src[J], lds_wave + kWBase + ws * kWPart);
@@ -266,22 +304,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
     dma4s<0>(t.sc + static_cast<size_t>(ks >> 1) * 4, t.s_src,
              lds0 + static_cast<uint32_t>(kSBase + ws * 1024 + wave * 256));
   };
-  // prologue loads of a tile (stage 0 and 1); the caller waits for stage 0 and synchronises
+  // prologue loads of a tile: activation rows of stage 0, weight rows of stages 0 .. kWS - 2
+  // (those that exist), activation rows of stage 1; then the wait for stage 0 and the barrier
   auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
-    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
+    static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
     static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 0, 0); });
     if constexpr (W8) load_s(t, 0, 0);
-    static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 1, 1); });
-    if constexpr (W8) load_s(t, 1, 1);
-    static_for<kLd>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 1, 1); });
+    static_for<kWS - 2>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int st = decltype(ic)::value + 1;
+      if (G == 0 || st < nk) {   // (256 x 256: nk >= 2)
+        static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, st, st); });
+        if constexpr (W8) load_s(t, st, st);
+      }
+    });
+    static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 1, 1); });
+    // stage 0 landed once at most the later stages' loads remain
+    if (G == 0 || nk >= kWS - 1) wait_vmcnt<(kWS - 2) * kStageLd + kLdA>();
+    else wait_vmcnt<0>();
+    block_barrier();
   };
 
   Tile cur;
   int L = tile_of(v);
   setup(L, cur);
   prologue(cur);
-  wait_vmcnt<kStageLd + kLd>();   // stage 0 landed; stage 1 may be in flight
-  block_barrier();
 
   for (;;) {
     const Tile& t = cur;   // (rewritten at the boundary, after the epilogue's last use)
@@ -291,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 #pragma unroll
       for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16_t{};
 
-    const int nblk = (t.mlast + 32) / 32;   // 32-row blocks that hold rows (1 .. 8)
+    const int nblk = (t.mlast + 32) / 32;   // 32-row blocks that hold rows
     const bool lay1 = kLay1 && (nblk & 1) != 0 && nblk <= kMB1;
     int act = lay1 ? nblk : (nblk - wm + 1) / 2;   // row blocks of this wave that hold rows
     act = lay1 ? act : (act < 0 ? 0 : (act > kMB ? kMB : act));
@@ -301,6 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       constexpr int LAY = decltype(lay_c)::value;      // 1: the 1 x 4 layout
       constexpr int MB = LAY ? kMB1 : kMB, NB = LAY ? kNB1 : kNB;
       constexpr int kReads = ACT > 0 ? ACT + NB : 0;   // fragment reads per k-step
+      constexpr int kSlots = kMB * kNB;                // MFMA slots of a k-step
       uint4 f0a[MB], f0b[NB], f1a[MB], f1b[NB];
       // fragment reads: lane l reads row l % 32 of a 32-row block, chunk 2 s + l / 32 of k-step
       // s (swizzled).  fb[s] is the lane's part of the LDS offset; the block's first row
@@ -338,24 +385,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
         else
           fa[r - NB] = *reinterpret_cast<const uint4*>(lds + fb[s] + (aoff + a_row(LAY, r - NB) * kRowB));
       };
-      // the MFMAs of a k-step on (ca, cb), 16 slots: MFMA i is row block i / NB and column
-      // block i % NB.  After slot i come a fragment read of the next k-step (into na, nb, when
-      // READ: read i / 2 after even slots in the 2 x 2 layout, read i in the 1 x 4 one) and
-      // then between(i), all held in place by scheduling fences: the wave never stalls on a
-      // burst of LDS or memory instructions while the matrix pipe has nothing queued.  In the
-      // 1 x 4 layout, row block m and column block n accumulate in acc[m / 2][m % 2 + 2 n].
+      // the MFMAs of a k-step on (ca, cb), kSlots slots: MFMA i is row block i / NB and
+      // column block i % NB.  After slot i come a fragment read of the next k-step (into na,
+      // nb, when READ: read i / 2 after even slots in the 2 x 2 layout of 256 x 256 tiles,
+      // read i otherwise) and then between(i), all held in place by scheduling fences: the
+      // wave never stalls on a burst of LDS or memory instructions while the matrix pipe has
+      // nothing queued.  In the 1 x 4 layout, row block m and column block n accumulate in
+      // acc[m / 2][m % 2 + 2 n].
       auto mfma_step = [&]<bool READ>(uint4(&ca)[MB], uint4(&cb)[NB], uint4(&na)[MB], uint4(&nb)[NB],
                                       int aoff, int boff, int s, const float(&scn)[NB], auto&& between)
           __attribute__((always_inline)) {
-        static_for<kMB * kNB>([&](auto ic) __attribute__((always_inline)) {
+        static_for<kSlots>([&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
           constexpr int m = i / NB, n = i % NB;
           if constexpr (m < ACT) {
             f32x16_t& c = LAY ? acc[m / 2][(m & 1) + 2 * n] : acc[m][n];
             c = mma_bf16(cb[n], ca[m], c);
+            // (an ordered use of the result: instruction selection otherwise may sink the MFMA,
+            // which reads no memory, past the slot's scheduling fence)
+            __asm__ volatile("" : "+a"(c));
           }
           __builtin_amdgcn_sched_barrier(0);
-          constexpr int rd = LAY ? i : ((i & 1) == 0 ? i / 2 : kReads);
+          constexpr int rd = (LAY || G == 1) ? i : ((i & 1) == 0 ? i / 2 : kReads);
           if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
           // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n, converted at 9 + 2 n
           if constexpr (W8 && READ && ACT > 0 && i >= 9 && (i & 1) == 1)
@@ -373,58 +424,86 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 #pragma unroll
         for (int n = 0; n < NB; ++n) f0b[n] = e4m3x8_scaled_to_bf16x8(wraw[n], sc_cur[n]);
       }
-      // stage ks: activation rows in buffer PAR = ks & 1, weight rows in ring slot ws = ks % 3.
-      // FULL: stage ks+2 exists; NEXT: stage ks+1 exists
-      auto stage = [&]<bool FULL, bool NEXT, int PAR>(int ks, int ws) __attribute__((always_inline)) {
+      // stage ks: activation rows in buffer PAR = ks & 1, weight rows in ring slot ws = ks % kWS.
+      // FULL: stage ks+2 exists; NEXT: stage ks+1 exists; WN: stage ks + kWS - 1 exists, and its
+      // weight rows load during stage ks, into the slot stage ks-1 used.
+      auto stage = [&]<bool FULL, bool NEXT, int PAR, bool WN>(int ks, int ws) __attribute__((always_inline)) {
         constexpr int buf = PAR, nbuf = PAR ^ 1;
-        const int ws1 = ws == 2 ? 0 : ws + 1, ws2 = ws1 == 2 ? 0 : ws1 + 1;
-        const int aoff = buf * kPart, boff = kWBase + ws * kWPart;
+        const int ws1 = ws == kWS - 1 ? 0 : ws + 1;
+        const int wsl = ws == 0 ? kWS - 1 : ws - 1;
+        const int aoff = buf * kPartA, boff = kWBase + ws * kWPart;
         mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 1, sc_cur, [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (FULL && (i & 3) == 1 && (i >> 2) < kLdW) load_w.template operator()<(i >> 2)>(t, ks + 2, ws2);
+          constexpr int jw = G == 0 ? ((i & 3) == 1 ? (i >> 2) : kLdW) : ((i & 1) == 1 ? (i >> 1) : kLdW);
+          if constexpr (WN && jw < kLdW) load_w.template operator()<jw>(t, ks + kWS - 1, wsl);
         });
         mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, sc_cur, [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (FULL && (i & 3) == 1 && 4 + (i >> 2) < kLdW) load_w.template operator()<4 + (i >> 2)>(t, ks + 2, ws2);
-          if constexpr (W8 && FULL && i == 1) load_s(t, ks + 2, ws2);
+          if constexpr (G == 0 && WN && (i & 3) == 1 && 4 + (i >> 2) < kLdW)
+            load_w.template operator()<4 + (i >> 2)>(t, ks + kWS - 1, wsl);
+          if constexpr (W8 && WN && i == 1) load_s(t, ks + kWS - 1, wsl);
         });
         mfma_step.template operator()<true>(f0a, f0b, f1a, f1b, aoff, boff, 3, sc_cur, nothing);
         if constexpr (NEXT) {
           // stage ks+1 (activation rows from k-step 3 of stage ks-1, weight rows (and scales)
-          // from k-steps 0-1 of stage ks-1) has landed once at most this stage's weight-side
-          // loads remain
+          // from k-steps 0-1 of an earlier stage) has landed once at most this stage's
+          // weight-side loads remain
           wait_lgkmcnt_all();
-          if constexpr (FULL) wait_vmcnt<kStageLd>();
+          if constexpr (WN) wait_vmcnt<kStageLd>();
           else wait_vmcnt<0>();
           block_barrier();
           if constexpr (W8 && ACT > 0) read_scales(ws1, sc_nxt);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPart, kWBase + ws1 * kWPart, 0, sc_nxt,
+        mfma_step.template operator()<NEXT>(f1a, f1b, f0a, f0b, nbuf * kPartA, kWBase + ws1 * kWPart, 0, sc_nxt,
                                             [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (FULL && (i & 1) == 1) load_a.template operator()<(i >> 1)>(t, ks + 2, buf);
+          constexpr int ja = G == 0 ? ((i & 1) == 1 ? (i >> 1) : kLdA) : i;   // activation load of slot i
+          if constexpr (FULL && ja < kLdA) load_a.template operator()<ja>(t, ks + 2, buf);
           // second-to-last stage (its wait for loads is behind it): take the next tile
           if constexpr (!FULL && NEXT && i == 0)
-            if (dynamic && tid == 0) grabbed = atomicAdd(p.tile_counter + xcd, 1);
+            if (dynamic && tid == 0) grabbed = atomicAdd(counter + xcd, 1);
         });
         if constexpr (W8 && NEXT && ACT > 0) {
 #pragma unroll
           for (int n = 0; n < NB; ++n) sc_cur[n] = sc_nxt[n];
         }
       };
+      // stages in pairs (nk is even): with weight loads, then (five-slot ring) the pair whose
+      // weight stages lie past the end, then the last two
+      constexpr int kAhead = kWS - 3;   // stages the weight ring runs ahead of the activations
+      // (nk through volatile assembly: the loop guards are then compared per tile, in scalar
+      // registers; hoisted out of the tile loop they were kept in a spilled register whose
+      // reload waited on every load of the tile's first stages)
+      int nkt;
+      __asm__ volatile("s_mov_b32 %0, %1" : "=s"(nkt) : "s"(nk));
       int ks = 0, ws = 0;
-      for (; ks < nk - 2; ks += 2) {
-        stage.template operator()<true, true, 0>(ks, ws);
-        ws = ws == 2 ? 0 : ws + 1;
-        stage.template operator()<true, true, 1>(ks + 1, ws);
-        ws = ws == 2 ? 0 : ws + 1;
+      auto adv = [&]() __attribute__((always_inline)) { ws = ws == kWS - 1 ? 0 : ws + 1; };
+      for (; ks < nkt - 2 - kAhead; ks += 2) {
+        stage.template operator()<true, true, 0, true>(ks, ws);
+        adv();
+        stage.template operator()<true, true, 1, true>(ks + 1, ws);
+        adv();
       }
-      stage.template operator()<false, true, 0>(nk - 2, ws);
-      ws = ws == 2 ? 0 : ws + 1;
-      stage.template operator()<false, false, 1>(nk - 1, ws);
+      static_assert(kAhead == 0 || kAhead == 2, "one pair without weight loads");
+      if constexpr (kAhead == 2) {
+        if (ks < nkt - 2) {
+          stage.template operator()<true, true, 0, false>(ks, ws);
+          adv();
+          stage.template operator()<true, true, 1, false>(ks + 1, ws);
+          adv();
+        }
+      }
+      stage.template operator()<false, true, 0, false>(nkt - 2, ws);
+      adv();
+      stage.template operator()<false, false, 1, false>(nkt - 1, ws);
     };
-    if (kLay1 && lay1) {
+    if constexpr (G == 1) {
+      // (the listed experts have 9 or 10 row blocks: 4 or 5 per wave; a wave with fewer
+      // would compute rows past the tile, which the epilogue does not store)
+      if (act >= 5) k_loop(std::integral_constant<int, 5>{}, std::integral_constant<int, 0>{});
+      else k_loop(std::integral_constant<int, 4>{}, std::integral_constant<int, 0>{});
+    } else if (kLay1 && lay1) {
       [&]<int... A>(std::integer_sequence<int, A...>) {
         ((act == 2 * A + 1 ? k_loop(std::integral_constant<int, 2 * A + 1>{}, std::integral_constant<int, 1>{})
                            : void()),
@@ -450,10 +529,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
     // ---- epilogue: block acc[mb][nb] holds, in lane l, token row rblk * 32 + l % 32 of the
     // tile and, in registers 4q .. 4q+3, output columns cblk + 8q + 4 (l / 32) + 0..3 (2 x 2:
-    // rblk = 2 mb + wm, cblk = 32 nb of the wave's 128 columns; 1 x 4: rblk = 2 mb + nb % 2,
+    // rblk = 2 mb + wm, cblk = 32 nb of the wave's 32 NB columns; 1 x 4: rblk = 2 mb + nb % 2,
     // cblk = 32 (nb / 2) of the wave's 64): one 8-byte store per run (16 bytes for fp32
     // router sums; n_cols % 4 == 0, so a run is all in or all out).  Gate/up pairs the gate
-    // block nb < 2 with the up block nb + 2 of the same rows and columns.
+    // block nb < NB / 2 with the up block nb + NB / 2 of the same rows and columns.
     auto row_of = [&](int mb, int h) __attribute__((always_inline)) {
       return t.m0 + (kLay1 && lay1 ? 2 * mb + h : 2 * mb + wm) * 32 + (lane & 31);
     };
@@ -478,20 +557,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       for (int q = 0; q < 4; ++q) {
         if (MODE == MODE_GATE_UP) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
+          for (int nb = 0; nb < kNB / 2; ++nb) {
             const int r = row_of(mb, nb);
-            const int col = t.c0 + (lay1 ? wave * 32 : wn * 64 + nb * 32) + 8 * q + 4 * hk;
+            const int col = t.c0 + (lay1 ? wave * 32 : wn * (kNB / 2) * 32 + nb * 32) + 8 * q + 4 * hk;
             if (r >= t.mend || col >= n_cols) continue;
             float hv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const float g = acc[mb][nb][4 * q + u];
-              const float up = acc[mb][nb + 2][4 * q + u];
+              const float up = acc[mb][nb + kNB / 2][4 * q + u];
               hv[u] = silu_f32(g) * up;
             }
             if (p.au != nullptr) {   // the pre-activations, for the backward pass
               const f32x16_t& ga = acc[mb][nb];
-              const f32x16_t& ua = acc[mb][nb + 2];
+              const f32x16_t& ua = acc[mb][nb + kNB / 2];
               uint16_t* arow = reinterpret_cast<uint16_t*>(p.au) + static_cast<size_t>(r) * 2 * p.I;
               *reinterpret_cast<uint2*>(arow + col) =
                   make_uint2(pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3]));
@@ -505,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
             const int r = row_of(mb, nb & 1);
-            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * 128 + nb * 32) + 8 * q + 4 * hk;
+            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 8 * q + 4 * hk;
             if (r >= t.mend || col >= n_cols) continue;
             const f32x16_t& a = acc[mb][nb];
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) +
@@ -516,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
             const int r = row_of(mb, nb & 1);
-            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * 128 + nb * 32) + 8 * q + 4 * hk;
+            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 8 * q + 4 * hk;
             if (r >= t.mend || col >= n_cols) continue;
             const float gs = gsv[mb];
             const f32x16_t& a = acc[mb][nb];
@@ -528,15 +607,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
       }
     }
     if (!more) break;
-    // the next tile's first stages load while these stores drain: the wait below covers the
-    // stores (older) and stage 0, and leaves stage 1 in flight
+    // the next tile's first stages load while these stores drain: the prologue's wait covers
+    // the stores (older) and stage 0, and leaves the later stages in flight
     setup(Ln, cur);
     prologue(cur);
-    wait_vmcnt<kStageLd + kLd>();
-    block_barrier();
     v = vn;
     L = Ln;
   }
+}
+
+// bf16 (or W8) grouped GEMM: for the bf16 down GEMM, the experts listed for 320 x 128 tiles
+// first (when the schedule lists any), then the 256 x 256 tiles.  A workgroup that runs out of
+// the first shape's tiles moves on to the second's without waiting for the others.  (The
+// gate/up GEMM keeps 256 x 256 tiles: there a 320-row tile re-reads the expert's gathered
+// token rows from twice as many n-blocks, and that costs more than streaming the weight
+// panel once saves.)
+template <int MODE, bool W8>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Geo<0, W8>::LdsTot];
+  if constexpr (MODE == MODE_DOWN && !W8) {
+    if (p.tall_list != nullptr) run_tiles<MODE, W8, 1>(p, lds);
+  }
+  run_tiles<MODE, W8, 0>(p, lds);
 }
 
 }  // namespace
@@ -544,6 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s, bool w8) {
   const dim3 grid(256), block(kThreads);   // persistent: one workgroup per CU, a multiple of the 8 XCDs
   if (w8 && mode != MODE_DOWN) return hipErrorNotSupported;
+  if ((w8 || mode != MODE_DOWN) && p.tall_list != nullptr) return hipErrorNotSupported;
   if (mode == MODE_GATE_UP)
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_GATE_UP, false>), grid, block, 0, s, p);
   else if (mode == MODE_DOWN && w8)

@@ -334,6 +334,12 @@ GEMM_CASES = [
     # weights converted as they are read (ragged tails, an empty expert, a one-row one)
     ("fp8_wide_down", [300, 520, 0, 700, 129, 257, 1, 640], 1024, 1024, "fp8"),
     ("bf16_wide_K", [200, 90], 7168, 256, "bf16"),
+    # experts of 257..320 rows as one 320-row tile, beside 256-row tiles with ragged column
+    # blocks (H = 640: two and a half 256-column blocks of the down GEMM)
+    ("bf16_tall", [257, 320, 288, 0, 289, 256, 321, 1], 640, 384, "bf16"),
+    # the same at K = 128 and K = 256 (fewer stages than the 320-row tile's weight ring runs ahead)
+    ("bf16_tall_k128", [300, 5, 260], 128, 128, "bf16"),
+    ("bf16_tall_k256", [300, 257, 40], 256, 256, "bf16"),
     # at most 16 rows per expert on average with e4m3 weights: the weight-streaming kernels
     ("fp8_decode_ragged", [0, 1, 2, 5, 16, 17, 33, 0, 3, 0, 9, 1, 4, 0, 7, 12], 1024, 256, "fp8"),
     ("fp8_decode_one_k_block", [1, 0], 128, 128, "fp8"),

@@ -3,9 +3,11 @@ full with the oracle.
 
 The bf16 expert GEMMs run one workgroup per CU (256) and hand tiles out from a counter per
 XCD, so a workgroup that finishes a tile takes the next index while its last stages run and
-loads that tile's first stages while its epilogue stores drain.  The small layer tests give
-few workgroups a second tile; here the routed segments and the shared segment make about
-four gate/up tiles and four down tiles per workgroup.  Every output row of every launch is
+loads that tile's first stages while its epilogue stores drain.  Experts of 257..320 rows run
+first, as one tile of 320 rows x 128 weight rows each (their own counters), then the rest on
+256 x 256 tiles.  The small layer tests give few workgroups a second tile; here the routed
+segments and the shared segment make about four gate/up tiles and four down tiles per
+workgroup, and the "tall" case more than three 320-row tiles per workgroup in each GEMM.  Every output row of every launch is
 compared with the oracle's expert FFN on the same rows, and every output buffer starts as
 NaN, so a tile that is skipped (or whose rows land elsewhere) cannot pass.
 
@@ -34,12 +36,21 @@ CASES = {
     "ragged": [420, 1260, 0, 717, 257, 896, 1078, 466, 1246, 256, 672, 840, 980, 532, 1148, 564],
     # one expert takes every token, the others are small or empty
     "hot": [2900, 33, 0, 300, 1, 700, 512, 31, 2900, 640, 260, 0, 900, 1333, 1050, 40],
+    # 26 experts of 257..320 rows (both ends, and 288 / 289 around the ninth 32-row block)
+    # beside 256, 321, empty, one-row and split ones
+    "tall": [257, 320, 288, 289, 300, 260, 319, 270, 301, 311, 258, 280, 295, 317, 263, 299, 305,
+             266, 284, 292, 313, 274, 308, 320, 256, 321, 0, 1, 640, 36, 287, 290],
 }
+TALL_ROWS = 320     # a routed expert of TILE_ROWS < n_e <= TALL_ROWS rows: one 320-row tile
 
 
-def _tiles(seg_rows, cols_per_tile, n_cols):
+def _tiles(seg_rows, cols_per_tile, n_cols, n_routed):
+    """(256-row tiles, 320-row tiles) of the schedule: the routed experts of 257..320 rows take
+    one 320-row tile per n-block of half the columns."""
     n_blk = -(-n_cols // cols_per_tile)
-    return sum(-(-r // TILE_ROWS) for r in seg_rows) * n_blk
+    tall = [i < n_routed and TILE_ROWS < r <= TALL_ROWS for i, r in enumerate(seg_rows)]
+    wide = sum(-(-r // TILE_ROWS) for r, t in zip(seg_rows, tall) if not t) * n_blk
+    return wide, sum(tall) * -(-n_cols // (cols_per_tile // 2))
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -50,10 +61,14 @@ def test_multitile_gate_up_down_every_row(case):
     N = idx.shape[0]
     rows = N * K
     segs = [c for c in n_e] + [N]
-    gu_tiles = _tiles(segs, 128, I)      # gate/up: 128 h columns (256 weight rows) per tile
-    dn_tiles = _tiles(segs, 256, H)      # down: 256 output columns per tile
-    say(f"multitile {case}: N={N} rows={rows} E={E} H={H} I={I}; gate/up tiles {gu_tiles}, down tiles {dn_tiles}")
-    assert gu_tiles >= 3.5 * WORKGROUPS and dn_tiles >= 3.5 * WORKGROUPS
+    gu_tiles = _tiles(segs, 128, I, E)   # gate/up: 128 h columns (256 weight rows) per tile
+    dn_tiles = _tiles(segs, 256, H, E)   # down: 256 output columns per tile
+    say(f"multitile {case}: N={N} rows={rows} E={E} H={H} I={I}; gate/up tiles (256, 320 rows) {gu_tiles}, "
+        f"down tiles {dn_tiles}")
+    if case == "tall":
+        assert gu_tiles[1] >= 3 * WORKGROUPS and dn_tiles[1] >= 3 * WORKGROUPS
+    else:
+        assert sum(gu_tiles) >= 3.5 * WORKGROUPS and sum(dn_tiles) >= 3.5 * WORKGROUPS
 
     bf = torch.bfloat16
     x = w.normal((N, H), w.stream_key(21, w.T_X, E), DEV, bf)
@@ -107,7 +122,7 @@ def test_multitile_gate_up_down_every_row(case):
     assert torch.equal(out[:rows].view(torch.int16), out_r.view(torch.int16))
 
 
-@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("case", ["ragged", "hot"])
 def test_multitile_down_e4m3_every_row(case):
     """The down GEMM on e4m3 weights with fp32 scales per 128-column block (an fp8 layer's),
     at the same ragged counts: at least three tiles per workgroup, every row of NaN-filled output
@@ -116,9 +131,9 @@ def test_multitile_down_e4m3_every_row(case):
     once), so the bar is the bf16 GEMM's."""
     n_e = CASES[case]
     E, rows = len(n_e), sum(n_e)
-    dn_tiles = _tiles(n_e, 256, H)
-    say(f"multitile e4m3 down {case}: rows={rows} E={E} H={H} K={I}; tiles {dn_tiles}")
-    assert dn_tiles >= 3 * WORKGROUPS
+    dn_tiles = _tiles(n_e, 256, H, 0)   # (e4m3 weights: every expert on 256 x 256 tiles)
+    say(f"multitile e4m3 down {case}: rows={rows} E={E} H={H} K={I}; tiles {dn_tiles[0]}")
+    assert dn_tiles[0] >= 3 * WORKGROUPS
     h = w.normal((rows, I), w.stream_key(23, w.T_EO, E), DEV, torch.bfloat16, std=1.0)
     bits = w.uniform_bits(E * H * I, w.stream_key(23, w.T_W2, E), "cpu")
     codes = (np.asarray(bits) >> 24).astype(np.uint8).reshape(E, H, I)
