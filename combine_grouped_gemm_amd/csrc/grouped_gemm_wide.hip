@@ -30,7 +30,8 @@
 // a fragment read (32 rows, two chunks) and an 8-row load both touch all 64 banks once.
 //
 // The weight fragment is the MFMA's first operand, so a lane's accumulator holds one token
-// row and runs of 4 adjacent output columns: the epilogue stores 8 bytes per lane.
+// row and runs of 4 adjacent output columns; pairing the runs of lanes l and l + 32 (one
+// cross-lane exchange), the epilogue stores 16 bytes per lane.
 //
 // Ragged tiles: an expert's n_e rows are split into ceil(n_e / 256) tiles of equal size
 // (a multiple of 32 rows).  A tile with an even number R of 32-row blocks deals them to the
@@ -85,6 +86,18 @@ struct Geo {
 static_assert(Geo<1, false>::LdsTot <= Geo<0, false>::LdsTot, "both shapes fit the kernel's LDS");
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Lanes l and l + 32 hold the same output row: lane l < 32 columns 8 q .. 8 q + 3 of register
+// group q, lane l + 32 columns 8 q + 4 .. 8 q + 7.  Exchanging group 2 u + 1 of lane l with
+// group 2 u of lane l + 32 (gfx950's v_permlane32_swap) leaves lane l with columns 16 u .. 16 u + 7
+// and lane l + 32 with 16 u + 8 .. 16 u + 15, in order: one 16-byte store per lane.  lo and hi
+// are this lane's groups 2 u and 2 u + 1 as packed bf16; every lane must take part.
+__device__ __forceinline__ uint4 lane_pair(uint2 lo, uint2 hi) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t a = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+  const u32x2_t b = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+  return make_uint4(a[0], b[0], a[1], b[1]);
+}
 // (W8) 64-byte weight rows: chunk c of row r sits in slot c ^ key4(r); a fragment read (32 rows,
 // 8 bytes of one chunk per lane) then spreads over 16 of the 32 eight-byte bank pairs
 __device__ __forceinline__ int key4(int r) { return (r >> 2) & 3; }
@@ -530,9 +543,11 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     // ---- epilogue: block acc[mb][nb] holds, in lane l, token row rblk * 32 + l % 32 of the
     // tile and, in registers 4q .. 4q+3, output columns cblk + 8q + 4 (l / 32) + 0..3 (2 x 2:
     // rblk = 2 mb + wm, cblk = 32 nb of the wave's 32 NB columns; 1 x 4: rblk = 2 mb + nb % 2,
-    // cblk = 32 (nb / 2) of the wave's 64): one 8-byte store per run (16 bytes for fp32
-    // router sums; n_cols % 4 == 0, so a run is all in or all out).  Gate/up pairs the gate
-    // block nb < NB / 2 with the up block nb + NB / 2 of the same rows and columns.
+    // cblk = 32 (nb / 2) of the wave's 64).  bf16 outputs: the runs of groups 2u and 2u + 1
+    // are exchanged between the lane halves, one 16-byte store per lane and pair (n_cols % 8
+    // == 0, so a lane's 8 columns are all in or all out); fp32 router sums: one 16-byte store
+    // per run (n_cols % 4 == 0).  Gate/up pairs the gate block nb < NB / 2 with the up block
+    // nb + NB / 2 of the same rows and columns.
     auto row_of = [&](int mb, int h) __attribute__((always_inline)) {
       return t.m0 + (kLay1 && lay1 ? 2 * mb + h : 2 * mb + wm) * 32 + (lane & 31);
     };
@@ -553,34 +568,9 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     if (MODE == MODE_DOWN) wait_vmcnt<0>();
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
+      if constexpr (MODE == MODE_ROUTER) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (MODE == MODE_GATE_UP) {
-#pragma unroll
-          for (int nb = 0; nb < kNB / 2; ++nb) {
-            const int r = row_of(mb, nb);
-            const int col = t.c0 + (lay1 ? wave * 32 : wn * (kNB / 2) * 32 + nb * 32) + 8 * q + 4 * hk;
-            if (r >= t.mend || col >= n_cols) continue;
-            float hv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float g = acc[mb][nb][4 * q + u];
-              const float up = acc[mb][nb + kNB / 2][4 * q + u];
-              hv[u] = silu_f32(g) * up;
-            }
-            if (p.au != nullptr) {   // the pre-activations, for the backward pass
-              const f32x16_t& ga = acc[mb][nb];
-              const f32x16_t& ua = acc[mb][nb + kNB / 2];
-              uint16_t* arow = reinterpret_cast<uint16_t*>(p.au) + static_cast<size_t>(r) * 2 * p.I;
-              *reinterpret_cast<uint2*>(arow + col) =
-                  make_uint2(pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3]));
-              *reinterpret_cast<uint2*>(arow + p.I + col) =
-                  make_uint2(pack_bf16x2(ua[4 * q], ua[4 * q + 1]), pack_bf16x2(ua[4 * q + 2], ua[4 * q + 3]));
-            }
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.I + col) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          }
-        } else if (MODE == MODE_ROUTER) {
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
             const int r = row_of(mb, nb & 1);
@@ -591,17 +581,54 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
                                        (static_cast<size_t>(t.kp) * p.rows + r) * p.n_out + col) =
                 make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
-        } else {
+        }
+      } else {
+        // bf16 rows: register groups 2 u and 2 u + 1 are paired across the lane halves, so a
+        // lane stores 8 adjacent columns (16 bytes) at column 16 u + 8 hk of its block
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) {
-            const int r = row_of(mb, nb & 1);
-            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 8 * q + 4 * hk;
-            if (r >= t.mend || col >= n_cols) continue;
-            const float gs = gsv[mb];
-            const f32x16_t& a = acc[mb][nb];
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.n_out + col) =
-                make_uint2(pack_bf16x2(a[4 * q] * gs, a[4 * q + 1] * gs),
-                           pack_bf16x2(a[4 * q + 2] * gs, a[4 * q + 3] * gs));
+        for (int u = 0; u < 2; ++u) {
+          if constexpr (MODE == MODE_GATE_UP) {
+#pragma unroll
+            for (int nb = 0; nb < kNB / 2; ++nb) {
+              const int r = row_of(mb, nb);
+              const int col = t.c0 + (lay1 ? wave * 32 : wn * (kNB / 2) * 32 + nb * 32) + 16 * u + 8 * hk;
+              const f32x16_t& ga = acc[mb][nb];
+              const f32x16_t& ua = acc[mb][nb + kNB / 2];
+              uint2 hq[2];
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                const int b0 = 8 * u + 4 * g;
+                hq[g] = make_uint2(pack_bf16x2(silu_f32(ga[b0]) * ua[b0], silu_f32(ga[b0 + 1]) * ua[b0 + 1]),
+                                   pack_bf16x2(silu_f32(ga[b0 + 2]) * ua[b0 + 2], silu_f32(ga[b0 + 3]) * ua[b0 + 3]));
+              }
+              const uint4 hv = lane_pair(hq[0], hq[1]);   // (every lane: the exchange reads both halves)
+              if (p.au != nullptr) {   // the pre-activations, for the backward pass
+                const uint4 gv = lane_pair(make_uint2(pack_bf16x2(ga[8 * u], ga[8 * u + 1]), pack_bf16x2(ga[8 * u + 2], ga[8 * u + 3])),
+                                           make_uint2(pack_bf16x2(ga[8 * u + 4], ga[8 * u + 5]), pack_bf16x2(ga[8 * u + 6], ga[8 * u + 7])));
+                const uint4 uv = lane_pair(make_uint2(pack_bf16x2(ua[8 * u], ua[8 * u + 1]), pack_bf16x2(ua[8 * u + 2], ua[8 * u + 3])),
+                                           make_uint2(pack_bf16x2(ua[8 * u + 4], ua[8 * u + 5]), pack_bf16x2(ua[8 * u + 6], ua[8 * u + 7])));
+                if (r < t.mend && col < n_cols) {
+                  uint16_t* arow = reinterpret_cast<uint16_t*>(p.au) + static_cast<size_t>(r) * 2 * p.I;
+                  *reinterpret_cast<uint4*>(arow + col) = gv;
+                  *reinterpret_cast<uint4*>(arow + p.I + col) = uv;
+                }
+              }
+              if (r < t.mend && col < n_cols)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.I + col) = hv;
+            }
+          } else {
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+              const int r = row_of(mb, nb & 1);
+              const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 16 * u + 8 * hk;
+              const float gs = gsv[mb];
+              const f32x16_t& a = acc[mb][nb];
+              const uint4 ov = lane_pair(
+                  make_uint2(pack_bf16x2(a[8 * u] * gs, a[8 * u + 1] * gs), pack_bf16x2(a[8 * u + 2] * gs, a[8 * u + 3] * gs)),
+                  make_uint2(pack_bf16x2(a[8 * u + 4] * gs, a[8 * u + 5] * gs), pack_bf16x2(a[8 * u + 6] * gs, a[8 * u + 7] * gs)));
+              if (r < t.mend && col < n_cols)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.n_out + col) = ov;
+            }
           }
         }
       }
