@@ -734,10 +734,18 @@ static bool wide_tiles_fit(int mode, int rows, int n_seg, int I, int n_out) {
   return static_cast<long long>(gemm_tile_cap(rows, n_seg)) * n_blocks * kNumXcd < (1LL << 31);
 }
 
+// the wide kernel stores a tile's outputs through a buffer window over its rows (at most 320):
+// the window and every offset in it stay below 2^31 bytes (gate/up: the pre-activation rows
+// of 4 I bytes too)
+static bool wide_out_fits(int mode, int I, int n_out) {
+  return static_cast<long long>(kWideTallRows) * 4 * (mode == MODE_GATE_UP ? I : n_out) < (1LL << 31);
+}
+
 bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long b_rows, int a_nrows,
                                    bool gathered) {
   const long long rbytes = 2LL * K;
-  return K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 8 == 0 && b_rows * rbytes < (1LL << 32) &&
+  return K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 8 == 0 && wide_out_fits(mode, I, n_out) &&
+         b_rows * rbytes < (1LL << 32) &&
          (gathered ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32);
 }
 
@@ -788,6 +796,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   // 256 x 256 tiles while every operand offset fits the kernel's 32-bit arithmetic
   const long long rbytes = 2LL * K;
   const bool wide_ok = dma && K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 8 == 0 &&
+                       wide_out_fits(mode, I, n_out) &&
                        b_rows * rbytes < (1LL << 32) &&
                        (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32) &&
                        wide_tiles_fit(mode, rows + shared_rows, n_seg, I, n_out);
@@ -798,6 +807,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   // e4m3 down weights at more than 16 rows per expert: the 256 x 256 kernel, which converts
   // each weight fragment (code times its block's scale) as it reads it from LDS
   const bool wide8 = mode == MODE_DOWN && ct == CT_BF16 && b8 && !stream && K % 128 == 0 && n_out % 8 == 0 &&
+                     wide_out_fits(mode, I, n_out) &&
                      b_rows * K < (1LL << 32) && b_rows * (K / 128) * 4 < (1LL << 32) &&
                      static_cast<long long>(kWideTileRows) * rbytes < (1LL << 32) && shared_rows == 0 &&
                      au == nullptr && a_rows == nullptr && wide_tiles_fit(mode, rows, n_seg, I, n_out);

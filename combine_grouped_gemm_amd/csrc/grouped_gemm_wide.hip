@@ -87,6 +87,17 @@ static_assert(Geo<1, false>::LdsTot <= Geo<0, false>::LdsTot, "both shapes fit t
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// A raw buffer resource over `bytes` bytes from `base`: a store whose 16 bytes do not all lie
+// inside writes nothing.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+__device__ __forceinline__ buf_rsrc_t make_window(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void store16(buf_rsrc_t w, uint32_t off, uint4 v) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4v{v.x, v.y, v.z, v.w}, w, static_cast<int>(off), 0, 0);
+}
+
 // Lanes l and l + 32 hold the same output row: lane l < 32 columns 8 q .. 8 q + 3 of register
 // group q, lane l + 32 columns 8 q + 4 .. 8 q + 7.  Exchanging group 2 u + 1 of lane l with
 // group 2 u of lane l + 32 (gfx950's v_permlane32_swap) leaves lane l with columns 16 u .. 16 u + 7
@@ -165,7 +176,6 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   const uint32_t rbw = W8 ? static_cast<uint32_t>(p.K) : rb;   // row bytes of the weights
   const uint32_t kblk = static_cast<uint32_t>(p.K) / 128;      // (W8) scale blocks per weight row
 
-  const int hk = lane >> 5;
   // first row of the wave's activation block m and weight block n, per layout (gate/up in
   // the 2 x 2 layout: the first NB / 2 weight blocks are W_gate rows, the rest the same W_up
   // rows; in the 1 x 4 layout wave w holds weight rows 64 w .. 64 w + 63, gate/up: W_gate
@@ -270,16 +280,29 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       t.a += static_cast<size_t>(kp) * kspan * 2;
       t.b += static_cast<size_t>(kp) * kspan * 2;
     }
+    int ra[kLdA];   // operand row of each of this lane's loads
 #pragma unroll
     for (int j = 0; j < kLdA; ++j) {
       const int r = (wave + 4 * j) * 8 + lrow;   // tile row of this lane's loads
-      int ra = r < t.mlast ? r : t.mlast;
-      if (p.a_rows) {   // (the shared segment's row r is token r - rows)
-        int tok = e < p.E ? p.a_rows[t.m0 + ra] / p.a_div : t.m0 + ra - p.rows;
-        ra = tok < 0 ? 0 : (tok < p.a_nrows ? tok : p.a_nrows - 1);
-      }
-      t.a_src[j] = static_cast<uint32_t>(ra) * rb + lchunk * 16;
+      ra[j] = r < t.mlast ? r : t.mlast;
     }
+    if (p.a_rows) {   // (the shared segment's row r is token r - rows)
+      int tok[kLdA];
+      if (e < p.E) {
+        // every index load issued before the first is used: one memory latency, not kLdA
+#pragma unroll
+        for (int j = 0; j < kLdA; ++j) tok[j] = p.a_rows[t.m0 + ra[j]];
+#pragma unroll
+        for (int j = 0; j < kLdA; ++j) tok[j] /= p.a_div;
+      } else {
+#pragma unroll
+        for (int j = 0; j < kLdA; ++j) tok[j] = t.m0 + ra[j] - p.rows;
+      }
+#pragma unroll
+      for (int j = 0; j < kLdA; ++j) ra[j] = tok[j] < 0 ? 0 : (tok[j] < p.a_nrows ? tok[j] : p.a_nrows - 1);
+    }
+#pragma unroll
+    for (int j = 0; j < kLdA; ++j) t.a_src[j] = static_cast<uint32_t>(ra[j]) * rb + lchunk * 16;
 #pragma unroll
     for (int j = 0; j < kLdW; ++j) {
       if constexpr (W8) {
@@ -318,8 +341,8 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
              lds0 + static_cast<uint32_t>(kSBase + ws * 1024 + wave * 256));
   };
   // prologue loads of a tile: activation rows of stage 0, weight rows of stages 0 .. kWS - 2
-  // (those that exist), activation rows of stage 1; then the wait for stage 0 and the barrier
-  auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
+  // (those that exist), activation rows of stage 1
+  auto prologue_loads = [&](const Tile& t) __attribute__((always_inline)) {
     static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
     static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 0, 0); });
     if constexpr (W8) load_s(t, 0, 0);
@@ -331,8 +354,11 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       }
     });
     static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 1, 1); });
-    // stage 0 landed once at most the later stages' loads remain
-    if (G == 0 || nk >= kWS - 1) wait_vmcnt<(kWS - 2) * kStageLd + kLdA>();
+  };
+  // then the wait for stage 0 and the barrier: stage 0 landed once at most the later stages'
+  // loads and the AFTER memory instructions issued behind them remain
+  auto prologue_wait = [&]<int AFTER>() __attribute__((always_inline)) {
+    if (G == 0 || nk >= kWS - 1) wait_vmcnt<(kWS - 2) * kStageLd + kLdA + AFTER>();
     else wait_vmcnt<0>();
     block_barrier();
   };
@@ -340,7 +366,8 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   Tile cur;
   int L = tile_of(v);
   setup(L, cur);
-  prologue(cur);
+  prologue_loads(cur);
+  prologue_wait.template operator()<0>();
 
   for (;;) {
     const Tile& t = cur;   // (rewritten at the boundary, after the epilogue's last use)
@@ -539,6 +566,8 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     }
     const bool more = vn < v_end;
     const int Ln = more ? tile_of(vn) : 0;
+    // the finished tile's rows and columns (cur is rewritten by the next tile's set-up)
+    const int em0 = t.m0, emend = t.mend, ec0 = t.c0, ekp = t.kp;
 
     // ---- epilogue: block acc[mb][nb] holds, in lane l, token row rblk * 32 + l % 32 of the
     // tile and, in registers 4q .. 4q+3, output columns cblk + 8q + 4 (l / 32) + 0..3 (2 x 2:
@@ -548,41 +577,63 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     // == 0, so a lane's 8 columns are all in or all out); fp32 router sums: one 16-byte store
     // per run (n_cols % 4 == 0).  Gate/up pairs the gate block nb < NB / 2 with the up block
     // nb + NB / 2 of the same rows and columns.
-    auto row_of = [&](int mb, int h) __attribute__((always_inline)) {
-      return t.m0 + (kLay1 && lay1 ? 2 * mb + h : 2 * mb + wm) * 32 + (lane & 31);
+    // (the lane's row and column half are derived here from the lane id: kept from before the
+    // K loop they would be spilled, and their reloads' waits would also wait for the next
+    // tile's first loads, issued ahead of them)
+    const int eln = static_cast<int>(opaque_lane());
+    const int erow = eln & 31, ehk = eln >> 5;
+    auto row_in = [&](int mb, int h) __attribute__((always_inline)) {   // row within the tile
+      return (kLay1 && lay1 ? 2 * mb + h : 2 * mb + wm) * 32 + erow;
     };
-    // down with gates: a routed row carries the gate of its slot (the shared rows gate 1).
-    // The gates are loaded first and waited for once: a load pending across the stores'
-    // row and column branches would make the compiler wait for every store before the next.
+    // down with gates: a routed row carries the gate of its slot (the shared rows gate 1),
+    // loaded and waited for before anything else is issued
     float gsv[kMB];   // (only the down GEMM has gates, and it runs the 2 x 2 layout)
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const int r = row_of(mb, 0);
-      gsv[mb] = 1.0f;
-      if (MODE == MODE_DOWN && p.row_gate != nullptr && r < p.rows && r < t.mend) {
-        int sl = p.row_slot[r];
-        sl = sl < 0 ? 0 : (sl < p.rows ? sl : p.rows - 1);
-        gsv[mb] = p.row_gate[sl];
+    for (int mb = 0; mb < kMB; ++mb) gsv[mb] = 1.0f;
+    if (MODE == MODE_DOWN && p.row_gate != nullptr) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        const int r = em0 + row_in(mb, 0);
+        if (r < p.rows && r < emend) {
+          int sl = p.row_slot[r];
+          sl = sl < 0 ? 0 : (sl < p.rows ? sl : p.rows - 1);
+          gsv[mb] = p.row_gate[sl];
+        }
       }
+      wait_vmcnt<0>();
     }
-    if (MODE == MODE_DOWN) wait_vmcnt<0>();
+    // bf16 outputs go out as buffer stores over the tile's rows, a fixed number per wave (a
+    // lane outside the tile's rows or the output's columns gets an offset past the window and
+    // writes nothing), so the next tile's set-up and first loads are issued before them and
+    // its wait for stage 0 leaves exactly these stores in flight
+    constexpr bool kEarly = MODE != MODE_ROUTER;
+    constexpr int kStores = MODE == MODE_GATE_UP ? kMB * (kNB / 2) * 2 : kMB * kNB * 2;
+    if (kEarly && more) {
+      setup(Ln, cur);
+      prologue_loads(cur);
+    }
+    const uint32_t orow = static_cast<uint32_t>(n_cols) * 2;   // bytes of an output row
+    constexpr uint32_t kNoWrite = 0x80000000u;                   // past every tile's window
+    if constexpr (MODE == MODE_ROUTER) {
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      if constexpr (MODE == MODE_ROUTER) {
+      for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int r = row_of(mb, nb & 1);
-            const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 8 * q + 4 * hk;
-            if (r >= t.mend || col >= n_cols) continue;
+            const int r = em0 + row_in(mb, nb & 1);
+            const int col = ec0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 8 * q + 4 * ehk;
+            if (r >= emend || col >= n_cols) continue;
             const f32x16_t& a = acc[mb][nb];
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) +
-                                       (static_cast<size_t>(t.kp) * p.rows + r) * p.n_out + col) =
+                                       (static_cast<size_t>(ekp) * p.rows + r) * p.n_out + col) =
                 make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
-        }
-      } else {
+    } else {
+      const uint32_t nrow = static_cast<uint32_t>(emend - em0);
+      const buf_rsrc_t out_w = make_window(reinterpret_cast<uint8_t*>(p.out) + static_cast<size_t>(em0) * orow, nrow * orow);
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
         // bf16 rows: register groups 2 u and 2 u + 1 are paired across the lane halves, so a
         // lane stores 8 adjacent columns (16 bytes) at column 16 u + 8 hk of its block
 #pragma unroll
@@ -590,8 +641,9 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
           if constexpr (MODE == MODE_GATE_UP) {
 #pragma unroll
             for (int nb = 0; nb < kNB / 2; ++nb) {
-              const int r = row_of(mb, nb);
-              const int col = t.c0 + (lay1 ? wave * 32 : wn * (kNB / 2) * 32 + nb * 32) + 16 * u + 8 * hk;
+              const int ri = row_in(mb, nb);
+              const int col = ec0 + (lay1 ? wave * 32 : wn * (kNB / 2) * 32 + nb * 32) + 16 * u + 8 * ehk;
+              const bool in = ri < static_cast<int>(nrow) && col < n_cols;
               const f32x16_t& ga = acc[mb][nb];
               const f32x16_t& ua = acc[mb][nb + kNB / 2];
               uint2 hq[2];
@@ -601,43 +653,48 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
                 hq[g] = make_uint2(pack_bf16x2(silu_f32(ga[b0]) * ua[b0], silu_f32(ga[b0 + 1]) * ua[b0 + 1]),
                                    pack_bf16x2(silu_f32(ga[b0 + 2]) * ua[b0 + 2], silu_f32(ga[b0 + 3]) * ua[b0 + 3]));
               }
-              const uint4 hv = lane_pair(hq[0], hq[1]);   // (every lane: the exchange reads both halves)
+              store16(out_w, in ? static_cast<uint32_t>(ri) * orow + static_cast<uint32_t>(col) * 2 : kNoWrite,
+                      lane_pair(hq[0], hq[1]));   // (every lane: the exchange reads both halves)
               if (p.au != nullptr) {   // the pre-activations, for the backward pass
-                const uint4 gv = lane_pair(make_uint2(pack_bf16x2(ga[8 * u], ga[8 * u + 1]), pack_bf16x2(ga[8 * u + 2], ga[8 * u + 3])),
-                                           make_uint2(pack_bf16x2(ga[8 * u + 4], ga[8 * u + 5]), pack_bf16x2(ga[8 * u + 6], ga[8 * u + 7])));
-                const uint4 uv = lane_pair(make_uint2(pack_bf16x2(ua[8 * u], ua[8 * u + 1]), pack_bf16x2(ua[8 * u + 2], ua[8 * u + 3])),
-                                           make_uint2(pack_bf16x2(ua[8 * u + 4], ua[8 * u + 5]), pack_bf16x2(ua[8 * u + 6], ua[8 * u + 7])));
-                if (r < t.mend && col < n_cols) {
-                  uint16_t* arow = reinterpret_cast<uint16_t*>(p.au) + static_cast<size_t>(r) * 2 * p.I;
-                  *reinterpret_cast<uint4*>(arow + col) = gv;
-                  *reinterpret_cast<uint4*>(arow + p.I + col) = uv;
-                }
+                const uint32_t arow = static_cast<uint32_t>(p.I) * 4;
+                const buf_rsrc_t au_w =
+                    make_window(reinterpret_cast<uint8_t*>(p.au) + static_cast<size_t>(em0) * arow, nrow * arow);
+                const uint32_t ao = in ? static_cast<uint32_t>(ri) * arow + static_cast<uint32_t>(col) * 2 : kNoWrite;
+                store16(au_w, ao,
+                        lane_pair(make_uint2(pack_bf16x2(ga[8 * u], ga[8 * u + 1]), pack_bf16x2(ga[8 * u + 2], ga[8 * u + 3])),
+                                  make_uint2(pack_bf16x2(ga[8 * u + 4], ga[8 * u + 5]), pack_bf16x2(ga[8 * u + 6], ga[8 * u + 7]))));
+                store16(au_w, in ? ao + static_cast<uint32_t>(p.I) * 2 : kNoWrite,
+                        lane_pair(make_uint2(pack_bf16x2(ua[8 * u], ua[8 * u + 1]), pack_bf16x2(ua[8 * u + 2], ua[8 * u + 3])),
+                                  make_uint2(pack_bf16x2(ua[8 * u + 4], ua[8 * u + 5]), pack_bf16x2(ua[8 * u + 6], ua[8 * u + 7]))));
               }
-              if (r < t.mend && col < n_cols)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.I + col) = hv;
             }
           } else {
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
-              const int r = row_of(mb, nb & 1);
-              const int col = t.c0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 16 * u + 8 * hk;
+              const int ri = row_in(mb, nb & 1);
+              const int col = ec0 + (lay1 ? wave * 64 + (nb >> 1) * 32 : wn * kNB * 32 + nb * 32) + 16 * u + 8 * ehk;
+              const bool in = ri < static_cast<int>(nrow) && col < n_cols;
               const float gs = gsv[mb];
               const f32x16_t& a = acc[mb][nb];
               const uint4 ov = lane_pair(
                   make_uint2(pack_bf16x2(a[8 * u] * gs, a[8 * u + 1] * gs), pack_bf16x2(a[8 * u + 2] * gs, a[8 * u + 3] * gs)),
                   make_uint2(pack_bf16x2(a[8 * u + 4] * gs, a[8 * u + 5] * gs), pack_bf16x2(a[8 * u + 6] * gs, a[8 * u + 7] * gs)));
-              if (r < t.mend && col < n_cols)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + static_cast<size_t>(r) * p.n_out + col) = ov;
+              store16(out_w, in ? static_cast<uint32_t>(ri) * orow + static_cast<uint32_t>(col) * 2 : kNoWrite, ov);
             }
           }
         }
       }
     }
     if (!more) break;
-    // the next tile's first stages load while these stores drain: the prologue's wait covers
-    // the stores (older) and stage 0, and leaves the later stages in flight
-    setup(Ln, cur);
-    prologue(cur);
+    if constexpr (kEarly) {
+      // stage 0 of the next tile has landed once at most its later stages' loads and this
+      // tile's stores (issued after them) remain: the stores drain under the next K loop
+      prologue_wait.template operator()<kStores>();
+    } else {
+      setup(Ln, cur);
+      prologue_loads(cur);
+      prologue_wait.template operator()<0>();
+    }
     v = vn;
     L = Ln;
   }
