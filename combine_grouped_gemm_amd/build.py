@@ -38,9 +38,15 @@ def _flags():
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source flags.  The wide GEMM takes its next tile with a single-lane atomicAdd whose result
+# is used only at the tile boundary; the atomic optimizer would turn it into a wave reduction
+# that reads the result at once (a wait for memory in the middle of a K loop stage).
+EXTRA_FLAGS = {"grouped_gemm_wide.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")

@@ -812,8 +812,9 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                      static_cast<long long>(kWideTileRows) * rbytes < (1LL << 32) && shared_rows == 0 &&
                      au == nullptr && a_rows == nullptr && wide_tiles_fit(mode, rows, n_seg, I, n_out);
   const int tile_rows = stream ? kStreamTileRows : (wide || wide8 ? kWideTileRows : (dma ? kDM : GBM));
-  // bf16 down GEMM on the 256 x 256 kernel: experts of 257..320 rows as one 320 x 128 tile
-  const bool tall = wide && mode == MODE_DOWN;
+  // bf16 GEMMs on the 256 x 256 kernel: experts of 257..320 rows as one tile (down: 320 x 128,
+  // gate/up: 320 x 256)
+  const bool tall = wide;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert, tile_counter, shared_rows, kWideTallRows,
                      tall ? tall_list : nullptr);

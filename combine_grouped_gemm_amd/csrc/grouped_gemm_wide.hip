@@ -61,19 +61,23 @@ constexpr int kThreads = 256;
 constexpr int kMB1 = 5, kNB1 = 2;   // at most 5 row blocks x 2 column blocks (1 x 4 layout)
 
 // Shape of a tile and of its LDS.  G = 0: 256 rows x 256 weight rows, two activation
-// buffers and a three-slot weight ring (5 x 32 KB).  G = 1 (an expert of 257-320 rows in one
-// tile): 320 rows x 128 weight rows, two activation buffers of 40 KB and a five-slot weight
-// ring of 16 KB slots, so the weight rows load 3.25-3.75 stages ahead.  W8: e4m3 weight
-// rows of 64 bytes per stage (G = 0 only).
+// buffers and a three-slot weight ring (5 x 32 KB).  G = 1 (down GEMM, an expert of 257-320
+// rows in one tile): 320 rows x 128 weight rows, two activation buffers of 40 KB and a
+// five-slot weight ring of 16 KB slots, so the weight rows load 3.25-3.75 stages ahead.
+// G = 2 (gate/up, an expert of 257-320 rows in one tile): 320 rows x 256 weight rows, two
+// activation buffers of 40 KB and a five-slot ring of 16 KB half-stages of weights (K = 32:
+// 64 bytes per row, chunks swizzled like the e4m3 rows), so the weight rows load 1-2 stages
+// ahead; its fifth row block's accumulators live in VGPRs (the first 256 in the AGPRs).  W8:
+// e4m3 weight rows of 64 bytes per stage (G = 0 only).
 template <int G, bool W8>
 struct Geo {
   static constexpr int TM = G ? kWideTallRows : kWideTileRows;
-  static constexpr int TN = G ? 128 : 256;
+  static constexpr int TN = G == 1 ? 128 : 256;
   static constexpr int MB = TM / 64, NB = TN / 64;   // 32 x 32 blocks per wave (2 x 2 layout)
-  static constexpr int WRowB = W8 ? 64 : kRowB;      // bytes of a weight row per stage
+  static constexpr int WRowB = W8 || G == 2 ? 64 : kRowB;   // bytes of a weight row per stage (G = 2: half)
   static constexpr int PartA = TM * kRowB;           // one stage of activation rows
   static constexpr int WPart = TN * WRowB;           // one stage of weight rows
-  static constexpr int WS = G ? 5 : 3;               // weight ring slots
+  static constexpr int WS = G != 0 ? 5 : 3;          // weight ring slots
   static constexpr int LdA = PartA / 4096;           // 1 KB loads per wave and stage (8; 10)
   static constexpr int LdW = WPart / 4096;           // (8, W8 4; 4)
   static constexpr int StageLd = LdW + (W8 ? 1 : 0); // + the scale gather (W8)
@@ -83,9 +87,16 @@ struct Geo {
   static_assert(!W8 || G == 0, "e4m3 weights: 256 x 256 tiles");
   static_assert(TM % 64 == 0 && TN % 64 == 0 && (TN / 2) % 32 == 0, "2 x 2 waves of 32-row blocks");
 };
-static_assert(Geo<1, false>::LdsTot <= Geo<0, false>::LdsTot, "both shapes fit the kernel's LDS");
+static_assert(Geo<1, false>::LdsTot <= Geo<0, false>::LdsTot && Geo<2, false>::LdsTot <= Geo<0, false>::LdsTot,
+              "every shape fits the kernel's LDS");
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// r * b + c for a row r and a row size b below 2^24 whose product fits 32 bits, as one 24-bit
+// multiply-add with a 32-bit result: a plain 32-bit multiply-add is formed as a 64-bit
+// v_mad_u64_u32 whose register pair stays live (and is spilled) when the value is kept
+// through the K loop.
+__device__ __forceinline__ uint32_t row_off(uint32_t r, uint32_t b, uint32_t c) { return __umul24(r, b) + c; }
 
 // A raw buffer resource over `bytes` bytes from `base`: a store whose 16 bytes do not all lie
 // inside writes nothing.
@@ -191,20 +202,20 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // Tiles: from the XCD's counter (dynamic), or every per_xcd-th of the XCD's range.  With
   // the counter, tiles adjacent in the order (the m-tiles sharing a weight panel, the
   // n-blocks sharing activation rows) start close together in time whatever the earlier
-  // tiles cost.  Wave 0 takes the next index during the tile's second-to-last stage (late
+  // tiles cost.  Wave 0 takes the next index early in the tile's second-to-last stage (late
   // enough that the take is still close to the start, early enough to hide its latency) and
   // hands it to the other waves at the tile boundary through the last word of the LDS array
   // (in the last weight ring slot, or the last scale slot with W8; no load writes that slot
   // between a boundary and the first stage).
-  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + S::LdsTot - 4);
+  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + Geo<0, W8>::LdsTot - 4);
   const bool dynamic = counter != nullptr;
-  int32_t grabbed = 0;   // (lane 0 of wave 0) the counter value taken for the next tile
   int v = slot;
   if (dynamic) {
     __syncthreads();   // (after a previous shape's tiles: every wave has read the word)
     if (tid == 0) *tile_word = atomicAdd(counter + xcd, 1);
     __syncthreads();
     v = __builtin_amdgcn_readfirstlane(*tile_word);
+    if constexpr (G == 2) block_barrier();   // (its prologue writes the slot that holds the word)
   }
   if (v >= v_end) return;
 
@@ -234,7 +245,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       mtile = local % mt_r;
       seg_lo = 0;
       seg_hi = p.rows;
-    } else if (G == 1) {   // one tile per listed expert: all of its rows
+    } else if (G != 0) {   // one tile per listed expert: all of its rows
       e = p.tall_list[1 + L / nN];
       mt_e = 1;
       nblk = L % nN;
@@ -302,7 +313,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       for (int j = 0; j < kLdA; ++j) ra[j] = tok[j] < 0 ? 0 : (tok[j] < p.a_nrows ? tok[j] : p.a_nrows - 1);
     }
 #pragma unroll
-    for (int j = 0; j < kLdA; ++j) t.a_src[j] = static_cast<uint32_t>(ra[j]) * rb + lchunk * 16;
+    for (int j = 0; j < kLdA; ++j) t.a_src[j] = row_off(static_cast<uint32_t>(ra[j]), rb, lchunk * 16);
 #pragma unroll
     for (int j = 0; j < kLdW; ++j) {
       if constexpr (W8) {
@@ -310,7 +321,14 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
         // of row l / 4 of the group, so it loads chunk (l % 4) ^ key4(row)
         const int r8 = (wave + 4 * j) * 16 + static_cast<int>(ln >> 2);
         const uint32_t w8 = static_cast<uint32_t>(t.c0 + (r8 < clast ? r8 : clast));
-        t.b_src[j] = w8 * rbw + static_cast<uint32_t>((ln & 3) ^ key4(r8)) * 16;
+        t.b_src[j] = row_off(w8, rbw, static_cast<uint32_t>((ln & 3) ^ key4(r8)) * 16);
+      } else if constexpr (G == 2) {
+        // half-stage rows of 64 bytes, laid out like the e4m3 rows; gate/up row mapping
+        const int r8 = (wave + 4 * j) * 16 + static_cast<int>(ln >> 2);
+        const int c = r8 % (kTN / 2);
+        const int cc = c < clast ? c : clast;
+        const uint32_t wr = (r8 < kTN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(t.c0 + cc);
+        t.b_src[j] = row_off(wr, rb, static_cast<uint32_t>((ln & 3) ^ key4(r8)) * 16);
       } else {
         const int r = (wave + 4 * j) * 8 + lrow;   // tile weight row of this lane's loads
         uint32_t wr;
@@ -321,7 +339,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
         } else {
           wr = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
         }
-        t.b_src[j] = wr * rb + lchunk * 16;
+        t.b_src[j] = row_off(wr, rb, lchunk * 16);
       }
     }
   };
@@ -343,6 +361,19 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // prologue loads of a tile: activation rows of stage 0, weight rows of stages 0 .. kWS - 2
   // (those that exist), activation rows of stage 1
   auto prologue_loads = [&](const Tile& t) __attribute__((always_inline)) {
+    if constexpr (G == 2) {
+      // activation rows of stage 0, weight halves 0-3 (stages 0 and 1), activation rows of
+      // stage 1, weight half 4 (when K holds it: nk is even, so nk >= 4)
+      static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
+      static_for<4>([&](auto hc) __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, h, h); });
+      });
+      static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 1, 1); });
+      if (nk >= 4)
+        static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 4, 4); });
+      return;
+    }
     static_for<kLdA>([&](auto j) __attribute__((always_inline)) { load_a.template operator()<j>(t, 0, 0); });
     static_for<kLdW>([&](auto j) __attribute__((always_inline)) { load_w.template operator()<j>(t, 0, 0); });
     if constexpr (W8) load_s(t, 0, 0);
@@ -358,7 +389,11 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // then the wait for stage 0 and the barrier: stage 0 landed once at most the later stages'
   // loads and the AFTER memory instructions issued behind them remain
   auto prologue_wait = [&]<int AFTER>() __attribute__((always_inline)) {
-    if (G == 0 || nk >= kWS - 1) wait_vmcnt<(kWS - 2) * kStageLd + kLdA + AFTER>();
+    if constexpr (G == 2) {   // (halves 2, 3, stage 1's activations and half 4 may remain)
+      if (nk >= 4) wait_vmcnt<3 * kLdW + kLdA + AFTER>();
+      else wait_vmcnt<2 * kLdW + kLdA + AFTER>();
+    }
+    else if (G == 0 || nk >= kWS - 1) wait_vmcnt<(kWS - 2) * kStageLd + kLdA + AFTER>();
     else wait_vmcnt<0>();
     block_barrier();
   };
@@ -371,11 +406,20 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
 
   for (;;) {
     const Tile& t = cur;   // (rewritten at the boundary, after the epilogue's last use)
+    // (lane 0 of wave 0) the counter value taken for the next tile; per tile, so that it is
+    // live only from the take to the boundary (carried across tiles it was spilled, and the
+    // take's pending result made the compiler wait for memory inside the next K loop)
+    int32_t grabbed;
     f32x16_t acc[kMB][kNB];
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
 #pragma unroll
       for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16_t{};
+    if constexpr (G == 2) {
+      // the VGPR accumulators' first reader is an MFMA in inline assembly, which the compiler's
+      // hazard checks do not see: two wait states after their VALU writes
+      __asm__ volatile("s_nop 1" : "+v"(acc[4][0]), "+v"(acc[4][1]), "+v"(acc[4][2]), "+v"(acc[4][3]));
+    }
 
     const int nblk = (t.mlast + 32) / 32;   // 32-row blocks that hold rows
     const bool lay1 = kLay1 && (nblk & 1) != 0 && nblk <= kMB1;
@@ -401,6 +445,13 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       // (W8) weight fragments: 8 codes at chunk s, half l / 32, of the 64-byte row; read raw,
       // then converted with the row's block scale (sc_cur: this stage's, sc_nxt: the next one's)
       uint32_t fbw[4];
+      // (G = 2) weight fragments from 64-byte half-stage rows: k-step s reads chunk
+      // 2 (s & 1) + l / 32 of its half
+      uint32_t fbh[2];
+      if constexpr (G == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fbh[j] = (ln & 31) * 64 + (((2 * j + (ln >> 5)) ^ key4(ln & 31)) * 16);
+      }
       uint2 wraw[NB];
       float sc_cur[NB], sc_nxt[NB];
       if constexpr (W8) {
@@ -419,6 +470,8 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
         else if (r <= NB) {
           if constexpr (W8)
             wraw[r - 1] = *reinterpret_cast<const uint2*>(lds + fbw[s] + (boff + b_row(LAY, r - 1) * kWRowB));
+          else if constexpr (G == 2)
+            fw[r - 1] = *reinterpret_cast<const uint4*>(lds + fbh[s & 1] + (boff + b_row(LAY, r - 1) * kWRowB));
           else
             fw[r - 1] = *reinterpret_cast<const uint4*>(lds + fb[s] + (boff + b_row(LAY, r - 1) * kRowB));
         }
@@ -440,14 +493,30 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
           constexpr int m = i / NB, n = i % NB;
           if constexpr (m < ACT) {
             f32x16_t& c = LAY ? acc[m / 2][(m & 1) + 2 * n] : acc[m][n];
-            c = mma_bf16(cb[n], ca[m], c);
-            // (an ordered use of the result: instruction selection otherwise may sink the MFMA,
-            // which reads no memory, past the slot's scheduling fence)
-            __asm__ volatile("" : "+a"(c));
+            if constexpr (G == 2 && m == 4) {
+              // (the 320 x 256 tile's fifth row block: accumulators in VGPRs)
+              __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                               : "+v"(c)
+                               : "v"(__builtin_bit_cast(u32x4_t, cb[n])), "v"(__builtin_bit_cast(u32x4_t, ca[m])));
+            } else {
+              c = mma_bf16(cb[n], ca[m], c);
+              // (an ordered use of the result: instruction selection otherwise may sink the
+              // MFMA, which reads no memory, past the slot's scheduling fence)
+              __asm__ volatile("" : "+a"(c));
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
-          constexpr int rd = (LAY || G == 1) ? i : ((i & 1) == 0 ? i / 2 : kReads);
-          if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
+          if constexpr (G == 2) {
+            // (one buffer of activation fragments: a[m] of the next k-step is read after this
+            // k-step's last MFMA on a[m], slot 4 m + 3; the weight fragments, which every row
+            // block uses, are read into the other buffer at slots 0 .. NB - 1)
+            if constexpr (READ && i < NB) read_frag(1 + i, aoff, boff, s, na, nb);
+            if constexpr (READ && (i & 3) == 3 && (i >> 2) < ACT)
+              read_frag((i >> 2) == 0 ? 0 : NB + (i >> 2), aoff, boff, s, na, nb);
+          } else {
+            constexpr int rd = (LAY || G == 1) ? i : ((i & 1) == 0 ? i / 2 : kReads);
+            if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
+          }
           // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n, converted at 9 + 2 n
           if constexpr (W8 && READ && ACT > 0 && i >= 9 && (i & 1) == 1)
             nb[(i - 9) / 2] = e4m3x8_scaled_to_bf16x8(wraw[(i - 9) / 2], scn[(i - 9) / 2]);
@@ -456,6 +525,13 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
         });
       };
       auto nothing = [](auto) __attribute__((always_inline)) {};
+      // the next tile's index, taken during k-step 0 of the second-to-last stage: that stage's
+      // wait for all loads (before its k-step 3) then also covers the take, so its result is
+      // never pending past the stage (a pending result makes the compiler add waits for memory
+      // inside later K loops), and three k-steps of MFMAs hide its latency
+      auto take_next = [&]() __attribute__((always_inline)) {
+        if (dynamic && tid == 0) grabbed = atomicAdd(counter + xcd, 1);
+      };
 
 #pragma unroll
       for (int r = 0; r < kReads; ++r) read_frag(r, 0, kWBase, 0, f0a, f0b);
@@ -476,6 +552,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
           constexpr int i = decltype(ic)::value;
           constexpr int jw = G == 0 ? ((i & 3) == 1 ? (i >> 2) : kLdW) : ((i & 1) == 1 ? (i >> 1) : kLdW);
           if constexpr (WN && jw < kLdW) load_w.template operator()<jw>(t, ks + kWS - 1, wsl);
+          if constexpr (!FULL && NEXT && i == 0) take_next();
         });
         mfma_step.template operator()<true>(f1a, f1b, f0a, f0b, aoff, boff, 2, sc_cur, [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
@@ -500,23 +577,76 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
           constexpr int i = decltype(ic)::value;
           constexpr int ja = G == 0 ? ((i & 1) == 1 ? (i >> 1) : kLdA) : i;   // activation load of slot i
           if constexpr (FULL && ja < kLdA) load_a.template operator()<ja>(t, ks + 2, buf);
-          // second-to-last stage (its wait for loads is behind it): take the next tile
-          if constexpr (!FULL && NEXT && i == 0)
-            if (dynamic && tid == 0) grabbed = atomicAdd(counter + xcd, 1);
         });
         if constexpr (W8 && NEXT && ACT > 0) {
 #pragma unroll
           for (int n = 0; n < NB; ++n) sc_cur[n] = sc_nxt[n];
         }
       };
+      // (G = 2) stage ks: activation rows in buffer PAR, weight halves 2 ks and 2 ks + 1 in ring
+      // slots wh = 2 ks mod 5 and the next.  After the barrier that ends k-step 2 every wave is
+      // past both halves, and k-step 3 loads, in this order, half 2 ks + 5 into slot wh
+      // (FULL: stage ks + 2 exists), the activation rows of stage ks + 2 into buffer PAR (FULL)
+      // and half 2 ks + 6 into the next slot (W6: stage ks + 3 exists).  The barrier's wait
+      // leaves only the most recent half in flight (FULL: it exists).
+      auto stage2 = [&]<bool FULL, bool NEXT, int PAR, bool W6>(int ks, int wh) __attribute__((always_inline)) {
+        constexpr int buf = PAR, nbuf = PAR ^ 1;
+        const int h1 = wh == kWS - 1 ? 0 : wh + 1;   // slot of half 2 ks + 1
+        const int h2 = h1 == kWS - 1 ? 0 : h1 + 1;   // slot of half 2 ks + 2 (the next stage's first)
+        const int aoff = buf * kPartA;
+        const int b0 = kWBase + wh * kWPart, b1 = kWBase + h1 * kWPart;
+        mfma_step.template operator()<true>(f0a, f0b, f0a, f1b, aoff, b0, 1, sc_cur, [&](auto ic) __attribute__((always_inline)) {
+          if constexpr (!FULL && NEXT && decltype(ic)::value == 0) take_next();
+        });
+        mfma_step.template operator()<true>(f0a, f1b, f0a, f0b, aoff, b1, 2, sc_cur, nothing);
+        mfma_step.template operator()<true>(f0a, f0b, f0a, f1b, aoff, b1, 3, sc_cur, nothing);
+        if constexpr (NEXT) {
+          wait_lgkmcnt_all();
+          if constexpr (FULL) wait_vmcnt<kLdW>();
+          else wait_vmcnt<0>();
+          block_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step.template operator()<NEXT>(f0a, f1b, f0a, f0b, nbuf * kPartA, kWBase + h2 * kWPart, 0, sc_nxt,
+                                            [&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int jw5 = i < kLdW ? i : kLdW;
+          constexpr int ja = i >= kLdW && i - kLdW < kLdA ? i - kLdW : kLdA;
+          constexpr int jw6 = i >= kLdW + kLdA && i - kLdW - kLdA < kLdW ? i - kLdW - kLdA : kLdW;
+          if constexpr (FULL && jw5 < kLdW) load_w.template operator()<jw5>(t, 2 * ks + 5, wh);
+          if constexpr (FULL && ja < kLdA) load_a.template operator()<ja>(t, ks + 2, buf);
+          if constexpr (W6 && jw6 < kLdW) load_w.template operator()<jw6>(t, 2 * ks + 6, h1);
+        });
+      };
+      static_assert(G != 2 || kSlots >= 2 * kLdW + kLdA, "k-step 3 has a slot for each load");
       // stages in pairs (nk is even): with weight loads, then (five-slot ring) the pair whose
       // weight stages lie past the end, then the last two
-      constexpr int kAhead = kWS - 3;   // stages the weight ring runs ahead of the activations
+      constexpr int kAhead = G == 2 ? 0 : kWS - 3;   // stages the weight ring runs ahead of the activations
       // (nk through volatile assembly: the loop guards are then compared per tile, in scalar
       // registers; hoisted out of the tile loop they were kept in a spilled register whose
       // reload waited on every load of the tile's first stages)
       int nkt;
       __asm__ volatile("s_mov_b32 %0, %1" : "=s"(nkt) : "s"(nk));
+      if constexpr (G == 2) {
+        int ks = 0, wh = 0;
+        auto adv2 = [&]() __attribute__((always_inline)) { wh = wh >= kWS - 2 ? wh - (kWS - 2) : wh + 2; };
+        for (; ks < nkt - 4; ks += 2) {
+          stage2.template operator()<true, true, 0, true>(ks, wh);
+          adv2();
+          stage2.template operator()<true, true, 1, true>(ks + 1, wh);
+          adv2();
+        }
+        if (ks < nkt - 2) {   // stages nk - 4 and nk - 3: the second has no half 2 ks + 6
+          stage2.template operator()<true, true, 0, true>(ks, wh);
+          adv2();
+          stage2.template operator()<true, true, 1, false>(ks + 1, wh);
+          adv2();
+        }
+        stage2.template operator()<false, true, 0, false>(nkt - 2, wh);
+        adv2();
+        stage2.template operator()<false, false, 1, false>(nkt - 1, wh);
+        return;
+      }
       int ks = 0, ws = 0;
       auto adv = [&]() __attribute__((always_inline)) { ws = ws == kWS - 1 ? 0 : ws + 1; };
       for (; ks < nkt - 2 - kAhead; ks += 2) {
@@ -538,11 +668,16 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       adv();
       stage.template operator()<false, false, 1, false>(nkt - 1, ws);
     };
-    if constexpr (G == 1) {
+    if constexpr (G != 0) {
       // (the listed experts have 9 or 10 row blocks: 4 or 5 per wave; a wave with fewer
       // would compute rows past the tile, which the epilogue does not store)
       if (act >= 5) k_loop(std::integral_constant<int, 5>{}, std::integral_constant<int, 0>{});
       else k_loop(std::integral_constant<int, 4>{}, std::integral_constant<int, 0>{});
+      if constexpr (G == 2) {
+        // results of the inline-assembly MFMAs (8 passes) are read by VALU instructions next:
+        // 11 wait states are required, 16 are given
+        __asm__ volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[4][0]), "+v"(acc[4][1]), "+v"(acc[4][2]), "+v"(acc[4][3]));
+      }
     } else if (kLay1 && lay1) {
       [&]<int... A>(std::integer_sequence<int, A...>) {
         ((act == 2 * A + 1 ? k_loop(std::integral_constant<int, 2 * A + 1>{}, std::integral_constant<int, 1>{})
@@ -563,6 +698,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       wait_lgkmcnt_all();
       block_barrier();
       vn = __builtin_amdgcn_readfirstlane(*tile_word);
+      if constexpr (G == 2) block_barrier();   // (its prologue writes the slot that holds the word)
     }
     const bool more = vn < v_end;
     const int Ln = more ? tile_of(vn) : 0;
@@ -712,6 +848,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   if constexpr (MODE == MODE_DOWN && !W8) {
     if (p.tall_list != nullptr) run_tiles<MODE, W8, 1>(p, lds);
   }
+  if constexpr (MODE == MODE_GATE_UP) {
+    if (p.tall_list != nullptr) run_tiles<MODE, W8, 2>(p, lds);
+  }
   run_tiles<MODE, W8, 0>(p, lds);
 }
 
@@ -720,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s, bool w8) {
   const dim3 grid(256), block(kThreads);   // persistent: one workgroup per CU, a multiple of the 8 XCDs
   if (w8 && mode != MODE_DOWN) return hipErrorNotSupported;
-  if ((w8 || mode != MODE_DOWN) && p.tall_list != nullptr) return hipErrorNotSupported;
+  if ((w8 || mode == MODE_ROUTER) && p.tall_list != nullptr) return hipErrorNotSupported;
   if (mode == MODE_GATE_UP)
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_GATE_UP, false>), grid, block, 0, s, p);
   else if (mode == MODE_DOWN && w8)

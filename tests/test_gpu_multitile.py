@@ -3,9 +3,9 @@ full with the oracle.
 
 The bf16 expert GEMMs run one workgroup per CU (256) and hand tiles out from a counter per
 XCD, so a workgroup that finishes a tile takes the next index while its last stages run and
-loads that tile's first stages while its epilogue stores drain.  Experts of 257..320 rows run
-first, as one tile of 320 rows x 128 weight rows each (their own counters), then the rest on
-256 x 256 tiles.  The small layer tests give few workgroups a second tile; here the routed
+issues that tile's set-up and first loads ahead of its epilogue stores.  Experts of 257..320
+rows run first, each as one tile of 320 rows (their own counters; 320 x 256 weight rows in the
+gate/up, 320 x 128 in the down), then the rest on 256 x 256 tiles.  The small layer tests give few workgroups a second tile; here the routed
 segments and the shared segment make about four gate/up tiles and four down tiles per
 workgroup, and the "tall" case more than three 320-row tiles per workgroup in each GEMM.  Every output row of every launch is
 compared with the oracle's expert FFN on the same rows, and every output buffer starts as
@@ -36,21 +36,23 @@ CASES = {
     "ragged": [420, 1260, 0, 717, 257, 896, 1078, 466, 1246, 256, 672, 840, 980, 532, 1148, 564],
     # one expert takes every token, the others are small or empty
     "hot": [2900, 33, 0, 300, 1, 700, 512, 31, 2900, 640, 260, 0, 900, 1333, 1050, 40],
-    # 26 experts of 257..320 rows (both ends, and 288 / 289 around the ninth 32-row block)
+    # 48 experts of 257..320 rows (both ends, and 288 / 289 around the ninth 32-row block)
     # beside 256, 321, empty, one-row and split ones
     "tall": [257, 320, 288, 289, 300, 260, 319, 270, 301, 311, 258, 280, 295, 317, 263, 299, 305,
-             266, 284, 292, 313, 274, 308, 320, 256, 321, 0, 1, 640, 36, 287, 290],
+             266, 284, 292, 313, 274, 308, 320, 256, 321, 0, 1, 640, 36, 287, 290,
+             262, 318, 291, 297, 303, 265, 276, 309, 314, 259, 282, 296, 316, 268, 271, 286,
+             293, 306, 312, 277, 285, 302],
 }
 TALL_ROWS = 320     # a routed expert of TILE_ROWS < n_e <= TALL_ROWS rows: one 320-row tile
 
 
-def _tiles(seg_rows, cols_per_tile, n_cols, n_routed):
+def _tiles(seg_rows, cols_per_tile, tall_cols_per_tile, n_cols, n_routed):
     """(256-row tiles, 320-row tiles) of the schedule: the routed experts of 257..320 rows take
-    one 320-row tile per n-block of half the columns."""
+    one 320-row tile per n-block of tall_cols_per_tile columns."""
     n_blk = -(-n_cols // cols_per_tile)
     tall = [i < n_routed and TILE_ROWS < r <= TALL_ROWS for i, r in enumerate(seg_rows)]
     wide = sum(-(-r // TILE_ROWS) for r, t in zip(seg_rows, tall) if not t) * n_blk
-    return wide, sum(tall) * -(-n_cols // (cols_per_tile // 2))
+    return wide, sum(tall) * -(-n_cols // tall_cols_per_tile)
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -61,8 +63,8 @@ def test_multitile_gate_up_down_every_row(case):
     N = idx.shape[0]
     rows = N * K
     segs = [c for c in n_e] + [N]
-    gu_tiles = _tiles(segs, 128, I, E)   # gate/up: 128 h columns (256 weight rows) per tile
-    dn_tiles = _tiles(segs, 256, H, E)   # down: 256 output columns per tile
+    gu_tiles = _tiles(segs, 128, 128, I, E)   # gate/up: 128 h columns (256 weight rows) per tile
+    dn_tiles = _tiles(segs, 256, 128, H, E)   # down: 256 output columns per tile, 128 per 320-row one
     say(f"multitile {case}: N={N} rows={rows} E={E} H={H} I={I}; gate/up tiles (256, 320 rows) {gu_tiles}, "
         f"down tiles {dn_tiles}")
     if case == "tall":
@@ -131,7 +133,7 @@ def test_multitile_down_e4m3_every_row(case):
     once), so the bar is the bf16 GEMM's."""
     n_e = CASES[case]
     E, rows = len(n_e), sum(n_e)
-    dn_tiles = _tiles(n_e, 256, H, 0)   # (e4m3 weights: every expert on 256 x 256 tiles)
+    dn_tiles = _tiles(n_e, 256, 128, H, 0)   # (e4m3 weights: every expert on 256 x 256 tiles)
     say(f"multitile e4m3 down {case}: rows={rows} E={E} H={H} K={I}; tiles {dn_tiles[0]}")
     assert dn_tiles[0] >= 3 * WORKGROUPS
     h = w.normal((rows, I), w.stream_key(23, w.T_EO, E), DEV, torch.bfloat16, std=1.0)
