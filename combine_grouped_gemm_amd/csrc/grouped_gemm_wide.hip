@@ -145,7 +145,10 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // the 1 x 4 layout for 256 x 256 gate/up tiles only: the down GEMM's epilogue would need the
   // gates of twice the rows per lane, and the extra registers cost its K loop more than the
   // layout saves
-  constexpr bool kLay1 = MODE == MODE_GATE_UP && G == 0;
+  constexpr bool kLay1 = MODE == MODE_GATE_UP && G != 1;
+  // row blocks a wave holds in the 1 x 4 layout: 5 (256 x 256 tiles), 10 (320 x 256 tiles,
+  // which always run 1 x 4: a 9-block expert then costs 18 MFMAs per k-step and wave, not 20)
+  constexpr int kMBL = G == 2 ? 2 * kMB : kMB1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
@@ -422,14 +425,14 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     }
 
     const int nblk = (t.mlast + 32) / 32;   // 32-row blocks that hold rows
-    const bool lay1 = kLay1 && (nblk & 1) != 0 && nblk <= kMB1;
+    const bool lay1 = G == 2 || (kLay1 && (nblk & 1) != 0 && nblk <= kMB1);
     int act = lay1 ? nblk : (nblk - wm + 1) / 2;   // row blocks of this wave that hold rows
     act = lay1 ? act : (act < 0 ? 0 : (act > kMB ? kMB : act));
 
     auto k_loop = [&](auto act_c, auto lay_c) __attribute__((always_inline)) {
       constexpr int ACT = decltype(act_c)::value;
       constexpr int LAY = decltype(lay_c)::value;      // 1: the 1 x 4 layout
-      constexpr int MB = LAY ? kMB1 : kMB, NB = LAY ? kNB1 : kNB;
+      constexpr int MB = LAY ? kMBL : kMB, NB = LAY ? kNB1 : kNB;
       constexpr int kReads = ACT > 0 ? ACT + NB : 0;   // fragment reads per k-step
       constexpr int kSlots = kMB * kNB;                // MFMA slots of a k-step
       uint4 f0a[MB], f0b[NB], f1a[MB], f1b[NB];
@@ -493,7 +496,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
           constexpr int m = i / NB, n = i % NB;
           if constexpr (m < ACT) {
             f32x16_t& c = LAY ? acc[m / 2][(m & 1) + 2 * n] : acc[m][n];
-            if constexpr (G == 2 && m == 4) {
+            if constexpr (G == 2 && (LAY ? m / 2 : m) == 4) {
               // (the 320 x 256 tile's fifth row block: accumulators in VGPRs)
               __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                                : "+v"(c)
@@ -508,11 +511,11 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (G == 2) {
             // (one buffer of activation fragments: a[m] of the next k-step is read after this
-            // k-step's last MFMA on a[m], slot 4 m + 3; the weight fragments, which every row
-            // block uses, are read into the other buffer at slots 0 .. NB - 1)
+            // k-step's last MFMA on a[m], slot NB m + NB - 1; the weight fragments, which every
+            // row block uses, are read into the other buffer at slots 0 .. NB - 1)
             if constexpr (READ && i < NB) read_frag(1 + i, aoff, boff, s, na, nb);
-            if constexpr (READ && (i & 3) == 3 && (i >> 2) < ACT)
-              read_frag((i >> 2) == 0 ? 0 : NB + (i >> 2), aoff, boff, s, na, nb);
+            if constexpr (READ && i % NB == NB - 1 && i / NB < ACT)
+              read_frag(i / NB == 0 ? 0 : NB + i / NB, aoff, boff, s, na, nb);
           } else {
             constexpr int rd = (LAY || G == 1) ? i : ((i & 1) == 0 ? i / 2 : kReads);
             if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
@@ -668,16 +671,18 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       adv();
       stage.template operator()<false, false, 1, false>(nkt - 1, ws);
     };
-    if constexpr (G != 0) {
+    if constexpr (G == 2) {
+      // (the listed experts have 9 or 10 row blocks, every wave all of them)
+      if (act >= 10) k_loop(std::integral_constant<int, 10>{}, std::integral_constant<int, 1>{});
+      else k_loop(std::integral_constant<int, 9>{}, std::integral_constant<int, 1>{});
+      // results of the inline-assembly MFMAs (8 passes) are read by VALU instructions next:
+      // 11 wait states are required, 16 are given
+      __asm__ volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[4][0]), "+v"(acc[4][1]), "+v"(acc[4][2]), "+v"(acc[4][3]));
+    } else if constexpr (G == 1) {
       // (the listed experts have 9 or 10 row blocks: 4 or 5 per wave; a wave with fewer
       // would compute rows past the tile, which the epilogue does not store)
       if (act >= 5) k_loop(std::integral_constant<int, 5>{}, std::integral_constant<int, 0>{});
       else k_loop(std::integral_constant<int, 4>{}, std::integral_constant<int, 0>{});
-      if constexpr (G == 2) {
-        // results of the inline-assembly MFMAs (8 passes) are read by VALU instructions next:
-        // 11 wait states are required, 16 are given
-        __asm__ volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[4][0]), "+v"(acc[4][1]), "+v"(acc[4][2]), "+v"(acc[4][3]));
-      }
     } else if (kLay1 && lay1) {
       [&]<int... A>(std::integer_sequence<int, A...>) {
         ((act == 2 * A + 1 ? k_loop(std::integral_constant<int, 2 * A + 1>{}, std::integral_constant<int, 1>{})
