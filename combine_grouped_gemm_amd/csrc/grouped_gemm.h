@@ -25,8 +25,9 @@ struct GemmArgs {
   int E, K, rows, I, n_out, tile_cap;
   long long b_rows;
   int out_f32;
-  int32_t* tile_counter;       // [kNumXcd] next tile of each XCD's range (zeroed by the schedule
-                               // prologue), or null: tiles dealt round-robin
+  int32_t* tile_counter;       // [kNumXcd + 1] next tile of each XCD's range, then the next tile
+                               // of the shared tail (zeroed by the schedule prologue), or null:
+                               // tiles dealt round-robin
   const uint8_t* shared_b;     // shared expert's weights [b_rows, K] (segment E), or null
   int shared_rows;             // rows of the shared segment [rows, rows + shared_rows); 0: none
   const int32_t* row_slot;     // down: routed output row r is scaled by row_gate[row_slot[r]]

@@ -74,13 +74,14 @@ __device__ int32_t block_scan_1024(int32_t x, int32_t* tot) {
 // shared expert) follows, and prefix has E + 2 entries.  With tall_list, the routed experts
 // of tile_rows < n_e <= tall_rows get no m-tiles and are listed instead (tall_list[0] = their
 // count, then the experts in order), and tall_list[E + 1 ..] holds kNumXcd zeroed counters.
+// tile_counter: n_counters zeroed counters (one per XCD, and the wide kernel's shared tail).
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int rows, int tile_rows, int tile_cap,
                                                            int32_t* __restrict__ prefix,
                                                            int32_t* __restrict__ tile_expert,
                                                            int32_t* __restrict__ tile_counter,
                                                            int shared_rows, int tall_rows,
-                                                           int32_t* __restrict__ tall_list) {
+                                                           int32_t* __restrict__ tall_list, int n_counters) {
   __shared__ int32_t tot[1024];
   const int e = threadIdx.x;
   const int n_seg = E + (shared_rows > 0 ? 1 : 0);
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     for (int i = 0; i < mt && start + i < tile_cap; ++i) tile_expert[start + i] = e;
   }
   if (e == n_seg - 1) prefix[n_seg] = end < tile_cap ? end : tile_cap;
-  if (e < kNumXcd) tile_counter[e] = 0;
+  if (e < n_counters) tile_counter[e] = 0;
   if (tall_list != nullptr) {
     const int32_t tend = block_scan_1024(tall, tot);
     if (tall) tall_list[tend] = e;
@@ -752,14 +753,14 @@ bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int rows, int tile_rows, int cap, int32_t* prefix,
                               int32_t* tile_expert, int32_t* tile_counter, hipStream_t s) {
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap, prefix,
-                     tile_expert, tile_counter, 0, 0, nullptr);
+                     tile_expert, tile_counter, 0, 0, nullptr, kNumXcd);
   return hipGetLastError();
 }
 
-// prefix [E + 1], tile_expert [cap], counters [8], list of 320-row experts [E + 1] and its
-// counters [8]
+// prefix [E + 1], tile_expert [cap], counters [8 + 1: one per XCD and the shared tail], list
+// of 320-row experts [E + 1] and its counters [8]
 size_t gemm_schedule_bytes(int rows, int E) {
-  const size_t n = 2 * (static_cast<size_t>(E) + 1 + kNumXcd) + gemm_tile_cap(rows, E);
+  const size_t n = 2 * (static_cast<size_t>(E) + 1 + kNumXcd) + 1 + gemm_tile_cap(rows, E);
   return (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 
@@ -785,7 +786,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   int32_t* tile_expert = prefix + n_seg + 1;
   const int cap = static_cast<int>(gemm_tile_cap(rows + shared_rows, n_seg));
   int32_t* tile_counter = tile_expert + cap;
-  int32_t* tall_list = tile_counter + kNumXcd;   // [E + 1] + [kNumXcd] counters
+  int32_t* tall_list = tile_counter + kNumXcd + 1;   // [E + 1] + [kNumXcd] counters
   // few rows per expert and e4m3 weights: the weight-streaming kernel (16-row m-tiles)
   const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) &&
                       static_cast<long long>(rows) <= static_cast<long long>(kStreamTileRows) * E &&
@@ -817,7 +818,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   const bool tall = wide;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert, tile_counter, shared_rows, kWideTallRows,
-                     tall ? tall_list : nullptr);
+                     tall ? tall_list : nullptr, kNumXcd + 1);
   GemmArgs p;
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.a_scale = a_scale;

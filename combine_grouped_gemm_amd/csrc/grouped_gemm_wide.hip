@@ -184,6 +184,11 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   auto tile_of = [&](int v) __attribute__((always_inline)) {
     return v < r_cnt ? r_beg + v : n_r + s_beg + (v - r_cnt);
   };
+  // tile v of XCD x's range
+  auto tile_of_x = [&](int x, int v) __attribute__((always_inline)) {
+    const int rb0 = n_r * x / kNumXcd, rc0 = n_r * (x + 1) / kNumXcd - rb0;
+    return v < rc0 ? rb0 + v : n_r + n_s * x / kNumXcd + (v - rc0);
+  };
   const int kspan = MODE == MODE_ROUTER ? p.K / p.k_split : p.K;   // K of one tile
   const int nk = kspan / 64;                                // even: kspan % 128 == 0
   const uint32_t rb = static_cast<uint32_t>(p.K) * 2;       // row bytes of the activations
@@ -212,15 +217,45 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // between a boundary and the first stage).
   int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + Geo<0, W8>::LdsTot - 4);
   const bool dynamic = counter != nullptr;
+  // The end of a launch: every XCD's range takes about the same time, but not exactly, and a
+  // workgroup whose range runs out would wait for the slowest XCD.  The last kTailT tiles of
+  // every range (G = 0, the launch's last tiles) form a tail shared by all XCDs: a workgroup
+  // takes its own range's tiles from its XCD's counter and then tail tiles from one shared
+  // counter, which deals them XCD by XCD in turn.  kTailT: one tile per workgroup of an XCD,
+  // two when K < 4096 (shorter tiles); none when a range is shorter than that.
+  int32_t* const tail_ctr = p.tile_counter + kNumXcd;
+  const int tail_per = G == 0 && MODE != MODE_ROUTER && dynamic ? per_xcd * (p.K < 4096 ? 2 : 1) : 0;
+  const int kTailT = n_r / kNumXcd + n_s / kNumXcd >= tail_per ? tail_per : 0;
+  constexpr int32_t kTailBit = 1 << 30, kTileMask = kTailBit - 1;   // (tile numbers < 2^28)
+  // (lane 0 of wave 0) the tile word for a counter value g taken from the tail counter (tail) or
+  // this XCD's: the tile's number, with kTailBit for a tail tile, or -1 when none is left
+  auto resolve = [&](int g, bool tail) __attribute__((always_inline)) -> int32_t {
+    if (!tail && g >= v_end - kTailT) {   // (this XCD's own tiles are all taken)
+      if (kTailT == 0) return -1;
+      tail = true;
+      g = atomicAdd(tail_ctr, 1);
+    }
+    if (!tail) return tile_of(g);
+    if (g >= kNumXcd * kTailT) return -1;
+    const int x = g % kNumXcd;   // tail tile g / kNumXcd of XCD x's range
+    const int v_end_x = (n_r * (x + 1) / kNumXcd - n_r * x / kNumXcd) + (n_s * (x + 1) / kNumXcd - n_s * x / kNumXcd);
+    return kTailBit | tile_of_x(x, v_end_x - kTailT + g / kNumXcd);
+  };
   int v = slot;
+  int L = 0, tail_mode = 0;   // (the current tile is a tail tile: the next take is the tail's)
   if (dynamic) {
     __syncthreads();   // (after a previous shape's tiles: every wave has read the word)
-    if (tid == 0) *tile_word = atomicAdd(counter + xcd, 1);
+    if (tid == 0) *tile_word = resolve(atomicAdd(counter + xcd, 1), false);
     __syncthreads();
-    v = __builtin_amdgcn_readfirstlane(*tile_word);
+    const int32_t word = __builtin_amdgcn_readfirstlane(*tile_word);
     if constexpr (G == 2) block_barrier();   // (its prologue writes the slot that holds the word)
+    if (word < 0) return;
+    L = word & kTileMask;
+    tail_mode = word >> 30;
+  } else {
+    if (v >= v_end) return;
+    L = tile_of(v);
   }
-  if (v >= v_end) return;
 
   struct Tile {
     int m0, mend, mlast, c0, kp;   // (kp: the router's column part)
@@ -402,7 +437,6 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   };
 
   Tile cur;
-  int L = tile_of(v);
   setup(L, cur);
   prologue_loads(cur);
   prologue_wait.template operator()<0>();
@@ -533,7 +567,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       // never pending past the stage (a pending result makes the compiler add waits for memory
       // inside later K loops), and three k-steps of MFMAs hide its latency
       auto take_next = [&]() __attribute__((always_inline)) {
-        if (dynamic && tid == 0) grabbed = atomicAdd(counter + xcd, 1);
+        if (dynamic && tid == 0) grabbed = atomicAdd(tail_mode ? tail_ctr : counter + xcd, 1);
       };
 
 #pragma unroll
@@ -697,16 +731,22 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
 
     // ---- tile boundary: every wave is past its last LDS reads; the next tile is known
     block_barrier();
-    int vn = v + per_xcd;
+    const int vn = v + per_xcd;
+    bool more;
+    int Ln, tail_next = 0;
     if (dynamic) {
-      if (tid == 0) *tile_word = grabbed;
+      if (tid == 0) *tile_word = resolve(grabbed, tail_mode != 0);
       wait_lgkmcnt_all();
       block_barrier();
-      vn = __builtin_amdgcn_readfirstlane(*tile_word);
+      const int32_t word = __builtin_amdgcn_readfirstlane(*tile_word);
       if constexpr (G == 2) block_barrier();   // (its prologue writes the slot that holds the word)
+      more = word >= 0;
+      Ln = word & kTileMask;
+      tail_next = word >> 30;
+    } else {
+      more = vn < v_end;
+      Ln = more ? tile_of(vn) : 0;
     }
-    const bool more = vn < v_end;
-    const int Ln = more ? tile_of(vn) : 0;
     // the finished tile's rows and columns (cur is rewritten by the next tile's set-up)
     const int em0 = t.m0, emend = t.mend, ec0 = t.c0, ekp = t.kp;
 
@@ -838,6 +878,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     }
     v = vn;
     L = Ln;
+    tail_mode = tail_next;
   }
 }
 
