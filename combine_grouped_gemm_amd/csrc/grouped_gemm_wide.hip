@@ -882,12 +882,10 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   }
 }
 
-// bf16 (or W8) grouped GEMM: for the bf16 down GEMM, the experts listed for 320 x 128 tiles
-// first (when the schedule lists any), then the 256 x 256 tiles.  A workgroup that runs out of
-// the first shape's tiles moves on to the second's without waiting for the others.  (The
-// gate/up GEMM keeps 256 x 256 tiles: there a 320-row tile re-reads the expert's gathered
-// token rows from twice as many n-blocks, and that costs more than streaming the weight
-// panel once saves.)
+// bf16 (or W8) grouped GEMM: the experts the schedule lists for 320-row tiles first (bf16 only:
+// one 320 x 256 gate/up tile or 320 x 128 down tile per expert and n-block), then the 256 x 256
+// tiles.  A workgroup that runs out of the first shape's tiles moves on to the second's without
+// waiting for the others.
 template <int MODE, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[Geo<0, W8>::LdsTot];
