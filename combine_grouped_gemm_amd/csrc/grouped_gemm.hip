@@ -774,6 +774,24 @@ static int persistent_grid() {
   return 256;
 }
 
+// bf16 copy of e4m3 rows [rows, K] with fp32 scales [rows, K / 128]: each value is its code times
+// the scale of its 128-column block, rounded to the nearest bf16 (even on ties).  One 16-byte
+// store per 8 codes; n8 = rows * K / 8 < 2^31.
+__global__ __launch_bounds__(256) void dequant_e4m3_kernel(const uint2* __restrict__ q,
+                                                           const float* __restrict__ scale, int n8, int K,
+                                                           uint4* __restrict__ out) {
+  const int g8 = K / 8, nblk = K / 128;
+  for (int i = blockIdx.x * 256 + static_cast<int>(threadIdx.x); i < n8; i += gridDim.x * 256) {
+    const int r = i / g8, c = i - r * g8;
+    out[i] = e4m3x8_scaled_to_bf16x8(q[i], scale[static_cast<size_t>(r) * nblk + c / 16]);
+  }
+}
+
+// bytes of the dequantized activations the fp8 gate/up keeps after its tile schedule
+size_t gemm_a8_bytes(int rows, int K) {
+  return (static_cast<size_t>(rows) * K * 2 + 255) & ~static_cast<size_t>(255);
+}
+
 hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,
                                const void* b, const float* b_scale, void* out, bool out_f32,
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,
@@ -794,6 +812,22 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                       static_cast<long long>(gemm_tile_cap(rows, E)) * (mode == MODE_GATE_UP ? I / 64 : n_out / 128) <
                           (1LL << 31);
   const bool dma = ct == CT_BF16 && !b8;   // bf16 operands: the direct-to-LDS kernels
+  // fp8 gate/up above decode sizes: the activations are dequantized to bf16 (into the workspace,
+  // after the schedule) and multiplied against the e4m3 weights on the 256 x 256 kernel, which
+  // loads the weights' codes and block scales straight to LDS and converts each fragment as it
+  // reads it
+  if (mode == MODE_GATE_UP && ct == CT_FP8 && !b8 && !stream && a_rows == nullptr && shared_rows == 0 &&
+      au == nullptr && K % 128 == 0 && I % 8 == 0 && wide_out_fits(mode, I, n_out) && b_rows * K < (1LL << 32) &&
+      static_cast<long long>(kWideTileRows) * 2 * K < (1LL << 32) &&
+      static_cast<long long>(rows) * K / 8 < (1LL << 31) && wide_tiles_fit(mode, rows, E, I, n_out)) {
+    void* deq = static_cast<uint8_t*>(sched) + gemm_schedule_bytes(rows, E);
+    const int n8 = static_cast<int>(static_cast<long long>(rows) * K / 8);
+    const int blocks = (n8 + 255) / 256 < 16384 ? (n8 + 255) / 256 : 16384;
+    hipLaunchKernelGGL(dequant_e4m3_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint2*>(a),
+                       a_scale, n8, K, reinterpret_cast<uint4*>(deq));
+    return launch_grouped_gemm(CT_BF16, true, mode, deq, nullptr, b, b_scale, out, out_f32, offsets, E, rows, K,
+                               I, n_out, b_rows, sched, s);
+  }
   // 256 x 256 tiles while every operand offset fits the kernel's 32-bit arithmetic
   const long long rbytes = 2LL * K;
   const bool wide_ok = dma && K % 128 == 0 && (mode == MODE_GATE_UP ? I : n_out) % 8 == 0 &&
@@ -805,9 +839,11 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
     return hipErrorNotSupported;   // (callers check first)
   const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr || au != nullptr ||
                                 mode == MODE_GATE_UP || E > 1);
-  // e4m3 down weights at more than 16 rows per expert: the 256 x 256 kernel, which converts
-  // each weight fragment (code times its block's scale) as it reads it from LDS
-  const bool wide8 = mode == MODE_DOWN && ct == CT_BF16 && b8 && !stream && K % 128 == 0 && n_out % 8 == 0 &&
+  // e4m3 weights (down; gate/up with its dequantized activations) at more than 16 rows per
+  // expert: the 256 x 256 kernel, which converts each weight fragment (code times its block's
+  // scale) as it reads it from LDS
+  const bool wide8 = (mode == MODE_DOWN || mode == MODE_GATE_UP) && ct == CT_BF16 && b8 && !stream && K % 128 == 0 &&
+                     n_out % 8 == 0 &&
                      wide_out_fits(mode, I, n_out) &&
                      b_rows * K < (1LL << 32) && b_rows * (K / 128) * 4 < (1LL << 32) &&
                      static_cast<long long>(kWideTileRows) * rbytes < (1LL << 32) && shared_rows == 0 &&

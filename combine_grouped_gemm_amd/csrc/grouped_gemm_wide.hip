@@ -145,7 +145,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // the 1 x 4 layout for 256 x 256 gate/up tiles only: the down GEMM's epilogue would need the
   // gates of twice the rows per lane, and the extra registers cost its K loop more than the
   // layout saves
-  constexpr bool kLay1 = MODE == MODE_GATE_UP && G != 1;
+  constexpr bool kLay1 = MODE == MODE_GATE_UP && G != 1 && !W8;   // (W8: the scales are read per 2 x 2 block)
   // row blocks a wave holds in the 1 x 4 layout: 5 (256 x 256 tiles), 10 (320 x 256 tiles,
   // which always run 1 x 4: a 9-block expert then costs 18 MFMAs per k-step and wave, not 20)
   constexpr int kMBL = G == 2 ? 2 * kMB : kMB1;
@@ -319,11 +319,19 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
     // last valid one
     t.a = p.a_rows ? p.a : p.a + static_cast<size_t>(t.m0) * rb;
     t.b = e < p.E ? p.b + static_cast<size_t>(e) * p.b_rows * rbw : p.shared_b;
+    // (W8) the weight row holding tile weight row r (gate/up: W_gate rows, then the same W_up
+    // rows; columns past the output re-read the last one)
+    auto w_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
+      if (MODE == MODE_GATE_UP) {
+        const int c = r % (kTN / 2);
+        return (r < kTN / 2 ? 0u : static_cast<uint32_t>(p.I)) + static_cast<uint32_t>(t.c0 + (c < clast ? c : clast));
+      }
+      return static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
+    };
     if constexpr (W8) {   // (no shared segment with W8: the launcher checks)
       t.sc = reinterpret_cast<const uint8_t*>(p.b_scale + static_cast<size_t>(e) * p.b_rows * kblk);
       // scale gather: wave w's lane l fetches the scale of tile weight row 64 w + l
-      const int r = wave * 64 + static_cast<int>(ln);
-      t.s_src = static_cast<uint32_t>(t.c0 + (r < clast ? r : clast)) * kblk * 4;
+      t.s_src = w_row(wave * 64 + static_cast<int>(ln)) * kblk * 4;
     }
     if (MODE == MODE_ROUTER) {
       t.a += static_cast<size_t>(kp) * kspan * 2;
@@ -358,8 +366,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
         // 64-byte rows: load j fills the 16-row group wave + 4 j; lane l fills LDS slot l % 4
         // of row l / 4 of the group, so it loads chunk (l % 4) ^ key4(row)
         const int r8 = (wave + 4 * j) * 16 + static_cast<int>(ln >> 2);
-        const uint32_t w8 = static_cast<uint32_t>(t.c0 + (r8 < clast ? r8 : clast));
-        t.b_src[j] = row_off(w8, rbw, static_cast<uint32_t>((ln & 3) ^ key4(r8)) * 16);
+        t.b_src[j] = row_off(w_row(r8), rbw, static_cast<uint32_t>((ln & 3) ^ key4(r8)) * 16);
       } else if constexpr (G == 2) {
         // half-stage rows of 64 bytes, laid out like the e4m3 rows; gate/up row mapping
         const int r8 = (wave + 4 * j) * 16 + static_cast<int>(ln >> 2);
@@ -892,7 +899,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
   if constexpr (MODE == MODE_DOWN && !W8) {
     if (p.tall_list != nullptr) run_tiles<MODE, W8, 1>(p, lds);
   }
-  if constexpr (MODE == MODE_GATE_UP) {
+  if constexpr (MODE == MODE_GATE_UP && !W8) {
     if (p.tall_list != nullptr) run_tiles<MODE, W8, 2>(p, lds);
   }
   run_tiles<MODE, W8, 0>(p, lds);
@@ -902,9 +909,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 
 hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s, bool w8) {
   const dim3 grid(256), block(kThreads);   // persistent: one workgroup per CU, a multiple of the 8 XCDs
-  if (w8 && mode != MODE_DOWN) return hipErrorNotSupported;
+  if (w8 && mode == MODE_ROUTER) return hipErrorNotSupported;
   if ((w8 || mode == MODE_ROUTER) && p.tall_list != nullptr) return hipErrorNotSupported;
-  if (mode == MODE_GATE_UP)
+  if (mode == MODE_GATE_UP && w8)
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_GATE_UP, true>), grid, block, 0, s, p);
+  else if (mode == MODE_GATE_UP)
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_GATE_UP, false>), grid, block, 0, s, p);
   else if (mode == MODE_DOWN && w8)
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_DOWN, true>), grid, block, 0, s, p);

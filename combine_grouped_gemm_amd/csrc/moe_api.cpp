@@ -72,10 +72,10 @@ size_t moe_workspace_bytes(int op, int N, int H, int I, int E, int k, int a_dt) 
       return layout_ws(N, k, E);
     case MOE_OP_EXPERT_GEMM:
       if (E < 1 || N == 0) return 0;
-      return moe::gemm_schedule_bytes(N, E);
+      return moe::gemm_schedule_bytes(N, E) + (a_dt == MOE_FP8_E4M3 && H > 0 ? moe::gemm_a8_bytes(N, H) : 0);
     case MOE_OP_GROUPED_FFN:
       if (E < 1 || N == 0 || I <= 0 || H <= 0) return 0;
-      return moe::gemm_schedule_bytes(N, E) + h_bytes(N, I, a_dt);
+      return moe_workspace_bytes(MOE_OP_EXPERT_GEMM, N, H, I, E, k, a_dt) + h_bytes(N, I, a_dt);
     case MOE_OP_EXPERT_DGRAD:
       if (E < 1 || N == 0) return 0;
       return moe::bwd_dgrad_ws_bytes(N, E);
@@ -194,6 +194,9 @@ moe_status moe_expert_gate_up(const void* a, const float* a_scale, moe_dtype a_d
   if (a == nullptr || w13 == nullptr || h == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w13)) return MOE_ERR_INVALID_ARG;
   if (a_dt == MOE_FP8_E4M3 && (a_scale == nullptr || w13_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  // (fp8: room for the bf16 copy of a after the schedule)
+  if (a_dt == MOE_FP8_E4M3 && ws_bytes < moe::gemm_schedule_bytes(rows, E) + moe::gemm_a8_bytes(rows, H))
+    return MOE_ERR_WORKSPACE;
   const int ct = a_dt == MOE_F32 ? 0 : (a_dt == MOE_BF16 ? 1 : 2);
   return hip_status(moe::launch_grouped_gemm(ct, false, 0, a, a_scale, w13, w13_scale, h,
                                              a_dt == MOE_F32, offsets, E, rows, H, I, I,
@@ -290,13 +293,16 @@ moe_status moe_grouped_ffn(const void* a, const float* a_scale, moe_dtype a_dt,
   const moe_status st = check_gemm(offsets, E, rows, H, I, ws, ws_bytes);
   if (st != MOE_OK) return st;
   if (rows == 0) return MOE_OK;
-  if (ws_bytes < moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt)) return MOE_ERR_WORKSPACE;
   if (a == nullptr || w13 == nullptr || w2 == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (a_dt == MOE_FP8_E4M3 && (a_scale == nullptr || w13_scale == nullptr || w2_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt)) return MOE_ERR_WORKSPACE;
   const size_t sched = moe::gemm_schedule_bytes(rows, E);
-  void* hbuf = static_cast<uint8_t*>(ws) + sched;
+  const size_t gu = moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, a_dt);   // (fp8: + bf16 a)
+  void* hbuf = static_cast<uint8_t*>(ws) + gu;
   const moe_dtype h_dt = a_dt == MOE_F32 ? MOE_F32 : MOE_BF16;
   moe_status s = moe_expert_gate_up(a, a_scale, a_dt, offsets, E, rows, H, I, w13, w13_scale, hbuf,
-                                    ws, sched, stream);
+                                    ws, gu, stream);
   if (s != MOE_OK) return s;
   return moe_expert_down(hbuf, h_dt, offsets, E, rows, I, H, w2, a_dt, w2_scale, out, out_dt, ws,
                          sched, stream);

@@ -59,6 +59,8 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int rows, int tile_
 
 size_t gemm_tile_cap(int rows, int E);
 size_t gemm_schedule_bytes(int rows, int E);
+// the fp8 gate/up's bf16 copy of its activations, kept after the schedule (rows x K)
+size_t gemm_a8_bytes(int rows, int K);
 hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const float* a_scale,
                                const void* b, const float* b_scale, void* out, bool out_f32,
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,

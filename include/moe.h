@@ -67,7 +67,7 @@ typedef enum {
 typedef enum {
   MOE_OP_DISPATCH_LAYOUT = 0,
   MOE_OP_GROUPED_FFN = 1, /* includes the [rows, I] intermediate h                      */
-  MOE_OP_EXPERT_GEMM = 2, /* moe_expert_gate_up / moe_expert_down: tile schedule only   */
+  MOE_OP_EXPERT_GEMM = 2, /* moe_expert_gate_up / moe_expert_down: tile schedule (fp8 gate/up: and a bf16 copy of a) */
   MOE_OP_ROUTER = 3,      /* moe_router_logits: fp32 partial sums (N, H, E, a_dt = x_dt) */
   MOE_OP_EXPERT_DGRAD = 4 /* moe_expert_dgrad: tile schedule (N = rows, E)               */
 } moe_op;
@@ -221,10 +221,14 @@ moe_status moe_quantize_fp8(const void* x, moe_dtype x_dt, int64_t rows, int col
  *             [E, H, I / 128] fp32 block scales, one per output row and 128 columns).
  *   out       [rows, H] of out_dt (MOE_F32 for f32 layers, else MOE_BF16).
  *   ws        workspace of moe_workspace_bytes(MOE_OP_GROUPED_FFN, ...) bytes; it holds
- *             the intermediate h [rows, I] (fp32 for f32 layers, else bf16).
- * Accumulation is fp32.  fp8 layers sum each 128-wide K block in fp32, then scale it by
- * the product of the two block scales; the down projection reads bf16 h against fp8
- * W_down, scaled per 128-wide K block.
+ *             the intermediate h [rows, I] (fp32 for f32 layers, else bf16) and, for fp8
+ *             layers, a bf16 copy of a.
+ * Accumulation is fp32.  fp8 layers: the gate/up GEMM at decode sizes (at most 16 rows per
+ * expert on average) sums each 128-wide K block of code products in fp32, then scales it by
+ * the product of the two block scales; above that, each fp8 operand value is its code times
+ * its block scale rounded to the nearest bf16 (relative error at most 2^-9 per value), and the
+ * products are summed in fp32.  The down projection reads bf16 h against fp8 W_down the same
+ * way.
  * Requires H % 128 == 0 and I % 128 == 0.
  */
 moe_status moe_grouped_ffn(const void* a, const float* a_scale, moe_dtype a_dt,
@@ -235,7 +239,9 @@ moe_status moe_grouped_ffn(const void* a, const float* a_scale, moe_dtype a_dt,
 /*
  * moe_expert_gate_up / moe_expert_down -- the two grouped GEMMs of moe_grouped_ffn as
  * separate calls (same definitions and argument meanings).  h is [rows, I], fp32 for f32
- * layers and bf16 otherwise.  ws needs moe_workspace_bytes(MOE_OP_EXPERT_GEMM, ...).
+ * layers and bf16 otherwise.  ws needs moe_workspace_bytes(MOE_OP_EXPERT_GEMM, ...) with
+ * the call's a_dt (fp8: the tile schedule and a bf16 copy of a, rows x H; MOE_ERR_WORKSPACE
+ * when smaller).
  */
 moe_status moe_expert_gate_up(const void* a, const float* a_scale, moe_dtype a_dt,
                               const int32_t* offsets, int E, int rows, int H, int I,

@@ -159,3 +159,52 @@ def test_multitile_down_e4m3_every_row(case):
         worst = max(worst, err)
         assert err <= BAR, (e, err)
     say(f"  every row of {E} segments within {worst:.2e}")
+
+
+@pytest.mark.parametrize("case", ["ragged", "hot"])
+def test_multitile_gate_up_e4m3_every_row(case):
+    """The gate/up GEMM of an fp8 layer (e4m3 activations and weights, fp32 scales per
+    128-column block) above decode sizes, at the same ragged counts: at least three 256 x 256
+    tiles per workgroup, every row of NaN-filled h compared with the oracle's SwiGLU of the
+    dequantized operands.  Codes (the NaN codes excluded) and scales are seeded and uniform.
+    The library converts both operands to bf16 (code times scale, rounded once) before the
+    products, so the bar is the bf16 GEMM's."""
+    n_e = CASES[case]
+    E, rows = len(n_e), sum(n_e)
+    gu_tiles = _tiles(n_e, 128, 128, I, 0)   # (e4m3 weights: every expert on 256 x 256 tiles)
+    say(f"multitile e4m3 gate/up {case}: rows={rows} E={E} K={H} I={I}; tiles {gu_tiles[0]}")
+    assert gu_tiles[0] >= 3 * WORKGROUPS
+
+    def seeded_codes(n, sub):
+        c = (np.asarray(w.uniform_bits(n, w.stream_key(25, sub, E), "cpu")) >> 24).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0
+        return c
+
+    def seeded_scales(n, sub):
+        bits = np.asarray(w.uniform_bits(n, w.stream_key(25, sub, E + 1), "cpu"))
+        return (2.0 ** -8 * (1.0 + (bits >> 8) / 2.0 ** 24)).astype(np.float32)
+
+    a_q = seeded_codes(rows * H, w.T_PERM).reshape(rows, H)
+    a_s = seeded_scales(rows * (H // 128), w.T_PERM).reshape(rows, H // 128)
+    w_q = seeded_codes(E * 2 * I * H, w.T_W13).reshape(E, 2 * I, H)
+    w_s = seeded_scales(E * 2 * I * (H // 128), w.T_W13).reshape(E, 2 * I, H // 128)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(n_e)]), dtype=torch.int32, device=DEV)
+    h = torch.full((rows, I), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gate_up(torch.from_numpy(a_q).to(DEV), offs, torch.from_numpy(w_q).to(DEV),
+                           a_scale=torch.from_numpy(a_s).to(DEV), w13_scale=torch.from_numpy(w_s).to(DEV), h=h)
+    sync()
+    assert bool(torch.isfinite(h).all()), "rows left unwritten"
+    hh = f64(h)
+    a = oracle.dequantize_blocks(a_q, a_s)
+    off = np.concatenate([[0], np.cumsum(n_e)])
+    no_down = np.zeros((1, I))
+    worst = 0.0
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        ref, _ = oracle.expert_ffn(a[lo:hi], oracle.dequantize_blocks(w_q[e], w_s[e]), no_down)
+        err = token_rel_err(hh[lo:hi], ref)
+        worst = max(worst, err)
+        assert err <= BAR, (e, err)
+    say(f"  every row of {E} segments within {worst:.2e}")
