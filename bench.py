@@ -651,7 +651,8 @@ def main():
     # the other workloads, each on its own after this one's buffers are released
     others = None
     if args.other_configs != "none" and not args.train:
-        names = ([n for n in workload.CONFIG_ORDER if n != cfg.name] if args.other_configs == "all"
+        # (the five workloads, then the DeepSeek-V3-shaped layer in fp8 at the prefill batch)
+        names = ([n for n in workload.CONFIG_ORDER + ["dsv3_fp8"] if n != cfg.name] if args.other_configs == "all"
                  else [n for n in args.other_configs.split(",") if n])
         del layer, inp, x, stages, step
         torch.cuda.empty_cache()
