@@ -117,15 +117,17 @@ def algorithmic(cfg, n_e, gather=False, fused=False):
     d["route"] = {"bytes": N * E * 4 + (E * 4 if cfg.zipf_s else 0) + rows * 8}
     d["layout"] = {"bytes": rows * 4 + (2 * E + 1) * 4 + 2 * rows * 4}
     d["permute"] = {"bytes": N * H * act + rows * H * (pay + fp8_scale)}
+    if gather and cfg.dtype == "fp8":   # each token quantized once (codes, scales), then its bf16 values
+        d["permute"] = {"bytes": N * H * act + 2 * N * H * (1 + fp8_scale) + N * H * act}
     a_bytes = N * H * act if gather else rows * H * (pay + fp8_scale)
     d["gate_up"] = {"bytes": touched * 2 * I * H * (wb + fp8_scale) + a_bytes + rows * I * 2,
                     "flops": 4.0 * rows * H * I}
     d["down"] = {"bytes": touched * H * I * (wb + fp8_scale) + rows * I * 2 + rows * H * act,
                  "flops": 2.0 * rows * H * I}
     if cfg.shared and fused:
-        d["gate_up"]["bytes"] += 2 * I * H * wb + N * I * 2     # x is read once for both
+        d["gate_up"]["bytes"] += 2 * I * H * (wb + fp8_scale) + N * I * 2     # x is read once for both
         d["gate_up"]["flops"] += 4.0 * N * H * I
-        d["down"]["bytes"] += H * I * wb + N * I * 2 + N * H * act
+        d["down"]["bytes"] += H * I * (wb + fp8_scale) + N * I * 2 + N * H * act
         d["down"]["flops"] += 2.0 * N * H * I
     elif cfg.shared:
         d["shared"] = {"bytes": 3 * I * H * wb + N * H * act + N * I * 2 + N * H * act,
@@ -255,7 +257,10 @@ def roofline(cfg, alg, per, fused, gather, with_traffic=True):
                 "peak": PEAK_MFMA[cfg.dtype] / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic
-    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU, routed rows gathered from x and the shared expert in the "
+    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU on e4m3 weights, routed rows gathered from the tokens' fp8 "
+                      "values and the shared expert in the same launch (moe_expert_gate_up_gathered_shared_e4m3)"
+                      if fused and cfg.dtype == "fp8" else
+                      "grouped gate/up GEMM + SwiGLU, routed rows gathered from x and the shared expert in the "
                       "same launch (moe_expert_gate_up_gathered_shared)" if fused else
                       "grouped gate/up GEMM + SwiGLU, rows gathered from x (moe_expert_gate_up_gathered)"
                       if gather else "grouped gate/up GEMM + SwiGLU (moe_expert_gate_up)")
@@ -288,7 +293,7 @@ def layer_stages(cfg, layer, x):
     stages = [("router", lambda: layer.router(x)),
               ("route", lambda: layer.route(layer.z)),
               ("layout", layer.dispatch)]
-    if not layer.gather:
+    if not layer.gather or layer.fp8:   # (gathered fp8: each token's quantize and dequantize)
         stages.append(("permute", lambda: layer.permute(x)))
     stages += [("gate_up", lambda: layer.gate_up(x)),
                ("down", layer.down)]
@@ -552,7 +557,8 @@ def main():
 
     n_e = layer.layout[0].cpu().numpy()
     alg = algorithmic(cfg, n_e, layer.gather, layer.fuse)
-    alg["permute (standalone)"] = alg["permute"]
+    # (the standalone permute copies x's rows: bf16 for the gathered fp8 layer as well)
+    alg["permute (standalone)"] = {"bytes": (cfg.N + cfg.N * cfg.k) * cfg.H * x.element_size()}
     if args.train:
         alg.update(algorithmic_backward(cfg, n_e))
     kernels = summarize(per, alg, cfg.dtype)

@@ -21,9 +21,10 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
     "MOE_OP_DISPATCH_LAYOUT", "MOE_OP_GROUPED_FFN", "MOE_OP_EXPERT_GEMM", "MOE_OP_ROUTER", "MOE_OP_EXPERT_DGRAD",
     "MOE_LAYOUT_SCRATCH_BYTES", "moe_router_logits", "moe_route", "moe_dispatch_layout",
-    "moe_dispatch_layout_noalloc", "moe_permute", "moe_quantize_fp8", "moe_expert_gate_up",
+    "moe_dispatch_layout_noalloc", "moe_permute", "moe_quantize_fp8", "moe_dequantize_fp8", "moe_expert_gate_up",
     "moe_expert_gate_up_gathered", "moe_expert_gate_up_gathered_shared", "moe_expert_down",
-    "moe_expert_down_shared", "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
+    "moe_expert_down_shared", "moe_expert_gate_up_gathered_shared_e4m3", "moe_expert_down_shared_e4m3",
+    "moe_grouped_ffn", "moe_combine", "moe_workspace_bytes", "moe_status_str",
     "moe_version", "moe_combine_backward", "moe_expert_gate_up_preact", "moe_swiglu_backward", "moe_expert_dgrad",
     "moe_expert_wgrad", "moe_router_backward", "moe_router_input_grad", "moe_stream_probe",
 ]
@@ -59,12 +60,16 @@ _SIGS = {
     "moe_dispatch_layout_noalloc": [_P, _I, _I, _I, _P, _P, _P, _P, _P],
     "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _I, _P, _P],
     "moe_quantize_fp8": [_P, _I, ctypes.c_int64, _I, _P, _P, _P],
+    "moe_dequantize_fp8": [_P, _P, ctypes.c_int64, _I, _P, _P],
     "moe_grouped_ffn": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "moe_expert_gate_up": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
     "moe_expert_gate_up_gathered": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P],
     "moe_expert_down": [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _SZ, _P],
     "moe_expert_gate_up_gathered_shared": [_P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_expert_down_shared": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P],
+    "moe_expert_gate_up_gathered_shared_e4m3": [_P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                                _P],
+    "moe_expert_down_shared_e4m3": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_combine": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
     "moe_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I],
     "moe_combine_backward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P],
@@ -253,6 +258,18 @@ def moe_quantize_fp8(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     return q, scale
 
 
+def moe_dequantize_fp8(q: torch.Tensor, scale: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """bf16 values (code times its block's scale, one rounding) of e4m3 codes q [..., cols]
+    with scales [..., cols / 128]."""
+    cols = q.shape[-1]
+    rows = q.numel() // cols
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check("moe_dequantize_fp8", lib().moe_dequantize_fp8(_ptr(q), _ptr(scale), rows, cols, _ptr(out),
+                                                          _stream(q)))
+    return out
+
+
 def moe_expert_gate_up(a: torch.Tensor, offsets: torch.Tensor, w13: torch.Tensor,
                        a_scale: Optional[torch.Tensor] = None, w13_scale: Optional[torch.Tensor] = None,
                        h: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
@@ -328,6 +345,43 @@ def moe_expert_down_shared(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Ten
     _check("moe_expert_down_shared", lib().moe_expert_down_shared(
         _ptr(h), _dt(h), _ptr(offsets), E, rows, n_shared, I, H, _ptr(w2), _ptr(shared_w2), _ptr(src_slot),
         _ptr(topk_gate), _ptr(out), _dt(out), _ptr(ws), ws.numel(), _stream(h)))
+    return out
+
+
+def moe_expert_gate_up_gathered_shared_e4m3(x: torch.Tensor, src_slot: torch.Tensor, k: int, offsets: torch.Tensor,
+                                            w13: torch.Tensor, w13_scale: torch.Tensor, shared_w13: torch.Tensor,
+                                            shared_w13_scale: torch.Tensor, rows: Optional[int] = None,
+                                            h: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """moe_expert_gate_up_gathered_shared on e4m3 weights (codes and block scales); x [N, H]
+    bf16 holds the tokens' fp8 payload values."""
+    N, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if rows is None:
+        rows = src_slot.numel()
+    if h is None:
+        h = torch.empty((rows + N, I), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, MOE_BF16), x.device)
+    _check("moe_expert_gate_up_gathered_shared_e4m3", lib().moe_expert_gate_up_gathered_shared_e4m3(
+        _ptr(x), N, _ptr(src_slot), k, _ptr(offsets), E, rows, H, I, _ptr(w13), _ptr(w13_scale), _ptr(shared_w13),
+        _ptr(shared_w13_scale), _ptr(h), _ptr(ws), ws.numel(), _stream(x)))
+    return h
+
+
+def moe_expert_down_shared_e4m3(h: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor, w2_scale: torch.Tensor,
+                                shared_w2: torch.Tensor, shared_w2_scale: torch.Tensor, rows: int,
+                                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """moe_expert_down_shared on e4m3 weights (codes and block scales)."""
+    total, I = h.shape
+    E, H, _ = w2.shape
+    if out is None:
+        out = torch.empty((total, H), dtype=torch.bfloat16, device=h.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, total, H, I, E + 1, 1, MOE_BF16), h.device)
+    _check("moe_expert_down_shared_e4m3", lib().moe_expert_down_shared_e4m3(
+        _ptr(h), _ptr(offsets), E, rows, total - rows, I, H, _ptr(w2), _ptr(w2_scale), _ptr(shared_w2),
+        _ptr(shared_w2_scale), _ptr(out), _ptr(ws), ws.numel(), _stream(h)))
     return out
 
 

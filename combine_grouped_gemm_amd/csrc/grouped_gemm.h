@@ -40,6 +40,7 @@ struct GemmArgs {
                                // the T experts with kWideTileRows < n_e <= kWideTallRows, which the
                                // prefix gives no m-tiles and which run as one 320-row tile; or null
   int32_t* tall_counter = nullptr;      // [kNumXcd] the counters of those tiles (zeroed by the prologue)
+  const float* shared_b_scale = nullptr;  // (B8) the shared expert's block scales [b_rows, K / 128]
 };
 
 // Segment [lo, hi) of expert e, clamped into [0, rows] so that malformed offsets cannot

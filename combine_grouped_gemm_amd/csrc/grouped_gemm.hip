@@ -787,6 +787,16 @@ __global__ __launch_bounds__(256) void dequant_e4m3_kernel(const uint2* __restri
   }
 }
 
+hipError_t launch_dequant_e4m3(const uint8_t* q, const float* scale, long long rows, int cols, void* out,
+                               hipStream_t s) {
+  const int n8 = static_cast<int>(rows * cols / 8);
+  if (n8 == 0) return hipSuccess;
+  const int blocks = (n8 + 255) / 256 < 16384 ? (n8 + 255) / 256 : 16384;
+  hipLaunchKernelGGL(dequant_e4m3_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint2*>(q), scale,
+                     n8, cols, reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
 // bytes of the dequantized activations the fp8 gate/up keeps after its tile schedule
 size_t gemm_a8_bytes(int rows, int K) {
   return (static_cast<size_t>(rows) * K * 2 + 255) & ~static_cast<size_t>(255);
@@ -797,7 +807,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                                const int32_t* offsets, int E, int rows, int K, int I, int n_out,
                                long long b_rows, void* sched, hipStream_t s, const int32_t* a_rows,
                                int a_div, int a_nrows, const void* shared_b, int shared_rows,
-                               const int32_t* row_slot, const float* row_gate, void* au) {
+                               const int32_t* row_slot, const float* row_gate, void* au,
+                               const float* shared_b_scale) {
   // with a shared segment the schedule covers E + 1 segments and rows + shared_rows rows
   const int n_seg = E + (shared_rows > 0 ? 1 : 0);
   int32_t* prefix = reinterpret_cast<int32_t*>(sched);
@@ -806,7 +817,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   int32_t* tile_counter = tile_expert + cap;
   int32_t* tall_list = tile_counter + kNumXcd + 1;   // [E + 1] + [kNumXcd] counters
   // few rows per expert and e4m3 weights: the weight-streaming kernel (16-row m-tiles)
-  const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) &&
+  const bool stream = (mode == MODE_GATE_UP ? ct == CT_FP8 : b8) && shared_rows == 0 && a_rows == nullptr &&
                       static_cast<long long>(rows) <= static_cast<long long>(kStreamTileRows) * E &&
                       (mode == MODE_GATE_UP ? I % 64 == 0 : n_out % 128 == 0) &&
                       static_cast<long long>(gemm_tile_cap(rows, E)) * (mode == MODE_GATE_UP ? I / 64 : n_out / 128) <
@@ -821,10 +832,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
       static_cast<long long>(kWideTileRows) * 2 * K < (1LL << 32) &&
       static_cast<long long>(rows) * K / 8 < (1LL << 31) && wide_tiles_fit(mode, rows, E, I, n_out)) {
     void* deq = static_cast<uint8_t*>(sched) + gemm_schedule_bytes(rows, E);
-    const int n8 = static_cast<int>(static_cast<long long>(rows) * K / 8);
-    const int blocks = (n8 + 255) / 256 < 16384 ? (n8 + 255) / 256 : 16384;
-    hipLaunchKernelGGL(dequant_e4m3_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint2*>(a),
-                       a_scale, n8, K, reinterpret_cast<uint4*>(deq));
+    const hipError_t e = launch_dequant_e4m3(static_cast<const uint8_t*>(a), a_scale, rows, K, deq, s);
+    if (e != hipSuccess) return e;
     return launch_grouped_gemm(CT_BF16, true, mode, deq, nullptr, b, b_scale, out, out_f32, offsets, E, rows, K,
                                I, n_out, b_rows, sched, s);
   }
@@ -835,19 +844,20 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                        b_rows * rbytes < (1LL << 32) &&
                        (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32) &&
                        wide_tiles_fit(mode, rows + shared_rows, n_seg, I, n_out);
-  if ((shared_rows > 0 || row_gate != nullptr || au != nullptr) && (!wide_ok || stream))
+  // e4m3 weights (down; gate/up with dequantized activations, gathered or not, and the shared
+  // expert's rows as one more segment) at more than 16 rows per expert: the 256 x 256 kernel,
+  // which converts each weight fragment (code times its block's scale) as it reads it from LDS
+  const bool wide8 = (mode == MODE_DOWN || mode == MODE_GATE_UP) && ct == CT_BF16 && b8 && !stream && K % 128 == 0 &&
+                     n_out % 8 == 0 && wide_out_fits(mode, I, n_out) &&
+                     b_rows * K < (1LL << 32) && b_rows * (K / 128) * 4 < (1LL << 32) &&
+                     (a_rows ? static_cast<long long>(a_nrows) : kWideTileRows) * rbytes < (1LL << 32) &&
+                     (shared_rows == 0 || shared_b_scale != nullptr) && row_gate == nullptr && au == nullptr &&
+                     (a_rows == nullptr || mode == MODE_GATE_UP) &&
+                     wide_tiles_fit(mode, rows + shared_rows, n_seg, I, n_out);
+  if ((shared_rows > 0 || row_gate != nullptr || au != nullptr) && (!(wide_ok || wide8) || stream))
     return hipErrorNotSupported;   // (callers check first)
   const bool wide = wide_ok && (shared_rows > 0 || row_gate != nullptr || au != nullptr ||
                                 mode == MODE_GATE_UP || E > 1);
-  // e4m3 weights (down; gate/up with its dequantized activations) at more than 16 rows per
-  // expert: the 256 x 256 kernel, which converts each weight fragment (code times its block's
-  // scale) as it reads it from LDS
-  const bool wide8 = (mode == MODE_DOWN || mode == MODE_GATE_UP) && ct == CT_BF16 && b8 && !stream && K % 128 == 0 &&
-                     n_out % 8 == 0 &&
-                     wide_out_fits(mode, I, n_out) &&
-                     b_rows * K < (1LL << 32) && b_rows * (K / 128) * 4 < (1LL << 32) &&
-                     static_cast<long long>(kWideTileRows) * rbytes < (1LL << 32) && shared_rows == 0 &&
-                     au == nullptr && a_rows == nullptr && wide_tiles_fit(mode, rows, n_seg, I, n_out);
   const int tile_rows = stream ? kStreamTileRows : (wide || wide8 ? kWideTileRows : (dma ? kDM : GBM));
   // bf16 GEMMs on the 256 x 256 kernel: experts of 257..320 rows as one tile (down: 320 x 128,
   // gate/up: 320 x 256)
@@ -882,6 +892,7 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
   p.row_gate = row_slot != nullptr ? row_gate : nullptr;
   p.k_split = 1;
   p.au = au;
+  p.shared_b_scale = shared_b_scale;
   if (stream) return launch_grouped_gemm_stream(mode, p, s);
   if (wide || wide8) {
     p.tile_counter = tile_counter;

@@ -328,8 +328,9 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
       }
       return static_cast<uint32_t>(t.c0 + (r < clast ? r : clast));
     };
-    if constexpr (W8) {   // (no shared segment with W8: the launcher checks)
-      t.sc = reinterpret_cast<const uint8_t*>(p.b_scale + static_cast<size_t>(e) * p.b_rows * kblk);
+    if constexpr (W8) {
+      t.sc = reinterpret_cast<const uint8_t*>(e < p.E ? p.b_scale + static_cast<size_t>(e) * p.b_rows * kblk
+                                                      : p.shared_b_scale);
       // scale gather: wave w's lane l fetches the scale of tile weight row 64 w + l
       t.s_src = w_row(wave * 64 + static_cast<int>(ln)) * kblk * 4;
     }

@@ -242,6 +242,58 @@ moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int
                                              shared_w13, N, nullptr, nullptr, au));
 }
 
+moe_status moe_expert_gate_up_gathered_shared_e4m3(const void* x, int N, const int32_t* src_slot, int k,
+                                                   const int32_t* offsets, int E, int rows, int H, int I,
+                                                   const uint8_t* w13, const float* w13_scale,
+                                                   const uint8_t* shared_w13, const float* shared_w13_scale,
+                                                   void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (E < 1 || rows < 0 || N < 0 || H <= 0 || I <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (E >= MOE_MAX_EXPERTS || H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(rows) + N >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (rows + N == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < moe::gemm_schedule_bytes(rows + N, E + 1)) return MOE_ERR_WORKSPACE;
+  if (x == nullptr || shared_w13 == nullptr || shared_w13_scale == nullptr || h == nullptr ||
+      (rows > 0 && (w13 == nullptr || w13_scale == nullptr || src_slot == nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(shared_w13) || (w13 != nullptr && !aligned16(w13))) return MOE_ERR_INVALID_ARG;
+  if (static_cast<long long>(N) * H * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  if (2LL * I * H >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_grouped_gemm(1, true, 0, x, nullptr, w13, w13_scale, h, false, offsets, E, rows, H,
+                                             I, I, 2ll * I, ws, stream, src_slot, k, N, shared_w13, N, nullptr,
+                                             nullptr, nullptr, shared_w13_scale));
+}
+
+moe_status moe_expert_down_shared_e4m3(const void* h, const int32_t* offsets, int E, int rows, int n_shared,
+                                       int I, int H, const uint8_t* w2, const float* w2_scale,
+                                       const uint8_t* shared_w2, const float* shared_w2_scale, void* out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (E < 1 || rows < 0 || n_shared < 0 || H <= 0 || I <= 0 || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (E >= MOE_MAX_EXPERTS || H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(rows) + n_shared >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (rows + n_shared == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < moe::gemm_schedule_bytes(rows + n_shared, E + 1)) return MOE_ERR_WORKSPACE;
+  if (h == nullptr || out == nullptr || (n_shared > 0 && (shared_w2 == nullptr || shared_w2_scale == nullptr)) ||
+      (rows > 0 && (w2 == nullptr || w2_scale == nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || (w2 != nullptr && !aligned16(w2)) || (shared_w2 != nullptr && !aligned16(shared_w2)))
+    return MOE_ERR_INVALID_ARG;
+  if (static_cast<long long>(H) * I >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_grouped_gemm(1, true, 1, h, nullptr, w2, w2_scale, out, false, offsets, E, rows, I,
+                                             I, H, static_cast<long long>(H), ws, stream, nullptr, 1, 0, shared_w2,
+                                             n_shared, nullptr, nullptr, nullptr, shared_w2_scale));
+}
+
+moe_status moe_dequantize_fp8(const uint8_t* q, const float* scale, int64_t rows, int cols, void* out,
+                              hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (cols % 128 != 0 || rows * cols / 8 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (q == nullptr || scale == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_dequant_e4m3(q, scale, rows, cols, out, stream));
+}
+
 moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                                   int n_shared, int I, int H, const void* w2, const void* shared_w2,
                                   const int32_t* src_slot, const float* topk_gate, void* out,

@@ -68,7 +68,11 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                                const int32_t* a_rows = nullptr, int a_div = 1, int a_nrows = 0,
                                const void* shared_b = nullptr, int shared_rows = 0,
                                const int32_t* row_slot = nullptr, const float* row_gate = nullptr,
-                               void* au = nullptr);
+                               void* au = nullptr, const float* shared_b_scale = nullptr);
+// bf16 values of e4m3 codes [rows, cols] with fp32 scales [rows, cols / 128] (code times the
+// scale of its 128-column block, rounded to nearest even); rows * cols / 8 < 2^31
+hipError_t launch_dequant_e4m3(const uint8_t* q, const float* scale, long long rows, int cols, void* out,
+                               hipStream_t s);
 // whether launch_grouped_gemm accepts a shared segment for these bf16 shapes
 bool grouped_gemm_shared_supported(int mode, int K, int I, int n_out, long long b_rows, int a_nrows,
                                    bool gathered);

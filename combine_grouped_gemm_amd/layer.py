@@ -11,10 +11,12 @@ only kernels: no allocation, no host synchronisation, no device-to-host copy.
 
 bf16 layers fold the permute into the gate/up GEMM by default (``gather=True``): its
 operand rows are read straight from x through the layout's src_slot map, so the
-permuted copy of x is never written.  f32 and fp8 layers (the fp8 permute also
-quantizes) run the permute kernel.  bf16 layers with gathered rows also run the shared
-expert inside the routed GEMM launches by default (``fuse_shared=True``): its rows follow
-the routed rows in h and in the expert outputs.
+permuted copy of x is never written.  f32 layers run the permute kernel.  fp8 layers with a
+shared expert and more than 16 rows per expert on average quantize each token once (its
+fp8 payload), turn the codes back into bf16 values once, and gather those rows the same way;
+other fp8 layers run the quantize-on-permute kernel.  Layers with gathered rows also run
+the shared expert inside the routed GEMM launches by default (``fuse_shared=True``): its
+rows follow the routed rows in h and in the expert outputs.
 """
 from __future__ import annotations
 
@@ -24,8 +26,9 @@ import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_OP_DISPATCH_LAYOUT, MOE_OP_EXPERT_DGRAD, MOE_OP_EXPERT_GEMM,
                MOE_OP_GROUPED_FFN, MOE_OP_ROUTER, moe_combine, moe_combine_backward, moe_dispatch_layout,
-               moe_expert_dgrad, moe_expert_down, moe_expert_down_shared, moe_expert_gate_up,
-               moe_expert_gate_up_gathered, moe_expert_gate_up_gathered_shared, moe_expert_gate_up_preact,
+               moe_dequantize_fp8, moe_expert_dgrad, moe_expert_down, moe_expert_down_shared,
+               moe_expert_down_shared_e4m3, moe_expert_gate_up, moe_expert_gate_up_gathered,
+               moe_expert_gate_up_gathered_shared, moe_expert_gate_up_gathered_shared_e4m3, moe_expert_gate_up_preact,
                moe_expert_wgrad, moe_grouped_ffn, moe_permute, moe_quantize_fp8, moe_route, moe_router_backward,
                moe_router_input_grad, moe_router_logits, moe_swiglu_backward, moe_workspace_bytes)
 
@@ -51,7 +54,10 @@ class MoELayer:
         dev = w13.device
         self.device = dev
         self.fp8 = dtype == "fp8"
-        self.gather = gather and dtype == "bf16"
+        # fp8 above decode sizes (more than 16 rows per expert on average) with a shared expert:
+        # the gathered, fused path on e4m3 weights; at decode sizes the weight-streaming kernels
+        self.fp8_gather = bool(self.fp8 and gather and fuse_shared and shared_w13 is not None and N * k > 16 * E)
+        self.gather = gather and (dtype == "bf16" or self.fp8_gather)
         act = torch.float32 if dtype == "f32" else torch.bfloat16
         self.act_dtype = act
         rows = N * k
@@ -68,7 +74,7 @@ class MoELayer:
         self.shared = shared_w13 is not None
         self.fuse = bool(fuse_shared and self.shared and self.gather)
         # the routed rows' gates applied in the down GEMM's epilogue (combine then sums)
-        self.gate_in_down = bool(gate_in_down and self.fuse)
+        self.gate_in_down = bool(gate_in_down and self.fuse and not self.fp8)
         i32 = dict(dtype=torch.int32, device=dev)
         self.w_r = w_r
         if w_r is not None:
@@ -86,15 +92,22 @@ class MoELayer:
         self.a_dt = a_dt
         self.x_perm = None if self.gather else torch.empty((rows, H), dtype=torch.uint8 if self.fp8 else act,
                                                           device=dev)
-        self.x_perm_scale = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+        self.x_perm_scale = (torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
+                             if self.fp8 and not self.gather else None)
+        if self.fp8_gather:
+            # each token's fp8 payload (codes and block scales) and its values as bf16 rows
+            self.x_q = torch.empty((N, H), dtype=torch.uint8, device=dev)
+            self.x_q_scale = torch.empty((N, H // 128), dtype=torch.float32, device=dev)
+            self.x_deq = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
         self.ffn_ws = None if self.fuse else torch.empty(
             max(moe_workspace_bytes(MOE_OP_GROUPED_FFN, rows, H, I, E, 1, a_dt), 256), dtype=torch.uint8, device=dev)
         if self.fuse:
             # routed rows then the shared expert's N rows, in h and in the expert outputs
             self.h_all = torch.empty((rows + N, I), dtype=torch.bfloat16, device=dev)
             self.out_all = torch.empty((rows + N, H), dtype=act, device=dev)
-            self.fused_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, a_dt),
-                                            256), dtype=torch.uint8, device=dev)
+            self.fused_ws = torch.empty(max(moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1,
+                                                                MOE_BF16 if self.fp8 else a_dt), 256),
+                                        dtype=torch.uint8, device=dev)
         else:
             self._expert_out = torch.empty((rows, H), dtype=act, device=dev)
         if self.shared and not self.fuse:
@@ -174,6 +187,9 @@ class MoELayer:
     def permute(self, x: torch.Tensor):
         """The permuted payload (nothing to do when the gate/up GEMM gathers its rows)."""
         send_pos = self.layout[2]
+        if self.fp8_gather:   # each token once: codes and scales, then their bf16 values
+            moe_quantize_fp8(x, self.x_q, self.x_q_scale)
+            return moe_dequantize_fp8(self.x_q, self.x_q_scale, self.x_deq)
         if self.gather:
             return None
         if self.fp8:
@@ -183,6 +199,10 @@ class MoELayer:
     def gate_up(self, x: torch.Tensor):
         """Grouped gate/up GEMM + SwiGLU into h (gathered layers read x directly; fused
         layers also compute the shared expert's rows)."""
+        if self.fuse and self.fp8:
+            return moe_expert_gate_up_gathered_shared_e4m3(self.x_deq, self.layout[3], self.k, self.layout[1],
+                                                           self.w13, self.w13_scale, self.sw13, self.sw13_scale,
+                                                           h=self.h_all, ws=self.fused_ws)
         if self.fuse:
             return moe_expert_gate_up_gathered_shared(x, self.layout[3], self.k, self.layout[1], self.w13,
                                                       self.sw13, h=self.h_all, ws=self.fused_ws,
@@ -195,6 +215,9 @@ class MoELayer:
 
     def down(self):
         """Grouped down GEMM of h into the expert outputs."""
+        if self.fuse and self.fp8:
+            return moe_expert_down_shared_e4m3(self.h_all, self.layout[1], self.w2, self.w2_scale, self.sw2,
+                                               self.sw2_scale, self.N * self.k, out=self.out_all, ws=self.fused_ws)
         if self.fuse:
             gates = (self.layout[3], self.topk_gate) if self.gate_in_down else (None, None)
             return moe_expert_down_shared(self.h_all, self.layout[1], self.w2, self.sw2, self.N * self.k,
@@ -236,7 +259,7 @@ class MoELayer:
         save_for_backward a bf16 layer that runs the shared expert inside the routed launches
         also keeps the gate/up pre-activations, which backward then reads instead of
         recomputing them."""
-        self.save_au = bool(save_for_backward and self.fuse)
+        self.save_au = bool(save_for_backward and self.fuse and not self.fp8)
         if self.save_au and self.au_all is None:
             self.au_all = torch.empty((self.N * self.k + self.N, 2 * self.I), dtype=torch.bfloat16,
                                       device=self.device)

@@ -199,6 +199,22 @@ moe_status moe_quantize_fp8(const void* x, moe_dtype x_dt, int64_t rows, int col
                             float* scale, hipStream_t stream);
 
 /*
+ * moe_dequantize_fp8 -- the values of e4m3 codes with their block scales, as bf16.
+ *
+ * Definition: the block-scaled fp8 format of moe_quantize_fp8 (value = code times the fp32
+ * scale of its row's 128-column block; "EP / DeepEP explanation" page, section 10, and
+ * "DeepEP" page, section 7: fp8 payload with per-block scales).  Each value is the fp32
+ * product of the decoded code and the scale, rounded to the nearest bf16 (even on ties); the
+ * NaN codes give NaN.
+ *
+ *   q [rows, cols] uint8 codes, scale [rows, cols / 128] fp32 -> out [rows, cols] bf16.
+ *   Requires cols % 128 == 0 and rows * cols / 8 < 2^31 (MOE_ERR_UNSUPPORTED otherwise);
+ *   q and out 16-byte aligned (MOE_ERR_INVALID_ARG otherwise).  rows == 0 returns MOE_OK.
+ */
+moe_status moe_dequantize_fp8(const uint8_t* q, const float* scale, int64_t rows, int cols, void* out,
+                              hipStream_t stream);
+
+/*
  * moe_grouped_ffn -- every expert's SwiGLU FFN on its rows, as grouped GEMMs.
  *
  * Definition: "MoE part 4" page, section 2 (one launch for many expert GEMMs with
@@ -226,7 +242,7 @@ moe_status moe_quantize_fp8(const void* x, moe_dtype x_dt, int64_t rows, int col
  * Accumulation is fp32.  fp8 layers: the gate/up GEMM at decode sizes (at most 16 rows per
  * expert on average) sums each 128-wide K block of code products in fp32, then scales it by
  * the product of the two block scales; above that, each fp8 operand value is its code times
- * its block scale rounded to the nearest bf16 (relative error at most 2^-9 per value), and the
+ * its block scale rounded to the nearest bf16 (relative error at most 2^-8 per value), and the
  * products are summed in fp32.  The down projection reads bf16 h against fp8 W_down the same
  * way.
  * Requires H % 128 == 0 and I % 128 == 0.
@@ -306,11 +322,30 @@ moe_status moe_expert_gate_up_gathered(const void* x, moe_dtype x_dt, int N, con
  *   ws        >= moe_workspace_bytes(MOE_OP_EXPERT_GEMM, rows + n, H, I, E + 1, 1, MOE_BF16).
  * bf16 only; requires E < MOE_MAX_EXPERTS, H % 128 == 0, I % 128 == 0 and N * H * 2 < 2^32
  * (MOE_ERR_UNSUPPORTED otherwise).  rows + n == 0 returns MOE_OK without launching.
+ *
+ * moe_expert_gate_up_gathered_shared_e4m3 / moe_expert_down_shared_e4m3 -- the same launches
+ * with e4m3 weights (an fp8 layer above decode sizes): w13 [E, 2I, H] and shared_w13 [2I, H]
+ * (or w2 [E, H, I] and shared_w2 [H, I]) uint8 codes, w13_scale [E, 2I, H / 128] and
+ * shared_w13_scale [2I, H / 128] (w2_scale [E, H, I / 128], shared_w2_scale [H, I / 128])
+ * fp32 block scales.  x [N, H] bf16 holds the tokens' fp8 payload as values
+ * (moe_quantize_fp8 then moe_dequantize_fp8 of x: each token quantized once, its k rows and
+ * its shared row gathered from the same values).  Each weight value is its code times its
+ * block scale rounded to bf16; products are summed in fp32.  No au, no gates in the epilogue.
+ * Same requirements and workspace; scales missing: MOE_ERR_INVALID_ARG.
  */
 moe_status moe_expert_gate_up_gathered_shared(const void* x, moe_dtype x_dt, int N, const int32_t* src_slot,
                                               int k, const int32_t* offsets, int E, int rows, int H, int I,
                                               const void* w13, const void* shared_w13, void* h, void* au,
                                               void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_expert_gate_up_gathered_shared_e4m3(const void* x, int N, const int32_t* src_slot, int k,
+                                                   const int32_t* offsets, int E, int rows, int H, int I,
+                                                   const uint8_t* w13, const float* w13_scale,
+                                                   const uint8_t* shared_w13, const float* shared_w13_scale,
+                                                   void* h, void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_expert_down_shared_e4m3(const void* h, const int32_t* offsets, int E, int rows, int n_shared,
+                                       int I, int H, const uint8_t* w2, const float* w2_scale,
+                                       const uint8_t* shared_w2, const float* shared_w2_scale, void* out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 moe_status moe_expert_down_shared(const void* h, moe_dtype h_dt, const int32_t* offsets, int E, int rows,
                                   int n_shared, int I, int H, const void* w2, const void* shared_w2,
                                   const int32_t* src_slot, const float* topk_gate, void* out,

@@ -187,6 +187,51 @@ def test_shared_segment_validation(L):
     assert dcall(gate=FAKE) == MOE_ERR_INVALID_ARG
 
 
+def test_fp8_weight_entry_points_validation(L):
+    """The e4m3-weight fused launches, the fp8 dequantizer and the fp8 gate/up workspace: every
+    check happens on the host, before anything is enqueued."""
+    rows, H, I, E, N, k = 65536, 7168, 2048, 256, 8192, 8
+    sched = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows + N, H, I, E + 1, 1, MOE_BF16)
+    f = L.moe_expert_gate_up_gathered_shared_e4m3
+    args = lambda **kw: dict(dict(x=FAKE, N=N, src_slot=FAKE, k=k, offsets=FAKE, E=E, rows=rows, H=H, I=I,
+                                  w13=FAKE, w13_s=FAKE, sw13=FAKE, sw13_s=FAKE, h=FAKE, ws=FAKE, ws_bytes=sched,
+                                  s=None), **kw)
+    call = lambda **kw: f(*args(**kw).values())
+    assert call(ws_bytes=sched - 1) == MOE_ERR_WORKSPACE
+    assert call(w13_s=None) == MOE_ERR_INVALID_ARG
+    assert call(sw13_s=None) == MOE_ERR_INVALID_ARG
+    assert call(src_slot=None) == MOE_ERR_INVALID_ARG
+    assert call(k=0) == MOE_ERR_INVALID_ARG
+    assert call(I=2000) == MOE_ERR_UNSUPPORTED
+    assert call(E=1024) == MOE_ERR_UNSUPPORTED
+    assert call(N=300000, ws_bytes=1 << 40) == MOE_ERR_UNSUPPORTED   # N * H * 2 >= 2^32
+    assert call(x=FAKE + 8) == MOE_ERR_INVALID_ARG
+    assert call(rows=0, N=0, ws=None, ws_bytes=0) == MOE_OK
+    g = L.moe_expert_down_shared_e4m3
+    dargs = lambda **kw: dict(dict(h=FAKE, offsets=FAKE, E=E, rows=rows, n=N, I=I, H=H, w2=FAKE, w2_s=FAKE,
+                                   sw2=FAKE, sw2_s=FAKE, out=FAKE, ws=FAKE, ws_bytes=sched, s=None), **kw)
+    dcall = lambda **kw: g(*dargs(**kw).values())
+    assert dcall(ws_bytes=sched - 1) == MOE_ERR_WORKSPACE
+    assert dcall(w2_s=None) == MOE_ERR_INVALID_ARG
+    assert dcall(sw2_s=None) == MOE_ERR_INVALID_ARG
+    assert dcall(n=-1) == MOE_ERR_INVALID_ARG
+    assert dcall(H=7000) == MOE_ERR_UNSUPPORTED
+    assert dcall(rows=0, n=0, ws=None, ws_bytes=0) == MOE_OK
+    d = L.moe_dequantize_fp8
+    assert d(FAKE, FAKE, 4, 200, FAKE, None) == MOE_ERR_UNSUPPORTED        # cols % 128
+    assert d(FAKE, FAKE, 1 << 31, 128, FAKE, None) == MOE_ERR_UNSUPPORTED  # rows * cols / 8 >= 2^31
+    assert d(FAKE, None, 4, 128, FAKE, None) == MOE_ERR_INVALID_ARG
+    assert d(FAKE, FAKE, 4, 128, FAKE + 8, None) == MOE_ERR_INVALID_ARG    # misaligned output
+    assert d(FAKE, FAKE, -1, 128, FAKE, None) == MOE_ERR_INVALID_ARG
+    assert d(None, None, 0, 128, None, None) == MOE_OK
+    # the fp8 gate/up keeps a bf16 copy of its activations after the schedule
+    gu = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_FP8_E4M3)
+    assert gu == moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_GEMM, rows, H, I, E, 1, MOE_BF16) + rows * H * 2
+    e = L.moe_expert_gate_up
+    assert e(FAKE, FAKE, MOE_FP8_E4M3, FAKE, E, rows, H, I, FAKE, FAKE, FAKE, FAKE, gu - 1, None) == MOE_ERR_WORKSPACE
+    assert moe.moe_workspace_bytes(moe.MOE_OP_GROUPED_FFN, rows, H, I, E, 1, MOE_FP8_E4M3) == gu + rows * I * 2
+
+
 def test_backward_validation_and_workspace(L):
     ws = moe.moe_workspace_bytes(moe.MOE_OP_EXPERT_DGRAD, 65536, 0, 0, 256, 0, 0)
     # prefix [E+1] + one entry per 128-row tile (rows / 128 + E) + 8 counters, int32, 256-byte rounded

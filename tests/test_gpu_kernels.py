@@ -305,6 +305,28 @@ def test_quantize_fp8_bit_exact(dt):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
+def test_dequantize_fp8_values():
+    """Every e4m3 code under scales spread over 2^-10 .. 2^10: each value is the exact product
+    (the oracle's dequantization, float64) rounded to fp32 and then to bf16, so it lies within
+    half a bf16 step (2^-8 relative) plus the fp32 rounding of it; the NaN codes give NaN; zero
+    codes give zero.  A scale taken
+    from the wrong block, or a code decoded wrongly, misses that bound."""
+    rows, cols = 64, 1024
+    say("dequantize fp8")
+    codes = ((np.arange(cols)[None, :] + 37 * np.arange(rows)[:, None]) % 256).astype(np.uint8)
+    bits = np.asarray(w.uniform_bits(rows * cols // 128, w.stream_key(29, w.T_PERM, 0), "cpu"))
+    scales = (2.0 ** ((bits >> 27).astype(np.int64) - 16) * (1.0 + (bits & 0xFFFFFF) / 2.0 ** 24)).astype(
+        np.float32).reshape(rows, cols // 128)
+    out = moe.moe_dequantize_fp8(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    sync()
+    got = f64(out)
+    ref = oracle.dequantize_blocks(codes, scales)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * rows * cols // 256 and np.array_equal(np.isnan(got), nan)
+    assert np.all(np.abs(got[~nan] - ref[~nan]) <= (2.0 ** -8 + 2.0 ** -23) * np.abs(ref[~nan]))
+    assert np.all((got[~nan] == 0) == (ref[~nan] == 0))
+
+
 def test_permute_fp8_bit_exact():
     N, H, E, k = 400, 2048, 16, 4
     say("permute fp8")

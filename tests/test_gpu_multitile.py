@@ -208,3 +208,68 @@ def test_multitile_gate_up_e4m3_every_row(case):
         worst = max(worst, err)
         assert err <= BAR, (e, err)
     say(f"  every row of {E} segments within {worst:.2e}")
+
+
+def test_multitile_fused_e4m3_every_row():
+    """The fp8 layer's fused path above decode sizes: each token quantized once (codes and
+    scales bit-exact against the oracle's codec), its bf16 values gathered by the routed rows
+    and the shared rows of one gate/up launch on e4m3 weights, then one down launch on e4m3
+    weights with the shared segment; several tiles per workgroup in both, NaN-filled outputs,
+    every row compared with the oracle's expert FFN on the dequantized operands."""
+    n_e = CASES["ragged"]
+    E = len(n_e)
+    idx = w.counted_route(n_e, K, seed=7)
+    N = idx.shape[0]
+    rows = N * K
+    segs = [c for c in n_e] + [N]
+    gu_tiles, dn_tiles = _tiles(segs, 128, 128, I, 0), _tiles(segs, 256, 128, H, 0)
+    say(f"multitile fused e4m3: N={N} rows={rows} E={E} H={H} I={I}; tiles {gu_tiles[0]} / {dn_tiles[0]}")
+    assert gu_tiles[0] >= 3 * WORKGROUPS and dn_tiles[0] >= 3 * WORKGROUPS
+
+    def seeded(shape, sub):
+        n = int(np.prod(shape))
+        c = (np.asarray(w.uniform_bits(n, w.stream_key(27, sub, E), "cpu")) >> 24).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0
+        bits = np.asarray(w.uniform_bits(n // 128, w.stream_key(27, sub, E + 1), "cpu"))
+        s = (2.0 ** -8 * (1.0 + (bits >> 8) / 2.0 ** 24)).astype(np.float32)
+        return c.reshape(shape), s.reshape(shape[:-1] + (shape[-1] // 128,))
+
+    w13q, w13s = seeded((E, 2 * I, H), w.T_W13)
+    w2q, w2s = seeded((E, H, I), w.T_W2)
+    s13q, s13s = seeded((2 * I, H), w.T_SW13)
+    s2q, s2s = seeded((H, I), w.T_SW2)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    x = w.normal((N, H), w.stream_key(27, w.T_X, E), DEV, torch.bfloat16)
+    xq, xs = moe.moe_quantize_fp8(x)
+    xd = moe.moe_dequantize_fp8(xq, xs)
+    ne_d, offs, sp, ss = moe.moe_dispatch_layout(idx.to(DEV), E)
+    nan = float("nan")
+    h = torch.full((rows + N, I), nan, dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gate_up_gathered_shared_e4m3(xd, ss, K, offs, dev(w13q), dev(w13s), dev(s13q), dev(s13s), h=h)
+    out = torch.full((rows + N, H), nan, dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_down_shared_e4m3(h, offs, dev(w2q), dev(w2s), dev(s2q), dev(s2s), rows, out=out)
+    sync()
+    for name, t in (("h", h), ("out", out)):
+        assert bool(torch.isfinite(t).all()), f"{name}: rows left unwritten"
+
+    rq, rs = oracle.quantize_blocks(x.float().cpu().numpy())
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
+    a = oracle.dequantize_blocks(rq, rs)
+    ref_ne, ref_off, _, ref_ss = oracle.dispatch_layout(idx.numpy(), E)
+    assert np.array_equal(ss.cpu().numpy(), ref_ss)
+    hh, oo = f64(h), f64(out)
+    worst = 0.0
+    for e in range(E + 1):
+        if e < E:
+            lo, hi = int(ref_off[e]), int(ref_off[e + 1])
+            if hi == lo:
+                continue
+            ae, w13e, w2e = a[ref_ss[lo:hi] // K], (w13q[e], w13s[e]), (w2q[e], w2s[e])
+        else:
+            lo, hi = rows, rows + N
+            ae, w13e, w2e = a, (s13q, s13s), (s2q, s2s)
+        rh, ro = oracle.expert_ffn(ae, oracle.dequantize_blocks(*w13e), oracle.dequantize_blocks(*w2e))
+        errs = [token_rel_err(hh[lo:hi], rh), token_rel_err(oo[lo:hi], ro)]
+        worst = max(worst, max(errs))
+        assert max(errs) <= BAR, (e, errs)
+    say(f"  every row of {E} segments + shared within {worst:.2e}")
