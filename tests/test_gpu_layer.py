@@ -146,6 +146,10 @@ def _check_permute(cfg, inp, layer, send_pos):
     x = inp["x"].cpu()
     if cfg.dtype == "fp8":
         q, s = _quantize_rows(x.to(torch.float32).numpy())
+        if layer.x_perm is None:   # (gathered fp8: each token's codes and scales, once)
+            assert np.array_equal(layer.x_q.cpu().numpy(), q)
+            assert np.array_equal(layer.x_q_scale.cpu().numpy(), s)
+            return None, (q, s)
         pq, ps = oracle.permute(q, send_pos, cfg.k), oracle.permute(s, send_pos, cfg.k)
         assert np.array_equal(layer.x_perm.cpu().numpy(), pq)
         assert np.array_equal(layer.x_perm_scale.cpu().numpy(), ps)
@@ -326,11 +330,11 @@ def test_layer_with_router_logits(name):
     assert err <= Y_BAR[cfg.dtype] and err <= Y_EXPECT[cfg.dtype]
 
 
-FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8"]
+FULL = ["mixtral_bf16", "dsv3_bf16", "dsv3_zipf_bf16", "decode_fp8", "dsv3_fp8"]
 # tokens of y computed by the oracle (decode: its fp8 weights are quantized by the oracle's
 # own codec, expert by expert, which takes seconds per expert on the host)
-SAMPLE_TOKENS = {"mixtral_bf16": 64, "dsv3_bf16": 64, "dsv3_zipf_bf16": 64, "decode_fp8": 4}
-SAMPLE_EXPERTS = {"mixtral_bf16": 8, "dsv3_bf16": 16, "dsv3_zipf_bf16": 16, "decode_fp8": 6}
+SAMPLE_TOKENS = {"mixtral_bf16": 64, "dsv3_bf16": 64, "dsv3_zipf_bf16": 64, "decode_fp8": 4, "dsv3_fp8": 4}
+SAMPLE_EXPERTS = {"mixtral_bf16": 8, "dsv3_bf16": 16, "dsv3_zipf_bf16": 16, "decode_fp8": 6, "dsv3_fp8": 8}
 
 
 def sampled_experts(n_e, n_blk, want):
@@ -384,7 +388,7 @@ def test_layer_full_size_sampled(name):
         return xs[toks]
 
     # every row of experts spread over the launch's tile order
-    if fp8:   # (the weight-streaming kernel: 16-row m-tiles; experts spread over the ids)
+    if fp8 and not layer.gather:   # (the weight-streaming kernel: 16-row m-tiles; experts spread over the ids)
         nz = np.nonzero(n_e)[0]
         experts = sorted({int(nz[np.argmax(n_e[nz])])} |
                          {int(e) for e in nz[np.linspace(0, len(nz) - 1, SAMPLE_EXPERTS[name] - 1).astype(int)]})
@@ -412,7 +416,11 @@ def test_layer_full_size_sampled(name):
         rows = np.array([r for _, r in by_expert[e]])
         _, eo_s[pos] = oracle.expert_ffn(a_rows(rows), ow.g13(e), ow.g2(e))
     sh = None
-    if cfg.shared:
+    if cfg.shared and fp8:   # (the tokens' fp8 values against the oracle's quantized shared weights)
+        sw = OracleWeights(inp["sw13"], inp["sw2"], True)
+        _, sh = oracle.expert_ffn(a_rows(sp[toks * cfg.k]), sw.g13(0), sw.g2(0))
+        assert token_rel_err(f64(layer.shared_out[torch.from_numpy(toks).to(DEV)]), sh) <= GEMM_BAR[cfg.dtype]
+    elif cfg.shared:
         _, sh = oracle.expert_ffn(xs[toks], f64(inp["sw13"][0]), f64(inp["sw2"][0]))
         assert token_rel_err(f64(layer.shared_out[torch.from_numpy(toks).to(DEV)]), sh) <= GEMM_BAR[cfg.dtype]
     ref = oracle.combine(eo_s, np.arange(S * cfg.k), rgate[toks], cfg.k, sh)
