@@ -562,9 +562,19 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
             constexpr int rd = (LAY || G == 1) ? i : ((i & 1) == 0 ? i / 2 : kReads);
             if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
           }
-          // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n, converted at 9 + 2 n
-          if constexpr (W8 && READ && ACT > 0 && i >= 9 && (i & 1) == 1)
-            nb[(i - 9) / 2] = e4m3x8_scaled_to_bf16x8(wraw[(i - 9) / 2], scn[(i - 9) / 2]);
+          // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n, converted over slots
+          // 8 + 2 n (codes 0-3) and 9 + 2 n (codes 4-7): 8 VALU instructions a slot, no more than
+          // the slot's MFMA takes, so the matrix pipe never waits for a conversion
+          if constexpr (W8 && READ && ACT > 0 && i >= 8 && (i - 8) / 2 < NB) {
+            constexpr int n = (i - 8) / 2;
+            if constexpr ((i & 1) == 0) {
+              nb[n].x = e4m3x2_scaled_to_bf16x2<false>(wraw[n].x, scn[n]);
+              nb[n].y = e4m3x2_scaled_to_bf16x2<true>(wraw[n].x, scn[n]);
+            } else {
+              nb[n].z = e4m3x2_scaled_to_bf16x2<false>(wraw[n].y, scn[n]);
+              nb[n].w = e4m3x2_scaled_to_bf16x2<true>(wraw[n].y, scn[n]);
+            }
+          }
           between(ic);
           __builtin_amdgcn_sched_barrier(0);
         });

@@ -95,14 +95,16 @@ __device__ __forceinline__ uint2 e4m3x4_scaled_to_bf16x4(uint32_t w, float s) {
 
 // 8 e4m3 codes (one 8-byte fragment) times one fp32 scale, as 8 bf16 values: each code is
 // decoded exactly by the hardware conversion, multiplied in fp32 and rounded to bf16
-__device__ __forceinline__ uint4 e4m3x8_scaled_to_bf16x8(uint2 raw, float s) {
+// the two e4m3 codes in the low (HI = false) or high half of w, times s, as packed bf16
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_scaled_to_bf16x2(uint32_t w, float s) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), false);
-  const f32x2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.x), true);
-  const f32x2_t p2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), false);
-  const f32x2_t p3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(raw.y), true);
-  return make_uint4(pack_bf16x2(p0.x * s, p0.y * s), pack_bf16x2(p1.x * s, p1.y * s),
-                    pack_bf16x2(p2.x * s, p2.y * s), pack_bf16x2(p3.x * s, p3.y * s));
+  const f32x2_t p = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+  return pack_bf16x2(p.x * s, p.y * s);
+}
+__device__ __forceinline__ uint4 e4m3x8_scaled_to_bf16x8(uint2 raw, float s) {
+  return make_uint4(e4m3x2_scaled_to_bf16x2<false>(raw.x, s), e4m3x2_scaled_to_bf16x2<true>(raw.x, s),
+                    e4m3x2_scaled_to_bf16x2<false>(raw.y, s), e4m3x2_scaled_to_bf16x2<true>(raw.y, s));
 }
 
 // ------------------------------------------------------------------------------------
