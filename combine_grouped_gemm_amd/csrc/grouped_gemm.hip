@@ -860,8 +860,8 @@ hipError_t launch_grouped_gemm(int ct, bool b8, int mode, const void* a, const f
                                 mode == MODE_GATE_UP || E > 1);
   const int tile_rows = stream ? kStreamTileRows : (wide || wide8 ? kWideTileRows : (dma ? kDM : GBM));
   // bf16 GEMMs on the 256 x 256 kernel: experts of 257..320 rows as one tile (down: 320 x 128,
-  // gate/up: 320 x 256)
-  const bool tall = wide;
+  // gate/up: 320 x 256); the down GEMM on e4m3 weights as well (320 x 128)
+  const bool tall = wide || (wide8 && mode == MODE_DOWN);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, rows, tile_rows, cap,
                      prefix, tile_expert, tile_counter, shared_rows, kWideTallRows,
                      tall ? tall_list : nullptr, kNumXcd + 1);

@@ -82,13 +82,19 @@ struct Geo {
   static constexpr int LdW = WPart / 4096;           // (8, W8 4; 4)
   static constexpr int StageLd = LdW + (W8 ? 1 : 0); // + the scale gather (W8)
   static constexpr int WBase = 2 * PartA;            // weight ring after the activation buffers
-  static constexpr int SBase = WBase + WS * WPart;   // (W8) scale ring: three slots of 1 KB
-  static constexpr int LdsTot = SBase + (W8 ? 3 * 1024 : 0);
-  static_assert(!W8 || G == 0, "e4m3 weights: 256 x 256 tiles");
+  static constexpr int SBase = WBase + WS * WPart;   // (W8) scale ring: a slot of 1 KB per weight slot
+  static constexpr int LdsTot = SBase + (W8 ? WS * 1024 : 0);
+  static_assert(!W8 || G != 2, "e4m3 weights: 256 x 256 and 320 x 128 tiles");
   static_assert(TM % 64 == 0 && TN % 64 == 0 && (TN / 2) % 32 == 0, "2 x 2 waves of 32-row blocks");
 };
 static_assert(Geo<1, false>::LdsTot <= Geo<0, false>::LdsTot && Geo<2, false>::LdsTot <= Geo<0, false>::LdsTot,
               "every shape fits the kernel's LDS");
+// the kernel's LDS array (W8: the 320 x 128 tiles' five slots of activation, weight and scale
+// stages take the most)
+template <bool W8>
+constexpr int kLdsBytes = W8 ? (Geo<1, true>::LdsTot > Geo<0, true>::LdsTot ? Geo<1, true>::LdsTot : Geo<0, true>::LdsTot)
+                             : Geo<0, false>::LdsTot;
+static_assert(kLdsBytes<true> <= Geo<0, false>::LdsTot, "the e4m3 shapes fit the LDS");
 
 __device__ __forceinline__ int slot_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -215,7 +221,7 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
   // hands it to the other waves at the tile boundary through the last word of the LDS array
   // (in the last weight ring slot, or the last scale slot with W8; no load writes that slot
   // between a boundary and the first stage).
-  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + Geo<0, W8>::LdsTot - 4);
+  int32_t* const tile_word = reinterpret_cast<int32_t*>(lds + kLdsBytes<W8> - 4);
   const bool dynamic = counter != nullptr;
   // The end of a launch: every XCD's range takes about the same time, but not exactly, and a
   // workgroup whose range runs out would wait for the slowest XCD.  The last kTailT tiles of
@@ -562,12 +568,14 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
             constexpr int rd = (LAY || G == 1) ? i : ((i & 1) == 0 ? i / 2 : kReads);
             if constexpr (READ && rd < kReads) read_frag(rd, aoff, boff, s, na, nb);
           }
-          // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n, converted over slots
-          // 8 + 2 n (codes 0-3) and 9 + 2 n (codes 4-7): 8 VALU instructions a slot, no more than
-          // the slot's MFMA takes, so the matrix pipe never waits for a conversion
-          if constexpr (W8 && READ && ACT > 0 && i >= 8 && (i - 8) / 2 < NB) {
-            constexpr int n = (i - 8) / 2;
-            if constexpr ((i & 1) == 0) {
+          // (W8) weight fragment n of the next k-step, read at slot 2 + 2 n (320 x 128 tiles: slot
+          // 1 + n), converted over slots c + 2 n (codes 0-3) and c + 2 n + 1 (codes 4-7), c = 8
+          // (5): 8 VALU instructions a slot, no more than the slot's MFMA takes, so the matrix
+          // pipe never waits for a conversion
+          constexpr int kCv = G == 0 ? 8 : 5;
+          if constexpr (W8 && READ && ACT > 0 && i >= kCv && (i - kCv) / 2 < NB) {
+            constexpr int n = (i - kCv) / 2;
+            if constexpr (((i - kCv) & 1) == 0) {
               nb[n].x = e4m3x2_scaled_to_bf16x2<false>(wraw[n].x, scn[n]);
               nb[n].y = e4m3x2_scaled_to_bf16x2<true>(wraw[n].x, scn[n]);
             } else {
@@ -906,8 +914,8 @@ __device__ __forceinline__ void run_tiles(const GemmArgs& p, uint8_t* lds) {
 // waiting for the others.
 template <int MODE, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Geo<0, W8>::LdsTot];
-  if constexpr (MODE == MODE_DOWN && !W8) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes<W8>];
+  if constexpr (MODE == MODE_DOWN) {
     if (p.tall_list != nullptr) run_tiles<MODE, W8, 1>(p, lds);
   }
   if constexpr (MODE == MODE_GATE_UP && !W8) {
@@ -921,7 +929,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(GemmArgs
 hipError_t launch_grouped_gemm_wide(int mode, const GemmArgs& p, hipStream_t s, bool w8) {
   const dim3 grid(256), block(kThreads);   // persistent: one workgroup per CU, a multiple of the 8 XCDs
   if (w8 && mode == MODE_ROUTER) return hipErrorNotSupported;
-  if ((w8 || mode == MODE_ROUTER) && p.tall_list != nullptr) return hipErrorNotSupported;
+  if (((w8 && mode != MODE_DOWN) || mode == MODE_ROUTER) && p.tall_list != nullptr) return hipErrorNotSupported;
   if (mode == MODE_GATE_UP && w8)
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<MODE_GATE_UP, true>), grid, block, 0, s, p);
   else if (mode == MODE_GATE_UP)
