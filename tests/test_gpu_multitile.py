@@ -273,3 +273,67 @@ def test_multitile_fused_e4m3_every_row():
         worst = max(worst, max(errs))
         assert max(errs) <= BAR, (e, errs)
     say(f"  every row of {E} segments + shared within {worst:.2e}")
+
+
+@pytest.mark.parametrize("n_e,N_only", [([0, 1, 3, 0, 37, 2], None), ([0, 0, 0], 5), ([1], None)],
+                         ids=["empty_and_one_row", "shared_rows_only", "one_token"])
+def test_fused_e4m3_edge_cases(n_e, N_only):
+    """The fused e4m3 launches on edge shapes: empty and one-row experts (a tile of one row in
+    a 256-row tile), a launch with no routed rows at all (only the shared segment), and a single
+    token; H = 256 and I = 128 (two and one 128-column blocks, one n-block); every row against
+    the oracle.  Bars: with K this short and uniform random codes (a few terms dominate a sum),
+    the operands' bf16 roundings (2^-8 each) do not average out, so the bound is taken without
+    averaging: pre-activations within 2^-7 relative, h (SwiGLU: about twice its inputs' relative
+    error, plus one bf16 rounding) within 2e-2, the output (h's error, one more operand rounding
+    and one output rounding) within 4e-2 of each token row's largest value."""
+    Hs, Is, k = 256, 128, 1
+    E = len(n_e)
+    if N_only is None:
+        idx = w.counted_route(n_e, k, seed=11)
+        N = idx.shape[0]
+    else:
+        N = N_only
+        idx = torch.zeros((N, 0), dtype=torch.int64)
+    rows = N * k if N_only is None else 0
+
+    def seeded(shape, sub):
+        n = int(np.prod(shape))
+        c = (np.asarray(w.uniform_bits(n, w.stream_key(31, sub, E), "cpu")) >> 24).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0
+        bits = np.asarray(w.uniform_bits(n // 128, w.stream_key(31, sub, E + 1), "cpu"))
+        s = (2.0 ** -6 * (1.0 + (bits >> 8) / 2.0 ** 24)).astype(np.float32)
+        return c.reshape(shape), s.reshape(shape[:-1] + (shape[-1] // 128,))
+
+    w13q, w13s = seeded((E, 2 * Is, Hs), w.T_W13)
+    w2q, w2s = seeded((E, Hs, Is), w.T_W2)
+    s13q, s13s = seeded((2 * Is, Hs), w.T_SW13)
+    s2q, s2s = seeded((Hs, Is), w.T_SW2)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    x = w.normal((N, Hs), w.stream_key(31, w.T_X, E), DEV, torch.bfloat16, std=1.0)
+    xq, xs = moe.moe_quantize_fp8(x)
+    xd = moe.moe_dequantize_fp8(xq, xs)
+    if rows:
+        _, offs, _, ss = moe.moe_dispatch_layout(idx.to(DEV), E)
+    else:
+        offs = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+        ss = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say(f"fused e4m3 edge: n_e={n_e} N={N} rows={rows}")
+    h = torch.full((rows + N, Is), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gate_up_gathered_shared_e4m3(xd, ss, k, offs, dev(w13q), dev(w13s), dev(s13q), dev(s13s),
+                                                rows=rows, h=h)
+    out = torch.full((rows + N, Hs), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_down_shared_e4m3(h, offs, dev(w2q), dev(w2s), dev(s2q), dev(s2s), rows, out=out)
+    sync()
+    assert bool(torch.isfinite(h).all()) and bool(torch.isfinite(out).all()), "rows left unwritten"
+    a = oracle.dequantize_blocks(*oracle.quantize_blocks(x.float().cpu().numpy()))
+    hh, oo = f64(h), f64(out)
+    segs = []
+    if rows:
+        _, ref_off, _, ref_ss = oracle.dispatch_layout(idx.numpy(), E)
+        segs = [(int(ref_off[e]), int(ref_off[e + 1]), a[ref_ss[ref_off[e]:ref_off[e + 1]] // k],
+                 (w13q[e], w13s[e]), (w2q[e], w2s[e])) for e in range(E) if ref_off[e + 1] > ref_off[e]]
+    segs.append((rows, rows + N, a, (s13q, s13s), (s2q, s2s)))
+    for lo, hi, ae, g13, g2 in segs:
+        rh, ro = oracle.expert_ffn(ae, oracle.dequantize_blocks(*g13), oracle.dequantize_blocks(*g2))
+        errs = token_rel_err(hh[lo:hi], rh), token_rel_err(oo[lo:hi], ro)
+        assert errs[0] <= 2e-2 and errs[1] <= 4e-2, (lo, hi, errs)
